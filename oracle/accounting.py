@@ -1,0 +1,38 @@
+"""Byte accounting of the decode step.
+
+"Persistent input/output feedback":
+
+* section "Persistent input/output feedback": ``retained_logical_bytes``
+  measures the visible tensor lengths, not the reserved capacity;
+* section "Opt-in storage auditing through runtime events": appending one
+  FLOAT token with head sizes Dk and Dv copies ``4 * (Dk + Dv)`` bytes, reuse
+  within capacity allocates nothing and copies no prefix, and the dense
+  fallback for B batches, H KV heads and an L-token prefix copies
+  ``4 * B * H * L * (Dk + Dv)`` prefix bytes plus ``4 * B * H * (Dk + Dv)``
+  append bytes per token.
+
+"Mutable execution cache", section "Memory planning": an in-place update
+counts as zero additional cache bytes; peak memory is workspace plus newly
+allocated pages.
+"""
+from __future__ import annotations
+
+
+def retained_logical_bytes(valid_len: int, batch: int, heads: int, head_sizes, elem_bytes: int) -> int:
+    """Visible bytes of the retained K/V tensors (sum over the tensors in ``head_sizes``)."""
+    return sum(int(valid_len) * batch * heads * d * elem_bytes for d in head_sizes)
+
+
+def append_bytes(new_tokens: int, batch: int, heads: int, head_sizes, elem_bytes: int) -> int:
+    """Bytes written by an in-place append of ``new_tokens`` tokens."""
+    return sum(int(new_tokens) * batch * heads * d * elem_bytes for d in head_sizes)
+
+
+def fallback_prefix_bytes(prefix_len: int, batch: int, heads: int, head_sizes, elem_bytes: int) -> int:
+    """Prefix bytes a concatenating (non in-place) update copies for one step."""
+    return sum(int(prefix_len) * batch * heads * d * elem_bytes for d in head_sizes)
+
+
+def in_place_extra_cache_bytes() -> int:
+    """Additional cache bytes of an in-place update (a second cache is never allocated)."""
+    return 0
