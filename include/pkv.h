@@ -1,0 +1,308 @@
+/*
+ * pkv.h -- C ABI of libpkv, a persistent-KV decode step for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library implements one per-token decode step over a KV cache that the
+ * caller owns and keeps alive between steps:
+ *
+ *   1. an in-place cache update whose result is the input storage
+ *      (contiguous or paged; optionally quantising new rows to INT4),
+ *   2. attention of the new queries over the valid cache prefix
+ *      (contiguous, paged bf16, paged INT4; a causal chunk variant),
+ *   3. greedy or seeded temperature sampling of final logits.
+ *
+ * Sources: the onnx-light documentation pages "Mutable execution cache"
+ * (in-place update contract, paged cache, runtime contract, memory planning),
+ * "Persistent input/output feedback" (attention, paged KV, generation and
+ * sampling semantics) and "Custom, quantized, and persistent values" (affine
+ * INT4 encoding).  Each entry point below names the section it follows.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Ownership.  The caller allocates every buffer, host or device, and keeps
+ *   it alive until the work enqueued on `stream` has finished.  The library
+ *   never allocates device memory and keeps no pointer after returning,
+ *   except inside pool and binding handles (host metadata only).
+ * - Tensors.  `pkv_tensor` describes a dense row-major array: `data` plus
+ *   dtype and shape, no strides.  Non-contiguous data is the caller's
+ *   problem: it is rejected by the binding layer, never copied.  Unless a
+ *   parameter says "host", `data` is device memory.
+ * - Streams.  `stream` is a `hipStream_t` (NULL = the null stream).  All
+ *   device work is enqueued on it; no call synchronises the device.
+ * - Errors.  Every argument is validated on the host before any HIP call.
+ *   On any error the function returns a non-zero `pkv_status`, enqueues no
+ *   work and leaves every buffer untouched; `pkv_last_error()` gives the
+ *   reason (thread-local).  `PKV_E_HIP` reports a failed launch.
+ * - Concurrency.  Calls that write the same cache storage must not overlap
+ *   on different streams; calls from several host threads are safe
+ *   otherwise (the binding registry is locked; a pool handle is not and
+ *   must be used by one thread at a time).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+#define PKV_MAX_DIMS 6
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_E_ARG = 1,       /* null pointer, bad size, bad enum, bad temperature   */
+    PKV_E_CAPACITY = 2,  /* position < 0 or position + update_length > capacity */
+    PKV_E_READONLY = 3,  /* cache storage is not inside a live writable binding */
+    PKV_E_ALIAS = 4,     /* input storage overlaps the storage being written    */
+    PKV_E_BUSY = 5,      /* writable binding overlaps an existing binding       */
+    PKV_E_PAGE = 6,      /* page not reserved / page id or sequence out of range */
+    PKV_E_NOMEM = 7,     /* page pool exhausted, or workspace too small         */
+    PKV_E_DTYPE = 8,     /* unsupported or mismatched element type             */
+    PKV_E_LAYOUT = 9,    /* rank or shape mismatch, unsupported head size       */
+    PKV_E_HIP = 10       /* a HIP runtime call failed                           */
+} pkv_status;
+
+typedef enum pkv_dtype {
+    PKV_F32 = 0,
+    PKV_BF16 = 1,
+    PKV_F16 = 2,
+    PKV_U8 = 3,
+    PKV_I32 = 4,
+    PKV_I64 = 5
+} pkv_dtype;
+
+typedef struct pkv_tensor {
+    void* data;                      /* first element                        */
+    int32_t dtype;                   /* pkv_dtype                            */
+    int32_t ndim;                    /* 1..PKV_MAX_DIMS                      */
+    int64_t shape[PKV_MAX_DIMS];     /* dense row-major                      */
+} pkv_tensor;
+
+typedef struct pkv_binding pkv_binding;
+typedef struct pkv_pool pkv_pool;
+
+/* ------------------------------------------------------------------------ */
+/* Library info                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Reason for the last non-OK status returned on this thread ("" if none).
+ * The string stays valid until the next library call on this thread. */
+const char* pkv_last_error(void);
+
+/* PKV_ABI_VERSION of the built library. */
+int32_t pkv_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Writable bindings                                                         */
+/* "Mutable execution cache", sections "Required alias" and "Runtime
+ * contract": the caller opts into mutation when binding the cache; one
+ * writable binding cannot be used concurrently by several users; immutable or
+ * shared storage is never accepted as a mutable cache.                      */
+/* ------------------------------------------------------------------------ */
+
+/* Register [base, base + bytes) as writable cache storage owned by the caller.
+ * Fails with PKV_E_BUSY if the range overlaps a live binding, PKV_E_ARG if
+ * base is NULL or bytes is 0.  The handle is freed by pkv_unbind. */
+pkv_status pkv_bind_writable(void* base, size_t bytes, pkv_binding** out);
+
+/* Release a binding (NULL is PKV_E_ARG).  Storage is not touched. */
+pkv_status pkv_unbind(pkv_binding* binding);
+
+/* ------------------------------------------------------------------------ */
+/* Contiguous in-place cache update                                          */
+/* "Mutable execution cache", sections "Value model", "ShapesContext",
+ * "Required alias" and "Model example": updated_cache = CacheUpdate(cache,
+ * values, position) writes only the range starting at position, the output
+ * is the input storage, position + update_length <= capacity is checked and
+ * overflow is an error (no growth, no copy fallback).                       */
+/* ------------------------------------------------------------------------ */
+
+/* cache  : [B, H, capacity, D], any dtype, inside a writable binding.
+ * values : [B, H, update_length, D], same dtype; must not overlap `cache`.
+ * position: host int32[B], the first row written for each batch row.
+ * Writes cache[b, h, position[b] + t, :] = values[b, h, t, :] for t <
+ * update_length and nothing else.  On success *out_cache = cache->data
+ * (pointer identity).  Errors: PKV_E_CAPACITY when any position[b] < 0 or
+ * position[b] + update_length > capacity; PKV_E_READONLY when the cache is
+ * not inside a live writable binding; PKV_E_ALIAS when values overlap it. */
+pkv_status pkv_cache_update(const pkv_tensor* cache, const pkv_tensor* values,
+                            const int32_t* position, int32_t update_length,
+                            void** out_cache, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Fixed page pool (host metadata)                                           */
+/* "Mutable execution cache", sections "Heterogeneous paged cache",
+ * "Runtime contract" and "Existing implementations / ONNX Runtime GenAI":
+ * a fixed pool of physical blocks and a per-request block table; only a
+ * missing page may be allocated, existing pages are updated in place, the
+ * pool never grows.                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Create the host bookkeeping of a pool of `num_blocks` physical pages of
+ * `block_size` tokens, for sequences 0..max_seqs-1 of up to
+ * max_blocks_per_seq pages each.  initial_free_order (host int32[num_blocks],
+ * a permutation of 0..num_blocks-1, or NULL for ascending order) is the order
+ * in which pages are handed out.  The physical K/V storage and the device
+ * page table int32[max_seqs, max_blocks_per_seq] are caller-owned. */
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, int32_t max_seqs,
+                           int32_t max_blocks_per_seq, const int32_t* initial_free_order,
+                           pkv_pool** out);
+
+pkv_status pkv_pool_destroy(pkv_pool* pool);
+
+/* For each i < n, make logical positions [0, new_len[i]) of sequence seqs[i]
+ * (host arrays) backed by pages, taking only pages the sequence does not
+ * hold yet.  All or nothing: PKV_E_NOMEM if the free pool is too small,
+ * PKV_E_PAGE if a sequence id is out of range, listed twice, or needs more
+ * than max_blocks_per_seq pages; nothing changes then.  When
+ * page_table_dev is not NULL the new entries are written to that device
+ * table on `stream` (ids travel as kernel arguments: nothing host-side must
+ * outlive the call).  Shrinking is a no-op. */
+pkv_status pkv_pool_reserve(pkv_pool* pool, int32_t n, const int32_t* seqs,
+                            const int32_t* new_len, int32_t* page_table_dev, void* stream);
+
+/* Return every page of `seq` to the back of the free list.  When
+ * page_table_dev is not NULL its row is reset to -1 on `stream`. */
+pkv_status pkv_pool_release(pkv_pool* pool, int32_t seq, int32_t* page_table_dev, void* stream);
+
+/* Host mirror queries.  held_pages / reserved_len may be NULL. */
+pkv_status pkv_pool_query(const pkv_pool* pool, int32_t seq, int32_t* held_pages,
+                          int32_t* reserved_len);
+pkv_status pkv_pool_free_count(const pkv_pool* pool, int32_t* free_pages);
+/* Copy the host page table int32[max_seqs, max_blocks_per_seq] (-1 = none). */
+pkv_status pkv_pool_table(const pkv_pool* pool, int32_t* out_host);
+
+/* ------------------------------------------------------------------------ */
+/* Paged in-place cache update                                               */
+/* "Mutable execution cache", sections "Heterogeneous paged cache" and
+ * "Runtime contract": updated_cache = PagedCacheUpdate(cache, page_id,
+ * values, position) aliases the cache, updates existing pages in place and
+ * allocates nothing (pages come from pkv_pool_reserve).                     */
+/* ------------------------------------------------------------------------ */
+
+/* pool_kv   : [num_blocks, H, block_size, D] physical pages (one pool per K
+ *             and per V), any dtype, inside a writable binding.
+ * page_table_dev: int32[max_seqs, max_blocks_per_seq] kept by
+ *             pkv_pool_reserve; row b of the batch is sequence b.
+ * values    : [B, H, update_length, D], same dtype, no overlap with pool_kv.
+ * position  : host int32[B]; logical position p of row b lives in slot
+ *             p % block_size of page page_table[b][p / block_size].
+ * Errors: PKV_E_PAGE when a written position lies on a page the pool has not
+ * reserved for that row (no implicit allocation); PKV_E_CAPACITY when
+ * position[b] < 0 or position[b] + update_length exceeds
+ * max_blocks_per_seq * block_size.  On success *out_pool = pool_kv->data. */
+pkv_status pkv_paged_cache_update(const pkv_pool* pool, const pkv_tensor* pool_kv,
+                                  const int32_t* page_table_dev, const pkv_tensor* values,
+                                  const int32_t* position, int32_t update_length,
+                                  void** out_pool, void* stream);
+
+/* INT4 variant: quantise the new rows on append.
+ * "Persistent input/output feedback", "Optional heterogeneous paged KV":
+ * affine append uses scalar parameters, rounds ties to even and saturates;
+ * "Custom, quantized, and persistent values", "Struct types and
+ * byte-encodable layouts": two 4-bit codes per byte, least-significant first.
+ * codes_pool : u8  [num_blocks, H, block_size, D/2]
+ * params_pool: f16 [num_blocks, H, block_size, D/32, 2] (scale, zero_point)
+ * values     : f32 or bf16 [B, H, update_length, D], D a multiple of 32.
+ * scale_f16, zero_point_f16: IEEE binary16 bit patterns; scale > 0 finite,
+ * zero_point an integer 0..15.  Code = clamp(rint(x / scale) + zp, 0, 15)
+ * with a correctly rounded float32 divide; every block's param slot of a
+ * written row receives (scale, zero_point).  Same checks as above. */
+pkv_status pkv_paged_cache_update_int4(const pkv_pool* pool, const pkv_tensor* codes_pool,
+                                       const pkv_tensor* params_pool,
+                                       const int32_t* page_table_dev, const pkv_tensor* values,
+                                       uint16_t scale_f16, uint16_t zero_point_f16,
+                                       const int32_t* position, int32_t update_length,
+                                       void** out_codes, void** out_params, void* stream);
+
+/* Materialise the logical [H, length, D] rows of sequence `seq` from the
+ * pages (a test/debug export; bit copy).  out must not overlap pool_kv. */
+pkv_status pkv_paged_gather(const pkv_tensor* pool_kv, const int32_t* page_table_dev,
+                            int32_t max_blocks_per_seq, int32_t seq, int32_t length,
+                            pkv_tensor* out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention                                                          */
+/* "Persistent input/output feedback", "Optional heterogeneous paged KV",
+ * sections "Versioned operator schema" and "Kernel implementation": query
+ * heads are a multiple of the K/V heads; only valid tokens are read; online
+ * softmax replaces K/V concatenation and any cache-length score matrix; the
+ * current K/V take part.  A single query sits at the last valid position, so
+ * the causal mask keeps the whole valid prefix.                             */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace (bytes) the decode entry points need for B rows, Hq query heads,
+ * head size D and contexts of up to max_len tokens with `num_splits` (0 =
+ * library choice, the same rule the call uses). */
+size_t pkv_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_len, int32_t num_splits);
+
+/* q       : [B, Hq, 1, D] or [B, Hq, D], f32 or bf16.
+ * k_cache, v_cache: [B, Hkv, capacity, D], same dtype as q, Hq % Hkv == 0.
+ * valid_len: host int32[B], 1 <= valid_len[b] <= capacity (includes the
+ *           token appended by this step).
+ * scale   : softmax scale; <= 0 means 1/sqrt(D).
+ * out     : same shape as q; dtype of q or f32.  Query head h reads K/V head
+ *           h / (Hq / Hkv).
+ * workspace: device scratch of pkv_decode_workspace_size(...) bytes, 256-byte
+ *           aligned; contents need no initialisation.
+ * num_splits: 0 lets the library split long contexts; otherwise each row's
+ *           context is cut into that many equal token ranges (at most). */
+pkv_status pkv_decode_attention(const pkv_tensor* q, const pkv_tensor* k_cache,
+                                const pkv_tensor* v_cache, const int32_t* valid_len,
+                                float scale, pkv_tensor* out, void* workspace,
+                                size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/* Paged bf16/f32: k_pool, v_pool [num_blocks, Hkv, block_size, D];
+ * page_table_dev int32[>= B, max_blocks_per_seq]; block_size must equal
+ * k_pool->shape[2].  When `pool` is not NULL every row must hold
+ * ceil(valid_len[b] / block_size) reserved pages (else PKV_E_PAGE). */
+pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                      const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                      int32_t max_blocks_per_seq, int32_t block_size,
+                                      const pkv_pool* pool, const int32_t* valid_len,
+                                      float scale, pkv_tensor* out, void* workspace,
+                                      size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/* Paged INT4: K/V rows decoded in registers as (code - zero_point) * scale
+ * per 32-element block ("Custom, quantized, and persistent values",
+ * "Quantization examples"); never materialised.  q and out are f32
+ * [B, Hq, (1,) D]; D == 128; codes/params pools as in
+ * pkv_paged_cache_update_int4. */
+pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor* k_codes,
+                                           const pkv_tensor* k_params, const pkv_tensor* v_codes,
+                                           const pkv_tensor* v_params,
+                                           const int32_t* page_table_dev,
+                                           int32_t max_blocks_per_seq, int32_t block_size,
+                                           const pkv_pool* pool, const int32_t* valid_len,
+                                           float scale, pkv_tensor* out, void* workspace,
+                                           size_t workspace_bytes, int32_t num_splits,
+                                           void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sampling                                                                  */
+/* "Persistent input/output feedback", section "Autoregressive generation":
+ * temperature 0 is greedy, a positive temperature samples
+ * softmax(logits / temperature), a seed makes the draw repeatable, the final
+ * position of [B, S, V] logits predicts the next token.                     */
+/* ------------------------------------------------------------------------ */
+
+size_t pkv_sample_workspace_size(int32_t B, int64_t V);
+
+/* logits : [B, V] or [B, S, V], f32, bf16 or f16, finite.
+ * temperature == 0: argmax, lowest index on ties.  temperature > 0: the
+ * Gumbel-max draw argmax_v (fl32(x_v * fl32(1/T)) - log(-log u_v)) with
+ * u_v = ((h >> 40) | 1) * 2^-24 and h output number b*V + v + 1 of
+ * SplitMix64 seeded with `seed`.  Negative or NaN temperature: PKV_E_ARG.
+ * out_ids: device int64[B]. */
+pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed,
+                      int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,392 @@
+"""Python binding of libpkv (include/pkv.h): argument marshalling only.
+
+Every function here has the name of its C entry point without the ``pkv_``
+prefix, converts torch tensors (or :class:`Raw` descriptors) to ``pkv_tensor``
+structs, passes the current HIP stream and raises :class:`PkvError` on a
+non-zero status.  Every step of the decode path runs in the HIP library; this
+module computes nothing and never copies or converts tensors (non-contiguous
+inputs are rejected).  If ``libpkv.so`` is missing, importing this package
+raises: there is no fallback.
+
+Build the library first:  ``python -m place_persistent_kv_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m place_persistent_kv_amd.build` "
+                      "(the decode path has no CPU fallback)")
+
+# torch supplies device memory and streams and ships its own HIP runtime.  It
+# is imported first so that libpkv's dependency on libamdhip64.so.7 resolves
+# to that same, already loaded runtime (same SONAME): two HIP runtimes in one
+# process would not share streams, synchronisation or allocations.
+import torch  # noqa: E402,F401
+
+_lib = C.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_loaded() -> list[str]:
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes_loaded()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process " + str(_hip_runtimes_loaded()) +
+                      "; import torch before anything that links /opt/rocm's libamdhip64")
+
+# ---------------------------------------------------------------------------
+# C types
+# ---------------------------------------------------------------------------
+MAX_DIMS = 6
+F32, BF16, F16, U8, I32, I64 = range(6)
+_ESIZE = {F32: 4, BF16: 2, F16: 2, U8: 1, I32: 4, I64: 8}
+
+OK, E_ARG, E_CAPACITY, E_READONLY, E_ALIAS, E_BUSY, E_PAGE, E_NOMEM, E_DTYPE, E_LAYOUT, E_HIP = range(11)
+STATUS_NAMES = {OK: "OK", E_ARG: "E_ARG", E_CAPACITY: "E_CAPACITY", E_READONLY: "E_READONLY",
+                E_ALIAS: "E_ALIAS", E_BUSY: "E_BUSY", E_PAGE: "E_PAGE", E_NOMEM: "E_NOMEM",
+                E_DTYPE: "E_DTYPE", E_LAYOUT: "E_LAYOUT", E_HIP: "E_HIP"}
+
+
+class PkvTensor(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("dtype", C.c_int32), ("ndim", C.c_int32),
+                ("shape", C.c_int64 * MAX_DIMS)]
+
+
+class PkvError(RuntimeError):
+    """A libpkv call returned a non-zero status; ``.status`` holds it."""
+
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_P = C.POINTER
+_T = _P(PkvTensor)
+_VP = C.c_void_p
+_I32P = _P(C.c_int32)
+_SIG = {
+    "pkv_last_error": (C.c_char_p, []),
+    "pkv_abi_version": (C.c_int32, []),
+    "pkv_bind_writable": (C.c_int, [_VP, C.c_size_t, _P(_VP)]),
+    "pkv_unbind": (C.c_int, [_VP]),
+    "pkv_cache_update": (C.c_int, [_T, _T, _I32P, C.c_int32, _P(_VP), _VP]),
+    "pkv_pool_create": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _I32P, _P(_VP)]),
+    "pkv_pool_destroy": (C.c_int, [_VP]),
+    "pkv_pool_reserve": (C.c_int, [_VP, C.c_int32, _I32P, _I32P, _VP, _VP]),
+    "pkv_pool_release": (C.c_int, [_VP, C.c_int32, _VP, _VP]),
+    "pkv_pool_query": (C.c_int, [_VP, C.c_int32, _I32P, _I32P]),
+    "pkv_pool_free_count": (C.c_int, [_VP, _I32P]),
+    "pkv_pool_table": (C.c_int, [_VP, _I32P]),
+    "pkv_paged_cache_update": (C.c_int, [_VP, _T, _VP, _T, _I32P, C.c_int32, _P(_VP), _VP]),
+    "pkv_paged_cache_update_int4": (C.c_int, [_VP, _T, _T, _VP, _T, C.c_uint16, C.c_uint16, _I32P,
+                                              C.c_int32, _P(_VP), _P(_VP), _VP]),
+    "pkv_paged_gather": (C.c_int, [_T, _VP, C.c_int32, C.c_int32, C.c_int32, _T, _VP]),
+    "pkv_decode_workspace_size": (C.c_size_t, [C.c_int32] * 6),
+    "pkv_decode_attention": (C.c_int, [_T, _T, _T, _I32P, C.c_float, _T, _VP, C.c_size_t, C.c_int32, _VP]),
+    "pkv_paged_decode_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
+                                             _T, _VP, C.c_size_t, C.c_int32, _VP]),
+    "pkv_paged_decode_attention_int4": (C.c_int, [_T, _T, _T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P,
+                                                  C.c_float, _T, _VP, C.c_size_t, C.c_int32, _VP]),
+    "pkv_sample_workspace_size": (C.c_size_t, [C.c_int32, C.c_int64]),
+    "pkv_sample": (C.c_int, [_T, C.c_float, C.c_uint64, _VP, _VP, C.c_size_t, _VP]),
+}
+
+for _name, (_res, _args) in _SIG.items():
+    _fn = getattr(_lib, _name, None)
+    if _fn is not None:
+        _fn.restype = _res
+        _fn.argtypes = _args
+
+
+def exported_symbols() -> list[str]:
+    """Names from the signature table that the loaded library exports."""
+    return [n for n in _SIG if getattr(_lib, n, None) is not None]
+
+
+def last_error() -> str:
+    return _lib.pkv_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(_lib.pkv_abi_version())
+
+
+def _check(status: int, func: str) -> None:
+    if status != OK:
+        raise PkvError(status, func, last_error())
+
+
+# ---------------------------------------------------------------------------
+# Descriptors
+# ---------------------------------------------------------------------------
+@dataclass
+class Raw:
+    """A tensor described by address, dtype code and shape (no torch needed)."""
+    ptr: int
+    dtype: int
+    shape: Sequence[int]
+
+    @property
+    def nbytes(self) -> int:
+        n = 1
+        for s in self.shape:
+            n *= int(s)
+        return n * _ESIZE[self.dtype]
+
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    table = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.uint8: U8,
+             torch.int32: I32, torch.int64: I64}
+    if t.dtype not in table:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return table[t.dtype]
+
+
+def desc(x) -> PkvTensor:
+    """``pkv_tensor`` for a torch tensor (contiguous, any device) or a :class:`Raw`."""
+    d = PkvTensor()
+    if isinstance(x, Raw):
+        d.data, d.dtype, shape = x.ptr, x.dtype, list(x.shape)
+    else:
+        if not x.is_contiguous():
+            raise ValueError("tensor must be contiguous (libpkv never copies inputs)")
+        d.data, d.dtype, shape = x.data_ptr(), _torch_dtype_code(x), list(x.shape)
+    if not 1 <= len(shape) <= MAX_DIMS:
+        raise ValueError(f"rank {len(shape)} not supported")
+    d.ndim = len(shape)
+    for i, s in enumerate(shape):
+        d.shape[i] = int(s)
+    return d
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, Raw):
+        return x.ptr
+    return x.data_ptr()
+
+
+def _nbytes(x) -> int:
+    if isinstance(x, Raw):
+        return x.nbytes
+    return x.numel() * x.element_size()
+
+
+def _i32_array(values) -> C.Array:
+    vals = [int(v) for v in values]
+    return (C.c_int32 * max(1, len(vals)))(*vals)
+
+
+def current_stream() -> Optional[int]:
+    """Handle of torch's current HIP stream (None when no GPU is visible)."""
+    import torch
+    if not torch.cuda.is_available():
+        return None
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Writable bindings
+# ---------------------------------------------------------------------------
+class Binding:
+    """Writable binding of a cache's storage ("Mutable execution cache", "Runtime contract")."""
+
+    def __init__(self, storage, nbytes: Optional[int] = None):
+        h = C.c_void_p()
+        n = _nbytes(storage) if nbytes is None else int(nbytes)
+        _check(_lib.pkv_bind_writable(_ptr(storage), n, C.byref(h)), "pkv_bind_writable")
+        self._h = h
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            _check(_lib.pkv_unbind(self._h), "pkv_unbind")
+        self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def bind_writable(storage, nbytes: Optional[int] = None) -> Binding:
+    return Binding(storage, nbytes)
+
+
+def unbind(binding: Binding) -> None:
+    binding.close()
+
+
+# ---------------------------------------------------------------------------
+# Cache updates
+# ---------------------------------------------------------------------------
+def cache_update(cache, values, position, update_length: int, stream=None) -> int:
+    """In-place ``CacheUpdate``; returns the address of the updated cache (== cache's)."""
+    out = C.c_void_p()
+    _check(_lib.pkv_cache_update(C.byref(desc(cache)), C.byref(desc(values)), _i32_array(position),
+                                 int(update_length), C.byref(out), _stream(stream)), "pkv_cache_update")
+    return out.value
+
+
+class Pool:
+    """Host bookkeeping of a fixed page pool (``pkv_pool_*``)."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int, max_blocks_per_seq: int,
+                 initial_free_order=None):
+        h = C.c_void_p()
+        order = None if initial_free_order is None else _i32_array(initial_free_order)
+        _check(_lib.pkv_pool_create(num_blocks, block_size, max_seqs, max_blocks_per_seq, order, C.byref(h)),
+               "pkv_pool_create")
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.max_seqs, self.max_blocks_per_seq = max_seqs, max_blocks_per_seq
+
+    @property
+    def handle(self):
+        return self._h
+
+    def reserve(self, seqs, new_lens, page_table=None, stream=None) -> None:
+        seqs, new_lens = list(seqs), list(new_lens)
+        _check(_lib.pkv_pool_reserve(self._h, len(seqs), _i32_array(seqs), _i32_array(new_lens),
+                                     _ptr(page_table), _stream(stream) if page_table is not None else None),
+               "pkv_pool_reserve")
+
+    def release(self, seq: int, page_table=None, stream=None) -> None:
+        _check(_lib.pkv_pool_release(self._h, seq, _ptr(page_table),
+                                     _stream(stream) if page_table is not None else None), "pkv_pool_release")
+
+    def query(self, seq: int) -> tuple[int, int]:
+        held, length = C.c_int32(), C.c_int32()
+        _check(_lib.pkv_pool_query(self._h, seq, C.byref(held), C.byref(length)), "pkv_pool_query")
+        return held.value, length.value
+
+    def free_count(self) -> int:
+        n = C.c_int32()
+        _check(_lib.pkv_pool_free_count(self._h, C.byref(n)), "pkv_pool_free_count")
+        return n.value
+
+    def table(self):
+        import numpy as np
+        out = np.empty((self.max_seqs, self.max_blocks_per_seq), dtype=np.int32)
+        _check(_lib.pkv_pool_table(self._h, out.ctypes.data_as(_I32P)), "pkv_pool_table")
+        return out
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            _check(_lib.pkv_pool_destroy(self._h), "pkv_pool_destroy")
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _pool_handle(pool):
+    return None if pool is None else pool.handle
+
+
+def paged_cache_update(pool: Pool, pool_kv, page_table, values, position, update_length: int,
+                       stream=None) -> int:
+    out = C.c_void_p()
+    _check(_lib.pkv_paged_cache_update(_pool_handle(pool), C.byref(desc(pool_kv)), _ptr(page_table),
+                                       C.byref(desc(values)), _i32_array(position), int(update_length),
+                                       C.byref(out), _stream(stream)), "pkv_paged_cache_update")
+    return out.value
+
+
+def paged_cache_update_int4(pool: Pool, codes_pool, params_pool, page_table, values, scale_f16_bits: int,
+                            zero_point_f16_bits: int, position, update_length: int, stream=None):
+    oc, op = C.c_void_p(), C.c_void_p()
+    _check(_lib.pkv_paged_cache_update_int4(_pool_handle(pool), C.byref(desc(codes_pool)),
+                                            C.byref(desc(params_pool)), _ptr(page_table), C.byref(desc(values)),
+                                            int(scale_f16_bits), int(zero_point_f16_bits), _i32_array(position),
+                                            int(update_length), C.byref(oc), C.byref(op), _stream(stream)),
+           "pkv_paged_cache_update_int4")
+    return oc.value, op.value
+
+
+def paged_gather(pool_kv, page_table, max_blocks_per_seq: int, seq: int, length: int, out, stream=None) -> None:
+    _check(_lib.pkv_paged_gather(C.byref(desc(pool_kv)), _ptr(page_table), max_blocks_per_seq, seq, length,
+                                 C.byref(desc(out)), _stream(stream)), "pkv_paged_gather")
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+def decode_workspace_size(B: int, Hq: int, Hkv: int, D: int, max_len: int, num_splits: int = 0) -> int:
+    return int(_lib.pkv_decode_workspace_size(B, Hq, Hkv, D, max_len, num_splits))
+
+
+def decode_attention(q, k_cache, v_cache, valid_len, out, workspace=None, scale: float = 0.0,
+                     num_splits: int = 0, stream=None) -> None:
+    ws = _ptr(workspace)
+    _check(_lib.pkv_decode_attention(C.byref(desc(q)), C.byref(desc(k_cache)), C.byref(desc(v_cache)),
+                                     _i32_array(valid_len), float(scale), C.byref(desc(out)), ws,
+                                     0 if workspace is None else _nbytes(workspace), int(num_splits),
+                                     _stream(stream)), "pkv_decode_attention")
+
+
+def paged_decode_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, block_size: int, valid_len,
+                           out, workspace=None, pool: Optional[Pool] = None, scale: float = 0.0,
+                           num_splits: int = 0, stream=None) -> None:
+    _check(_lib.pkv_paged_decode_attention(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+                                           _ptr(page_table), int(max_blocks_per_seq), int(block_size),
+                                           _pool_handle(pool), _i32_array(valid_len), float(scale),
+                                           C.byref(desc(out)), _ptr(workspace),
+                                           0 if workspace is None else _nbytes(workspace), int(num_splits),
+                                           _stream(stream)), "pkv_paged_decode_attention")
+
+
+def paged_decode_attention_int4(q, k_codes, k_params, v_codes, v_params, page_table, max_blocks_per_seq: int,
+                                block_size: int, valid_len, out, workspace=None, pool: Optional[Pool] = None,
+                                scale: float = 0.0, num_splits: int = 0, stream=None) -> None:
+    _check(_lib.pkv_paged_decode_attention_int4(
+        C.byref(desc(q)), C.byref(desc(k_codes)), C.byref(desc(k_params)), C.byref(desc(v_codes)),
+        C.byref(desc(v_params)), _ptr(page_table), int(max_blocks_per_seq), int(block_size), _pool_handle(pool),
+        _i32_array(valid_len), float(scale), C.byref(desc(out)), _ptr(workspace),
+        0 if workspace is None else _nbytes(workspace), int(num_splits), _stream(stream)),
+        "pkv_paged_decode_attention_int4")
+
+
+# ---------------------------------------------------------------------------
+# Sampling
+# ---------------------------------------------------------------------------
+def sample_workspace_size(B: int, V: int) -> int:
+    return int(_lib.pkv_sample_workspace_size(B, V))
+
+
+def sample(logits, temperature: float, seed: int, out_ids, workspace=None, stream=None) -> None:
+    _check(_lib.pkv_sample(C.byref(desc(logits)), float(temperature), C.c_uint64(seed & (2 ** 64 - 1)),
+                           _ptr(out_ids), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
+                           _stream(stream)), "pkv_sample")

@@ -1,0 +1,175 @@
+// In-place cache updates for gfx950: contiguous rows, paged rows, INT4
+// quantise-on-append, page-table writes and the paged gather export.
+//
+// "Mutable execution cache", sections "Value model" and "Model example":
+// CacheUpdate writes only the rows starting at `position`; the output is the
+// input storage.  Section "Heterogeneous paged cache": PagedCacheUpdate
+// writes existing pages in place.  All of these are byte copies (or a
+// per-element quantisation) with integer address arithmetic: they are
+// bound by HBM writes and use 16-byte vector accesses where the row size and
+// alignment allow.
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename V>
+__global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyRowsArgs a, int64_t total) {
+    // thread i copies vector c of row-slab (b, h): the n rows written for (b, h)
+    // are contiguous both in `values` and at `position` in the cache.
+    const int64_t vec_per_bh = a.n * a.row_bytes / int64_t(sizeof(V));
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kThreads) {
+        const int64_t bh = i / vec_per_bh;
+        const int64_t c = i - bh * vec_per_bh;
+        const int32_t b = static_cast<int32_t>(bh / a.H);
+        const int32_t h = static_cast<int32_t>(bh - int64_t(b) * a.H);
+        const V* src = reinterpret_cast<const V*>(a.src + bh * a.n * a.row_bytes);
+        V* dst = reinterpret_cast<V*>(a.dst + ((int64_t(b) * a.H + h) * a.cap + a.pos[b]) * a.row_bytes);
+        dst[c] = src[c];
+    }
+}
+
+template <typename V>
+__global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedCopyArgs a, int64_t total) {
+    const int64_t vec_per_row = a.row_bytes / int64_t(sizeof(V));
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kThreads) {
+        const int64_t r = i / vec_per_row;          // source row index (b, h, t)
+        const int64_t c = i - r * vec_per_row;
+        const int32_t t = static_cast<int32_t>(r % a.n);
+        const int64_t bh = r / a.n;
+        const int32_t h = static_cast<int32_t>(bh % a.H);
+        const int32_t b = static_cast<int32_t>(bh / a.H);
+        const int32_t p = a.pos[b] + t;
+        const int32_t page = a.page_table[int64_t(a.row0 + b) * a.maxb + p / a.bs];
+        const int32_t slot = p % a.bs;
+        const V* src = reinterpret_cast<const V*>(a.src + r * a.row_bytes);
+        V* dst = reinterpret_cast<V*>(a.pool + ((int64_t(page) * a.H + h) * a.bs + slot) * a.row_bytes);
+        dst[c] = src[c];
+    }
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// One thread per 32-element block of one written row: 16 bytes of codes
+// (element 2k in the low nibble of byte k) and one (scale, zero point) slot.
+__global__ __launch_bounds__(kThreads) void paged_int4_kernel(PagedInt4Args a, int64_t total) {
+    const int nblk = a.D / 32;
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kThreads) {
+        const int32_t blk = static_cast<int32_t>(i % nblk);
+        const int64_t r = i / nblk;                 // source row (b, h, t)
+        const int32_t t = static_cast<int32_t>(r % a.n);
+        const int64_t bh = r / a.n;
+        const int32_t h = static_cast<int32_t>(bh % a.H);
+        const int32_t b = static_cast<int32_t>(bh / a.H);
+        const int32_t p = a.pos[b] + t;
+        const int32_t page = a.page_table[int64_t(a.row0 + b) * a.maxb + p / a.bs];
+        const int64_t row = (int64_t(page) * a.H + h) * a.bs + p % a.bs;
+
+        uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const int64_t src_idx = r * a.D + blk * 32 + e;
+            const float x = a.src_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.src)[src_idx])
+                                       : static_cast<const float*>(a.src)[src_idx];
+            // correctly rounded float32 divide, round half to even, saturate
+            float c = rintf(x / a.scale) + a.zero_point;
+            c = fminf(fmaxf(c, 0.0f), 15.0f);
+            packed[e / 8] |= uint32_t(c) << (4 * (e % 8));
+        }
+        uint4 v;
+        v.x = packed[0];
+        v.y = packed[1];
+        v.z = packed[2];
+        v.w = packed[3];
+        *reinterpret_cast<uint4*>(a.codes + row * (a.D / 2) + blk * 16) = v;
+        *reinterpret_cast<uint32_t*>(a.params + (row * nblk + blk) * 2) =
+            uint32_t(a.scale_bits) | (uint32_t(a.zp_bits) << 16);
+    }
+}
+
+__global__ void table_write_kernel(TableWriteArgs a) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < a.count) a.table[a.index[i]] = a.value[i];
+}
+
+template <typename V>
+__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a, int64_t total) {
+    const int64_t vec_per_row = a.row_bytes / int64_t(sizeof(V));
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kThreads) {
+        const int64_t r = i / vec_per_row;          // output row (h, p)
+        const int64_t c = i - r * vec_per_row;
+        const int32_t p = static_cast<int32_t>(r % a.length);
+        const int32_t h = static_cast<int32_t>(r / a.length);
+        const int32_t page = a.table_row[p / a.bs];
+        const V* src = reinterpret_cast<const V*>(a.pool + ((int64_t(page) * a.H + h) * a.bs + p % a.bs) * a.row_bytes);
+        reinterpret_cast<V*>(a.out + r * a.row_bytes)[c] = src[c];
+    }
+}
+
+int vec_bytes(int64_t row_bytes, const void* p0, const void* p1) {
+    const uintptr_t al = reinterpret_cast<uintptr_t>(p0) | reinterpret_cast<uintptr_t>(p1);
+    if (row_bytes % 16 == 0 && al % 16 == 0) return 16;
+    if (row_bytes % 4 == 0 && al % 4 == 0) return 4;
+    return 1;
+}
+
+dim3 grid_for(int64_t total) {
+    int64_t blocks = (total + kThreads - 1) / kThreads;
+    if (blocks > 65536) blocks = 65536;  // grid-stride loops cover the rest
+    if (blocks < 1) blocks = 1;
+    return dim3(static_cast<unsigned>(blocks));
+}
+
+}  // namespace
+
+hipError_t launch_copy_rows(const CopyRowsArgs& a, hipStream_t s) {
+    const int vb = vec_bytes(a.row_bytes, a.src, a.dst);
+    const int64_t total = int64_t(a.rows) * a.H * a.n * a.row_bytes / vb;
+    if (total == 0) return hipSuccess;
+    if (vb == 16) hipLaunchKernelGGL(copy_rows_kernel<uint4>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    else if (vb == 4) hipLaunchKernelGGL(copy_rows_kernel<uint32_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    else hipLaunchKernelGGL(copy_rows_kernel<uint8_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_paged_copy(const PagedCopyArgs& a, hipStream_t s) {
+    const int vb = vec_bytes(a.row_bytes, a.src, a.pool);
+    const int64_t total = int64_t(a.rows) * a.H * a.n * a.row_bytes / vb;
+    if (total == 0) return hipSuccess;
+    if (vb == 16) hipLaunchKernelGGL(paged_copy_kernel<uint4>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    else if (vb == 4) hipLaunchKernelGGL(paged_copy_kernel<uint32_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    else hipLaunchKernelGGL(paged_copy_kernel<uint8_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_paged_int4_append(const PagedInt4Args& a, hipStream_t s) {
+    const int64_t total = int64_t(a.rows) * a.H * a.n * (a.D / 32);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(paged_int4_kernel, grid_for(total), dim3(kThreads), 0, s, a, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_table_write(const TableWriteArgs& a, hipStream_t s) {
+    if (a.count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(table_write_kernel, dim3((a.count + 255) / 256), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+    const int vb = vec_bytes(a.row_bytes, a.pool, a.out);
+    const int64_t total = int64_t(a.H) * a.length * a.row_bytes / vb;
+    if (total == 0) return hipSuccess;
+    if (vb == 16) hipLaunchKernelGGL(gather_kernel<uint4>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    else if (vb == 4) hipLaunchKernelGGL(gather_kernel<uint32_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    else hipLaunchKernelGGL(gather_kernel<uint8_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

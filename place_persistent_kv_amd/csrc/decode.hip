@@ -1,0 +1,394 @@
+// Decode attention for gfx950: one new query per (row, head) over the valid
+// cache prefix, contiguous or paged, with a split over long contexts and a
+// log-sum-exp merge.
+//
+// What is computed -- "Persistent input/output feedback", "Optional
+// heterogeneous paged KV", sections "Versioned operator schema" and "Kernel
+// implementation": grouped-query attention (query head h reads K/V head
+// h / G), only valid tokens are read, online softmax instead of K/V
+// concatenation or a cache-length score matrix.
+//
+// The single-token step is a bandwidth-bound GEMV (about 4 flops per K/V
+// byte at G = 4), so it runs on the vector ALUs, not MFMA:
+//
+//  * fast kernel (bf16, D = 128, G <= 8): a workgroup of 4 waves owns one
+//    (row, kv head, split); each wave streams its quarter of the split 16
+//    tokens at a time.  Eight lanes cover one 256-byte K or V row with two
+//    16-byte loads each (lane j reads dims 8j..8j+7 and 64+8j..64+8j+7), so
+//    every load instruction moves eight full 128-byte lines.  The G query
+//    heads of the group reuse each K/V row from registers.  Q.K uses
+//    v_dot2_f32_bf16 on packed bf16 pairs; the 8-lane sum uses three DPP
+//    adds (row_half_mirror, quad_perm [1,0,3,2], quad_perm [2,3,0,1]).
+//    Each 8-lane group keeps its own running max / sum / output; the max is
+//    refreshed lazily (only when a score exceeds it by 2^8), so the output
+//    rescale is off the common path.  Groups and waves are merged at the end
+//    through cross-lane shuffles and LDS.
+//  * generic kernel (any D <= 256, f32/bf16/f16, any block size): one wave
+//    per (row, query head, split) with scores staged in LDS.
+//  * merge kernel: o = sum_i o_i 2^(m_i - m*) / sum_i l_i 2^(m_i - m*).
+
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kD = 128;
+constexpr float kLazy = 8.0f;  // rescale only when a score exceeds the running max by 2^8
+
+template <int G, bool PAGED>
+__global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
+    __shared__ float s_o[kWaves][G][kD];
+    __shared__ float s_ml[kWaves][G][2];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 3;  // token within an 8-token slab
+    const int j = lane & 7;     // 16-byte chunk within each half row
+
+    const int work = blockIdx.x;
+    const int kvh = work % a.Hkv;
+    const int r = work / a.Hkv;
+    const int b = find_row(a.split_begin, a.rows, r);
+    const int split = r - a.split_begin[b];
+    const int nsplit = a.split_begin[b + 1] - a.split_begin[b];
+    const int L = a.len[b];
+    const int t0 = split * a.tps;
+    const int t1 = min(L, t0 + a.tps);
+    const int quarter = a.tps / kWaves;
+    const int wbeg = t0 + wave * quarter;
+    const int wend = min(t1, wbeg + quarter);
+
+    const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
+    const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+    const int32_t* __restrict__ pt = PAGED ? a.page_table + int64_t(b) * a.maxb : nullptr;
+
+    // queries of the group, as packed bf16 pairs
+    uint4 qa[G], qb[G];
+    {
+        const uint16_t* Q = static_cast<const uint16_t*>(a.q) + (int64_t(b) * a.Hq + kvh * G) * kD;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            qa[g] = ld16(Q + g * kD + j * 8);
+            qb[g] = ld16(Q + g * kD + 64 + j * 8);
+        }
+    }
+
+    float m[G], l[G], o[G][16];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -FLT_MAX;
+        l[g] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) o[g][d] = 0.0f;
+    }
+
+    // Element offset of this lane's 8 dims (chunk A) of token t, clamped into
+    // [t_lo, t1) so that every load is a valid row of the same page.
+    auto row_offset = [&](int ts, int t) -> int64_t {
+        const int tc = min(t, t1 - 1);
+        if constexpr (PAGED) {
+            const int page = pt[ts / a.bs];  // wave-uniform
+            return ((int64_t(page) * a.Hkv + kvh) * a.bs + (tc % a.bs)) * kD + j * 8;
+        } else {
+            return ((int64_t(b) * a.Hkv + kvh) * a.cap + tc) * kD + j * 8;
+        }
+    };
+
+    struct Buf {
+        uint4 ka0, kb0, ka1, kb1, va0, vb0, va1, vb1;
+    };
+    auto load = [&](Buf& u, int ts) {
+        const int64_t o0 = row_offset(ts, ts + grp);
+        const int64_t o1 = row_offset(ts, ts + 8 + grp);
+        u.ka0 = ld16(K + o0);
+        u.kb0 = ld16(K + o0 + 64);
+        u.ka1 = ld16(K + o1);
+        u.kb1 = ld16(K + o1 + 64);
+        u.va0 = ld16(V + o0);
+        u.vb0 = ld16(V + o0 + 64);
+        u.va1 = ld16(V + o1);
+        u.vb1 = ld16(V + o1 + 64);
+    };
+
+    auto compute = [&](const Buf& u, int ts) {
+        const bool live0 = ts + grp < t1;
+        const bool live1 = ts + 8 + grp < t1;
+        float s0[G], s1[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float x = 0.0f, y = 0.0f;
+            x = dot2_bf16(qa[g].x, u.ka0.x, x);
+            y = dot2_bf16(qa[g].x, u.ka1.x, y);
+            x = dot2_bf16(qa[g].y, u.ka0.y, x);
+            y = dot2_bf16(qa[g].y, u.ka1.y, y);
+            x = dot2_bf16(qa[g].z, u.ka0.z, x);
+            y = dot2_bf16(qa[g].z, u.ka1.z, y);
+            x = dot2_bf16(qa[g].w, u.ka0.w, x);
+            y = dot2_bf16(qa[g].w, u.ka1.w, y);
+            x = dot2_bf16(qb[g].x, u.kb0.x, x);
+            y = dot2_bf16(qb[g].x, u.kb1.x, y);
+            x = dot2_bf16(qb[g].y, u.kb0.y, x);
+            y = dot2_bf16(qb[g].y, u.kb1.y, y);
+            x = dot2_bf16(qb[g].z, u.kb0.z, x);
+            y = dot2_bf16(qb[g].z, u.kb1.z, y);
+            x = dot2_bf16(qb[g].w, u.kb0.w, x);
+            y = dot2_bf16(qb[g].w, u.kb1.w, y);
+            s0[g] = group8_sum(x) * a.scale_log2;
+            s1[g] = group8_sum(y) * a.scale_log2;
+            s0[g] = live0 ? s0[g] : -INFINITY;
+            s1[g] = live1 ? s1[g] : -INFINITY;
+        }
+        float v0[16], v1[16];
+        {
+            const uint32_t w0[8] = {u.va0.x, u.va0.y, u.va0.z, u.va0.w, u.vb0.x, u.vb0.y, u.vb0.z, u.vb0.w};
+            const uint32_t w1[8] = {u.va1.x, u.va1.y, u.va1.z, u.va1.w, u.vb1.x, u.vb1.y, u.vb1.z, u.vb1.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                v0[2 * k] = bf_lo(w0[k]);
+                v0[2 * k + 1] = bf_hi(w0[k]);
+                v1[2 * k] = bf_lo(w1[k]);
+                v1[2 * k + 1] = bf_hi(w1[k]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mx = fmaxf(s0[g], s1[g]);
+            if (mx > m[g] + kLazy) {
+                const float c = exp2_fast(m[g] - mx);
+                l[g] *= c;
+#pragma unroll
+                for (int d = 0; d < 16; ++d) o[g][d] *= c;
+                m[g] = mx;
+            }
+            const float p0 = exp2_fast(s0[g] - m[g]);
+            const float p1 = exp2_fast(s1[g] - m[g]);
+            l[g] += p0 + p1;
+#pragma unroll
+            for (int d = 0; d < 16; ++d) o[g][d] = fmaf(p1, v1[d], fmaf(p0, v0[d], o[g][d]));
+        }
+    };
+
+    if (wbeg < wend) {
+        Buf A, Bf;
+        load(A, wbeg);
+        for (int ts = wbeg;; ts += 2 * kSlabTokens) {
+            const bool has1 = ts + kSlabTokens < wend;
+            if (has1) load(Bf, ts + kSlabTokens);
+            compute(A, ts);
+            if (!has1) break;
+            const bool has2 = ts + 2 * kSlabTokens < wend;
+            if (has2) load(A, ts + 2 * kSlabTokens);
+            compute(Bf, ts + kSlabTokens);
+            if (!has2) break;
+        }
+    }
+
+    // merge the eight token groups of the wave (lanes with the same j)
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mo = __shfl_xor(m[g], off);
+            const float lo = __shfl_xor(l[g], off);
+            const float mn = fmaxf(m[g], mo);
+            const float cs = exp2_fast(m[g] - mn);
+            const float co = exp2_fast(mo - mn);
+            l[g] = l[g] * cs + lo * co;
+#pragma unroll
+            for (int d = 0; d < 16; ++d) o[g][d] = o[g][d] * cs + __shfl_xor(o[g][d], off) * co;
+            m[g] = mn;
+        }
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                s_o[wave][g][j * 8 + d] = o[g][d];
+                s_o[wave][g][64 + j * 8 + d] = o[g][8 + d];
+            }
+            if (j == 0) {
+                s_ml[wave][g][0] = m[g];
+                s_ml[wave][g][1] = l[g];
+            }
+        }
+    }
+    __syncthreads();
+
+    // merge the four waves; thread t handles (g, d) pairs t, t + 256, ...
+    for (int e = threadIdx.x; e < G * kD; e += 256) {
+        const int g = e / kD;
+        const int d = e % kD;
+        float mn = -FLT_MAX;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mn = fmaxf(mn, s_ml[w][g][0]);
+        float ls = 0.0f, os = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float c = exp2_fast(s_ml[w][g][0] - mn);
+            ls += s_ml[w][g][1] * c;
+            os += s_o[w][g][d] * c;
+        }
+        const int h = kvh * G + g;
+        const int64_t bh = int64_t(b) * a.Hq + h;
+        if (nsplit == 1) {
+            const float y = os / ls;
+            if (a.out_f32) static_cast<float*>(a.out)[bh * kD + d] = y;
+            else static_cast<uint16_t*>(a.out)[bh * kD + d] = f32_to_bf16_rne(y);
+        } else {
+            const int64_t slot = bh * a.S_max + split;
+            a.ws_o[slot * kD + d] = os;
+            if (d == 0) {
+                a.ws_ml[slot * 2 + 0] = mn;
+                a.ws_ml[slot * 2 + 1] = ls;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel: one wave per (row, query head, split), any D <= 256.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+template <>
+__device__ __forceinline__ float to_f32<_Float16>(_Float16 x) { return float(x); }
+
+template <typename T>
+__global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
+    __shared__ float s_p[kGenericMaxTps];
+    const int lane = threadIdx.x;
+    const int work = blockIdx.x;
+    const int h = work % a.Hq;
+    const int r = work / a.Hq;
+    const int b = find_row(a.split_begin, a.rows, r);
+    const int split = r - a.split_begin[b];
+    const int L = a.len[b];
+    const int t0 = split * a.tps;
+    const int t1 = min(L, t0 + a.tps);
+    const int G = a.Hq / a.Hkv;
+    const int kvh = h / G;
+    const int D = a.D;
+    const T* Q = static_cast<const T*>(a.q) + (int64_t(b) * a.Hq + h) * D;
+    const T* K = static_cast<const T*>(a.k);
+    const T* V = static_cast<const T*>(a.v);
+
+    auto row = [&](int t) -> int64_t {  // element offset of token t's row
+        if (a.page_table) {
+            const int page = a.page_table[int64_t(b) * a.maxb + t / a.bs];
+            return ((int64_t(page) * a.Hkv + kvh) * a.bs + t % a.bs) * D;
+        }
+        return ((int64_t(b) * a.Hkv + kvh) * a.cap + t) * D;
+    };
+
+    // pass 1: scores (lanes over tokens)
+    float mx = -FLT_MAX;
+    for (int t = t0 + lane; t < t1; t += 64) {
+        const int64_t off = row(t);
+        float s = 0.0f;
+        for (int d = 0; d < D; ++d) s = fmaf(to_f32(Q[d]), to_f32(K[off + d]), s);
+        s *= a.scale_log2;
+        s_p[t - t0] = s;
+        mx = fmaxf(mx, s);
+    }
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float ls = 0.0f;
+    for (int t = t0 + lane; t < t1; t += 64) {
+        const float p = exp2_fast(s_p[t - t0] - mx);
+        s_p[t - t0] = p;
+        ls += p;
+    }
+    for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
+    __syncthreads();
+
+    // pass 2: weighted values (lanes over dims)
+    const int64_t slot = (int64_t(b) * a.Hq + h) * a.S_max + split;
+    for (int d = lane; d < D; d += 64) {
+        float acc = 0.0f;
+        for (int t = t0; t < t1; ++t) acc = fmaf(s_p[t - t0], to_f32(V[row(t) + d]), acc);
+        a.ws_o[slot * D + d] = acc;
+    }
+    if (lane == 0) {
+        a.ws_ml[slot * 2 + 0] = mx;
+        a.ws_ml[slot * 2 + 1] = ls;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: one workgroup per (row, query head).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+    const int bh = blockIdx.x;
+    const int b = bh / a.Hq;
+    const int n = a.nsplit[b];
+    if (n < a.min_splits) return;
+    const int64_t gbh = int64_t(b) * a.Hq + (bh % a.Hq);
+    const float* ml = a.ws_ml + gbh * a.S_max * 2;
+    float mn = -FLT_MAX;
+    for (int s = 0; s < n; ++s) mn = fmaxf(mn, ml[2 * s]);
+    float ls = 0.0f;
+    for (int s = 0; s < n; ++s) ls += ml[2 * s + 1] * exp2_fast(ml[2 * s] - mn);
+    const float inv = 1.0f / ls;
+    for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
+        float os = 0.0f;
+        for (int s = 0; s < n; ++s) os += a.ws_o[(gbh * a.S_max + s) * a.D + d] * exp2_fast(ml[2 * s] - mn);
+        const float y = os * inv;
+        const int64_t idx = gbh * a.D + d;
+        if (a.out_kind == kKvF32) static_cast<float*>(a.out)[idx] = y;
+        else if (a.out_kind == kKvBF16) static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16_rne(y);
+        else static_cast<_Float16*>(a.out)[idx] = static_cast<_Float16>(y);
+    }
+}
+
+}  // namespace
+
+bool fast_decode_supported(int kv_kind, int D, int G, bool paged, int bs) {
+    if (kv_kind != kKvBF16 || D != kD) return false;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+    if (paged && (bs <= 0 || bs % kSlabTokens != 0)) return false;
+    return true;
+}
+
+hipError_t launch_decode_fast(const DecodeArgs& a, int G, int total_work, hipStream_t s) {
+    if (total_work <= 0) return hipSuccess;
+    const dim3 grid(total_work), block(256);
+    const bool paged = a.page_table != nullptr;
+#define PKV_FAST(GG)                                                                              \
+    if (G == GG) {                                                                                \
+        if (paged) hipLaunchKernelGGL((decode_fast_kernel<GG, true>), grid, block, 0, s, a);     \
+        else hipLaunchKernelGGL((decode_fast_kernel<GG, false>), grid, block, 0, s, a);          \
+        return hipGetLastError();                                                                 \
+    }
+    PKV_FAST(1)
+    PKV_FAST(2)
+    PKV_FAST(4)
+    PKV_FAST(8)
+#undef PKV_FAST
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_generic(const DecodeArgs& a, int total_work, hipStream_t s) {
+    if (total_work <= 0) return hipSuccess;
+    const dim3 grid(total_work), block(64);
+    switch (a.kv_kind) {
+        case kKvF32: hipLaunchKernelGGL(decode_generic_kernel<float>, grid, block, 0, s, a); break;
+        case kKvBF16: hipLaunchKernelGGL(decode_generic_kernel<uint16_t>, grid, block, 0, s, a); break;
+        case kKvF16: hipLaunchKernelGGL(decode_generic_kernel<_Float16>, grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+    const int blocks = a.rows * a.Hq;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(a.D <= 128 ? 128 : 256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

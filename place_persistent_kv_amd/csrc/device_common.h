@@ -1,0 +1,56 @@
+// Device helpers shared by the decode kernels (gfx950, wave64).
+#pragma once
+
+#include "pkv_internal.h"
+
+#include <float.h>
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 8 lanes of a half-row; every lane of the group gets the total.
+__device__ __forceinline__ float group8_sum(float x) {
+    x += dpp<0x141>(x);  // row_half_mirror: lane i <- lane 7 - i
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    return x;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// largest b with split_begin[b] <= r (split_begin is non-decreasing, split_begin[rows] > r)
+__device__ __forceinline__ int find_row(const int32_t* split_begin, int rows, int r) {
+    int lo = 0, hi = rows;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (split_begin[mid] <= r) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace
+}  // namespace pkv

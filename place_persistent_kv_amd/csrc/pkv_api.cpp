@@ -1,0 +1,986 @@
+// Host layer of libpkv: the extern "C" entry points of include/pkv.h.
+//
+// Every entry point validates its arguments completely before the first HIP
+// call, so an error never enqueues work or touches a buffer ("Mutable
+// execution cache", "Runtime contract"; "Persistent input/output feedback",
+// "Lifecycle and validation": a failed call publishes no partial update).
+// The library never allocates device memory: caches, pools, page tables,
+// outputs and workspaces all belong to the caller ("Mutable execution
+// cache", "Memory planning": an in-place update costs zero extra cache bytes).
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <mutex>
+#include <string>
+#include <vector>
+
+using namespace pkv;
+
+// ---------------------------------------------------------------------------
+// Errors
+// ---------------------------------------------------------------------------
+namespace {
+
+thread_local std::string g_err;
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+pkv_status ok() {
+    g_err.clear();
+    return PKV_OK;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+    return fail(PKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define PKV_TRY(expr)                        \
+    do {                                     \
+        pkv_status _s = (expr);              \
+        if (_s != PKV_OK) return _s;         \
+    } while (0)
+
+#define PKV_HIP(expr, what)                  \
+    do {                                     \
+        hipError_t _e = (expr);              \
+        if (_e != hipSuccess) return hip_fail(_e, what); \
+    } while (0)
+
+// ---------------------------------------------------------------------------
+// Tensor descriptors
+// ---------------------------------------------------------------------------
+int64_t dtype_size(int32_t dt) {
+    switch (dt) {
+        case PKV_F32: return 4;
+        case PKV_BF16: return 2;
+        case PKV_F16: return 2;
+        case PKV_U8: return 1;
+        case PKV_I32: return 4;
+        case PKV_I64: return 8;
+        default: return 0;
+    }
+}
+
+int64_t numel(const pkv_tensor* t) {
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+    return n;
+}
+
+int64_t nbytes(const pkv_tensor* t) { return numel(t) * dtype_size(t->dtype); }
+
+pkv_status check_tensor(const pkv_tensor* t, const char* name, int ndim_lo, int ndim_hi) {
+    if (!t) return fail(PKV_E_ARG, "%s: null descriptor", name);
+    if (t->ndim < ndim_lo || t->ndim > ndim_hi)
+        return fail(PKV_E_LAYOUT, "%s: rank %d not in [%d, %d]", name, t->ndim, ndim_lo, ndim_hi);
+    if (dtype_size(t->dtype) == 0) return fail(PKV_E_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+    for (int i = 0; i < t->ndim; ++i)
+        if (t->shape[i] < 0 || t->shape[i] > (int64_t(1) << 40))
+            return fail(PKV_E_LAYOUT, "%s: bad extent %lld on axis %d", name, (long long)t->shape[i], i);
+    if (!t->data && numel(t) > 0) return fail(PKV_E_ARG, "%s: null data pointer", name);
+    return PKV_OK;
+}
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, int64_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + static_cast<uintptr_t>(bytes)};
+}
+Span span(const pkv_tensor* t) { return span(t->data, nbytes(t)); }
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// ---------------------------------------------------------------------------
+// Writable-binding registry ("Mutable execution cache", "Runtime contract")
+// ---------------------------------------------------------------------------
+std::mutex g_bind_mu;
+std::vector<pkv_binding*> g_bindings;
+
+}  // namespace
+
+struct pkv_binding {
+    Span range;
+};
+
+namespace {
+
+bool inside_writable_binding(Span s) {
+    std::lock_guard<std::mutex> lk(g_bind_mu);
+    for (const pkv_binding* b : g_bindings)
+        if (b->range.lo <= s.lo && s.hi <= b->range.hi) return true;
+    return false;
+}
+
+pkv_status check_writable(const pkv_tensor* t, const char* name) {
+    if (numel(t) == 0) return PKV_OK;
+    if (!inside_writable_binding(span(t)))
+        return fail(PKV_E_READONLY, "%s: storage is not inside a writable binding "
+                                    "(bind it with pkv_bind_writable first)", name);
+    return PKV_OK;
+}
+
+pkv_status check_disjoint(const pkv_tensor* a, const char* an, Span b, const char* bn) {
+    if (overlap(span(a), b)) return fail(PKV_E_ALIAS, "%s overlaps %s", an, bn);
+    return PKV_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Page pool
+// ---------------------------------------------------------------------------
+struct pkv_pool {
+    int32_t num_blocks, block_size, max_seqs, maxb;
+    std::deque<int32_t> free_list;   // front = next page handed out
+    std::vector<int32_t> table;      // [max_seqs * maxb], -1 = none
+    std::vector<int32_t> held;       // pages held per sequence
+    std::vector<int32_t> length;     // reserved logical length per sequence
+};
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+pkv_status write_table(int32_t* table_dev, const std::vector<int32_t>& idx,
+                       const std::vector<int32_t>& val, hipStream_t stream) {
+    for (size_t i = 0; i < idx.size(); i += kMaxTableWrites) {
+        TableWriteArgs a;
+        a.table = table_dev;
+        a.count = static_cast<int32_t>(std::min<size_t>(kMaxTableWrites, idx.size() - i));
+        for (int j = 0; j < a.count; ++j) {
+            a.index[j] = idx[i + j];
+            a.value[j] = val[i + j];
+        }
+        PKV_HIP(launch_table_write(a, stream), "page-table write");
+    }
+    return PKV_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Decode split planning
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kTargetWorkgroups = 2048;  // ~8 per CU on 256 CUs
+constexpr int kMinAutoTps = 256;         // tokens per split, library choice
+constexpr int kTpsQuantum = 64;          // fast kernel: 4 waves x 16 tokens
+
+struct Plan {
+    int32_t tps = 0;
+    int32_t S_max = 0;
+    std::vector<int32_t> nsplit;  // per row
+};
+
+// Splits of one launch.  `units_per_token` weights tokens by the number of
+// workgroups that stream them (Hkv for the fast kernels, Hq for the generic).
+Plan plan_splits(const int32_t* len, int B, int units, int num_splits, int max_tps) {
+    Plan p;
+    int64_t total = 0;
+    int32_t lmax = 1;
+    for (int b = 0; b < B; ++b) {
+        total += len[b];
+        lmax = std::max(lmax, len[b]);
+    }
+    int64_t tps;
+    if (num_splits > 0) {
+        tps = std::max<int64_t>(kTpsQuantum, ceil_div(ceil_div(lmax, num_splits), kTpsQuantum) * kTpsQuantum);
+    } else {
+        tps = ceil_div(total * units, kTargetWorkgroups);
+        tps = std::max<int64_t>(kMinAutoTps, ceil_div(tps, kTpsQuantum) * kTpsQuantum);
+    }
+    if (max_tps > 0) tps = std::min<int64_t>(tps, max_tps);
+    p.tps = static_cast<int32_t>(tps);
+    p.nsplit.resize(B);
+    for (int b = 0; b < B; ++b) {
+        p.nsplit[b] = static_cast<int32_t>(ceil_div(len[b], tps));
+        p.S_max = std::max(p.S_max, p.nsplit[b]);
+    }
+    return p;
+}
+
+int64_t split_bound(int32_t max_len, int32_t num_splits) {
+    int64_t s_auto = ceil_div(std::max(max_len, 1), kMinAutoTps);
+    int64_t s_gen = ceil_div(std::max(max_len, 1), kGenericMaxTps);
+    if (num_splits > 0) return std::max<int64_t>(num_splits, s_gen);
+    return std::max(s_auto, s_gen);
+}
+
+size_t ws_bytes_for(int64_t B, int64_t Hq, int64_t D, int64_t S) {
+    // [B, Hq, S, D] partial outputs + [B, Hq, S, 2] (max, sum), each 256-aligned
+    size_t o = static_cast<size_t>(B * Hq * S * D) * 4;
+    size_t ml = static_cast<size_t>(B * Hq * S * 2) * 4;
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    return up(o) + up(ml);
+}
+
+}  // namespace
+
+// ===========================================================================
+// extern "C"
+// ===========================================================================
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+// ---------------------------------------------------------------------------
+pkv_status pkv_bind_writable(void* base, size_t bytes, pkv_binding** out) {
+    if (!base || bytes == 0 || !out) return fail(PKV_E_ARG, "bind_writable: null base, zero size or null out");
+    Span s = span(base, static_cast<int64_t>(bytes));
+    std::lock_guard<std::mutex> lk(g_bind_mu);
+    for (const pkv_binding* b : g_bindings)
+        if (overlap(b->range, s))
+            return fail(PKV_E_BUSY, "bind_writable: range overlaps a live writable binding");
+    pkv_binding* b = new pkv_binding{s};
+    g_bindings.push_back(b);
+    *out = b;
+    return ok();
+}
+
+pkv_status pkv_unbind(pkv_binding* binding) {
+    if (!binding) return fail(PKV_E_ARG, "unbind: null binding");
+    std::lock_guard<std::mutex> lk(g_bind_mu);
+    auto it = std::find(g_bindings.begin(), g_bindings.end(), binding);
+    if (it == g_bindings.end()) return fail(PKV_E_ARG, "unbind: unknown binding");
+    g_bindings.erase(it);
+    delete binding;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+pkv_status pkv_cache_update(const pkv_tensor* cache, const pkv_tensor* values,
+                            const int32_t* position, int32_t update_length,
+                            void** out_cache, void* stream) {
+    PKV_TRY(check_tensor(cache, "cache", 4, 4));
+    PKV_TRY(check_tensor(values, "values", 4, 4));
+    if (!out_cache) return fail(PKV_E_ARG, "cache_update: null out_cache");
+    if (update_length < 0) return fail(PKV_E_ARG, "cache_update: negative update_length");
+    const int64_t B = cache->shape[0], H = cache->shape[1], cap = cache->shape[2], D = cache->shape[3];
+    if (values->dtype != cache->dtype) return fail(PKV_E_DTYPE, "cache_update: values dtype != cache dtype");
+    if (values->shape[0] != B || values->shape[1] != H || values->shape[2] != update_length ||
+        values->shape[3] != D)
+        return fail(PKV_E_LAYOUT, "cache_update: values must be [B, H, update_length, D] of the cache");
+    if (B > 0 && !position) return fail(PKV_E_ARG, "cache_update: null position");
+    for (int64_t b = 0; b < B; ++b)
+        if (position[b] < 0 || int64_t(position[b]) + update_length > cap)
+            return fail(PKV_E_CAPACITY, "cache_update: row %lld: position %d + update_length %d > capacity %lld",
+                        (long long)b, position[b], update_length, (long long)cap);
+    PKV_TRY(check_writable(cache, "cache"));
+    PKV_TRY(check_disjoint(values, "values", span(cache), "cache"));
+    *out_cache = cache->data;
+    if (numel(values) == 0) return ok();
+
+    const int64_t row_bytes = D * dtype_size(cache->dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        CopyRowsArgs a;
+        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
+        a.src = static_cast<const uint8_t*>(values->data) + b0 * H * update_length * row_bytes;
+        a.dst = static_cast<uint8_t*>(cache->data) + b0 * H * cap * row_bytes;
+        a.row_bytes = row_bytes;
+        a.H = static_cast<int32_t>(H);
+        a.n = update_length;
+        a.cap = static_cast<int32_t>(cap);
+        for (int i = 0; i < a.rows; ++i) a.pos[i] = position[b0 + i];
+        PKV_HIP(launch_copy_rows(a, s), "cache_update launch");
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, int32_t max_seqs,
+                           int32_t max_blocks_per_seq, const int32_t* initial_free_order,
+                           pkv_pool** out) {
+    if (!out) return fail(PKV_E_ARG, "pool_create: null out");
+    if (num_blocks <= 0 || block_size <= 0 || max_seqs <= 0 || max_blocks_per_seq <= 0)
+        return fail(PKV_E_ARG, "pool_create: dimensions must be positive");
+    if (int64_t(max_seqs) * max_blocks_per_seq > (int64_t(1) << 31) - 1 ||
+        int64_t(max_blocks_per_seq) * block_size > (int64_t(1) << 31) - 1)
+        return fail(PKV_E_ARG, "pool_create: page table too large for int32 indexing");
+    auto* p = new pkv_pool;
+    p->num_blocks = num_blocks;
+    p->block_size = block_size;
+    p->max_seqs = max_seqs;
+    p->maxb = max_blocks_per_seq;
+    if (initial_free_order) {
+        std::vector<char> seen(num_blocks, 0);
+        for (int32_t i = 0; i < num_blocks; ++i) {
+            int32_t id = initial_free_order[i];
+            if (id < 0 || id >= num_blocks || seen[id]) {
+                delete p;
+                return fail(PKV_E_ARG, "pool_create: initial_free_order is not a permutation of 0..num_blocks-1");
+            }
+            seen[id] = 1;
+            p->free_list.push_back(id);
+        }
+    } else {
+        for (int32_t i = 0; i < num_blocks; ++i) p->free_list.push_back(i);
+    }
+    p->table.assign(size_t(max_seqs) * max_blocks_per_seq, -1);
+    p->held.assign(max_seqs, 0);
+    p->length.assign(max_seqs, 0);
+    *out = p;
+    return ok();
+}
+
+pkv_status pkv_pool_destroy(pkv_pool* pool) {
+    if (!pool) return fail(PKV_E_ARG, "pool_destroy: null pool");
+    delete pool;
+    return ok();
+}
+
+pkv_status pkv_pool_reserve(pkv_pool* pool, int32_t n, const int32_t* seqs,
+                            const int32_t* new_len, int32_t* page_table_dev, void* stream) {
+    if (!pool) return fail(PKV_E_ARG, "pool_reserve: null pool");
+    if (n < 0 || (n > 0 && (!seqs || !new_len))) return fail(PKV_E_ARG, "pool_reserve: bad arrays");
+    std::vector<char> listed(pool->max_seqs, 0);
+    int64_t missing_total = 0;
+    std::vector<int32_t> missing(n, 0);
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t s = seqs[i];
+        if (s < 0 || s >= pool->max_seqs) return fail(PKV_E_PAGE, "pool_reserve: sequence %d out of range", s);
+        if (listed[s]) return fail(PKV_E_PAGE, "pool_reserve: sequence %d listed twice", s);
+        listed[s] = 1;
+        if (new_len[i] < 0) return fail(PKV_E_ARG, "pool_reserve: negative length");
+        int64_t need = ceil_div(new_len[i], pool->block_size);
+        if (need > pool->maxb)
+            return fail(PKV_E_PAGE, "pool_reserve: sequence %d needs %lld pages > max_blocks_per_seq %d", s,
+                        (long long)need, pool->maxb);
+        missing[i] = static_cast<int32_t>(std::max<int64_t>(0, need - pool->held[s]));
+        missing_total += missing[i];
+    }
+    if (missing_total > static_cast<int64_t>(pool->free_list.size()))
+        return fail(PKV_E_NOMEM, "pool_reserve: need %lld pages, %zu free", (long long)missing_total,
+                    pool->free_list.size());
+    std::vector<int32_t> idx, val;
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t s = seqs[i];
+        for (int32_t k = 0; k < missing[i]; ++k) {
+            int32_t phys = pool->free_list.front();
+            pool->free_list.pop_front();
+            int32_t slot = pool->held[s] + k;
+            pool->table[size_t(s) * pool->maxb + slot] = phys;
+            idx.push_back(s * pool->maxb + slot);
+            val.push_back(phys);
+        }
+        pool->held[s] += missing[i];
+        pool->length[s] = std::max(pool->length[s], new_len[i]);
+    }
+    if (page_table_dev && !idx.empty())
+        PKV_TRY(write_table(page_table_dev, idx, val, static_cast<hipStream_t>(stream)));
+    return ok();
+}
+
+pkv_status pkv_pool_release(pkv_pool* pool, int32_t seq, int32_t* page_table_dev, void* stream) {
+    if (!pool) return fail(PKV_E_ARG, "pool_release: null pool");
+    if (seq < 0 || seq >= pool->max_seqs) return fail(PKV_E_PAGE, "pool_release: sequence %d out of range", seq);
+    std::vector<int32_t> idx, val;
+    for (int32_t k = 0; k < pool->held[seq]; ++k) {
+        int32_t& e = pool->table[size_t(seq) * pool->maxb + k];
+        pool->free_list.push_back(e);
+        e = -1;
+        idx.push_back(seq * pool->maxb + k);
+        val.push_back(-1);
+    }
+    pool->held[seq] = 0;
+    pool->length[seq] = 0;
+    if (page_table_dev && !idx.empty())
+        PKV_TRY(write_table(page_table_dev, idx, val, static_cast<hipStream_t>(stream)));
+    return ok();
+}
+
+pkv_status pkv_pool_query(const pkv_pool* pool, int32_t seq, int32_t* held_pages, int32_t* reserved_len) {
+    if (!pool) return fail(PKV_E_ARG, "pool_query: null pool");
+    if (seq < 0 || seq >= pool->max_seqs) return fail(PKV_E_PAGE, "pool_query: sequence %d out of range", seq);
+    if (held_pages) *held_pages = pool->held[seq];
+    if (reserved_len) *reserved_len = pool->length[seq];
+    return ok();
+}
+
+pkv_status pkv_pool_free_count(const pkv_pool* pool, int32_t* free_pages) {
+    if (!pool || !free_pages) return fail(PKV_E_ARG, "pool_free_count: null argument");
+    *free_pages = static_cast<int32_t>(pool->free_list.size());
+    return ok();
+}
+
+pkv_status pkv_pool_table(const pkv_pool* pool, int32_t* out_host) {
+    if (!pool || !out_host) return fail(PKV_E_ARG, "pool_table: null argument");
+    std::memcpy(out_host, pool->table.data(), pool->table.size() * sizeof(int32_t));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+// Checks shared by the paged updates: pages of every written position are
+// reserved for the row, positions fit the page table.
+pkv_status check_paged_positions(const pkv_pool* pool, int64_t B, const int32_t* position, int32_t n) {
+    if (!pool) return fail(PKV_E_ARG, "paged update: a pool handle is required");
+    if (B > pool->max_seqs) return fail(PKV_E_PAGE, "paged update: batch %lld > max_seqs %d", (long long)B, pool->max_seqs);
+    if (B > 0 && !position) return fail(PKV_E_ARG, "paged update: null position");
+    const int64_t cap = int64_t(pool->maxb) * pool->block_size;
+    for (int64_t b = 0; b < B; ++b) {
+        if (position[b] < 0 || int64_t(position[b]) + n > cap)
+            return fail(PKV_E_CAPACITY, "paged update: row %lld: position %d + update_length %d > %lld",
+                        (long long)b, position[b], n, (long long)cap);
+        if (n > 0 && ceil_div(int64_t(position[b]) + n, pool->block_size) > pool->held[b])
+            return fail(PKV_E_PAGE, "paged update: row %lld writes past its %d reserved pages "
+                                    "(reserve with pkv_pool_reserve first)", (long long)b, pool->held[b]);
+    }
+    return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status pkv_paged_cache_update(const pkv_pool* pool, const pkv_tensor* pool_kv,
+                                  const int32_t* page_table_dev, const pkv_tensor* values,
+                                  const int32_t* position, int32_t update_length,
+                                  void** out_pool, void* stream) {
+    PKV_TRY(check_tensor(pool_kv, "pool_kv", 4, 4));
+    PKV_TRY(check_tensor(values, "values", 4, 4));
+    if (!out_pool) return fail(PKV_E_ARG, "paged_cache_update: null out_pool");
+    if (update_length < 0) return fail(PKV_E_ARG, "paged_cache_update: negative update_length");
+    if (!pool) return fail(PKV_E_ARG, "paged_cache_update: a pool handle is required");
+    const int64_t NB = pool_kv->shape[0], H = pool_kv->shape[1], bs = pool_kv->shape[2], D = pool_kv->shape[3];
+    const int64_t B = values->shape[0];
+    if (NB != pool->num_blocks || bs != pool->block_size)
+        return fail(PKV_E_LAYOUT, "paged_cache_update: pool_kv is [%lld, H, %lld, D] but the pool has %d blocks of %d",
+                    (long long)NB, (long long)bs, pool->num_blocks, pool->block_size);
+    if (values->dtype != pool_kv->dtype) return fail(PKV_E_DTYPE, "paged_cache_update: values dtype != pool dtype");
+    if (values->shape[1] != H || values->shape[2] != update_length || values->shape[3] != D)
+        return fail(PKV_E_LAYOUT, "paged_cache_update: values must be [B, H, update_length, D] of the pool");
+    if (!page_table_dev && B > 0 && update_length > 0) return fail(PKV_E_ARG, "paged_cache_update: null page table");
+    PKV_TRY(check_paged_positions(pool, B, position, update_length));
+    PKV_TRY(check_writable(pool_kv, "pool_kv"));
+    PKV_TRY(check_disjoint(values, "values", span(pool_kv), "pool_kv"));
+    *out_pool = pool_kv->data;
+    if (numel(values) == 0) return ok();
+
+    const int64_t row_bytes = D * dtype_size(pool_kv->dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        PagedCopyArgs a;
+        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
+        a.src = static_cast<const uint8_t*>(values->data) + b0 * H * update_length * row_bytes;
+        a.pool = static_cast<uint8_t*>(pool_kv->data);
+        a.page_table = page_table_dev;
+        a.row_bytes = row_bytes;
+        a.H = static_cast<int32_t>(H);
+        a.n = update_length;
+        a.bs = static_cast<int32_t>(bs);
+        a.maxb = pool->maxb;
+        a.row0 = static_cast<int32_t>(b0);
+        for (int i = 0; i < a.rows; ++i) a.pos[i] = position[b0 + i];
+        PKV_HIP(launch_paged_copy(a, s), "paged_cache_update launch");
+    }
+    return ok();
+}
+
+pkv_status pkv_paged_cache_update_int4(const pkv_pool* pool, const pkv_tensor* codes_pool,
+                                       const pkv_tensor* params_pool,
+                                       const int32_t* page_table_dev, const pkv_tensor* values,
+                                       uint16_t scale_f16, uint16_t zero_point_f16,
+                                       const int32_t* position, int32_t update_length,
+                                       void** out_codes, void** out_params, void* stream) {
+    PKV_TRY(check_tensor(codes_pool, "codes_pool", 4, 4));
+    PKV_TRY(check_tensor(params_pool, "params_pool", 5, 5));
+    PKV_TRY(check_tensor(values, "values", 4, 4));
+    if (!out_codes || !out_params) return fail(PKV_E_ARG, "paged_cache_update_int4: null output pointer");
+    if (update_length < 0) return fail(PKV_E_ARG, "paged_cache_update_int4: negative update_length");
+    if (!pool) return fail(PKV_E_ARG, "paged_cache_update_int4: a pool handle is required");
+    const int64_t NB = codes_pool->shape[0], H = codes_pool->shape[1], bs = codes_pool->shape[2];
+    const int64_t D = codes_pool->shape[3] * 2;
+    const int64_t B = values->shape[0];
+    if (codes_pool->dtype != PKV_U8 || params_pool->dtype != PKV_F16)
+        return fail(PKV_E_DTYPE, "paged_cache_update_int4: codes must be u8 and params f16");
+    if (values->dtype != PKV_F32 && values->dtype != PKV_BF16)
+        return fail(PKV_E_DTYPE, "paged_cache_update_int4: values must be f32 or bf16");
+    if (NB != pool->num_blocks || bs != pool->block_size)
+        return fail(PKV_E_LAYOUT, "paged_cache_update_int4: codes pool does not match the pool handle");
+    if (D % 32 != 0 || D == 0) return fail(PKV_E_LAYOUT, "paged_cache_update_int4: D must be a positive multiple of 32");
+    const int64_t ps[5] = {NB, H, bs, D / 32, 2};
+    for (int i = 0; i < 5; ++i)
+        if (params_pool->shape[i] != ps[i])
+            return fail(PKV_E_LAYOUT, "paged_cache_update_int4: params must be [NB, H, bs, D/32, 2]");
+    if (values->shape[1] != H || values->shape[2] != update_length || values->shape[3] != D)
+        return fail(PKV_E_LAYOUT, "paged_cache_update_int4: values must be [B, H, update_length, D]");
+    // scale: positive, finite binary16; zero point: integer 0..15 in binary16
+    const uint16_t se = (scale_f16 >> 10) & 0x1F;
+    if ((scale_f16 & 0x8000) || se == 0x1F || (scale_f16 & 0x7FFF) == 0)
+        return fail(PKV_E_ARG, "paged_cache_update_int4: scale must be positive and finite");
+    float zp = -1.0f;
+    for (int c = 0; c <= 15; ++c) {
+        // binary16 encoding of the integer c
+        uint16_t bits = 0;
+        if (c > 0) {
+            int e = 0;
+            while ((c >> (e + 1)) != 0) ++e;
+            bits = static_cast<uint16_t>(((e + 15) << 10) | (((c << 10) >> e) & 0x3FF));
+        }
+        if (bits == zero_point_f16) zp = float(c);
+    }
+    if (zp < 0) return fail(PKV_E_ARG, "paged_cache_update_int4: zero point must be an integer 0..15");
+    if (!page_table_dev && B > 0 && update_length > 0) return fail(PKV_E_ARG, "paged_cache_update_int4: null page table");
+    PKV_TRY(check_paged_positions(pool, B, position, update_length));
+    PKV_TRY(check_writable(codes_pool, "codes_pool"));
+    PKV_TRY(check_writable(params_pool, "params_pool"));
+    PKV_TRY(check_disjoint(values, "values", span(codes_pool), "codes_pool"));
+    PKV_TRY(check_disjoint(values, "values", span(params_pool), "params_pool"));
+    if (overlap(span(codes_pool), span(params_pool))) return fail(PKV_E_ALIAS, "codes_pool overlaps params_pool");
+    *out_codes = codes_pool->data;
+    *out_params = params_pool->data;
+    if (numel(values) == 0) return ok();
+
+    // widen the binary16 scale exactly
+    const int sm = scale_f16 & 0x3FF;
+    const float scale = se == 0 ? std::ldexp(float(sm), -24) : std::ldexp(float(sm | 0x400), se - 25);
+    const int64_t esz = dtype_size(values->dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        PagedInt4Args a;
+        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
+        a.src = static_cast<const uint8_t*>(values->data) + b0 * H * update_length * D * esz;
+        a.codes = static_cast<uint8_t*>(codes_pool->data);
+        a.params = static_cast<uint16_t*>(params_pool->data);
+        a.page_table = page_table_dev;
+        a.src_bf16 = values->dtype == PKV_BF16;
+        a.H = static_cast<int32_t>(H);
+        a.n = update_length;
+        a.bs = static_cast<int32_t>(bs);
+        a.maxb = pool->maxb;
+        a.D = static_cast<int32_t>(D);
+        a.row0 = static_cast<int32_t>(b0);
+        a.scale = scale;
+        a.zero_point = zp;
+        a.scale_bits = scale_f16;
+        a.zp_bits = zero_point_f16;
+        for (int i = 0; i < a.rows; ++i) a.pos[i] = position[b0 + i];
+        PKV_HIP(launch_paged_int4_append(a, s), "paged_cache_update_int4 launch");
+    }
+    return ok();
+}
+
+pkv_status pkv_paged_gather(const pkv_tensor* pool_kv, const int32_t* page_table_dev,
+                            int32_t max_blocks_per_seq, int32_t seq, int32_t length,
+                            pkv_tensor* out, void* stream) {
+    PKV_TRY(check_tensor(pool_kv, "pool_kv", 4, 4));
+    PKV_TRY(check_tensor(out, "out", 3, 3));
+    if (!page_table_dev || max_blocks_per_seq <= 0 || seq < 0 || length < 0)
+        return fail(PKV_E_ARG, "paged_gather: bad page table, sequence or length");
+    const int64_t H = pool_kv->shape[1], bs = pool_kv->shape[2], D = pool_kv->shape[3];
+    if (ceil_div(length, bs) > max_blocks_per_seq) return fail(PKV_E_PAGE, "paged_gather: length exceeds the page table row");
+    if (out->dtype != pool_kv->dtype || out->shape[0] != H || out->shape[1] != length || out->shape[2] != D)
+        return fail(PKV_E_LAYOUT, "paged_gather: out must be [H, length, D] of the pool's dtype");
+    PKV_TRY(check_disjoint(out, "out", span(pool_kv), "pool_kv"));
+    if (length == 0 || H == 0 || D == 0) return ok();
+    GatherArgs a;
+    a.pool = static_cast<const uint8_t*>(pool_kv->data);
+    a.table_row = page_table_dev + int64_t(seq) * max_blocks_per_seq;
+    a.out = static_cast<uint8_t*>(out->data);
+    a.row_bytes = D * dtype_size(pool_kv->dtype);
+    a.H = static_cast<int32_t>(H);
+    a.bs = static_cast<int32_t>(bs);
+    a.length = length;
+    PKV_HIP(launch_gather(a, static_cast<hipStream_t>(stream)), "paged_gather launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t pkv_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_len,
+                                 int32_t num_splits) {
+    (void)Hkv;
+    if (B <= 0 || Hq <= 0 || D <= 0 || max_len <= 0 || num_splits < 0) return 0;
+    return ws_bytes_for(B, Hq, D, split_bound(max_len, num_splits));
+}
+
+namespace {
+
+int kv_kind_of(int32_t dt) {
+    switch (dt) {
+        case PKV_F32: return kKvF32;
+        case PKV_BF16: return kKvBF16;
+        case PKV_F16: return kKvF16;
+        default: return -1;
+    }
+}
+
+struct QView {
+    int64_t B, Hq, D;
+};
+
+pkv_status check_q_out(const pkv_tensor* q, const pkv_tensor* out, QView* v) {
+    PKV_TRY(check_tensor(q, "q", 3, 4));
+    PKV_TRY(check_tensor(out, "out", 3, 4));
+    if (q->ndim == 4 && q->shape[2] != 1) return fail(PKV_E_LAYOUT, "q must be [B, Hq, 1, D] or [B, Hq, D]");
+    v->B = q->shape[0];
+    v->Hq = q->shape[1];
+    v->D = q->shape[q->ndim - 1];
+    if (out->ndim != q->ndim) return fail(PKV_E_LAYOUT, "out must have the shape of q");
+    for (int i = 0; i < q->ndim; ++i)
+        if (out->shape[i] != q->shape[i]) return fail(PKV_E_LAYOUT, "out must have the shape of q");
+    return PKV_OK;
+}
+
+// Shared body of the bf16/f32 decode entry points.
+pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_tensor* v,
+                         bool paged, const int32_t* page_table, int32_t maxb, int32_t bs,
+                         const pkv_pool* pool, const int32_t* valid_len, float scale,
+                         pkv_tensor* out, void* ws, size_t ws_bytes, int32_t num_splits,
+                         void* stream) {
+    QView qv;
+    PKV_TRY(check_q_out(q, out, &qv));
+    PKV_TRY(check_tensor(k, "k", 4, 4));
+    PKV_TRY(check_tensor(v, "v", 4, 4));
+    const int64_t B = qv.B, Hq = qv.Hq, D = qv.D;
+    const int64_t Hkv = k->shape[1];
+    const int kind = kv_kind_of(q->dtype);
+    if (kind < 0) return fail(PKV_E_DTYPE, "q must be f32, bf16 or f16");
+    if (k->dtype != q->dtype || v->dtype != q->dtype) return fail(PKV_E_DTYPE, "q, k and v must share a dtype");
+    if (out->dtype != q->dtype && out->dtype != PKV_F32) return fail(PKV_E_DTYPE, "out must have q's dtype or f32");
+    for (int i = 0; i < 4; ++i)
+        if (v->shape[i] != k->shape[i]) return fail(PKV_E_LAYOUT, "k and v must have the same shape");
+    if (k->shape[3] != D) return fail(PKV_E_LAYOUT, "k/v head size %lld != q head size %lld", (long long)k->shape[3], (long long)D);
+    if (Hkv <= 0 || Hq % Hkv != 0) return fail(PKV_E_LAYOUT, "query heads %lld must be a multiple of K/V heads %lld", (long long)Hq, (long long)Hkv);
+    if (D <= 0 || D > 256) return fail(PKV_E_LAYOUT, "head size must be in [1, 256]");
+    if (num_splits < 0) return fail(PKV_E_ARG, "num_splits must be >= 0");
+    int64_t cap;
+    if (paged) {
+        if (!page_table) return fail(PKV_E_ARG, "null page table");
+        if (bs <= 0 || bs != k->shape[2]) return fail(PKV_E_LAYOUT, "block_size %d != pool slot count %lld", bs, (long long)k->shape[2]);
+        if (maxb <= 0) return fail(PKV_E_ARG, "max_blocks_per_seq must be positive");
+        cap = int64_t(maxb) * bs;
+        if (pool) {
+            if (pool->block_size != bs || pool->num_blocks != k->shape[0] || pool->maxb != maxb)
+                return fail(PKV_E_LAYOUT, "pool handle does not match the K/V pools");
+            if (B > pool->max_seqs) return fail(PKV_E_PAGE, "batch larger than the pool's max_seqs");
+        }
+    } else {
+        if (k->shape[0] != B) return fail(PKV_E_LAYOUT, "cache batch %lld != q batch %lld", (long long)k->shape[0], (long long)B);
+        cap = k->shape[2];
+    }
+    if (B > 0 && !valid_len) return fail(PKV_E_ARG, "null valid_len");
+    for (int64_t b = 0; b < B; ++b) {
+        if (valid_len[b] < 1 || valid_len[b] > cap)
+            return fail(PKV_E_CAPACITY, "row %lld: valid_len %d not in [1, %lld]", (long long)b, valid_len[b], (long long)cap);
+        if (paged && pool && ceil_div(valid_len[b], bs) > pool->held[b])
+            return fail(PKV_E_PAGE, "row %lld: valid_len %d needs %lld pages, %d reserved", (long long)b, valid_len[b],
+                        (long long)ceil_div(valid_len[b], bs), pool->held[b]);
+    }
+    if (!(scale == scale) || std::isinf(scale)) return fail(PKV_E_ARG, "scale must be finite");
+    const Span os = span(out);
+    PKV_TRY(check_disjoint(q, "q", os, "out"));
+    PKV_TRY(check_disjoint(k, "k", os, "out"));
+    PKV_TRY(check_disjoint(v, "v", os, "out"));
+    if (B == 0 || Hq == 0) return ok();
+
+    const int G = static_cast<int>(Hq / Hkv);
+    const bool fast = fast_decode_supported(kind, static_cast<int>(D), G, paged, bs);
+    // size the workspace for the whole call (all row groups share it)
+    Plan full = plan_splits(valid_len, static_cast<int>(B), fast ? static_cast<int>(Hkv) : static_cast<int>(Hq),
+                            num_splits, fast ? 0 : kGenericMaxTps);
+    const size_t need = ws_bytes_for(B, Hq, D, full.S_max);
+    if (full.S_max > 1 || !fast) {
+        if (!ws || ws_bytes < need)
+            return fail(PKV_E_NOMEM, "workspace of %zu bytes needed, %zu given (pkv_decode_workspace_size)", need, ws_bytes);
+        const Span wss = span(ws, static_cast<int64_t>(need));
+        if (overlap(wss, os) || overlap(wss, span(q)) || overlap(wss, span(k)) || overlap(wss, span(v)))
+            return fail(PKV_E_ALIAS, "workspace overlaps an input or the output");
+        if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(PKV_E_ARG, "workspace must be 256-byte aligned");
+    }
+    const size_t o_bytes = (static_cast<size_t>(B * Hq * full.S_max * D) * 4 + 255) & ~size_t(255);
+    float* ws_o = static_cast<float*>(ws);
+    float* ws_ml = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes) : nullptr;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t esz = dtype_size(q->dtype);
+    const int64_t out_esz = dtype_size(out->dtype);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        const int rows = static_cast<int>(std::min<int64_t>(kMaxRows, B - b0));
+        DecodeArgs a;
+        a.q = static_cast<const uint8_t*>(q->data) + b0 * Hq * D * esz;
+        if (paged) {
+            a.k = k->data;
+            a.v = v->data;
+            a.page_table = page_table + b0 * maxb;
+        } else {
+            a.k = static_cast<const uint8_t*>(k->data) + b0 * Hkv * cap * D * esz;
+            a.v = static_cast<const uint8_t*>(v->data) + b0 * Hkv * cap * D * esz;
+            a.page_table = nullptr;
+        }
+        a.out = static_cast<uint8_t*>(out->data) + b0 * Hq * D * out_esz;
+        a.ws_o = ws_o ? ws_o + b0 * Hq * full.S_max * D : nullptr;
+        a.ws_ml = ws_ml ? ws_ml + b0 * Hq * full.S_max * 2 : nullptr;
+        a.kv_kind = kind;
+        a.out_f32 = out->dtype == PKV_F32 && q->dtype != PKV_F32;
+        a.Hq = static_cast<int32_t>(Hq);
+        a.Hkv = static_cast<int32_t>(Hkv);
+        a.D = static_cast<int32_t>(D);
+        a.cap = static_cast<int32_t>(paged ? 0 : cap);
+        a.bs = paged ? bs : 0;
+        a.maxb = paged ? maxb : 0;
+        a.S_max = full.S_max;
+        a.tps = full.tps;
+        a.row0 = static_cast<int32_t>(b0);
+        a.rows = rows;
+        const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
+        a.scale_log2 = sc * 1.4426950408889634f;
+        int total = 0;
+        bool any_split = false;
+        for (int i = 0; i < rows; ++i) {
+            a.len[i] = valid_len[b0 + i];
+            a.split_begin[i] = total;
+            total += full.nsplit[b0 + i];
+            any_split |= full.nsplit[b0 + i] > 1;
+        }
+        a.split_begin[rows] = total;
+        if (fast) {
+            PKV_HIP(launch_decode_fast(a, G, total * static_cast<int>(Hkv), s), "decode launch");
+        } else {
+            PKV_HIP(launch_decode_generic(a, total * static_cast<int>(Hq), s), "decode launch");
+        }
+        if (any_split || !fast) {
+            MergeArgs m;
+            m.ws_o = a.ws_o;
+            m.ws_ml = a.ws_ml;
+            m.out = a.out;
+            m.out_kind = kv_kind_of(out->dtype);
+            m.Hq = a.Hq;
+            m.D = a.D;
+            m.S_max = a.S_max;
+            m.row0 = a.row0;
+            m.rows = rows;
+            m.min_splits = fast ? 2 : 1;  // the fast kernel finishes single-split rows itself
+            for (int i = 0; i < rows; ++i) m.nsplit[i] = full.nsplit[b0 + i];
+            PKV_HIP(launch_merge(m, s), "merge launch");
+        }
+    }
+    return ok();
+}
+
+}  // namespace
+
+pkv_status pkv_decode_attention(const pkv_tensor* q, const pkv_tensor* k_cache,
+                                const pkv_tensor* v_cache, const int32_t* valid_len,
+                                float scale, pkv_tensor* out, void* workspace,
+                                size_t workspace_bytes, int32_t num_splits, void* stream) {
+    return decode_common(q, k_cache, v_cache, false, nullptr, 0, 0, nullptr, valid_len, scale, out,
+                         workspace, workspace_bytes, num_splits, stream);
+}
+
+pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                      const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                      int32_t max_blocks_per_seq, int32_t block_size,
+                                      const pkv_pool* pool, const int32_t* valid_len,
+                                      float scale, pkv_tensor* out, void* workspace,
+                                      size_t workspace_bytes, int32_t num_splits, void* stream) {
+    return decode_common(q, k_pool, v_pool, true, page_table_dev, max_blocks_per_seq, block_size, pool,
+                         valid_len, scale, out, workspace, workspace_bytes, num_splits, stream);
+}
+
+
+pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor* k_codes,
+                                           const pkv_tensor* k_params, const pkv_tensor* v_codes,
+                                           const pkv_tensor* v_params,
+                                           const int32_t* page_table_dev,
+                                           int32_t max_blocks_per_seq, int32_t block_size,
+                                           const pkv_pool* pool, const int32_t* valid_len,
+                                           float scale, pkv_tensor* out, void* workspace,
+                                           size_t workspace_bytes, int32_t num_splits,
+                                           void* stream) {
+    QView qv;
+    PKV_TRY(check_q_out(q, out, &qv));
+    PKV_TRY(check_tensor(k_codes, "k_codes", 4, 4));
+    PKV_TRY(check_tensor(v_codes, "v_codes", 4, 4));
+    PKV_TRY(check_tensor(k_params, "k_params", 5, 5));
+    PKV_TRY(check_tensor(v_params, "v_params", 5, 5));
+    const int64_t B = qv.B, Hq = qv.Hq, D = qv.D;
+    if (q->dtype != PKV_F32 || out->dtype != PKV_F32) return fail(PKV_E_DTYPE, "int4 decode: q and out must be f32");
+    if (k_codes->dtype != PKV_U8 || v_codes->dtype != PKV_U8 || k_params->dtype != PKV_F16 ||
+        v_params->dtype != PKV_F16)
+        return fail(PKV_E_DTYPE, "int4 decode: codes must be u8 and params f16");
+    if (D != kFastD) return fail(PKV_E_LAYOUT, "int4 decode: head size must be %d", kFastD);
+    const int64_t NB = k_codes->shape[0], Hkv = k_codes->shape[1], bs = k_codes->shape[2];
+    for (int i = 0; i < 4; ++i)
+        if (v_codes->shape[i] != k_codes->shape[i]) return fail(PKV_E_LAYOUT, "int4 decode: K and V code pools differ");
+    if (k_codes->shape[3] != D / 2) return fail(PKV_E_LAYOUT, "int4 decode: codes must be [NB, Hkv, bs, D/2]");
+    const int64_t ps[5] = {NB, Hkv, bs, D / 32, 2};
+    for (int i = 0; i < 5; ++i)
+        if (k_params->shape[i] != ps[i] || v_params->shape[i] != ps[i])
+            return fail(PKV_E_LAYOUT, "int4 decode: params must be [NB, Hkv, bs, D/32, 2]");
+    if (Hkv <= 0 || Hq % Hkv != 0) return fail(PKV_E_LAYOUT, "int4 decode: Hq must be a multiple of Hkv");
+    const int G = static_cast<int>(Hq / Hkv);
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_E_LAYOUT, "int4 decode: Hq / Hkv must be 1, 2, 4 or 8");
+    if (!page_table_dev) return fail(PKV_E_ARG, "int4 decode: null page table");
+    if (block_size != bs || bs % kSlabTokens != 0)
+        return fail(PKV_E_LAYOUT, "int4 decode: block_size must equal the pool's and be a multiple of %d", kSlabTokens);
+    if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "int4 decode: max_blocks_per_seq must be positive");
+    if (num_splits < 0) return fail(PKV_E_ARG, "num_splits must be >= 0");
+    if (pool && (pool->block_size != bs || pool->num_blocks != NB || pool->maxb != max_blocks_per_seq))
+        return fail(PKV_E_LAYOUT, "int4 decode: pool handle does not match the pools");
+    if (pool && B > pool->max_seqs) return fail(PKV_E_PAGE, "int4 decode: batch larger than the pool's max_seqs");
+    const int64_t cap = int64_t(max_blocks_per_seq) * bs;
+    if (B > 0 && !valid_len) return fail(PKV_E_ARG, "null valid_len");
+    for (int64_t b = 0; b < B; ++b) {
+        if (valid_len[b] < 1 || valid_len[b] > cap)
+            return fail(PKV_E_CAPACITY, "row %lld: valid_len %d not in [1, %lld]", (long long)b, valid_len[b], (long long)cap);
+        if (pool && ceil_div(valid_len[b], bs) > pool->held[b])
+            return fail(PKV_E_PAGE, "row %lld: valid_len %d needs more pages than reserved", (long long)b, valid_len[b]);
+    }
+    if (!(scale == scale) || std::isinf(scale)) return fail(PKV_E_ARG, "scale must be finite");
+    const Span os = span(out);
+    PKV_TRY(check_disjoint(q, "q", os, "out"));
+    for (const pkv_tensor* t : {k_codes, v_codes, k_params, v_params}) PKV_TRY(check_disjoint(t, "K/V pool", os, "out"));
+    if (B == 0) return ok();
+
+    Plan full = plan_splits(valid_len, static_cast<int>(B), static_cast<int>(Hkv), num_splits, 0);
+    const size_t need = ws_bytes_for(B, Hq, D, full.S_max);
+    if (full.S_max > 1) {
+        if (!workspace || workspace_bytes < need)
+            return fail(PKV_E_NOMEM, "workspace of %zu bytes needed, %zu given (pkv_decode_workspace_size)", need,
+                        workspace_bytes);
+        const Span wss = span(workspace, static_cast<int64_t>(need));
+        if (overlap(wss, os) || overlap(wss, span(q))) return fail(PKV_E_ALIAS, "workspace overlaps q or out");
+        if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(PKV_E_ARG, "workspace must be 256-byte aligned");
+    }
+    const size_t o_bytes = (static_cast<size_t>(B * Hq * full.S_max * D) * 4 + 255) & ~size_t(255);
+    float* ws_o = static_cast<float*>(workspace);
+    float* ws_ml = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes) : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        const int rows = static_cast<int>(std::min<int64_t>(kMaxRows, B - b0));
+        Int4DecodeArgs a;
+        a.q = static_cast<const float*>(q->data) + b0 * Hq * D;
+        a.kc = static_cast<const uint8_t*>(k_codes->data);
+        a.kp = static_cast<const uint16_t*>(k_params->data);
+        a.vc = static_cast<const uint8_t*>(v_codes->data);
+        a.vp = static_cast<const uint16_t*>(v_params->data);
+        a.page_table = page_table_dev + b0 * max_blocks_per_seq;
+        a.out = static_cast<float*>(out->data) + b0 * Hq * D;
+        a.ws_o = ws_o ? ws_o + b0 * Hq * full.S_max * D : nullptr;
+        a.ws_ml = ws_ml ? ws_ml + b0 * Hq * full.S_max * 2 : nullptr;
+        a.Hq = static_cast<int32_t>(Hq);
+        a.Hkv = static_cast<int32_t>(Hkv);
+        a.bs = block_size;
+        a.maxb = max_blocks_per_seq;
+        a.S_max = full.S_max;
+        a.tps = full.tps;
+        a.row0 = static_cast<int32_t>(b0);
+        a.rows = rows;
+        const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
+        a.scale_log2 = sc * 1.4426950408889634f;
+        int total = 0;
+        bool any_split = false;
+        for (int i = 0; i < rows; ++i) {
+            a.len[i] = valid_len[b0 + i];
+            a.split_begin[i] = total;
+            total += full.nsplit[b0 + i];
+            any_split |= full.nsplit[b0 + i] > 1;
+        }
+        a.split_begin[rows] = total;
+        PKV_HIP(launch_decode_int4(a, G, total * static_cast<int>(Hkv), s), "int4 decode launch");
+        if (any_split) {
+            MergeArgs m;
+            m.ws_o = a.ws_o;
+            m.ws_ml = a.ws_ml;
+            m.out = a.out;
+            m.out_kind = kKvF32;
+            m.Hq = a.Hq;
+            m.D = static_cast<int32_t>(D);
+            m.S_max = a.S_max;
+            m.row0 = a.row0;
+            m.rows = rows;
+            m.min_splits = 2;
+            for (int i = 0; i < rows; ++i) m.nsplit[i] = full.nsplit[b0 + i];
+            PKV_HIP(launch_merge(m, s), "merge launch");
+        }
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+struct SamplePlan {
+    int32_t chunks;
+    int64_t chunk_len;
+};
+
+SamplePlan plan_sample(int64_t B, int64_t V) {
+    // about 2048 workgroups in total, chunks of at least 4096 logits
+    int64_t chunks = std::max<int64_t>(1, ceil_div(2048, std::max<int64_t>(B, 1)));
+    chunks = std::min<int64_t>(chunks, std::max<int64_t>(1, ceil_div(V, 4096)));
+    int64_t len = ceil_div(ceil_div(V, chunks), 1024) * 1024;
+    return {static_cast<int32_t>(ceil_div(V, len)), len};
+}
+
+}  // namespace
+
+size_t pkv_sample_workspace_size(int32_t B, int64_t V) {
+    if (B <= 0 || V <= 0) return 0;
+    const SamplePlan p = plan_sample(B, V);
+    const size_t n = size_t(B) * p.chunks;
+    return ((n * 4 + 255) & ~size_t(255)) + ((n * 4 + 255) & ~size_t(255));
+}
+
+pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed,
+                      int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream) {
+    PKV_TRY(check_tensor(logits, "logits", 2, 3));
+    const int kind = kv_kind_of(logits->dtype);
+    if (kind < 0) return fail(PKV_E_DTYPE, "sample: logits must be f32, bf16 or f16");
+    if (!(temperature >= 0.0f) || std::isinf(temperature))
+        return fail(PKV_E_ARG, "sample: temperature must be finite and >= 0");
+    if (!out_ids) return fail(PKV_E_ARG, "sample: null out_ids");
+    const int64_t B = logits->shape[0];
+    const int64_t S = logits->ndim == 3 ? logits->shape[1] : 1;
+    const int64_t V = logits->shape[logits->ndim - 1];
+    if (B <= 0 || S <= 0 || V <= 0) return fail(PKV_E_LAYOUT, "sample: empty logits");
+    if (V > INT32_MAX) return fail(PKV_E_LAYOUT, "sample: vocabulary too large");
+    const size_t need = pkv_sample_workspace_size(static_cast<int32_t>(B), V);
+    if (!workspace || workspace_bytes < need)
+        return fail(PKV_E_NOMEM, "sample: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    const Span wss = span(workspace, static_cast<int64_t>(need));
+    if (overlap(wss, span(logits)) || overlap(wss, span(out_ids, B * 8)) || overlap(span(logits), span(out_ids, B * 8)))
+        return fail(PKV_E_ALIAS, "sample: workspace, logits and out_ids must not overlap");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(PKV_E_ARG, "sample: workspace must be 256-byte aligned");
+    const SamplePlan p = plan_sample(B, V);
+    SampleArgs a;
+    a.row_stride = S * V;
+    a.logits = static_cast<const uint8_t*>(logits->data) + (S - 1) * V * dtype_size(logits->dtype);
+    a.V = V;
+    a.kind = kind;
+    a.B = static_cast<int32_t>(B);
+    a.chunks = p.chunks;
+    a.chunk_len = p.chunk_len;
+    a.greedy = temperature == 0.0f;
+    a.inv_t = a.greedy ? 0.0f : static_cast<float>(1.0 / static_cast<double>(temperature));
+    a.seed = seed;
+    const size_t n = size_t(B) * p.chunks;
+    a.part_val = static_cast<float*>(workspace);
+    a.part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ((n * 4 + 255) & ~size_t(255)));
+    a.out = out_ids;
+    PKV_HIP(launch_sample(a, static_cast<hipStream_t>(stream)), "sample launch");
+    return ok();
+}
+
+}  // extern "C"

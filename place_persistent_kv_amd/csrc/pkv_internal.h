@@ -1,0 +1,168 @@
+// Internal interface between the host layer (pkv_api.cpp) and the gfx950
+// kernels (*.hip).  Per-row data (positions, lengths, split offsets) travels
+// in kernel arguments, so a launch never depends on host memory that could
+// change after the call returns; rows are processed in groups of kMaxRows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kMaxRows = 256;        // batch rows per launch
+constexpr int kMaxTableWrites = 448; // page-table entries per launch
+constexpr int kSlabTokens = 16;      // tokens a wave handles per step in the fast decode kernel
+constexpr int kFastD = 128;          // head size of the fast bf16 / INT4 decode kernels
+
+// ---------------------------------------------------------------------------
+// Cache updates
+// ---------------------------------------------------------------------------
+struct CopyRowsArgs {            // contiguous: dst[b,h,pos_b+t,:] = src[b,h,t,:]
+    const uint8_t* src;          // [rows, H, n, row_bytes]
+    uint8_t* dst;                // [rows, H, cap, row_bytes]
+    int64_t row_bytes;
+    int32_t H, n, cap, rows;
+    int32_t pos[kMaxRows];
+};
+
+struct PagedCopyArgs {           // paged: pool[pt[b][p/bs], h, p%bs, :] = src[b,h,t,:]
+    const uint8_t* src;          // [rows, H, n, row_bytes]
+    uint8_t* pool;               // [NB, H, bs, row_bytes]
+    const int32_t* page_table;   // row (row0 + b) of [*, maxb]
+    int64_t row_bytes;
+    int32_t H, n, bs, maxb, row0, rows;
+    int32_t pos[kMaxRows];
+};
+
+struct PagedInt4Args {           // paged INT4 quantise-on-append
+    const void* src;             // [rows, H, n, D] f32 or bf16
+    uint8_t* codes;              // [NB, H, bs, D/2]
+    uint16_t* params;            // [NB, H, bs, D/32, 2]
+    const int32_t* page_table;
+    int32_t src_bf16;
+    int32_t H, n, bs, maxb, D, row0, rows;
+    float scale;                 // fp16 scale widened to f32
+    float zero_point;            // integer 0..15
+    uint16_t scale_bits, zp_bits;
+    int32_t pos[kMaxRows];
+};
+
+struct TableWriteArgs {
+    int32_t* table;
+    int32_t count;
+    int32_t index[kMaxTableWrites];
+    int32_t value[kMaxTableWrites];
+};
+
+struct GatherArgs {              // out[h, p, :] = pool[pt[seq][p/bs], h, p%bs, :]
+    const uint8_t* pool;
+    const int32_t* table_row;
+    uint8_t* out;
+    int64_t row_bytes;
+    int32_t H, bs, length;
+};
+
+hipError_t launch_copy_rows(const CopyRowsArgs& a, hipStream_t s);
+hipError_t launch_paged_copy(const PagedCopyArgs& a, hipStream_t s);
+hipError_t launch_paged_int4_append(const PagedInt4Args& a, hipStream_t s);
+hipError_t launch_table_write(const TableWriteArgs& a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Decode attention
+// ---------------------------------------------------------------------------
+enum KvKind : int32_t { kKvF32 = 0, kKvBF16 = 1, kKvF16 = 2 };
+
+struct DecodeArgs {
+    const void* q;               // [B, Hq, D]
+    const void* k;               // contiguous [B, Hkv, cap, D] or pool [NB, Hkv, bs, D]
+    const void* v;
+    const int32_t* page_table;   // nullptr for the contiguous layout
+    void* out;                   // [B, Hq, D]
+    float* ws_o;                 // [B, Hq, S_max, D] unnormalised partial outputs
+    float* ws_ml;                // [B, Hq, S_max, 2]  (running max (log2 units), sum)
+    int32_t kv_kind;             // KvKind of q/k/v
+    int32_t out_f32;             // 1: out is f32, 0: out has the KV element type
+    int32_t Hq, Hkv, D;
+    int32_t cap;                 // contiguous capacity (tokens per row)
+    int32_t bs, maxb;            // paged block size, page-table row length
+    int32_t S_max;               // split slots per (b, h) in the workspace
+    int32_t tps;                 // tokens per split
+    int32_t row0, rows;          // batch rows handled by this launch
+    float scale_log2;            // softmax scale * log2(e)
+    int32_t len[kMaxRows];       // valid length per row
+    int32_t split_begin[kMaxRows + 1];  // prefix sum of splits per row
+};
+
+struct Int4DecodeArgs {
+    const float* q;              // [B, Hq, 128]
+    const uint8_t* kc;           // [NB, Hkv, bs, 64]
+    const uint16_t* kp;          // [NB, Hkv, bs, 4, 2]
+    const uint8_t* vc;
+    const uint16_t* vp;
+    const int32_t* page_table;
+    float* out;                  // [B, Hq, 128]
+    float* ws_o;
+    float* ws_ml;
+    int32_t Hq, Hkv, bs, maxb, S_max, tps, row0, rows;
+    float scale_log2;
+    int32_t len[kMaxRows];
+    int32_t split_begin[kMaxRows + 1];
+};
+
+struct MergeArgs {
+    const float* ws_o;
+    const float* ws_ml;
+    void* out;
+    int32_t out_kind;            // KvKind of out
+    int32_t Hq, D, S_max, row0, rows;
+    int32_t min_splits;          // rows with fewer partials were finished by the attention kernel
+    int32_t nsplit[kMaxRows];
+};
+
+// Fast path: bf16, D == 128, G in {1, 2, 4, 8}, block_size % 16 == 0 (or contiguous).
+bool fast_decode_supported(int kv_kind, int D, int G, bool paged, int bs);
+hipError_t launch_decode_fast(const DecodeArgs& a, int G, int total_work, hipStream_t s);
+// Any D <= 256, f32/bf16/f16, any block size; tps <= kGenericMaxTps.
+constexpr int kGenericMaxTps = 1024;
+hipError_t launch_decode_generic(const DecodeArgs& a, int total_work, hipStream_t s);
+hipError_t launch_decode_int4(const Int4DecodeArgs& a, int G, int total_work, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Chunk attention (MFMA)
+// ---------------------------------------------------------------------------
+struct ChunkArgs {
+    const uint16_t* q;           // [B, Hq, C, 128] bf16
+    const uint16_t* k;           // pool [NB, Hkv, bs, 128]
+    const uint16_t* v;
+    const int32_t* page_table;
+    uint16_t* out;               // [B, Hq, C, 128]
+    int32_t Hq, Hkv, C, bs, maxb, row0, rows;
+    float scale_log2;
+    int32_t p0[kMaxRows];
+};
+bool chunk_supported(int D, int G, int bs, int C);
+hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Sampling
+// ---------------------------------------------------------------------------
+struct SampleArgs {
+    const void* logits;          // row b at logits + (b * row_stride) elements
+    int64_t row_stride;          // elements between rows
+    int64_t V;
+    int32_t kind;                // KvKind of the logits
+    int32_t B;
+    int32_t chunks;              // vocab chunks per row
+    int64_t chunk_len;           // elements per chunk (multiple of 1024)
+    int32_t greedy;
+    float inv_t;
+    uint64_t seed;
+    float* part_val;             // [B, chunks]
+    int32_t* part_idx;           // [B, chunks]
+    int64_t* out;                // [B]
+};
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
+
+}  // namespace pkv

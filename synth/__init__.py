@@ -50,8 +50,11 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Inputs are finite by construction, so no NaN handling is needed.
     """
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 

@@ -1,0 +1,249 @@
+"""The C ABI on the host (no GPU): exported symbols and every validation error.
+
+Validation runs before any HIP call, so these calls fail on the CPU with the
+documented status and never touch the (fake) device addresses they are given.
+Page-pool bookkeeping is host-only and is compared bit for bit with the
+oracle's pool on the same hand-out order.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import place_persistent_kv_amd as pkv
+import synth
+from oracle import cache as ocache
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
+FAKE = 0x7F0000000000          # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if getattr(pkv._lib, n, None) is None]
+    assert not missing, missing
+    assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
+    assert pkv.abi_version() == 1
+
+
+def R(ptr, dtype, shape):
+    return pkv.Raw(ptr, dtype, shape)
+
+
+def status_of(fn, *a, **k):
+    with pytest.raises(pkv.PkvError) as e:
+        fn(*a, **k)
+    return e.value.status
+
+
+# --------------------------------------------------------------------------- bindings
+def test_bindings_are_exclusive():
+    b1 = pkv.bind_writable(R(FAKE, pkv.U8, [4096]))
+    try:
+        assert status_of(pkv.bind_writable, R(FAKE + 4095, pkv.U8, [10])) == pkv.E_BUSY
+        b2 = pkv.bind_writable(R(FAKE + 4096, pkv.U8, [10]))      # adjacent: fine
+        b2.close()
+    finally:
+        b1.close()
+    b3 = pkv.bind_writable(R(FAKE, pkv.U8, [4096]))              # released range can be bound again
+    b3.close()
+    assert status_of(pkv.bind_writable, R(0, pkv.U8, [10])) == pkv.E_ARG
+
+
+# --------------------------------------------------------------------------- contiguous update
+CACHE = R(FAKE, pkv.BF16, [2, 3, 16, 8])
+CACHE_BYTES = 2 * 3 * 16 * 8 * 2
+VALS = R(FAKE + 0x100000, pkv.BF16, [2, 3, 4, 8])
+
+
+@pytest.mark.parametrize("pos", [[13, 0], [0, -1], [0, 17]])
+def test_cache_update_capacity_error(pos):
+    with pkv.bind_writable(CACHE):
+        assert status_of(pkv.cache_update, CACHE, VALS, pos, 4) == pkv.E_CAPACITY
+
+
+def test_cache_update_requires_a_writable_binding():
+    assert status_of(pkv.cache_update, CACHE, VALS, [0, 12], 4) == pkv.E_READONLY
+    with pkv.bind_writable(R(FAKE, pkv.U8, [CACHE_BYTES - 2])):   # binding one element short
+        assert status_of(pkv.cache_update, CACHE, VALS, [0, 12], 4) == pkv.E_READONLY
+
+
+def test_cache_update_rejects_values_inside_the_cache():
+    with pkv.bind_writable(CACHE):
+        inside = R(FAKE + 64, pkv.BF16, [2, 3, 4, 8])
+        assert status_of(pkv.cache_update, CACHE, inside, [0, 0], 4) == pkv.E_ALIAS
+
+
+def test_cache_update_shape_and_dtype_errors():
+    with pkv.bind_writable(CACHE):
+        assert status_of(pkv.cache_update, CACHE, R(VALS.ptr, pkv.F32, [2, 3, 4, 8]), [0, 0], 4) == pkv.E_DTYPE
+        assert status_of(pkv.cache_update, CACHE, R(VALS.ptr, pkv.BF16, [2, 3, 4, 4]), [0, 0], 4) == pkv.E_LAYOUT
+        assert status_of(pkv.cache_update, CACHE, VALS, [0, 0], 3) == pkv.E_LAYOUT
+        assert status_of(pkv.cache_update, CACHE, VALS, [0, 0], -1) == pkv.E_ARG
+
+
+# --------------------------------------------------------------------------- pool
+def test_pool_matches_the_oracle_pool():
+    g = synth.rng(500)
+    NB, bs, S, maxb = 64, 4, 6, 12
+    order = synth.permutation(g, NB)
+    lib = pkv.Pool(NB, bs, S, maxb, order)
+    ref = ocache.PagePool(NB, bs, S, maxb, order)
+    lens = np.zeros(S, np.int64)
+    for it in range(12):
+        seqs = sorted(g.choice(S, size=int(g.integers(1, S + 1)), replace=False).tolist())
+        new = [int(lens[s] + g.integers(0, 9)) for s in seqs]
+        need = sum(max(0, ocache.pages_for(n, bs) - ref.held[s]) for s, n in zip(seqs, new))
+        if any(ocache.pages_for(n, bs) > maxb for n in new):
+            assert status_of(lib.reserve, seqs, new) == pkv.E_PAGE
+        elif need > len(ref.free):
+            assert status_of(lib.reserve, seqs, new) == pkv.E_NOMEM
+        else:
+            lib.reserve(seqs, new)
+            for s, n in zip(seqs, new):
+                ref.reserve(s, n)
+                lens[s] = max(lens[s], n)
+        if it % 5 == 4:
+            lib.release(seqs[0])
+            ref.release(seqs[0])
+            lens[seqs[0]] = 0
+        assert np.array_equal(lib.table(), ref.table)
+        assert lib.free_count() == len(ref.free)
+        for s in range(S):
+            assert lib.query(s)[0] == ref.held[s]
+
+
+def test_pool_errors_change_nothing():
+    lib = pkv.Pool(7, 4, 2, 4)
+    lib.reserve([0], [9])                     # 3 pages, 4 left
+    table, free = lib.table(), lib.free_count()
+    assert status_of(lib.reserve, [0, 1], [12, 17]) == pkv.E_PAGE     # 5 pages > max 4
+    assert status_of(lib.reserve, [1, 1], [1, 1]) == pkv.E_PAGE       # listed twice
+    assert status_of(lib.reserve, [1], [4 * 6]) == pkv.E_PAGE
+    assert status_of(lib.reserve, [0, 1], [16, 16]) == pkv.E_NOMEM    # needs 1 + 4 > 4 free
+    assert status_of(lib.reserve, [2], [1]) == pkv.E_PAGE             # sequence out of range
+    assert np.array_equal(lib.table(), table) and lib.free_count() == free
+    assert status_of(pkv.Pool, 4, 4, 1, 1, [0, 1, 1, 3]) == pkv.E_ARG
+
+
+# --------------------------------------------------------------------------- paged update
+def test_paged_update_needs_reserved_pages_and_capacity():
+    pool = pkv.Pool(16, 4, 2, 4)
+    pool.reserve([0, 1], [5, 4])              # row 0: 2 pages, row 1: 1 page
+    kv = R(FAKE, pkv.BF16, [16, 2, 4, 8])
+    vals = R(FAKE + 0x100000, pkv.BF16, [2, 2, 1, 8])
+    table = R(FAKE + 0x200000, pkv.I32, [2, 4])
+    with pkv.bind_writable(kv):
+        assert status_of(pkv.paged_cache_update, pool, kv, table, vals, [7, 4], 1) == pkv.E_PAGE   # row 1 page 1
+        assert status_of(pkv.paged_cache_update, pool, kv, table, vals, [16, 0], 1) == pkv.E_CAPACITY
+        assert status_of(pkv.paged_cache_update, None, kv, table, vals, [0, 0], 1) == pkv.E_ARG
+        bad = R(FAKE, pkv.BF16, [16, 2, 8, 8])
+    assert status_of(pkv.paged_cache_update, pool, kv, table, vals, [0, 0], 1) == pkv.E_READONLY
+    with pkv.bind_writable(bad):
+        assert status_of(pkv.paged_cache_update, pool, bad, table, vals, [0, 0], 1) == pkv.E_LAYOUT
+
+
+def test_int4_update_parameter_checks():
+    pool = pkv.Pool(16, 4, 2, 4)
+    pool.reserve([0, 1], [4, 4])
+    codes = R(FAKE, pkv.U8, [16, 2, 4, 32])
+    params = R(FAKE + 0x100000, pkv.F16, [16, 2, 4, 2, 2])
+    vals = R(FAKE + 0x200000, pkv.F32, [2, 2, 1, 64])
+    table = R(FAKE + 0x300000, pkv.I32, [2, 4])
+    one = int(synth.f16_bits(np.float32(1.0)))
+    with pkv.bind_writable(codes), pkv.bind_writable(params):
+        for s_bits, z_bits in [(int(synth.f16_bits(np.float32(-0.5))), 0), (0, 0), (0x7C00, 0), (0x7E00, 0),
+                               (one, int(synth.f16_bits(np.float32(0.5)))),
+                               (one, int(synth.f16_bits(np.float32(16.0)))),
+                               (one, int(synth.f16_bits(np.float32(-1.0))))]:
+            assert status_of(pkv.paged_cache_update_int4, pool, codes, params, table, vals, s_bits, z_bits,
+                             [0, 0], 1) == pkv.E_ARG
+        odd = R(FAKE + 0x200000, pkv.F32, [2, 2, 1, 48])
+        assert status_of(pkv.paged_cache_update_int4, pool, R(FAKE, pkv.U8, [16, 2, 4, 24]), params, table,
+                         odd, one, 0, [0, 0], 1) == pkv.E_LAYOUT
+        assert status_of(pkv.paged_cache_update_int4, pool, codes, params, table,
+                         R(vals.ptr, pkv.U8, [2, 2, 1, 64]), one, 0, [0, 0], 1) == pkv.E_DTYPE
+
+
+# --------------------------------------------------------------------------- decode
+Q = R(FAKE, pkv.BF16, [2, 8, 1, 128])
+OUT = R(FAKE + 0x10000, pkv.BF16, [2, 8, 1, 128])
+KC = R(FAKE + 0x100000, pkv.BF16, [2, 2, 64, 128])
+VC = R(FAKE + 0x200000, pkv.BF16, [2, 2, 64, 128])
+
+
+@pytest.mark.parametrize("L", [[0, 5], [65, 5], [-3, 1]])
+def test_decode_valid_len_range(L):
+    assert status_of(pkv.decode_attention, Q, KC, VC, L, OUT) == pkv.E_CAPACITY
+
+
+def test_decode_shape_and_dtype_errors():
+    assert status_of(pkv.decode_attention, R(FAKE, pkv.BF16, [2, 6, 1, 128]), R(KC.ptr, pkv.BF16, [2, 4, 64, 128]),
+                     R(VC.ptr, pkv.BF16, [2, 4, 64, 128]), [1, 1], R(OUT.ptr, pkv.BF16, [2, 6, 1, 128])) == pkv.E_LAYOUT
+    assert status_of(pkv.decode_attention, Q, R(KC.ptr, pkv.F32, KC.shape), VC, [1, 1], OUT) == pkv.E_DTYPE
+    assert status_of(pkv.decode_attention, Q, KC, VC, [1, 1], R(OUT.ptr, pkv.F16, OUT.shape)) == pkv.E_DTYPE
+    assert status_of(pkv.decode_attention, Q, KC, VC, [1, 1], R(OUT.ptr, pkv.BF16, [2, 8, 1, 64])) == pkv.E_LAYOUT
+    assert status_of(pkv.decode_attention, Q, KC, VC, [1, 1], R(Q.ptr, pkv.BF16, Q.shape)) == pkv.E_ALIAS
+
+
+def test_decode_workspace_is_checked():
+    # 64 tokens with 8 splits of 64-token minimum -> 1 split: no workspace needed on the fast path;
+    # force splits on a longer cache instead
+    kc = R(FAKE + 0x100000, pkv.BF16, [2, 2, 1024, 128])
+    vc = R(FAKE + 0x900000, pkv.BF16, [2, 2, 1024, 128])
+    assert status_of(pkv.decode_attention, Q, kc, vc, [1000, 900], OUT, num_splits=4) == pkv.E_NOMEM
+    need = pkv.decode_workspace_size(2, 8, 2, 128, 1024, 4)
+    small = R(FAKE + 0x2000000, pkv.U8, [need - 256])
+    assert status_of(pkv.decode_attention, Q, kc, vc, [1000, 900], OUT, workspace=small, num_splits=4) == pkv.E_NOMEM
+    inside = R(kc.ptr, pkv.U8, [need])
+    assert status_of(pkv.decode_attention, Q, kc, vc, [1000, 900], OUT, workspace=inside, num_splits=4) == pkv.E_ALIAS
+
+
+def test_workspace_bound_covers_any_lengths():
+    for B, Hq, D, L, S in [(32, 32, 128, 32768, 0), (8, 32, 128, 4096, 0), (1, 1, 4, 16, 0), (3, 8, 64, 5000, 7)]:
+        n = pkv.decode_workspace_size(B, Hq, Hq // 4 or 1, D, L, S)
+        assert n >= B * Hq * D * 4 and n % 256 == 0
+    assert pkv.decode_workspace_size(0, 8, 2, 128, 16, 0) == 0
+
+
+def test_paged_decode_checks_reserved_pages():
+    pool = pkv.Pool(32, 16, 2, 8)
+    pool.reserve([0, 1], [40, 16])
+    kp = R(FAKE + 0x100000, pkv.BF16, [32, 2, 16, 128])
+    vp = R(FAKE + 0x900000, pkv.BF16, [32, 2, 16, 128])
+    table = R(FAKE + 0x2000000, pkv.I32, [2, 8])
+    assert status_of(pkv.paged_decode_attention, Q, kp, vp, table, 8, 16, [40, 17], OUT, pool=pool) == pkv.E_PAGE
+    assert status_of(pkv.paged_decode_attention, Q, kp, vp, table, 8, 32, [40, 16], OUT, pool=pool) == pkv.E_LAYOUT
+    assert status_of(pkv.paged_decode_attention, Q, kp, vp, table, 8, 16, [129, 16], OUT) == pkv.E_CAPACITY
+
+
+# --------------------------------------------------------------------------- sampling
+@pytest.mark.parametrize("T", [-1.0, float("nan"), float("-inf")])
+def test_sample_rejects_bad_temperature(T):
+    logits = R(FAKE, pkv.F32, [4, 1000])
+    ids = R(FAKE + 0x100000, pkv.I64, [4])
+    ws = R(FAKE + 0x200000, pkv.U8, [pkv.sample_workspace_size(4, 1000)])
+    assert status_of(pkv.sample, logits, T, 0, ids, ws) == pkv.E_ARG
+
+
+def test_sample_shape_errors():
+    ids = R(FAKE + 0x100000, pkv.I64, [4])
+    ws = R(FAKE + 0x200000, pkv.U8, [pkv.sample_workspace_size(4, 1000)])
+    assert status_of(pkv.sample, R(FAKE, pkv.I32, [4, 1000]), 0.0, 0, ids, ws) == pkv.E_DTYPE
+    assert status_of(pkv.sample, R(FAKE, pkv.F32, [4000]), 0.0, 0, ids, ws) == pkv.E_LAYOUT
+    assert status_of(pkv.sample, R(FAKE, pkv.F32, [4, 1000]), 0.0, 0, ids, None) == pkv.E_NOMEM
+
+
+def test_one_hip_runtime_in_the_process():
+    """libpkv must run on torch's HIP runtime: a second runtime would not share torch's streams."""
+    maps = open("/proc/self/maps").read()
+    libs = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln and "/" in ln}
+    assert len(libs) == 1, libs

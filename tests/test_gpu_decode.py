@@ -1,0 +1,286 @@
+"""GPU parity of decode attention (contiguous, paged bf16, generic paths, INT4)
+against the float64 oracle, the tiny stateful == stateless fixture, and the
+invariances the method implies (split count, page order, layout)."""
+import numpy as np
+import pytest
+import torch
+
+import place_persistent_kv_amd as pkv
+import synth
+from oracle import affine as oaffine
+from oracle import attention as oattn
+from oracle import cache as ocache
+from oracle import numeric as onum
+from oracle import stateless as ostate
+from synth import workloads
+from tests.gpu_util import DEV, bf16_dev, bits_host, rel_err_rows, require_gpu, workspace
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "int4": 1e-3}
+
+
+def _out_f64(out: torch.Tensor) -> np.ndarray:
+    if out.dtype == torch.bfloat16:
+        return onum.bf16_to_f64(bits_host(out))
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+def test_tiny_fixture_stateful_equals_stateless():
+    """1-token prompt + 15 appends into capacity 16, attention after each, then the overflow step."""
+    require_gpu()
+    w = workloads.tiny()
+    q, k, v = w["q"], w["k"], w["v"]
+    cap = w["capacity"]
+    ref = ostate.stateless_decode(q[:cap].astype(np.float64), k[:cap].astype(np.float64), v[:cap].astype(np.float64))
+    kc = torch.zeros((1, 1, cap, 4), device=DEV)
+    vc = torch.zeros((1, 1, cap, 4), device=DEV)
+    ws = workspace(pkv.decode_workspace_size(1, 1, 1, 4, cap))
+    out = torch.empty((1, 1, 1, 4), device=DEV)
+    with pkv.bind_writable(kc), pkv.bind_writable(vc):
+        for t in range(cap):
+            kt = torch.from_numpy(k[t]).reshape(1, 1, 1, 4).to(DEV)
+            vt = torch.from_numpy(v[t]).reshape(1, 1, 1, 4).to(DEV)
+            assert pkv.cache_update(kc, kt, [t], 1) == kc.data_ptr()
+            assert pkv.cache_update(vc, vt, [t], 1) == vc.data_ptr()
+            pkv.decode_attention(torch.from_numpy(q[t]).reshape(1, 1, 1, 4).to(DEV), kc, vc, [t + 1], out, ws)
+            assert rel_err_rows(_out_f64(out), ref[t][None]) <= TOL["f32"], t
+            # retained logical bytes grow by exactly one 16-byte row per tensor per step
+            assert kc[:, :, :t + 1].numel() * 4 == 16 * (t + 1)
+        before = (kc.clone(), vc.clone())
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.cache_update(kc, torch.from_numpy(k[cap]).reshape(1, 1, 1, 4).to(DEV), [cap], 1)
+        assert e.value.status == pkv.E_CAPACITY
+        assert torch.equal(kc, before[0]) and torch.equal(vc, before[1])
+
+
+def _contig_inputs(seed, B, Hq, Hkv, D, cap, lengths, kind="bf16"):
+    g = synth.rng(seed)
+    if kind == "bf16":
+        kb = synth.f32_to_bf16_bits(synth.normal(g, (B, Hkv, cap, D)))
+        vb = synth.f32_to_bf16_bits(synth.normal(g, (B, Hkv, cap, D)))
+        qb = synth.f32_to_bf16_bits(synth.normal(g, (B, Hq, D)))
+        return (bf16_dev(qb), bf16_dev(kb), bf16_dev(vb),
+                onum.bf16_to_f64(qb), onum.bf16_to_f64(kb), onum.bf16_to_f64(vb))
+    tdt = {"f32": torch.float32, "f16": torch.float16}[kind]
+    kf, vf, qf = (synth.normal(g, s) for s in [(B, Hkv, cap, D), (B, Hkv, cap, D), (B, Hq, D)])
+    if kind == "f16":
+        kf, vf, qf = (x.astype(np.float16).astype(np.float32) for x in (kf, vf, qf))
+    dev = [torch.from_numpy(x).to(DEV).to(tdt) for x in (qf, kf, vf)]
+    return (*dev, qf.astype(np.float64), kf.astype(np.float64), vf.astype(np.float64))
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_contiguous_bf16_matches_oracle(G):
+    require_gpu()
+    B, Hkv, D, cap = 4, 2, 128, 700
+    Hq = Hkv * G
+    lengths = np.array([1, 17, 333, 700], np.int32)
+    q, kc, vc, qh, kh, vh = _contig_inputs(700 + G, B, Hq, Hkv, D, cap, lengths)
+    ref = oattn.decode_attention(qh, kh, vh, lengths)
+    out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, cap))
+    pkv.decode_attention(q.reshape(B, Hq, 1, D), kc, vc, lengths, out, ws)
+    assert rel_err_rows(_out_f64(out), ref) <= TOL["bf16"]
+    out32 = torch.empty((B, Hq, 1, D), dtype=torch.float32, device=DEV)
+    pkv.decode_attention(q.reshape(B, Hq, 1, D), kc, vc, lengths, out32, ws)
+    assert rel_err_rows(_out_f64(out32), ref) <= 4e-3                 # no bf16 output rounding
+
+
+def test_split_count_does_not_change_the_result():
+    require_gpu()
+    B, Hq, Hkv, D, cap = 3, 8, 2, 128, 2000
+    lengths = np.array([2000, 1003, 64], np.int32)
+    q, kc, vc, qh, kh, vh = _contig_inputs(710, B, Hq, Hkv, D, cap, lengths)
+    ref = oattn.decode_attention(qh, kh, vh, lengths)
+    outs = []
+    for S in [1, 2, 7, 16, 64, 0]:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+        ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, cap, S))
+        pkv.decode_attention(q, kc, vc, lengths, out, ws, num_splits=S)
+        got = _out_f64(out)
+        assert rel_err_rows(got, ref) <= 4e-3, S
+        outs.append(got)
+    for got in outs[1:]:
+        assert rel_err_rows(got, outs[0]) <= 1e-5
+
+
+def _encode(x32, kind):
+    """float32 draws -> (storage array, exact float64 values) for the given element type."""
+    if kind == "bf16":
+        bits = synth.f32_to_bf16_bits(x32)
+        return bits, onum.bf16_to_f64(bits)
+    if kind == "f16":
+        bits = synth.f16_bits(x32)
+        return bits, onum.f16_to_f64(bits)
+    return x32, x32.astype(np.float64)
+
+
+def _to_dev(arr, kind):
+    if kind == "bf16":
+        return bf16_dev(arr)
+    if kind == "f16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(DEV).view(torch.float16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+
+
+def _paged_inputs(seed, B, Hq, Hkv, D, bs, lengths, maxb, extra_blocks=3, order=None, kind="bf16"):
+    """Logical rows on the host, laid out through the oracle pool; the library pool writes the device table."""
+    g = synth.rng(seed)
+    NB = int(sum(-(-int(L) // bs) for L in lengths)) + extra_blocks
+    order = synth.permutation(g, NB) if order is None else order
+    ref_pool = ocache.PagePool(NB, bs, B, maxb, order)
+    lib_pool = pkv.Pool(NB, bs, B, maxb, order)
+    table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+    lib_pool.reserve(range(B), lengths.tolist(), table)
+    k_log, v_log = [], []
+    store = np.float32 if kind == "f32" else np.uint16
+    kp = np.zeros((NB, Hkv, bs, D), store)
+    vp = np.zeros((NB, Hkv, bs, D), store)
+    for b in range(B):
+        ref_pool.reserve(b, int(lengths[b]))
+        kr, kf = _encode(synth.normal(synth.rng(seed, 1, b), (1, Hkv, int(lengths[b]), D)), kind)
+        vr, vf = _encode(synth.normal(synth.rng(seed, 2, b), (1, Hkv, int(lengths[b]), D)), kind)
+        ocache.paged_cache_update(kp, ref_pool.table[b:b + 1], kr, [0], int(lengths[b]), bs)
+        ocache.paged_cache_update(vp, ref_pool.table[b:b + 1], vr, [0], int(lengths[b]), bs)
+        k_log.append(kf[0])
+        v_log.append(vf[0])
+    assert np.array_equal(table.cpu().numpy(), ref_pool.table)
+    qs, qh = _encode(synth.normal(synth.rng(seed, 3), (B, Hq, D)), kind)
+    return dict(q=_to_dev(qs, kind), qh=qh, kp=_to_dev(kp, kind), vp=_to_dev(vp, kind), table=table,
+                pool=lib_pool, ref_pool=ref_pool, k_log=k_log, v_log=v_log, NB=NB, order=order,
+                kp_host=kp, vp_host=vp)
+
+
+def _paged_ref(d, lengths):
+    out = []
+    for b, L in enumerate(lengths):
+        Hq = d["qh"].shape[1]
+        G = Hq // d["k_log"][b].shape[0]
+        out.append(np.stack([oattn.attend(d["qh"][b, h], d["k_log"][b][h // G], d["v_log"][b][h // G],
+                                          1 / np.sqrt(d["qh"].shape[2])) for h in range(Hq)]))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("G,bs", [(4, 16), (2, 16), (1, 32), (8, 64)])
+def test_paged_bf16_matches_oracle(G, bs):
+    require_gpu()
+    B, Hkv, D, maxb = 6, 2, 128, 40
+    Hq = Hkv * G
+    lengths = np.array([1, 15, 16, 17, 300, 40 * bs - 3], np.int32)
+    d = _paged_inputs(720 + G, B, Hq, Hkv, D, bs, lengths, maxb)
+    ref = _paged_ref(d, lengths)
+    for S in [0, 1, 5]:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+        ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, maxb * bs, S))
+        pkv.paged_decode_attention(d["q"], d["kp"], d["vp"], d["table"], maxb, bs, lengths, out, ws,
+                                   pool=d["pool"], num_splits=S)
+        assert rel_err_rows(_out_f64(out), ref) <= TOL["bf16"], S
+
+
+def test_page_order_and_layout_do_not_change_the_bits():
+    """Two page permutations of the same logical rows, and the contiguous layout, give identical outputs."""
+    require_gpu()
+    B, Hq, Hkv, D, bs, maxb = 4, 16, 4, 128, 16, 20
+    lengths = np.array([5, 160, 233, 320], np.int32)
+    d1 = _paged_inputs(730, B, Hq, Hkv, D, bs, lengths, maxb)
+    d2 = _paged_inputs(730, B, Hq, Hkv, D, bs, lengths, maxb, order=d1["order"][::-1].copy())
+    assert not np.array_equal(d1["ref_pool"].table, d2["ref_pool"].table)
+    cap = maxb * bs
+    kc = np.zeros((B, Hkv, cap, D), np.uint16)
+    vc = np.zeros((B, Hkv, cap, D), np.uint16)
+    for b in range(B):
+        L = int(lengths[b])
+        kc[b, :, :L] = ocache.paged_gather(d1["kp_host"], d1["ref_pool"].table[b], L, bs)
+        vc[b, :, :L] = ocache.paged_gather(d1["vp_host"], d1["ref_pool"].table[b], L, bs)
+    outs = []
+    for S in [0, 3]:
+        ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, cap, S))
+        res = []
+        for d in (d1, d2):
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+            pkv.paged_decode_attention(d["q"], d["kp"], d["vp"], d["table"], maxb, bs, lengths, out, ws,
+                                       pool=d["pool"], num_splits=S)
+            res.append(_out_f64(out))
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+        pkv.decode_attention(d1["q"], bf16_dev(kc), bf16_dev(vc), lengths, out, ws, num_splits=S)
+        res.append(_out_f64(out))
+        assert np.array_equal(res[0], res[1]) and np.array_equal(res[0], res[2]), S
+        outs.append(res[0])
+    assert rel_err_rows(outs[0], _paged_ref(d1, lengths)) <= 4e-3
+
+
+@pytest.mark.parametrize("kind,D,bs,G", [("bf16", 64, 16, 4), ("bf16", 128, 8, 4), ("f32", 32, 16, 2),
+                                         ("f16", 128, 16, 4), ("bf16", 128, 16, 3), ("f32", 256, 4, 1)])
+def test_generic_paths_match_oracle(kind, D, bs, G):
+    require_gpu()
+    B, Hkv, maxb = 3, 2, 80
+    Hq = Hkv * G
+    cap = 250
+    lengths = np.array([1, 129, 250], np.int32)
+    tol = TOL["f32"] if kind == "f32" else TOL["bf16"]
+    q, kc, vc, qh, kh, vh = _contig_inputs(740 + D + bs, B, Hq, Hkv, D, cap, lengths, kind)
+    ref = oattn.decode_attention(qh, kh, vh, lengths)
+    out = torch.empty((B, Hq, D), dtype=q.dtype, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, cap))
+    pkv.decode_attention(q, kc, vc, lengths, out, ws)
+    torch.cuda.synchronize()
+    assert rel_err_rows(out.double().cpu().numpy(), ref) <= tol
+    d = _paged_inputs(741 + D + bs, B, Hq, Hkv, D, bs, lengths, maxb, kind=kind)
+    out = torch.empty((B, Hq, D), dtype=q.dtype, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, maxb * bs))
+    pkv.paged_decode_attention(d["q"], d["kp"], d["vp"], d["table"], maxb, bs, lengths, out, ws, pool=d["pool"])
+    torch.cuda.synchronize()
+    assert rel_err_rows(out.double().cpu().numpy(), _paged_ref(d, lengths)) <= tol
+
+
+def test_int4_paged_decode_matches_oracle():
+    require_gpu()
+    B, Hq, Hkv, D, bs, maxb = 4, 8, 2, 128, 16, 30
+    lengths = np.array([1, 16, 250, 480], np.int32)
+    g = synth.rng(750)
+    NB = int(sum(-(-int(L) // bs) for L in lengths)) + 2
+    order = synth.permutation(g, NB)
+    ref_pool = ocache.PagePool(NB, bs, B, maxb, order)
+    lib_pool = pkv.Pool(NB, bs, B, maxb, order)
+    table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+    lib_pool.reserve(range(B), lengths.tolist(), table)
+    kc = np.zeros((NB, Hkv, bs, D // 2), np.uint8)
+    vc = np.zeros_like(kc)
+    kp = np.zeros((NB, Hkv, bs, D // 32, 2), np.uint16)
+    vp = np.zeros_like(kp)
+    k_log, v_log = [], []
+    for b in range(B):
+        L = int(lengths[b])
+        ref_pool.reserve(b, L)
+        rows = {}
+        for name, st in (("kc", 1), ("vc", 2)):
+            rows[name] = synth.rng(750, st, b).integers(0, 256, size=(1, Hkv, L, D // 2), dtype=np.uint8)
+        for name, st in (("kp", 3), ("vp", 4)):
+            gg = synth.rng(750, st, b)
+            p = np.empty((1, Hkv, L, D // 32, 2), np.uint16)
+            p[..., 0] = synth.f16_bits(synth.uniform(gg, (1, Hkv, L, D // 32), 0.01, 0.1))
+            p[..., 1] = synth.f16_bits(gg.integers(0, 16, size=(1, Hkv, L, D // 32)).astype(np.float32))
+            rows[name] = p
+        ocache.paged_cache_update(kc, ref_pool.table[b:b + 1], rows["kc"], [0], L, bs)
+        ocache.paged_cache_update(vc, ref_pool.table[b:b + 1], rows["vc"], [0], L, bs)
+        ocache.paged_cache_update(kp.reshape(NB, Hkv, bs, -1), ref_pool.table[b:b + 1],
+                                  rows["kp"].reshape(1, Hkv, L, -1), [0], L, bs)
+        ocache.paged_cache_update(vp.reshape(NB, Hkv, bs, -1), ref_pool.table[b:b + 1],
+                                  rows["vp"].reshape(1, Hkv, L, -1), [0], L, bs)
+        k_log.append(oaffine.int4_dequant_rows(rows["kc"][0], rows["kp"][0]))
+        v_log.append(oaffine.int4_dequant_rows(rows["vc"][0], rows["vp"][0]))
+    q = synth.normal(g, (B, Hq, D))
+    G = Hq // Hkv
+    ref = np.stack([np.stack([oattn.attend(q[b, h].astype(np.float64), k_log[b][h // G], v_log[b][h // G],
+                                           1 / np.sqrt(D)) for h in range(Hq)]) for b in range(B)])
+    kc_d, vc_d = torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV)
+    kp_d = torch.from_numpy(kp.view(np.int16)).to(DEV).view(torch.float16)
+    vp_d = torch.from_numpy(vp.view(np.int16)).to(DEV).view(torch.float16)
+    for S in [0, 1, 4]:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+        ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, maxb * bs, S))
+        pkv.paged_decode_attention_int4(torch.from_numpy(q).to(DEV), kc_d, kp_d, vc_d, vp_d, table, maxb, bs,
+                                        lengths, out, ws, pool=lib_pool, num_splits=S)
+        assert rel_err_rows(_out_f64(out), ref) <= TOL["int4"], S
