@@ -282,6 +282,23 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
                                            size_t workspace_bytes, int32_t num_splits,
                                            void* stream);
 
+/* Causal chunk attention after a chunk of C tokens was appended at position
+ * p0[b] (host int32[B]) with pkv_paged_cache_update: query t of row b sits at
+ * p0[b] + t and attends keys [0, p0[b] + t] ("Persistent input/output
+ * feedback", "Optional heterogeneous paged KV", "Versioned operator schema":
+ * causal by default, unbounded left window, equal new Q/K/V lengths).
+ * q, out: bf16 [B, Hq, C, D] with D == 128 and Hq / Hkv in {1, 2, 4, 8};
+ * k_pool, v_pool: bf16 [num_blocks, Hkv, block_size, D]; page_table_dev as
+ * for pkv_paged_decode_attention.  Errors: PKV_E_CAPACITY when p0[b] < 0 or
+ * p0[b] + C exceeds max_blocks_per_seq * block_size; PKV_E_PAGE when `pool` is
+ * given and a row holds fewer than ceil((p0[b] + C) / block_size) pages.
+ * Runs on the bf16 matrix cores with fp32 accumulation; no workspace. */
+pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
+                               const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                               int32_t max_blocks_per_seq, int32_t block_size,
+                               const pkv_pool* pool, const int32_t* p0, float scale,
+                               pkv_tensor* out, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Sampling                                                                  */
 /* "Persistent input/output feedback", section "Autoregressive generation":

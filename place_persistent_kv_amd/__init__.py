@@ -98,6 +98,7 @@ _SIG = {
                                              _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_paged_decode_attention_int4": (C.c_int, [_T, _T, _T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P,
                                                   C.c_float, _T, _VP, C.c_size_t, C.c_int32, _VP]),
+    "pkv_chunk_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float, _T, _VP]),
     "pkv_sample_workspace_size": (C.c_size_t, [C.c_int32, C.c_int64]),
     "pkv_sample": (C.c_int, [_T, C.c_float, C.c_uint64, _VP, _VP, C.c_size_t, _VP]),
 }
@@ -377,6 +378,14 @@ def paged_decode_attention_int4(q, k_codes, k_params, v_codes, v_params, page_ta
         _i32_array(valid_len), float(scale), C.byref(desc(out)), _ptr(workspace),
         0 if workspace is None else _nbytes(workspace), int(num_splits), _stream(stream)),
         "pkv_paged_decode_attention_int4")
+
+
+def chunk_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, block_size: int, p0, out,
+                    pool: Optional[Pool] = None, scale: float = 0.0, stream=None) -> None:
+    _check(_lib.pkv_chunk_attention(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+                                    _ptr(page_table), int(max_blocks_per_seq), int(block_size), _pool_handle(pool),
+                                    _i32_array(p0), float(scale), C.byref(desc(out)), _stream(stream)),
+           "pkv_chunk_attention")
 
 
 # ---------------------------------------------------------------------------

@@ -919,6 +919,73 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
 }
 
 // ---------------------------------------------------------------------------
+pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
+                               const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                               int32_t max_blocks_per_seq, int32_t block_size,
+                               const pkv_pool* pool, const int32_t* p0, float scale,
+                               pkv_tensor* out, void* stream) {
+    PKV_TRY(check_tensor(q, "q", 4, 4));
+    PKV_TRY(check_tensor(out, "out", 4, 4));
+    PKV_TRY(check_tensor(k_pool, "k_pool", 4, 4));
+    PKV_TRY(check_tensor(v_pool, "v_pool", 4, 4));
+    const int64_t B = q->shape[0], Hq = q->shape[1], C = q->shape[2], D = q->shape[3];
+    if (q->dtype != PKV_BF16 || out->dtype != PKV_BF16 || k_pool->dtype != PKV_BF16 || v_pool->dtype != PKV_BF16)
+        return fail(PKV_E_DTYPE, "chunk attention: q, pools and out must be bf16");
+    for (int i = 0; i < 4; ++i) {
+        if (out->shape[i] != q->shape[i]) return fail(PKV_E_LAYOUT, "chunk attention: out must have q's shape");
+        if (v_pool->shape[i] != k_pool->shape[i]) return fail(PKV_E_LAYOUT, "chunk attention: K and V pools differ");
+    }
+    const int64_t NB = k_pool->shape[0], Hkv = k_pool->shape[1], bs = k_pool->shape[2];
+    if (k_pool->shape[3] != D) return fail(PKV_E_LAYOUT, "chunk attention: head size mismatch");
+    if (Hkv <= 0 || Hq % Hkv != 0) return fail(PKV_E_LAYOUT, "chunk attention: Hq must be a multiple of Hkv");
+    const int G = static_cast<int>(Hq / Hkv);
+    if (!chunk_supported(static_cast<int>(D), G, static_cast<int>(bs), static_cast<int>(C)))
+        return fail(PKV_E_LAYOUT, "chunk attention: needs D == 128, Hq / Hkv in {1, 2, 4, 8} and C >= 1");
+    if (!page_table_dev) return fail(PKV_E_ARG, "chunk attention: null page table");
+    if (block_size != bs) return fail(PKV_E_LAYOUT, "chunk attention: block_size != pool slot count");
+    if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "chunk attention: max_blocks_per_seq must be positive");
+    if (pool && (pool->block_size != bs || pool->num_blocks != NB || pool->maxb != max_blocks_per_seq))
+        return fail(PKV_E_LAYOUT, "chunk attention: pool handle does not match the pools");
+    if (pool && B > pool->max_seqs) return fail(PKV_E_PAGE, "chunk attention: batch larger than max_seqs");
+    if (B > 0 && !p0) return fail(PKV_E_ARG, "chunk attention: null p0");
+    const int64_t cap = int64_t(max_blocks_per_seq) * bs;
+    for (int64_t b = 0; b < B; ++b) {
+        if (p0[b] < 0 || p0[b] + C > cap)
+            return fail(PKV_E_CAPACITY, "chunk attention: row %lld: p0 %d + C %lld > %lld", (long long)b, p0[b],
+                        (long long)C, (long long)cap);
+        if (pool && ceil_div(p0[b] + C, bs) > pool->held[b])
+            return fail(PKV_E_PAGE, "chunk attention: row %lld holds fewer pages than p0 + C needs", (long long)b);
+    }
+    if (!(scale == scale) || std::isinf(scale)) return fail(PKV_E_ARG, "scale must be finite");
+    const Span os = span(out);
+    PKV_TRY(check_disjoint(q, "q", os, "out"));
+    PKV_TRY(check_disjoint(k_pool, "k_pool", os, "out"));
+    PKV_TRY(check_disjoint(v_pool, "v_pool", os, "out"));
+    if (B == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        ChunkArgs a;
+        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
+        a.q = static_cast<const uint16_t*>(q->data) + b0 * Hq * C * D;
+        a.k = static_cast<const uint16_t*>(k_pool->data);
+        a.v = static_cast<const uint16_t*>(v_pool->data);
+        a.page_table = page_table_dev + b0 * max_blocks_per_seq;
+        a.out = static_cast<uint16_t*>(out->data) + b0 * Hq * C * D;
+        a.Hq = static_cast<int32_t>(Hq);
+        a.Hkv = static_cast<int32_t>(Hkv);
+        a.C = static_cast<int32_t>(C);
+        a.bs = block_size;
+        a.maxb = max_blocks_per_seq;
+        a.row0 = static_cast<int32_t>(b0);
+        const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
+        a.scale_log2 = sc * 1.4426950408889634f;
+        for (int i = 0; i < a.rows; ++i) a.p0[i] = p0[b0 + i];
+        PKV_HIP(launch_chunk(a, G, s), "chunk attention launch");
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
 namespace {
 
 struct SamplePlan {

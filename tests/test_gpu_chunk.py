@@ -1,0 +1,105 @@
+"""GPU parity of the chunked in-place append + causal chunk attention (MFMA)
+against the float64 oracle, and its reduction to single-token decode."""
+import numpy as np
+import pytest
+import torch
+
+import place_persistent_kv_amd as pkv
+import synth
+from oracle import attention as oattn
+from oracle import cache as ocache
+from oracle import numeric as onum
+from tests.gpu_util import DEV, bf16_dev, bits_host, rel_err_rows, require_gpu, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(seed, B, Hq, Hkv, D, bs, p0, C, maxb):
+    """Prefix of p0[b] tokens already in the pages; returns device state and the host mirror."""
+    g = synth.rng(seed)
+    NB = int(sum(-(-(int(x) + C) // bs) for x in p0)) + 2
+    order = synth.permutation(g, NB)
+    ref_pool = ocache.PagePool(NB, bs, B, maxb, order)
+    lib_pool = pkv.Pool(NB, bs, B, maxb, order)
+    table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+    kp = np.zeros((NB, Hkv, bs, D), np.uint16)
+    vp = np.zeros_like(kp)
+    for b in range(B):
+        ref_pool.reserve(b, int(p0[b]) + C)
+        L = int(p0[b])
+        if L:
+            kr = synth.f32_to_bf16_bits(synth.normal(synth.rng(seed, 1, b), (1, Hkv, L, D)))
+            vr = synth.f32_to_bf16_bits(synth.normal(synth.rng(seed, 2, b), (1, Hkv, L, D)))
+            ocache.paged_cache_update(kp, ref_pool.table[b:b + 1], kr, [0], L, bs)
+            ocache.paged_cache_update(vp, ref_pool.table[b:b + 1], vr, [0], L, bs)
+    lib_pool.reserve(range(B), (np.asarray(p0) + C).tolist(), table)
+    assert np.array_equal(table.cpu().numpy(), ref_pool.table)
+    new_k = synth.f32_to_bf16_bits(synth.normal(synth.rng(seed, 3), (B, Hkv, C, D)))
+    new_v = synth.f32_to_bf16_bits(synth.normal(synth.rng(seed, 4), (B, Hkv, C, D)))
+    q = synth.f32_to_bf16_bits(synth.normal(synth.rng(seed, 5), (B, Hq, C, D)))
+    return dict(kp=kp, vp=vp, kd=bf16_dev(kp), vd=bf16_dev(vp), table=table, lib_pool=lib_pool,
+                ref_pool=ref_pool, new_k=new_k, new_v=new_v, q=q)
+
+
+@pytest.mark.parametrize("G,C,bs", [(2, 100, 16), (1, 64, 16), (4, 7, 16), (8, 130, 32), (2, 1, 16), (2, 300, 8)])
+def test_chunk_append_and_causal_attention_match_oracle(G, C, bs):
+    require_gpu()
+    B, Hkv, D = 3, 2, 128
+    Hq = Hkv * G
+    p0 = np.array([0, 37, 200], np.int32)
+    maxb = -(-(int(p0.max()) + C) // bs) + 1
+    d = _setup(900 + G + C, B, Hq, Hkv, D, bs, p0, C, maxb)
+    with pkv.bind_writable(d["kd"]), pkv.bind_writable(d["vd"]):
+        pkv.paged_cache_update(d["lib_pool"], d["kd"], d["table"], bf16_dev(d["new_k"]), p0, C)
+        pkv.paged_cache_update(d["lib_pool"], d["vd"], d["table"], bf16_dev(d["new_v"]), p0, C)
+    ocache.paged_cache_update(d["kp"], d["ref_pool"].table, d["new_k"], p0, C, bs, d["ref_pool"].held)
+    ocache.paged_cache_update(d["vp"], d["ref_pool"].table, d["new_v"], p0, C, bs, d["ref_pool"].held)
+    assert np.array_equal(bits_host(d["kd"]), d["kp"]) and np.array_equal(bits_host(d["vd"]), d["vp"])
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    pkv.chunk_attention(bf16_dev(d["q"]), d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"])
+    got = onum.bf16_to_f64(bits_host(out))
+    qh = onum.bf16_to_f64(d["q"])
+    for b in range(B):
+        L = int(p0[b]) + C
+        K = onum.bf16_to_f64(ocache.paged_gather(d["kp"], d["ref_pool"].table[b], L, bs))
+        V = onum.bf16_to_f64(ocache.paged_gather(d["vp"], d["ref_pool"].table[b], L, bs))
+        ref = oattn.chunk_attention(qh[b], K, V, int(p0[b]))
+        assert rel_err_rows(got[b], ref) <= 2e-2, b
+
+
+def test_last_chunk_query_equals_decode():
+    require_gpu()
+    B, Hkv, G, D, bs, C = 2, 2, 2, 128, 16, 48
+    Hq = Hkv * G
+    p0 = np.array([10, 333], np.int32)
+    maxb = 30
+    d = _setup(950, B, Hq, Hkv, D, bs, p0, C, maxb)
+    with pkv.bind_writable(d["kd"]), pkv.bind_writable(d["vd"]):
+        pkv.paged_cache_update(d["lib_pool"], d["kd"], d["table"], bf16_dev(d["new_k"]), p0, C)
+        pkv.paged_cache_update(d["lib_pool"], d["vd"], d["table"], bf16_dev(d["new_v"]), p0, C)
+    q = bf16_dev(d["q"])
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"])
+    dec = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    lens = (p0 + C).tolist()
+    pkv.paged_decode_attention(q[:, :, -1, :].contiguous(), d["kd"], d["vd"], d["table"], maxb, bs, lens, dec,
+                               workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, maxb * bs)), pool=d["lib_pool"])
+    torch.cuda.synchronize()
+    last = onum.bf16_to_f64(bits_host(out[:, :, -1, :].contiguous()))
+    assert rel_err_rows(last, dec.double().cpu().numpy()) <= 2e-2
+
+
+def test_chunk_capacity_and_page_errors():
+    require_gpu()
+    B, Hkv, D, bs, C = 1, 1, 128, 16, 20
+    d = _setup(960, B, 2, Hkv, D, bs, np.array([5], np.int32), C, 2)
+    out = torch.empty((B, 2, C, D), dtype=torch.bfloat16, device=DEV)
+    q = bf16_dev(d["q"])
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], 2, bs, [13], out, pool=d["lib_pool"])
+    assert e.value.status == pkv.E_CAPACITY
+    small = pkv.Pool(d["lib_pool"].num_blocks, bs, 1, 2)
+    small.reserve([0], [16])
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], 2, bs, [5], out, pool=small)
+    assert e.value.status == pkv.E_PAGE
