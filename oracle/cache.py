@@ -78,9 +78,8 @@ def cache_update(cache: np.ndarray, values: np.ndarray, position, update_length:
         raise ValueError("one position per batch row")
     check_capacity(position, n, cap)
     for b in range(B):
-        for h in range(H):
-            for t in range(n):
-                cache[b, h, position[b] + t, :] = values[b, h, t, :]
+        for t in range(n):
+            cache[b, :, position[b] + t, :] = values[b, :, t, :]   # every head of the token row
     return cache
 
 
@@ -191,8 +190,7 @@ def paged_cache_update(pool: np.ndarray, page_table: np.ndarray, values: np.ndar
     for b in range(B):
         for t in range(n):
             phys, slot = physical_slot(page_table[b], int(position[b]) + t, bs)
-            for h in range(H):
-                pool[phys, h, slot, :] = values[b, h, t, :]
+            pool[phys, :, slot, :] = values[b, :, t, :]       # every head of the token row
     return pool
 
 

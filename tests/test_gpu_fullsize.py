@@ -1,0 +1,249 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench
+uses (library split choice, full pools), on sampled rows the oracle computes
+one by one.
+
+Large K/V pools are drawn on the device with a seeded torch generator; the
+pages of the sampled rows are read back as oracle inputs before any library
+kernel touches them.  The page tables are checked bit for bit against the
+oracle's pool on the same hand-out order."""
+import numpy as np
+import pytest
+import torch
+
+import place_persistent_kv_amd as pkv
+import synth
+from oracle import affine as oaffine
+from oracle import attention as oattn
+from oracle import cache as ocache
+from oracle import numeric as onum
+from oracle import sampling as osamp
+from synth import workloads
+from tests.gpu_util import DEV, bf16_dev, bits_host, bytes_host, rel_err_rows, require_gpu, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _randn_bf16(shape, gen):
+    return torch.randn(shape, generator=gen, device=DEV, dtype=torch.bfloat16)
+
+
+def _pages_host(pool_dev, ids):
+    idx = torch.from_numpy(np.asarray(ids, np.int64)).to(DEV)
+    return bits_host(pool_dev.index_select(0, idx).contiguous())
+
+
+def _paged_decode_case(spec, seed, rows_to_check):
+    """Append one token per row at position L-1, attend over L tokens, check sampled rows."""
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    B, Hq, Hkv, D, bs, NB, maxb = spec.B, spec.Hq, spec.Hkv, spec.D, spec.bs, spec.NB, spec.maxb
+    L = spec.lengths.astype(np.int32)
+    kd, vd = _randn_bf16((NB, Hkv, bs, D), gen), _randn_bf16((NB, Hkv, bs, D), gen)
+    q = _randn_bf16((B, Hq, D), gen)
+    nk, nv = _randn_bf16((B, Hkv, 1, D), gen), _randn_bf16((B, Hkv, 1, D), gen)
+    lib_pool = pkv.Pool(NB, bs, B, maxb, spec.order)
+    ref_pool = ocache.PagePool(NB, bs, B, maxb, spec.order)
+    table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+    lib_pool.reserve(range(B), L.tolist(), table)
+    for b in range(B):
+        ref_pool.reserve(b, int(L[b]))
+    assert np.array_equal(table.cpu().numpy(), ref_pool.table)
+    host = {}
+    for b in rows_to_check:
+        ids = ref_pool.table[b, :spec.pages(b)]
+        host[b] = (ids, _pages_host(kd, ids), _pages_host(vd, ids))
+    qh, nkh, nvh = (bits_host(x) for x in (q, nk, nv))
+
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, int(L.max())))
+    pos = (L - 1).tolist()
+    with pkv.bind_writable(kd), pkv.bind_writable(vd):
+        pkv.paged_cache_update(lib_pool, kd, table, nk, pos, 1)
+        pkv.paged_cache_update(lib_pool, vd, table, nv, pos, 1)
+    pkv.paged_decode_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, ws, pool=lib_pool)
+    got = onum.bf16_to_f64(bits_host(out))
+    G = Hq // Hkv
+    for b in rows_to_check:
+        ids, kp, vp = host[b]
+        local = np.arange(len(ids), dtype=np.int32)[None]          # the row's pages, renumbered 0..n-1
+        ocache.paged_cache_update(kp, local, nkh[b:b + 1], [int(L[b]) - 1], 1, bs)
+        ocache.paged_cache_update(vp, local, nvh[b:b + 1], [int(L[b]) - 1], 1, bs)
+        assert np.array_equal(_pages_host(kd, ids), kp) and np.array_equal(_pages_host(vd, ids), vp)
+        K = onum.bf16_to_f64(ocache.paged_gather(kp, local[0], int(L[b]), bs))
+        V = onum.bf16_to_f64(ocache.paged_gather(vp, local[0], int(L[b]), bs))
+        qb = onum.bf16_to_f64(qh[b])
+        ref = np.stack([oattn.attend(qb[h], K[h // G], V[h // G], 1 / np.sqrt(D)) for h in range(Hq)])
+        assert rel_err_rows(got[b], ref) <= 2e-2, b
+    return got
+
+
+def test_paged32k_full_size_step():
+    """The headline workload exactly as bench.py runs it: 32 x 32768 tokens, a full 65536-page pool."""
+    require_gpu()
+    spec = workloads.paged32k()
+    _paged_decode_case(spec, 3, [0, 13, 31])
+
+
+def test_paged_lognormal_full_size():
+    require_gpu()
+    spec = workloads.paged()
+    order = np.argsort(spec.lengths)
+    rows = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    _paged_decode_case(spec, 2, rows)
+
+
+def test_contiguous_full_size_32_steps():
+    """8 x 8 x 4096 x 128 bf16 caches, initial lengths U{512..4064}, 32 appends + attention each step."""
+    require_gpu()
+    w = workloads.contig()
+    B, Hq, Hkv, D, cap, S, seed = w["B"], w["Hq"], w["Hkv"], w["D"], w["cap"], w["steps"], w["seed"]
+    L0 = w["lengths"]
+    kh = np.zeros((B, Hkv, cap, D), np.uint16)
+    vh = np.zeros_like(kh)
+    for b in range(B):
+        kh[b, :, :L0[b]] = workloads.contig_cache_row(seed, 1, b, Hkv, int(L0[b]), D)
+        vh[b, :, :L0[b]] = workloads.contig_cache_row(seed, 2, b, Hkv, int(L0[b]), D)
+    kc, vc = bf16_dev(kh), bf16_dev(vh)
+    out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, cap))
+    lengths = L0.copy()
+    G = Hq // Hkv
+    with pkv.bind_writable(kc), pkv.bind_writable(vc):
+        for step in range(S):
+            qs, ks, vs = workloads.contig_step(seed, step, B, Hq, Hkv, D)
+            assert pkv.cache_update(kc, bf16_dev(ks), lengths, 1) == kc.data_ptr()
+            assert pkv.cache_update(vc, bf16_dev(vs), lengths, 1) == vc.data_ptr()
+            ocache.cache_update(kh, ks, lengths, 1)
+            ocache.cache_update(vh, vs, lengths, 1)
+            lengths = lengths + 1
+            pkv.decode_attention(bf16_dev(qs).reshape(B, Hq, 1, D), kc, vc, lengths, out, ws)
+            if step in (0, 17, S - 1):
+                got = onum.bf16_to_f64(bits_host(out))[:, :, 0]
+                qd = onum.bf16_to_f64(qs)
+                for b in range(B):
+                    K = onum.bf16_to_f64(kh[b, :, :lengths[b]])
+                    V = onum.bf16_to_f64(vh[b, :, :lengths[b]])
+                    ref = np.stack([oattn.attend(qd[b, h], K[h // G], V[h // G], 1 / np.sqrt(D)) for h in range(Hq)])
+                    assert rel_err_rows(got[b], ref) <= 2e-2, (step, b)
+    assert np.array_equal(bits_host(kc), kh) and np.array_equal(bits_host(vc), vh)   # every cache byte
+
+
+def test_int4_full_size():
+    require_gpu()
+    spec = workloads.int4()
+    B, Hq, Hkv, D, bs, NB, maxb = spec.B, spec.Hq, spec.Hkv, spec.D, spec.bs, spec.NB, spec.maxb
+    ref_pool = ocache.PagePool(NB, bs, B, maxb, spec.order)
+    lib_pool = pkv.Pool(NB, bs, B, maxb, spec.order)
+    table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+    lib_pool.reserve(range(B), spec.lengths.tolist(), table)
+    kc = np.zeros((NB, Hkv, bs, D // 2), np.uint8)
+    vc = np.zeros_like(kc)
+    kp = np.zeros((NB, Hkv, bs, D // 32, 2), np.uint16)
+    vp = np.zeros_like(kp)
+    check = [0, 17, 31]
+    logical = {}
+    for b in range(B):
+        ref_pool.reserve(b, int(spec.lengths[b]))
+        L = int(spec.lengths[b])
+        rows = (spec.codes_row(b), spec.params_row(b), spec.v_codes_row(b), spec.v_params_row(b))
+        for dst, src in zip((kc, kp.reshape(NB, Hkv, bs, -1), vc, vp.reshape(NB, Hkv, bs, -1)),
+                            (rows[0], rows[1].reshape(Hkv, L, -1), rows[2], rows[3].reshape(Hkv, L, -1))):
+            ocache.paged_cache_update(dst, ref_pool.table[b:b + 1], src[None], [0], L, bs)
+        if b in check:
+            logical[b] = (oaffine.int4_dequant_rows(rows[0], rows[1]), oaffine.int4_dequant_rows(rows[2], rows[3]))
+    assert np.array_equal(table.cpu().numpy(), ref_pool.table)
+    dev16 = lambda a: torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.float16)
+    q = spec.q_f32()
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, int(spec.lengths.max())))
+    pkv.paged_decode_attention_int4(torch.from_numpy(q).to(DEV), torch.from_numpy(kc).to(DEV), dev16(kp),
+                                    torch.from_numpy(vc).to(DEV), dev16(vp), table, maxb, bs,
+                                    spec.lengths.tolist(), out, ws, pool=lib_pool)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    G = Hq // Hkv
+    for b in check:
+        K, V = logical[b]
+        ref = np.stack([oattn.attend(q[b, h].astype(np.float64), K[h // G], V[h // G], 1 / np.sqrt(D))
+                        for h in range(Hq)])
+        assert rel_err_rows(got[b], ref) <= 1e-3, b
+
+
+def test_qwen_shaped_layer_decode_chunk_and_sampling():
+    """One of the 28 layers at full size: decode append + attention, a 512-token chunk append +
+    causal chunk attention (sampled queries), and greedy / T=0.7 sampling of [128, 151936] logits."""
+    require_gpu()
+    w = workloads.qwen()
+    B, Hq, Hkv, D, bs, C, maxb = w["B"], w["Hq"], w["Hkv"], w["D"], w["bs"], w["chunk"], w["maxb"]
+    L = w["lengths"].astype(np.int32)
+    NB = w["NB"]
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    kd, vd = _randn_bf16((NB, Hkv, bs, D), gen), _randn_bf16((NB, Hkv, bs, D), gen)
+    lib_pool = pkv.Pool(NB, bs, B, maxb, w["order"])
+    ref_pool = ocache.PagePool(NB, bs, B, maxb, w["order"])
+    table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+    lib_pool.reserve(range(B), (L + C).tolist(), table)
+    for b in range(B):
+        ref_pool.reserve(b, int(L[b]) + C)
+    assert np.array_equal(table.cpu().numpy(), ref_pool.table)
+    check = [int(np.argmin(L)), int(np.argmax(L))]
+    host = {}
+    for b in check:
+        ids = ref_pool.table[b, :-(-(int(L[b]) + C) // bs)]
+        host[b] = (ids, _pages_host(kd, ids), _pages_host(vd, ids))
+    # (i) chunk: append C tokens at p0 = L, causal attention of the C queries
+    nk, nv = _randn_bf16((B, Hkv, C, D), gen), _randn_bf16((B, Hkv, C, D), gen)
+    q = _randn_bf16((B, Hq, C, D), gen)
+    nkh, nvh, qh = bits_host(nk), bits_host(nv), bits_host(q)
+    with pkv.bind_writable(kd), pkv.bind_writable(vd):
+        pkv.paged_cache_update(lib_pool, kd, table, nk, L.tolist(), C)
+        pkv.paged_cache_update(lib_pool, vd, table, nv, L.tolist(), C)
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    pkv.chunk_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, pool=lib_pool)
+    got = onum.bf16_to_f64(bits_host(out))
+    G = Hq // Hkv
+    for b in check:
+        ids, kp, vp = host[b]
+        local = np.arange(len(ids), dtype=np.int32)[None]
+        ocache.paged_cache_update(kp, local, nkh[b:b + 1], [int(L[b])], C, bs)
+        ocache.paged_cache_update(vp, local, nvh[b:b + 1], [int(L[b])], C, bs)
+        assert np.array_equal(_pages_host(kd, ids), kp) and np.array_equal(_pages_host(vd, ids), vp)
+        K = onum.bf16_to_f64(ocache.paged_gather(kp, local[0], int(L[b]) + C, bs))
+        V = onum.bf16_to_f64(ocache.paged_gather(vp, local[0], int(L[b]) + C, bs))
+        for t in (0, 1, 255, C - 1):
+            last = int(L[b]) + t
+            qt = onum.bf16_to_f64(qh[b, :, t])
+            ref = np.stack([oattn.attend(qt[h], K[h // G, :last + 1], V[h // G, :last + 1], 1 / np.sqrt(D))
+                            for h in range(Hq)])
+            assert rel_err_rows(got[b, :, t], ref) <= 2e-2, (b, t)
+    # (ii) decode over the full prefix + chunk (L + C tokens)
+    dq = _randn_bf16((B, Hq, D), gen)
+    dout = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, int((L + C).max())))
+    pkv.paged_decode_attention(dq, kd, vd, table, maxb, bs, (L + C).tolist(), dout, ws, pool=lib_pool)
+    dgot = onum.bf16_to_f64(bits_host(dout))
+    dqh = onum.bf16_to_f64(bits_host(dq))
+    for b in check:
+        ids, kp, vp = host[b]
+        local = np.arange(len(ids), dtype=np.int32)
+        K = onum.bf16_to_f64(ocache.paged_gather(kp, local, int(L[b]) + C, bs))
+        V = onum.bf16_to_f64(ocache.paged_gather(vp, local, int(L[b]) + C, bs))
+        ref = np.stack([oattn.attend(dqh[b, h], K[h // G], V[h // G], 1 / np.sqrt(D)) for h in range(Hq)])
+        assert rel_err_rows(dgot[b], ref) <= 2e-2, b
+    # (iii) sampling of [128, 151936] logits ~ N(0, 3)
+    logits = workloads.logits(w["seed"], B, w["vocab"])
+    ld = torch.from_numpy(logits).to(DEV)
+    ids = torch.empty((B,), dtype=torch.int64, device=DEV)
+    sws = workspace(pkv.sample_workspace_size(B, w["vocab"]))
+    pkv.sample(ld, 0.0, 5, ids, sws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), osamp.greedy(logits))
+    pkv.sample(ld, 0.7, 5, ids, sws)
+    torch.cuda.synchronize()
+    got_ids = ids.cpu().numpy()
+    want = osamp.sample(logits, 0.7, 5)
+    for b in np.nonzero(got_ids != want)[0]:
+        sc = osamp.gumbel_scores(logits[b], 0.7, 5, b)
+        assert abs(sc[got_ids[b]] - sc[want[b]]) <= 1e-5 * max(1.0, abs(sc[want[b]]))
+    assert (got_ids == want).mean() >= 0.99
