@@ -32,6 +32,13 @@
 namespace pkv {
 namespace {
 
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 1
+#endif
+#ifndef PKV_DECODE_PREFETCH
+#define PKV_DECODE_PREFETCH 1
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kD = 128;
 constexpr float kLazy = 8.0f;  // rescale only when a score exceeds the running max by 2^8
@@ -98,17 +105,18 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     struct Buf {
         uint4 ka0, kb0, ka1, kb1, va0, vb0, va1, vb1;
     };
+    auto ldkv = [](const uint16_t* p) { return PKV_DECODE_NT ? ld16_nt(p) : ld16(p); };
     auto load = [&](Buf& u, int ts) {
         const int64_t o0 = row_offset(ts, ts + grp);
         const int64_t o1 = row_offset(ts, ts + 8 + grp);
-        u.ka0 = ld16(K + o0);
-        u.kb0 = ld16(K + o0 + 64);
-        u.ka1 = ld16(K + o1);
-        u.kb1 = ld16(K + o1 + 64);
-        u.va0 = ld16(V + o0);
-        u.vb0 = ld16(V + o0 + 64);
-        u.va1 = ld16(V + o1);
-        u.vb1 = ld16(V + o1 + 64);
+        u.ka0 = ldkv(K + o0);
+        u.kb0 = ldkv(K + o0 + 64);
+        u.ka1 = ldkv(K + o1);
+        u.kb1 = ldkv(K + o1 + 64);
+        u.va0 = ldkv(V + o0);
+        u.vb0 = ldkv(V + o0 + 64);
+        u.va1 = ldkv(V + o1);
+        u.vb1 = ldkv(V + o1 + 64);
     };
 
     auto compute = [&](const Buf& u, int ts) {
@@ -169,19 +177,39 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
         }
     };
 
+    // stream the wave's range 16 tokens at a time, keeping PKV_DECODE_PREFETCH
+    // steps of loads in flight ahead of the step being computed
+    constexpr int S16 = kSlabTokens;
     if (wbeg < wend) {
+#if PKV_DECODE_PREFETCH >= 2
+        Buf A, Bf, Cf;
+        load(A, wbeg);
+        if (wbeg + S16 < wend) load(Bf, wbeg + S16);
+        for (int ts = wbeg;; ts += 3 * S16) {
+            if (ts + 2 * S16 < wend) load(Cf, ts + 2 * S16);
+            compute(A, ts);
+            if (ts + S16 >= wend) break;
+            if (ts + 3 * S16 < wend) load(A, ts + 3 * S16);
+            compute(Bf, ts + S16);
+            if (ts + 2 * S16 >= wend) break;
+            if (ts + 4 * S16 < wend) load(Bf, ts + 4 * S16);
+            compute(Cf, ts + 2 * S16);
+            if (ts + 3 * S16 >= wend) break;
+        }
+#else
         Buf A, Bf;
         load(A, wbeg);
-        for (int ts = wbeg;; ts += 2 * kSlabTokens) {
-            const bool has1 = ts + kSlabTokens < wend;
-            if (has1) load(Bf, ts + kSlabTokens);
+        for (int ts = wbeg;; ts += 2 * S16) {
+            const bool has1 = ts + S16 < wend;
+            if (has1) load(Bf, ts + S16);
             compute(A, ts);
             if (!has1) break;
-            const bool has2 = ts + 2 * kSlabTokens < wend;
-            if (has2) load(A, ts + 2 * kSlabTokens);
-            compute(Bf, ts + kSlabTokens);
+            const bool has2 = ts + 2 * S16 < wend;
+            if (has2) load(A, ts + 2 * S16);
+            compute(Bf, ts + S16);
             if (!has2) break;
         }
+#endif
     }
 
     // merge the eight token groups of the wave (lanes with the same j)

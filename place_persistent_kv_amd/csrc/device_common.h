@@ -41,6 +41,15 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal: K/V rows are streamed once per call, so
+// they should not displace reusable lines in L2 / MALL.
+__device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // largest b with split_begin[b] <= r (split_begin is non-decreasing, split_begin[rows] > r)
 __device__ __forceinline__ int find_row(const int32_t* split_begin, int rows, int r) {
     int lo = 0, hi = rows;
