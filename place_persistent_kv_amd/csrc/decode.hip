@@ -35,9 +35,6 @@ namespace {
 #ifndef PKV_DECODE_NT
 #define PKV_DECODE_NT 1
 #endif
-#ifndef PKV_DECODE_PREFETCH
-#define PKV_DECODE_PREFETCH 1
-#endif
 
 constexpr int kWaves = 4;
 constexpr int kD = 128;
@@ -90,15 +87,15 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
         for (int d = 0; d < 16; ++d) o[g][d] = 0.0f;
     }
 
-    // Element offset of this lane's 8 dims (chunk A) of token t, clamped into
-    // [t_lo, t1) so that every load is a valid row of the same page.
-    auto row_offset = [&](int ts, int t) -> int64_t {
-        const int tc = min(t, t1 - 1);
+    // Element offset of the first row of the 16-token step at ts (wave-uniform):
+    // ts is a multiple of 16 and block_size a power-of-two multiple of 16, so
+    // the whole step lies in one page.
+    auto step_base = [&](int ts) -> int64_t {
         if constexpr (PAGED) {
-            const int page = pt[ts / a.bs];  // wave-uniform
-            return ((int64_t(page) * a.Hkv + kvh) * a.bs + (tc % a.bs)) * kD + j * 8;
+            const int page = pt[ts >> a.log2bs];
+            return ((int64_t(page) * a.Hkv + kvh) * a.bs + (ts & (a.bs - 1))) * kD;
         } else {
-            return ((int64_t(b) * a.Hkv + kvh) * a.cap + tc) * kD + j * 8;
+            return ((int64_t(b) * a.Hkv + kvh) * a.cap + ts) * kD;
         }
     };
 
@@ -106,17 +103,23 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
         uint4 ka0, kb0, ka1, kb1, va0, vb0, va1, vb1;
     };
     auto ldkv = [](const uint16_t* p) { return PKV_DECODE_NT ? ld16_nt(p) : ld16(p); };
+    // Lane rows are clamped to the split's last token, so a partial last step
+    // re-reads a valid row of the same page instead of leaving it.
     auto load = [&](Buf& u, int ts) {
-        const int64_t o0 = row_offset(ts, ts + grp);
-        const int64_t o1 = row_offset(ts, ts + 8 + grp);
-        u.ka0 = ldkv(K + o0);
-        u.kb0 = ldkv(K + o0 + 64);
-        u.ka1 = ldkv(K + o1);
-        u.kb1 = ldkv(K + o1 + 64);
-        u.va0 = ldkv(V + o0);
-        u.vb0 = ldkv(V + o0 + 64);
-        u.va1 = ldkv(V + o1);
-        u.vb1 = ldkv(V + o1 + 64);
+        const int64_t base = step_base(ts);
+        const int last = t1 - 1 - ts;
+        const uint32_t o0 = uint32_t(min(grp, last)) * kD + j * 8;
+        const uint32_t o1 = uint32_t(min(grp + 8, last)) * kD + j * 8;
+        const uint16_t* kb = K + base;
+        const uint16_t* vb = V + base;
+        u.ka0 = ldkv(kb + o0);
+        u.kb0 = ldkv(kb + o0 + 64);
+        u.ka1 = ldkv(kb + o1);
+        u.kb1 = ldkv(kb + o1 + 64);
+        u.va0 = ldkv(vb + o0);
+        u.vb0 = ldkv(vb + o0 + 64);
+        u.va1 = ldkv(vb + o1);
+        u.vb1 = ldkv(vb + o1 + 64);
     };
 
     auto compute = [&](const Buf& u, int ts) {
@@ -177,39 +180,30 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
         }
     };
 
-    // stream the wave's range 16 tokens at a time, keeping PKV_DECODE_PREFETCH
-    // steps of loads in flight ahead of the step being computed
-    constexpr int S16 = kSlabTokens;
+    // Stream the wave's range 16 tokens per step with the next step's loads in
+    // flight.  The two-step main loop is straight-line code whose prefetch is
+    // always valid, so the wait before each compute covers only that step's
+    // own loads; the last one or two steps are finished after it.
     if (wbeg < wend) {
-#if PKV_DECODE_PREFETCH >= 2
-        Buf A, Bf, Cf;
-        load(A, wbeg);
-        if (wbeg + S16 < wend) load(Bf, wbeg + S16);
-        for (int ts = wbeg;; ts += 3 * S16) {
-            if (ts + 2 * S16 < wend) load(Cf, ts + 2 * S16);
-            compute(A, ts);
-            if (ts + S16 >= wend) break;
-            if (ts + 3 * S16 < wend) load(A, ts + 3 * S16);
-            compute(Bf, ts + S16);
-            if (ts + 2 * S16 >= wend) break;
-            if (ts + 4 * S16 < wend) load(Bf, ts + 4 * S16);
-            compute(Cf, ts + 2 * S16);
-            if (ts + 3 * S16 >= wend) break;
-        }
-#else
+        const int nsteps = (wend - wbeg + kSlabTokens - 1) / kSlabTokens;
         Buf A, Bf;
         load(A, wbeg);
-        for (int ts = wbeg;; ts += 2 * S16) {
-            const bool has1 = ts + S16 < wend;
-            if (has1) load(Bf, ts + S16);
+        int i = 0;
+        for (; i + 2 < nsteps; i += 2) {
+            const int ts = wbeg + i * kSlabTokens;
+            load(Bf, ts + kSlabTokens);
             compute(A, ts);
-            if (!has1) break;
-            const bool has2 = ts + 2 * S16 < wend;
-            if (has2) load(A, ts + 2 * S16);
-            compute(Bf, ts + S16);
-            if (!has2) break;
+            load(A, ts + 2 * kSlabTokens);
+            compute(Bf, ts + kSlabTokens);
         }
-#endif
+        const int ts = wbeg + i * kSlabTokens;
+        if (i + 1 < nsteps) {
+            load(Bf, ts + kSlabTokens);
+            compute(A, ts);
+            compute(Bf, ts + kSlabTokens);
+        } else {
+            compute(A, ts);
+        }
     }
 
     // merge the eight token groups of the wave (lanes with the same j)
@@ -378,7 +372,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 bool fast_decode_supported(int kv_kind, int D, int G, bool paged, int bs) {
     if (kv_kind != kKvBF16 || D != kD) return false;
     if (G != 1 && G != 2 && G != 4 && G != 8) return false;
-    if (paged && (bs <= 0 || bs % kSlabTokens != 0)) return false;
+    if (paged && (bs < kSlabTokens || (bs & (bs - 1)) != 0)) return false;
     return true;
 }
 

@@ -181,7 +181,7 @@ pkv_status write_table(int32_t* table_dev, const std::vector<int32_t>& idx,
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kTargetWorkgroups = 2048;  // ~8 per CU on 256 CUs
+constexpr int kTargetWorkgroups = 1024;  // 4 per CU on 256 CUs: 2 resident x 2 rounds
 constexpr int kMinAutoTps = 256;         // tokens per split, library choice
 constexpr int kTpsQuantum = 64;          // fast kernel: 4 waves x 16 tokens
 
@@ -739,6 +739,8 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         a.cap = static_cast<int32_t>(paged ? 0 : cap);
         a.bs = paged ? bs : 0;
         a.maxb = paged ? maxb : 0;
+        a.log2bs = 0;
+        while (paged && (1 << a.log2bs) < bs) ++a.log2bs;
         a.S_max = full.S_max;
         a.tps = full.tps;
         a.row0 = static_cast<int32_t>(b0);
@@ -832,8 +834,8 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
     const int G = static_cast<int>(Hq / Hkv);
     if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_E_LAYOUT, "int4 decode: Hq / Hkv must be 1, 2, 4 or 8");
     if (!page_table_dev) return fail(PKV_E_ARG, "int4 decode: null page table");
-    if (block_size != bs || bs % kSlabTokens != 0)
-        return fail(PKV_E_LAYOUT, "int4 decode: block_size must equal the pool's and be a multiple of %d", kSlabTokens);
+    if (block_size != bs || bs < kSlabTokens || (bs & (bs - 1)) != 0)
+        return fail(PKV_E_LAYOUT, "int4 decode: block_size must equal the pool's and be a power of two >= %d", kSlabTokens);
     if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "int4 decode: max_blocks_per_seq must be positive");
     if (num_splits < 0) return fail(PKV_E_ARG, "num_splits must be >= 0");
     if (pool && (pool->block_size != bs || pool->num_blocks != NB || pool->maxb != max_blocks_per_seq))
@@ -883,6 +885,8 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
         a.Hkv = static_cast<int32_t>(Hkv);
         a.bs = block_size;
         a.maxb = max_blocks_per_seq;
+        a.log2bs = 0;
+        while ((1 << a.log2bs) < block_size) ++a.log2bs;
         a.S_max = full.S_max;
         a.tps = full.tps;
         a.row0 = static_cast<int32_t>(b0);

@@ -86,6 +86,7 @@ struct DecodeArgs {
     int32_t Hq, Hkv, D;
     int32_t cap;                 // contiguous capacity (tokens per row)
     int32_t bs, maxb;            // paged block size, page-table row length
+    int32_t log2bs;              // log2(bs) (fast kernel: bs is a power of two >= 16)
     int32_t S_max;               // split slots per (b, h) in the workspace
     int32_t tps;                 // tokens per split
     int32_t row0, rows;          // batch rows handled by this launch
@@ -105,6 +106,7 @@ struct Int4DecodeArgs {
     float* ws_o;
     float* ws_ml;
     int32_t Hq, Hkv, bs, maxb, S_max, tps, row0, rows;
+    int32_t log2bs;
     float scale_log2;
     int32_t len[kMaxRows];
     int32_t split_begin[kMaxRows + 1];
@@ -120,7 +122,7 @@ struct MergeArgs {
     int32_t nsplit[kMaxRows];
 };
 
-// Fast path: bf16, D == 128, G in {1, 2, 4, 8}, block_size % 16 == 0 (or contiguous).
+// Fast path: bf16, D == 128, G in {1, 2, 4, 8}, block_size a power of two >= 16 (or contiguous).
 bool fast_decode_supported(int kv_kind, int D, int G, bool paged, int bs);
 hipError_t launch_decode_fast(const DecodeArgs& a, int G, int total_work, hipStream_t s);
 // Any D <= 256, f32/bf16/f16, any block size; tps <= kGenericMaxTps.
