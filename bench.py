@@ -195,6 +195,428 @@ def run_cpu_baseline(budget_s: float = 12.0):
                       f"{VOCAB} logits) in {el:.1f} s, numpy float64 with 1 BLAS thread"}
 
 
+# ---------------------------------------------------------------------------
+# Other rows of the decode path, one JSON line each (python bench.py --workload X)
+# ---------------------------------------------------------------------------
+def _timed(fn, steps, warmup, stream):
+    """Average duration (us) of fn() over `steps` calls, each bracketed by HIP events."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn(warmup + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3
+
+
+def _line(metric, value, unit, steps, warmup, us, dtype, config, roofline, cpu=None, **extra):
+    r = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+         "ms_per_step": round(us / 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+         "dtype": dtype, "data": "synthetic", "config": config, "roofline": roofline}
+    r.update(extra)
+    if cpu is not None:
+        r["cpu_baseline"] = cpu
+    return r
+
+
+def _hbm_roofline(nbytes, us):
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+
+
+def _cpu_loop(budget_s, body):
+    """Run body(i) under one BLAS thread until budget_s elapses; returns (iterations, seconds)."""
+    from threadpoolctl import threadpool_limits
+    n = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            body(n)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return n, el
+
+
+def _oracle_decode_rows(L_list, Hq, Hkv, D, budget_s, seed):
+    """Oracle attention of whole rows (all heads) of the given lengths; returns rows/s."""
+    import numpy as np
+    import synth
+    from oracle import attention
+    g = synth.rng(seed, 77)
+    Lmax = max(L_list)
+    K = synth.normal(g, (Hkv, Lmax, D)).astype(np.float64)
+    V = synth.normal(g, (Hkv, Lmax, D)).astype(np.float64)
+    q = synth.normal(g, (Hq, D)).astype(np.float64)
+    G = Hq // Hkv
+
+    def body(i):
+        L = L_list[i % len(L_list)]
+        for h in range(Hq):
+            attention.attend(q[h], K[h // G, :L], V[h // G, :L], 1.0 / np.sqrt(D))
+    n, el = _cpu_loop(budget_s, body)
+    return n / el, n, el
+
+
+def bench_contig(steps, warmup, cpu):
+    """Contiguous bf16 cache [8, 8, 4096, 128]: append one K/V row + decode attention per step.
+    Six cache replicas are rotated so that each step reads K/V from HBM, not from the 256 MB MALL."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    w = workloads.contig()
+    Bc, Hq, Hkv, Dc, cap, S = w["B"], w["Hq"], w["Hkv"], w["D"], w["cap"], w["steps"]
+    L0 = w["lengths"].astype(np.int64)
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    R = 6
+    kc = [torch.randn((Bc, Hkv, cap, Dc), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(R)]
+    vc = [torch.randn((Bc, Hkv, cap, Dc), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(R)]
+    q = torch.randn((Bc, Hq, 1, Dc), generator=gen, device=dev, dtype=torch.bfloat16)
+    nk = torch.randn((Bc, Hkv, 1, Dc), generator=gen, device=dev, dtype=torch.bfloat16)
+    nv = torch.randn((Bc, Hkv, 1, Dc), generator=gen, device=dev, dtype=torch.bfloat16)
+    out = torch.empty((Bc, Hq, 1, Dc), device=dev, dtype=torch.bfloat16)
+    ws = torch.empty(pkv.decode_workspace_size(Bc, Hq, Hkv, Dc, cap), device=dev, dtype=torch.uint8)
+    binds = [pkv.bind_writable(t) for t in kc + vc]
+    stream = torch.cuda.current_stream()
+
+    def step(i, rot=True):
+        r = i % R if rot else 0
+        pos = (L0 + i % S).tolist()
+        pkv.cache_update(kc[r], nk, pos, 1)
+        pkv.cache_update(vc[r], nv, pos, 1)
+        pkv.decode_attention(q, kc[r], vc[r], [p + 1 for p in pos], out, ws)
+
+    def attn_only(i, rot=True):
+        r = i % R if rot else 0
+        pkv.decode_attention(q, kc[r], vc[r], (L0 + i % S + 1).tolist(), out, ws)
+
+    us_step = _timed(step, steps, warmup, stream)
+    us_attn = _timed(attn_only, steps, warmup, stream)
+    us_warm = _timed(lambda i: attn_only(i, False), steps, warmup, stream)
+    for bnd in binds:
+        bnd.close()
+    mean_L = float(np.mean(L0 + (np.arange(steps) % S)[:, None] + 1))
+    nbytes = int(mean_L * Bc * Hkv * Dc * 2 * 2 + Bc * Hq * Dc * 2 * 2)
+    cpu_res = None
+    if cpu:
+        rate, n, el = _oracle_decode_rows([int(x) for x in L0 + 16], Hq, Hkv, Dc, 10.0, 1)
+        cpu_res = {"value": round(rate, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n} rows of 32-head decode attention at the workload's lengths in {el:.1f} s"}
+    return _line("decode tokens/s, contiguous bf16 GQA cache", Bc / (us_step * 1e-6), "tokens/s", steps, warmup,
+                 us_step, "bf16", {"workload": "contig", "batch": Bc, "capacity": cap, "q_heads": Hq, "kv_heads": Hkv,
+                                   "head_dim": Dc, "replicas_rotated": R},
+                 _hbm_roofline(nbytes, us_attn), cpu_res, attn_us=round(us_attn, 2),
+                 attn_us_warm=round(us_warm, 2), attn_algorithmic_bytes=nbytes)
+
+
+def bench_paged(steps, warmup, cpu):
+    """Paged bf16 pool of 65536 x 16 tokens, 64 rows with lognormal(8, 1) lengths in [16, 32768]."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    spec = workloads.paged()
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+    Bp, Hq, Hkv, Dp, bs, NBp, maxb = spec.B, spec.Hq, spec.Hkv, spec.D, spec.bs, spec.NB, spec.maxb
+    L = spec.lengths.astype(np.int64)
+    kd = torch.randn((NBp, Hkv, bs, Dp), generator=gen, device=dev, dtype=torch.bfloat16)
+    vd = torch.randn((NBp, Hkv, bs, Dp), generator=gen, device=dev, dtype=torch.bfloat16)
+    q = torch.randn((Bp, Hq, Dp), generator=gen, device=dev, dtype=torch.bfloat16)
+    nk = torch.randn((Bp, Hkv, 1, Dp), generator=gen, device=dev, dtype=torch.bfloat16)
+    nv = torch.randn((Bp, Hkv, 1, Dp), generator=gen, device=dev, dtype=torch.bfloat16)
+    out = torch.empty((Bp, Hq, Dp), device=dev, dtype=torch.bfloat16)
+    pool = pkv.Pool(NBp, bs, Bp, maxb, spec.order)
+    table = torch.full((Bp, maxb), -1, device=dev, dtype=torch.int32)
+    pool.reserve(range(Bp), L.tolist(), table)
+    ws = torch.empty(pkv.decode_workspace_size(Bp, Hq, Hkv, Dp, int(L.max())), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    bk, bv = pkv.bind_writable(kd), pkv.bind_writable(vd)
+    pos = (L - 1).tolist()
+
+    def step(i):
+        pkv.paged_cache_update(pool, kd, table, nk, pos, 1)
+        pkv.paged_cache_update(pool, vd, table, nv, pos, 1)
+        pkv.paged_decode_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, ws, pool=pool)
+
+    us_step = _timed(step, steps, warmup, stream)
+    us_attn = _timed(lambda i: pkv.paged_decode_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, ws,
+                                                          pool=pool), steps, warmup, stream)
+    bk.close()
+    bv.close()
+    nbytes = int(L.sum() * Hkv * Dp * 4 + sum(-(-int(x) // bs) for x in L) * 4 + Bp * Hq * Dp * 4)
+    cpu_res = None
+    if cpu:
+        order = np.argsort(L)
+        sample_L = [int(L[order[len(L) // 2]])]
+        rate, n, el = _oracle_decode_rows(sample_L, Hq, Hkv, Dp, 10.0, 2)
+        per_token = (1.0 / rate) * float(L.mean()) / sample_L[0]
+        cpu_res = {"value": round(1.0 / per_token, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n} median-length rows ({sample_L[0]} tokens) in {el:.1f} s, scaled to the mean length"}
+    return _line("decode tokens/s, paged bf16 GQA, lognormal contexts", Bp / (us_step * 1e-6), "tokens/s", steps,
+                 warmup, us_step, "bf16", {"workload": "paged", "batch": Bp, "num_blocks": NBp, "block_size": bs,
+                                           "q_heads": Hq, "kv_heads": Hkv, "head_dim": Dp,
+                                           "mean_ctx": round(float(L.mean()), 1), "max_ctx": int(L.max())},
+                 _hbm_roofline(nbytes, us_attn), cpu_res, attn_us=round(us_attn, 2), attn_algorithmic_bytes=nbytes)
+
+
+def bench_int4(steps, warmup, cpu):
+    """INT4 paged pool (16384 x 16 tokens), 32 rows x 8192 tokens: quantise-on-append + INT4 decode.
+    Three pool replicas are rotated (each ~288 MB, the MALL is 256 MB)."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    spec = workloads.int4()
+    dev = "cuda:0"
+    Bi, Hq, Hkv, Di, bs, NBi, maxb = spec.B, spec.Hq, spec.Hkv, spec.D, spec.bs, spec.NB, spec.maxb
+    L = spec.lengths.astype(np.int64)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    R = 3
+
+    def codes():
+        return torch.randint(0, 256, (NBi, Hkv, bs, Di // 2), generator=gen, device=dev, dtype=torch.uint8)
+
+    def params():
+        p = torch.empty((NBi, Hkv, bs, Di // 32, 2), device=dev, dtype=torch.float16)
+        p[..., 0].uniform_(0.01, 0.1, generator=gen)
+        p[..., 1].copy_(torch.randint(0, 16, p[..., 1].shape, generator=gen, device=dev).to(torch.float16))
+        return p
+    kc, kp, vc, vp = [codes() for _ in range(R)], [params() for _ in range(R)], [codes() for _ in range(R)], \
+        [params() for _ in range(R)]
+    q = torch.randn((Bi, Hq, Di), generator=gen, device=dev, dtype=torch.float32)
+    newv = torch.randn((Bi, Hkv, 1, Di), generator=gen, device=dev, dtype=torch.float32) * 0.3
+    out = torch.empty((Bi, Hq, Di), device=dev, dtype=torch.float32)
+    pool = pkv.Pool(NBi, bs, Bi, maxb, spec.order)
+    table = torch.full((Bi, maxb), -1, device=dev, dtype=torch.int32)
+    pool.reserve(range(Bi), L.tolist(), table)
+    ws = torch.empty(pkv.decode_workspace_size(Bi, Hq, Hkv, Di, int(L.max())), device=dev, dtype=torch.uint8)
+    binds = [pkv.bind_writable(t) for t in kc + kp + vc + vp]
+    stream = torch.cuda.current_stream()
+    s_bits = int(np.float16(0.05).view(np.uint16))
+    z_bits = int(np.float16(8.0).view(np.uint16))
+    pos = (L - 1).tolist()
+
+    def attn(i):
+        r = i % R
+        pkv.paged_decode_attention_int4(q, kc[r], kp[r], vc[r], vp[r], table, maxb, bs, L.tolist(), out, ws,
+                                        pool=pool)
+
+    def step(i):
+        r = i % R
+        pkv.paged_cache_update_int4(pool, kc[r], kp[r], table, newv, s_bits, z_bits, pos, 1)
+        pkv.paged_cache_update_int4(pool, vc[r], vp[r], table, newv, s_bits, z_bits, pos, 1)
+        attn(i)
+
+    us_step = _timed(step, steps, warmup, stream)
+    us_attn = _timed(attn, steps, warmup, stream)
+    for bnd in binds:
+        bnd.close()
+    nbytes = int(L.sum() * Hkv * 160 + Bi * (int(L[0]) // bs) * 4 + Bi * Hq * Di * 4 * 2)
+    cpu_res = None
+    if cpu:
+        from oracle import affine, attention
+        import synth as sy
+
+        def body(i):
+            b = i % Bi
+            K = affine.int4_dequant_rows(spec.codes_row(b), spec.params_row(b))
+            V = affine.int4_dequant_rows(spec.v_codes_row(b), spec.v_params_row(b))
+            qq = sy.normal(sy.rng(4, 6, b), (Hq, Di)).astype(np.float64)
+            for h in range(Hq):
+                attention.attend(qq[h], K[h // (Hq // Hkv)], V[h // (Hq // Hkv)], 1 / np.sqrt(Di))
+        n, el = _cpu_loop(10.0, body)
+        cpu_res = {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n} rows (8192 tokens, 32 heads, dequantise + attention) in {el:.1f} s"}
+    return _line("decode tokens/s, paged INT4 blockwise-affine GQA", Bi / (us_step * 1e-6), "tokens/s", steps, warmup,
+                 us_step, "int4/f32", {"workload": "int4", "batch": Bi, "ctx": int(L[0]), "num_blocks": NBi,
+                                       "block_size": bs, "q_heads": Hq, "kv_heads": Hkv, "head_dim": Di,
+                                       "replicas_rotated": R},
+                 _hbm_roofline(nbytes, us_attn), cpu_res, attn_us=round(us_attn, 2), attn_algorithmic_bytes=nbytes)
+
+
+def _qwen_pools(w, extra, layers, gen):
+    import torch
+    import place_persistent_kv_amd as pkv
+    dev = "cuda:0"
+    L = w["lengths"]
+    bs = w["bs"]
+    NBq = int(sum(-(-(int(x) + extra) // bs) for x in L))
+    base_k = torch.randn((NBq, w["Hkv"], bs, w["D"]), generator=gen, device=dev, dtype=torch.bfloat16)
+    base_v = torch.randn((NBq, w["Hkv"], bs, w["D"]), generator=gen, device=dev, dtype=torch.bfloat16)
+    ks, vs = [base_k], [base_v]
+    for _ in range(layers - 1):
+        ks.append(base_k.clone())
+        vs.append(base_v.clone())
+    import synth
+    pool = pkv.Pool(NBq, bs, w["B"], w["maxb"], synth.permutation(synth.rng(w["seed"], 1), NBq))
+    table = torch.full((w["B"], w["maxb"]), -1, device=dev, dtype=torch.int32)
+    pool.reserve(range(w["B"]), [int(x) + extra for x in L], table)
+    return ks, vs, pool, table, NBq
+
+
+def bench_qwen_decode(steps, warmup, cpu, layers=28):
+    """28 layers of paged bf16 caches (one shared page table), 128 rows, 16/8 heads, ctx U[1024, 16384]:
+    per layer an in-place K/V append and paged decode attention."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    w = workloads.qwen()
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    ks, vs, pool, table, NBq = _qwen_pools(w, 1, layers, gen)
+    Bq, Hq, Hkv, Dq, bs, maxb = w["B"], w["Hq"], w["Hkv"], w["D"], w["bs"], w["maxb"]
+    L = w["lengths"].astype(np.int64) + 1
+    q = torch.randn((Bq, Hq, Dq), generator=gen, device=dev, dtype=torch.bfloat16)
+    nk = torch.randn((Bq, Hkv, 1, Dq), generator=gen, device=dev, dtype=torch.bfloat16)
+    out = torch.empty((Bq, Hq, Dq), device=dev, dtype=torch.bfloat16)
+    ws = torch.empty(pkv.decode_workspace_size(Bq, Hq, Hkv, Dq, int(L.max())), device=dev, dtype=torch.uint8)
+    binds = [pkv.bind_writable(t) for t in ks + vs]
+    stream = torch.cuda.current_stream()
+    pos = (L - 1).tolist()
+    lens = L.tolist()
+
+    def step(i):
+        for layer in range(layers):
+            pkv.paged_cache_update(pool, ks[layer], table, nk, pos, 1)
+            pkv.paged_cache_update(pool, vs[layer], table, nk, pos, 1)
+            pkv.paged_decode_attention(q, ks[layer], vs[layer], table, maxb, bs, lens, out, ws, pool=pool)
+
+    us_step = _timed(step, steps, warmup, stream)
+    us_attn = _timed(lambda i: pkv.paged_decode_attention(q, ks[i % layers], vs[i % layers], table, maxb, bs, lens,
+                                                          out, ws, pool=pool), steps * 4, warmup, stream)
+    for bnd in binds:
+        bnd.close()
+    nbytes = int(L.sum() * Hkv * Dq * 4 + sum(-(-int(x) // bs) for x in L) * 4 + Bq * Hq * Dq * 4)
+    cpu_res = None
+    if cpu:
+        rate, n, el = _oracle_decode_rows([int(np.median(L))], Hq, Hkv, Dq, 10.0, 5)
+        cpu_res = {"value": round(rate / layers * float(np.median(L)) / float(L.mean()), 4), "unit": "tokens/s",
+                   "cores": 1, "kind": "oracle",
+                   "sample": f"{n} median-length rows of one layer in {el:.1f} s, scaled to {layers} layers"}
+    return _line("decode tokens/s, Qwen-shaped 28-layer paged bf16 step", Bq / (us_step * 1e-6), "tokens/s", steps,
+                 warmup, us_step, "bf16", {"workload": "qwen-decode", "layers": layers, "batch": Bq, "q_heads": Hq,
+                                           "kv_heads": Hkv, "head_dim": Dq, "block_size": bs,
+                                           "blocks_per_layer": NBq, "mean_ctx": round(float(L.mean()), 1)},
+                 _hbm_roofline(nbytes, us_attn), cpu_res, attn_us_per_layer=round(us_attn, 2),
+                 attn_algorithmic_bytes_per_layer=nbytes)
+
+
+def bench_qwen_chunk(steps, warmup, cpu):
+    """One layer: a 512-token chunk appended in place to 128 paged rows (prefix U[1024, 16384]) and the
+    causal chunk attention on the bf16 matrix cores."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    w = workloads.qwen()
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    C = w["chunk"]
+    ks, vs, pool, table, NBq = _qwen_pools(w, C, 1, gen)
+    Bq, Hq, Hkv, Dq, bs, maxb = w["B"], w["Hq"], w["Hkv"], w["D"], w["bs"], w["maxb"]
+    P0 = w["lengths"].astype(np.int64)
+    q = torch.randn((Bq, Hq, C, Dq), generator=gen, device=dev, dtype=torch.bfloat16)
+    nk = torch.randn((Bq, Hkv, C, Dq), generator=gen, device=dev, dtype=torch.bfloat16)
+    out = torch.empty((Bq, Hq, C, Dq), device=dev, dtype=torch.bfloat16)
+    binds = [pkv.bind_writable(t) for t in ks + vs]
+    stream = torch.cuda.current_stream()
+    p0 = P0.tolist()
+
+    def attn(i):
+        pkv.chunk_attention(q, ks[0], vs[0], table, maxb, bs, p0, out, pool=pool)
+
+    def step(i):
+        pkv.paged_cache_update(pool, ks[0], table, nk, p0, C)
+        pkv.paged_cache_update(pool, vs[0], table, nk, p0, C)
+        attn(i)
+
+    us_step = _timed(step, steps, warmup, stream)
+    us_attn = _timed(attn, steps, warmup, stream)
+    for bnd in binds:
+        bnd.close()
+    flops = 4.0 * Hq * Dq * float(np.sum(C * P0 + C * (C + 1) / 2))
+    tflops = flops / (us_attn * 1e-6) / 1e12
+    peak = 2500.0
+    cpu_res = None
+    if cpu:
+        import synth as sy
+        from oracle import attention
+        g = sy.rng(5, 78)
+        Lr = int(np.median(P0)) + C
+        K = sy.normal(g, (Hkv, Lr, Dq)).astype(np.float64)
+        V = sy.normal(g, (Hkv, Lr, Dq)).astype(np.float64)
+        qq = sy.normal(g, (Hq, Dq)).astype(np.float64)
+        done = [0.0]
+
+        def body(i):
+            t = (i * 37) % C
+            last = Lr - C + t
+            for h in range(Hq):
+                attention.attend(qq[h], K[h // 2, :last + 1], V[h // 2, :last + 1], 1 / np.sqrt(Dq))
+            done[0] += 4.0 * Hq * Dq * (last + 1)
+        n, el = _cpu_loop(10.0, body)
+        cpu_res = {"value": round(done[0] / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n} chunk queries (16 heads each) of a median row in {el:.1f} s"}
+    return _line("causal chunk attention TFLOP/s (512-token chunk, MFMA bf16)", tflops, "TFLOP/s", steps, warmup,
+                 us_step, "bf16", {"workload": "qwen-chunk", "batch": Bq, "chunk": C, "q_heads": Hq, "kv_heads": Hkv,
+                                   "head_dim": Dq, "mean_prefix": round(float(P0.mean()), 1)},
+                 {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                  "frac": round(tflops / peak, 4), "traffic": None}, cpu_res,
+                 attn_us=round(us_attn, 2), step_us=round(us_step, 2), attn_flops=flops,
+                 chunk_tokens_per_s=round(Bq * C / (us_step * 1e-6), 1))
+
+
+def bench_sample(steps, warmup, cpu):
+    """Greedy and T = 0.7 sampling of [128, 151936] float32 logits; four logit replicas are rotated
+    (78 MB each) so the reads come from HBM."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    w = workloads.qwen()
+    dev = "cuda:0"
+    Bs, Vs = w["B"], w["vocab"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    R = 4
+    lg = [torch.randn((Bs, Vs), generator=gen, device=dev) * 3.0 for _ in range(R)]
+    ids = torch.empty((Bs,), device=dev, dtype=torch.int64)
+    sws = torch.empty(pkv.sample_workspace_size(Bs, Vs), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    us_greedy = _timed(lambda i: pkv.sample(lg[i % R], 0.0, i, ids, sws), steps, warmup, stream)
+    us_temp = _timed(lambda i: pkv.sample(lg[i % R], 0.7, i, ids, sws), steps, warmup, stream)
+    nbytes = Bs * Vs * 4
+    cpu_res = None
+    if cpu:
+        from oracle import sampling
+        x = workloads.logits(5, 4, Vs)
+        n, el = _cpu_loop(10.0, lambda i: sampling.sample(x[i % 4:i % 4 + 1], 0.7, i))
+        cpu_res = {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n} rows of T=0.7 draws over {Vs} logits in {el:.1f} s"}
+    return _line("sampling tokens/s, T=0.7 over [128, 151936] logits", Bs / (us_temp * 1e-6), "tokens/s", steps,
+                 warmup, us_temp, "f32", {"workload": "sample", "batch": Bs, "vocab": Vs, "replicas_rotated": R},
+                 _hbm_roofline(nbytes, us_temp), cpu_res, greedy_us=round(us_greedy, 2),
+                 greedy_roofline=_hbm_roofline(nbytes, us_greedy), temperature_us=round(us_temp, 2))
+
+
+WORKLOADS = {"contig": bench_contig, "paged": bench_paged, "int4": bench_int4, "qwen-decode": bench_qwen_decode,
+             "qwen-chunk": bench_qwen_chunk, "sample": bench_sample}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,11 +625,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--workload", default="paged32k", choices=["paged32k", *WORKLOADS],
+                    help="paged32k (default) is the headline decode step; the others measure the other rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the decode step would shard)", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "paged32k":
+        print(json.dumps(WORKLOADS[args.workload](args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
+        return
 
     g = run_gpu(args.steps, args.warmup, args.profile_copy)
     attn_bytes = attention_algorithmic_bytes()

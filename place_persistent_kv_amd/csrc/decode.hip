@@ -36,6 +36,7 @@ namespace {
 #define PKV_DECODE_NT 1
 #endif
 
+
 constexpr int kWaves = 4;
 constexpr int kD = 128;
 constexpr float kLazy = 8.0f;  // rescale only when a score exceeds the running max by 2^8
@@ -150,17 +151,15 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
             s0[g] = live0 ? s0[g] : -INFINITY;
             s1[g] = live1 ? s1[g] : -INFINITY;
         }
+        const uint32_t w0[8] = {u.va0.x, u.va0.y, u.va0.z, u.va0.w, u.vb0.x, u.vb0.y, u.vb0.z, u.vb0.w};
+        const uint32_t w1[8] = {u.va1.x, u.va1.y, u.va1.z, u.va1.w, u.vb1.x, u.vb1.y, u.vb1.z, u.vb1.w};
         float v0[16], v1[16];
-        {
-            const uint32_t w0[8] = {u.va0.x, u.va0.y, u.va0.z, u.va0.w, u.vb0.x, u.vb0.y, u.vb0.z, u.vb0.w};
-            const uint32_t w1[8] = {u.va1.x, u.va1.y, u.va1.z, u.va1.w, u.vb1.x, u.vb1.y, u.vb1.z, u.vb1.w};
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                v0[2 * k] = bf_lo(w0[k]);
-                v0[2 * k + 1] = bf_hi(w0[k]);
-                v1[2 * k] = bf_lo(w1[k]);
-                v1[2 * k + 1] = bf_hi(w1[k]);
-            }
+        for (int k = 0; k < 8; ++k) {
+            v0[2 * k] = bf_lo(w0[k]);
+            v0[2 * k + 1] = bf_hi(w0[k]);
+            v1[2 * k] = bf_lo(w1[k]);
+            v1[2 * k + 1] = bf_hi(w1[k]);
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
