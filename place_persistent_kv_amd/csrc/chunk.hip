@@ -22,11 +22,12 @@
 //   B[k][j]: lane l holds k = 8 (l / 32) + e, j = l % 32
 //   C[i][j]: lane l, register r holds i = 8 (r / 4) + 4 (l / 32) + r % 4, j = l % 32
 //
-// Workgroup: 4 waves, 128 query rows (128 / G positions x G heads of one kv
-// head); key tiles of 64 tokens staged in LDS (K row-major, V transposed,
-// rows padded against bank conflicts), next tile prefetched into registers
-// while the current one is consumed.  Workgroups of the same (row, kv head)
-// are placed on the same XCD so they share its L2.
+// Workgroup: 4 waves, 256 query rows (256 / G positions x G heads of one kv
+// head); each wave owns two groups of 32 rows, so every K and V^T operand read
+// from LDS feeds two MFMAs.  Key tiles of 64 tokens are staged in LDS (K
+// row-major, V transposed, rows padded against bank conflicts) with the next
+// two tiles' loads in flight in registers.  Workgroups of the same (row, kv
+// head) are placed on the same XCD so they share its L2.
 
 #include "device_common.h"
 
@@ -35,9 +36,12 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kCD = 128;        // head size
-constexpr int kRows = 128;      // query rows per workgroup
+constexpr int kRowGroups = 2;   // MFMA column groups of 32 query rows per wave
+constexpr int kRows = 4 * kRowGroups * 32;  // query rows per workgroup (4 waves)
 constexpr int kKeys = 64;       // keys per tile
 constexpr int kKPad = kCD + 8;  // K row stride in LDS (bf16)
 constexpr int kVPad = kKeys + 8;  // V^T row stride in LDS (bf16)
@@ -47,7 +51,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return uint32_t(f32_to_bf16_rne(lo)) | (uint32_t(f32_to_bf16_rne(hi)) << 16);
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 template <int G>
 __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int hl = lane >> 5;     // which half of the wave
-    const int col = lane & 31;    // MFMA column = query row within the wave
+    const int col = lane & 31;    // MFMA column = query row within a row group
 
     // ---- work item: (row b, kv head, query tile), XCD-grouped when possible
     const int n_qt = (a.C + P - 1) / P;
@@ -81,179 +85,242 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
     const int t0 = qt * P;
     const int p0 = a.p0[b];
     const int32_t* pt = a.page_table + int64_t(b) * a.maxb;
-
-    // this lane's query row
-    const int r = wave * 32 + col;           // 0..127
-    const int t = t0 + r / G;                // position in the chunk
-    const int g = r % G;
-    const int h = kvh * G + g;
-    const bool row_valid = t < a.C;
-    const int limit = p0 + min(t, a.C - 1);  // last key this row attends
     const int wg_last_key = p0 + min(t0 + P, a.C) - 1;
     const int wg_first_limit = p0 + t0;      // smallest limit in the workgroup
 
+    // this lane's two query rows (row groups rg = 0, 1 of the wave)
+    int t[kRowGroups], h[kRowGroups], limit[kRowGroups];
+#pragma unroll
+    for (int rg = 0; rg < kRowGroups; ++rg) {
+        const int r = (wave * kRowGroups + rg) * 32 + col;
+        t[rg] = t0 + r / G;
+        h[rg] = kvh * G + r % G;
+        limit[rg] = p0 + min(t[rg], a.C - 1);
+    }
+
     // Q^T operand (B of S^T = K Q^T): lane holds dims 8 hl + 16 s .. +7 of its row
-    uint4 qB[8];
-    {
-        const uint16_t* Q = a.q + ((int64_t(b) * a.Hq + h) * a.C + min(t, a.C - 1)) * kCD;
+    u32x4_t qB[kRowGroups][8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) qB[s] = *reinterpret_cast<const uint4*>(Q + 16 * s + 8 * hl);
+    for (int rg = 0; rg < kRowGroups; ++rg) {
+        const uint16_t* Q = a.q + ((int64_t(b) * a.Hq + h[rg]) * a.C + min(t[rg], a.C - 1)) * kCD;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qB[rg][s] = *reinterpret_cast<const u32x4_t*>(Q + 16 * s + 8 * hl);
     }
 
-    f32x16_t o[4];
+    f32x16_t o[kRowGroups][4];
+    float m[kRowGroups], l[kRowGroups];
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
-    float m = -FLT_MAX, l = 0.0f;
-
-    // ---- global -> register staging of one 64-key tile
-    // K: thread handles 16-byte chunks c = tid + 256 i (key c / 16, dims 8 (c % 16) ..)
-    // V: thread handles dims 2 (tid % 64), 2 (tid % 64) + 1 of keys 16 (tid / 64) .. +15
-    struct Stage {
-        uint4 k[4];
-        uint32_t v[16];
-    };
-    auto key_row = [&](int key) -> int64_t {  // element offset of a key's row, key clamped to the valid range
-        const int kc = min(key, wg_last_key);
-        const int page = pt[kc / a.bs];
-        return ((int64_t(page) * a.Hkv + kvh) * a.bs + kc % a.bs) * kCD;
-    };
-    auto stage_load = [&](Stage& st, int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
-            st.k[i] = *reinterpret_cast<const uint4*>(a.k + key_row(k0 + c / 16) + 8 * (c % 16));
-        }
-        const int d2 = 2 * (tid % 64);
-        const int kb = 16 * (tid / 64);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            st.v[i] = *reinterpret_cast<const uint32_t*>(a.v + key_row(k0 + kb + i) + d2);
-    };
-    auto stage_store = [&](const Stage& st) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
-            *reinterpret_cast<uint4*>(sK + (c / 16) * kKPad + 8 * (c % 16)) = st.k[i];
-        }
-        const int d2 = 2 * (tid % 64);
-        const int kb = 16 * (tid / 64);
-        uint32_t lo[8], hi[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            // keys kb + 2i, kb + 2i + 1: low halves -> dim d2, high halves -> dim d2 + 1
-            lo[i] = __builtin_amdgcn_perm(st.v[2 * i + 1], st.v[2 * i], 0x05040100u);
-            hi[i] = __builtin_amdgcn_perm(st.v[2 * i + 1], st.v[2 * i], 0x07060302u);
-        }
-        uint4* r0 = reinterpret_cast<uint4*>(sVt + d2 * kVPad + kb);
-        uint4* r1 = reinterpret_cast<uint4*>(sVt + (d2 + 1) * kVPad + kb);
-        r0[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        r0[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
-        r1[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        r1[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
-    };
-
-    const int n_tiles = wg_last_key / kKeys + 1;
-    Stage st;
-    stage_load(st, 0);
-    for (int it = 0; it < n_tiles; ++it) {
-        const int k0 = it * kKeys;
-        __syncthreads();               // the previous tile is consumed
-        stage_store(st);
-        __syncthreads();
-        if (it + 1 < n_tiles) stage_load(st, k0 + kKeys);
-
-        // S^T for keys k0 .. k0+31 (s[0]) and k0+32 .. k0+63 (s[1])
-        f32x16_t s[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[half][e] = 0.0f;
-            const uint16_t* krow = sK + (half * 32 + col) * kKPad + 8 * hl;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const uint4 kA = *reinterpret_cast<const uint4*>(krow + 16 * ks);
-                s[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kA), as_bf16x8(qB[ks]), s[half], 0, 0, 0);
-            }
-        }
-        // scale, causal mask, tile max of this query row
-        const bool need_mask = k0 + kKeys - 1 > wg_first_limit;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float x = s[half][e] * a.scale_log2;
-                if (need_mask) {
-                    const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
-                    x = key <= limit ? x : -INFINITY;
-                }
-                s[half][e] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (mx > m + kLazyC) {
-            const float c = exp2_fast(m - mx);
-            l *= c;
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[d][e] *= c;
-            m = mx;
-        }
-        // P^T as B operands: chunk q covers keys 16 q .. 16 q + 15 of the tile,
-        // element e of this lane = register 8 (q % 2) + e of s[q / 2]
-        uint4 pB[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = exp2_fast(s[q / 2][8 * (q % 2) + e] - m);
-                l += p[e];
-            }
-            pB[q] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                               pack_bf16x2(p[6], p[7]));
-        }
-        // O^T += V^T P^T: A[i = dim][k] with the keys of chunk q taken as
-        // 16 q + 4 hl + 0..3 and 16 q + 8 + 4 hl + 0..3 (the order of pB)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint16_t* vrow = sVt + (32 * d + col) * kVPad + 4 * hl;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint2 x0 = *reinterpret_cast<const uint2*>(vrow + 16 * q);
-                const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + 16 * q + 8);
-                const uint4 vA = make_uint4(x0.x, x0.y, x1.x, x1.y);
-                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vA), as_bf16x8(pB[q]), o[d], 0, 0, 0);
-            }
-        }
-    }
-
-    // ---- normalise and store: lane holds dims 32 d + 8 (e / 4) + 4 hl + e % 4 of its row
-    l += __shfl_xor(l, 32);
-    if (row_valid) {
-        const float inv = 1.0f / l;
-        uint16_t* O = a.out + ((int64_t(b) * a.Hq + h) * a.C + t) * kCD;
+    for (int rg = 0; rg < kRowGroups; ++rg) {
+        m[rg] = -FLT_MAX;
+        l[rg] = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d)
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int dim = 32 * d + 8 * e4 + 4 * hl;
-                uint2 w;
-                w.x = pack_bf16x2(o[d][4 * e4 + 0] * inv, o[d][4 * e4 + 1] * inv);
-                w.y = pack_bf16x2(o[d][4 * e4 + 2] * inv, o[d][4 * e4 + 3] * inv);
-                *reinterpret_cast<uint2*>(O + dim) = w;
+            for (int e = 0; e < 16; ++e) o[rg][d][e] = 0.0f;
+    }
+
+    // ---- global -> register staging of one 64-key tile
+    // K: thread handles 16-byte chunks c = tid + 256 i (key c / 16, dims 8 (c % 16) ..)
+    // V: thread handles dims 8 (tid % 16) .. +7 of keys 4 (tid / 16) .. +3, which
+    //    lie in one page (block_size is a power of two >= 4)
+    // Keys past the workgroup's last key are clamped to it (valid rows, masked
+    // later).  The page ids a tile needs are loaded one tile ahead of its K/V
+    // rows, so no K/V load waits on a page-table load issued just before it.
+    struct Pages {
+        i32x4_t k;
+        int v;
+    };
+    struct Stage {
+        u32x4_t k[4];
+        u32x4_t v[4];
+    };
+    const int kb = 4 * (tid / 16);
+    const int d8 = 8 * (tid % 16);
+    auto page_load = [&](int k0) -> Pages {
+        Pages pg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pg.k[i] = pt[min(k0 + tid / 16 + 16 * i, wg_last_key) >> a.log2bs];
+        pg.v = pt[min(k0 + kb, wg_last_key) >> a.log2bs];
+        return pg;
+    };
+    auto row_of = [&](int page, int key) -> int64_t {
+        return ((int64_t(page) * a.Hkv + kvh) * a.bs + (min(key, wg_last_key) & (a.bs - 1))) * kCD;
+    };
+    auto stage_load = [&](int k0, const Pages& pg) -> Stage {
+        Stage st;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;
+            st.k[i] = *reinterpret_cast<const u32x4_t*>(a.k + row_of(pg.k[i], k0 + c / 16) + 8 * (c % 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st.v[i] = *reinterpret_cast<const u32x4_t*>(a.v + row_of(pg.v, k0 + kb + i) + d8);
+        return st;
+    };
+    auto stage_store = [&](Stage st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;
+            *reinterpret_cast<u32x4_t*>(sK + (c / 16) * kKPad + 8 * (c % 16)) = st.k[i];
+        }
+        // transpose: dim 8 (tid % 16) + 2m takes the low halves of the four keys, + 2m + 1 the high halves
+        const uint32_t w[4][4] = {{st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w},
+                                  {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w},
+                                  {st.v[2].x, st.v[2].y, st.v[2].z, st.v[2].w},
+                                  {st.v[3].x, st.v[3].y, st.v[3].z, st.v[3].w}};
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+            u32x2_t lo, hi;
+            lo.x = __builtin_amdgcn_perm(w[1][mm], w[0][mm], 0x05040100u);
+            lo.y = __builtin_amdgcn_perm(w[3][mm], w[2][mm], 0x05040100u);
+            hi.x = __builtin_amdgcn_perm(w[1][mm], w[0][mm], 0x07060302u);
+            hi.y = __builtin_amdgcn_perm(w[3][mm], w[2][mm], 0x07060302u);
+            *reinterpret_cast<u32x2_t*>(sVt + (d8 + 2 * mm) * kVPad + kb) = lo;
+            *reinterpret_cast<u32x2_t*>(sVt + (d8 + 2 * mm + 1) * kVPad + kb) = hi;
+        }
+    };
+
+    // ---- one 64-key tile from LDS, as two halves of 32 keys: S^T = K Q^T,
+    // online softmax, O^T += V^T P^T
+    auto compute = [&](int k0) {
+        const bool need_mask = k0 + kKeys - 1 > wg_first_limit;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            f32x16_t s[kRowGroups];
+#pragma unroll
+            for (int rg = 0; rg < kRowGroups; ++rg)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s[rg][e] = 0.0f;
+            const uint16_t* krow = sK + (half * 32 + col) * kKPad + 8 * hl;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const u32x4_t kA = *reinterpret_cast<const u32x4_t*>(krow + 16 * ks);
+#pragma unroll
+                for (int rg = 0; rg < kRowGroups; ++rg)
+                    s[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kA), as_bf16x8(qB[rg][ks]), s[rg],
+                                                                   0, 0, 0);
             }
+            u32x4_t pB[kRowGroups][2];
+#pragma unroll
+            for (int rg = 0; rg < kRowGroups; ++rg) {
+                // scale, causal mask, max of this query row over the 32 keys
+                float mx = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float x = s[rg][e] * a.scale_log2;
+                    if (need_mask) {
+                        const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
+                        x = key <= limit[rg] ? x : -INFINITY;
+                    }
+                    s[rg][e] = x;
+                    mx = fmaxf(mx, x);
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                if (mx > m[rg] + kLazyC) {
+                    const float c = exp2_fast(m[rg] - mx);
+                    l[rg] *= c;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) o[rg][d][e] *= c;
+                    m[rg] = mx;
+                }
+                // P^T as B operands: chunk qq covers keys 16 qq .. 16 qq + 15 of
+                // the half, element e of this lane = register 8 qq + e of s
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) {
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        p[e] = exp2_fast(s[rg][8 * qq + e] - m[rg]);
+                        l[rg] += p[e];
+                    }
+                    pB[rg][qq] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+                }
+            }
+            // O^T += V^T P^T: A[i = dim][k] with the keys of chunk qq taken as
+            // 16 qq + 4 hl + 0..3 and 16 qq + 8 + 4 hl + 0..3 (the order of pB)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint16_t* vrow = sVt + (32 * d + col) * kVPad + 32 * half + 4 * hl;
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) {
+                    const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(vrow + 16 * qq);
+                    const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(vrow + 16 * qq + 8);
+                    const u32x4_t vA = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+#pragma unroll
+                    for (int rg = 0; rg < kRowGroups; ++rg)
+                        o[rg][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vA), as_bf16x8(pB[rg][qq]),
+                                                                          o[rg][d], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Tiles go in pairs with two register stages A and B (no copies between
+    // them, so a wait is only ever for the stage about to be stored).  At a
+    // step the stage is stored to LDS, refilled with the K/V rows two tiles
+    // ahead, whose page ids were requested two steps earlier, and the ids four
+    // tiles ahead are requested.  Loads past the last tile re-read the last one
+    // (always valid); an odd tile count ends with one fully masked tile.
+    const int n_tiles = wg_last_key / kKeys + 1;
+    auto tile_key = [&](int it) { return min(it, n_tiles - 1) * kKeys; };
+    // (the prologue keeps the loop's issue order, so that the waits at the
+    // loop head are the same on entry as on every later pass)
+    Pages pgA = page_load(0);
+    Pages pgB = page_load(tile_key(1));
+    __builtin_amdgcn_sched_barrier(0);
+    Stage A = stage_load(0, pgA);
+    __builtin_amdgcn_sched_barrier(0);
+    pgA = page_load(tile_key(2));
+    __builtin_amdgcn_sched_barrier(0);
+    Stage B = stage_load(tile_key(1), pgB);
+    __builtin_amdgcn_sched_barrier(0);
+    pgB = page_load(tile_key(3));
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = 0; it < n_tiles; it += 2) {
+        __syncthreads();               // the previous tile is consumed
+        stage_store(A);
+        __syncthreads();
+        A = stage_load(tile_key(it + 2), pgA);
+        pgA = page_load(tile_key(it + 4));
+        compute(it * kKeys);
+
+        __syncthreads();
+        stage_store(B);
+        __syncthreads();
+        B = stage_load(tile_key(it + 3), pgB);
+        pgB = page_load(tile_key(it + 5));
+        compute((it + 1) * kKeys);
+    }
+
+    // ---- normalise and store: lane holds dims 32 d + 8 (e / 4) + 4 hl + e % 4 of its row
+#pragma unroll
+    for (int rg = 0; rg < kRowGroups; ++rg) {
+        const float lt = l[rg] + __shfl_xor(l[rg], 32);
+        if (t[rg] < a.C) {
+            const float inv = 1.0f / lt;
+            uint16_t* O = a.out + ((int64_t(b) * a.Hq + h[rg]) * a.C + t[rg]) * kCD;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int dim = 32 * d + 8 * e4 + 4 * hl;
+                    u32x2_t w;
+                    w.x = pack_bf16x2(o[rg][d][4 * e4 + 0] * inv, o[rg][d][4 * e4 + 1] * inv);
+                    w.y = pack_bf16x2(o[rg][d][4 * e4 + 2] * inv, o[rg][d][4 * e4 + 3] * inv);
+                    *reinterpret_cast<u32x2_t*>(O + dim) = w;
+                }
+        }
     }
 }
 
 }  // namespace
 
 bool chunk_supported(int D, int G, int bs, int C) {
-    (void)bs;
-    return D == kCD && (G == 1 || G == 2 || G == 4 || G == 8) && C >= 1;
+    return D == kCD && (G == 1 || G == 2 || G == 4 || G == 8) && bs >= 4 && C >= 1;
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s) {

@@ -944,9 +944,10 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
     if (Hkv <= 0 || Hq % Hkv != 0) return fail(PKV_E_LAYOUT, "chunk attention: Hq must be a multiple of Hkv");
     const int G = static_cast<int>(Hq / Hkv);
     if (!chunk_supported(static_cast<int>(D), G, static_cast<int>(bs), static_cast<int>(C)))
-        return fail(PKV_E_LAYOUT, "chunk attention: needs D == 128, Hq / Hkv in {1, 2, 4, 8} and C >= 1");
+        return fail(PKV_E_LAYOUT, "chunk attention: needs D == 128, Hq / Hkv in {1, 2, 4, 8}, block_size >= 4 and C >= 1");
     if (!page_table_dev) return fail(PKV_E_ARG, "chunk attention: null page table");
     if (block_size != bs) return fail(PKV_E_LAYOUT, "chunk attention: block_size != pool slot count");
+    if ((bs & (bs - 1)) != 0) return fail(PKV_E_LAYOUT, "chunk attention: block_size must be a power of two");
     if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "chunk attention: max_blocks_per_seq must be positive");
     if (pool && (pool->block_size != bs || pool->num_blocks != NB || pool->maxb != max_blocks_per_seq))
         return fail(PKV_E_LAYOUT, "chunk attention: pool handle does not match the pools");
@@ -980,6 +981,8 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
         a.C = static_cast<int32_t>(C);
         a.bs = block_size;
         a.maxb = max_blocks_per_seq;
+        a.log2bs = 0;
+        while ((1 << a.log2bs) < block_size) ++a.log2bs;
         a.row0 = static_cast<int32_t>(b0);
         const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
         a.scale_log2 = sc * 1.4426950408889634f;

@@ -141,6 +141,7 @@ struct ChunkArgs {
     const int32_t* page_table;
     uint16_t* out;               // [B, Hq, C, 128]
     int32_t Hq, Hkv, C, bs, maxb, row0, rows;
+    int32_t log2bs;              // block_size is a power of two
     float scale_log2;
     int32_t p0[kMaxRows];
 };
