@@ -47,8 +47,21 @@ constexpr int kKPad = kCD + 8;  // K row stride in LDS (bf16)
 constexpr int kVPad = kKeys + 8;  // V^T row stride in LDS (bf16)
 constexpr float kLazyC = 8.0f;
 
+// two floats -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return uint32_t(f32_to_bf16_rne(lo)) | (uint32_t(f32_to_bf16_rne(hi)) << 16);
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// the value of the lane 32 positions away, combined: lanes l and l ^ 32 hold
+// the two halves of one query row's keys (v_permlane32_swap_b32)
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -204,11 +217,12 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
             u32x4_t pB[kRowGroups][2];
 #pragma unroll
             for (int rg = 0; rg < kRowGroups; ++rg) {
-                // scale, causal mask, max of this query row over the 32 keys
+                // causal mask and max of this query row over the 32 keys, in raw
+                // score units (the scale is positive)
                 float mx = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    float x = s[rg][e] * a.scale_log2;
+                    float x = s[rg][e];
                     if (need_mask) {
                         const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
                         x = key <= limit[rg] ? x : -INFINITY;
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
                     s[rg][e] = x;
                     mx = fmaxf(mx, x);
                 }
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = max_halves(mx) * a.scale_log2;
                 if (mx > m[rg] + kLazyC) {
                     const float c = exp2_fast(m[rg] - mx);
                     l[rg] *= c;
@@ -226,6 +240,7 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
                         for (int e = 0; e < 16; ++e) o[rg][d][e] *= c;
                     m[rg] = mx;
                 }
+                const float neg_m = -m[rg];
                 // P^T as B operands: chunk qq covers keys 16 qq .. 16 qq + 15 of
                 // the half, element e of this lane = register 8 qq + e of s
 #pragma unroll
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
                     float p[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        p[e] = exp2_fast(s[rg][8 * qq + e] - m[rg]);
+                        p[e] = exp2_fast(fmaf(s[rg][8 * qq + e], a.scale_log2, neg_m));
                         l[rg] += p[e];
                     }
                     pB[rg][qq] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
@@ -299,7 +314,7 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
     // ---- normalise and store: lane holds dims 32 d + 8 (e / 4) + 4 hl + e % 4 of its row
 #pragma unroll
     for (int rg = 0; rg < kRowGroups; ++rg) {
-        const float lt = l[rg] + __shfl_xor(l[rg], 32);
+        const float lt = sum_halves(l[rg]);
         if (t[rg] < a.C) {
             const float inv = 1.0f / lt;
             uint16_t* O = a.out + ((int64_t(b) * a.Hq + h[rg]) * a.C + t[rg]) * kCD;
