@@ -1001,8 +1001,8 @@ struct SamplePlan {
 };
 
 SamplePlan plan_sample(int64_t B, int64_t V) {
-    // about 2048 workgroups in total, chunks of at least 4096 logits
-    int64_t chunks = std::max<int64_t>(1, ceil_div(2048, std::max<int64_t>(B, 1)));
+    // about 1024 workgroups in total, chunks of at least 4096 logits
+    int64_t chunks = std::max<int64_t>(1, ceil_div(1024, std::max<int64_t>(B, 1)));
     chunks = std::min<int64_t>(chunks, std::max<int64_t>(1, ceil_div(V, 4096)));
     int64_t len = ceil_div(ceil_div(V, chunks), 1024) * 1024;
     return {static_cast<int32_t>(ceil_div(V, len)), len};

@@ -17,6 +17,7 @@
 #include "pkv_internal.h"
 
 #include <float.h>
+#include <stdint.h>
 
 namespace pkv {
 namespace {
@@ -37,6 +38,17 @@ __device__ __forceinline__ float logit_at(const void* p, int64_t i) {
     else return static_cast<float>(static_cast<const _Float16*>(p)[i]);
 }
 
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
+// element e (a constant) of a 16-byte vector of logits
+template <int KIND>
+__device__ __forceinline__ float logit_of(u32x4v_t w, int e) {
+    if constexpr (KIND == kKvF32) return __uint_as_float(w[e]);
+    const uint32_t h = (e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xFFFFu);
+    if constexpr (KIND == kKvBF16) return __uint_as_float(h << 16);
+    else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
 // (score, index) order: larger score wins, equal scores -> lower index
 __device__ __forceinline__ bool better(float s, int32_t i, float bs, int32_t bi) {
     return s > bs || (s == bs && i < bi);
@@ -54,11 +66,34 @@ __device__ __forceinline__ void wave_argmax(float& s, int32_t& i) {
     }
 }
 
-template <int KIND, bool GREEDY>
-__global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs a) {
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Gumbel-perturbed score of logit x whose SplitMix64 state (seed + k * gamma)
+// is `state`: y - ln(-ln u) with y = fl32(x * invT).  Only the top 24 bits of
+// the output are used.  The logarithms are the hardware base-2 ones
+// (v_log_f32, about 1 ulp), scaled by ln 2.
+__device__ __forceinline__ float gumbel_score(float x, float inv_t, uint64_t state) {
 #pragma clang fp contract(off)
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    const uint32_t top = static_cast<uint32_t>((z ^ (z >> 31)) >> 40);
+    const float u = static_cast<float>(top | 1u) * 0x1p-24f;
+    const float e = -__builtin_amdgcn_logf(u) * kLn2;        // -ln u, an Exp(1) draw
+    const float y = x * inv_t;                                // rounded product (no contraction)
+    return y - __builtin_amdgcn_logf(e) * kLn2;
+}
+
+// One workgroup reduces one vocabulary chunk of one row to (best score,
+// index).  VEC: the row is 16-byte aligned and the chunk is read in 16-byte
+// vectors, four per thread in flight; the ragged end of the row is read per
+// element.
+template <int KIND, bool GREEDY, bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs a) {
     __shared__ float s_val[kSampleThreads / 64];
     __shared__ int32_t s_idx[kSampleThreads / 64];
+    constexpr int W = KIND == kKvF32 ? 4 : 8;   // logits per 16-byte vector
     const int b = blockIdx.y;
     const int c = blockIdx.x;
     const int64_t beg = int64_t(c) * a.chunk_len;
@@ -67,23 +102,47 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs
                                      : static_cast<const void*>(static_cast<const uint16_t*>(a.logits) + b * a.row_stride);
     float best = -INFINITY;
     int32_t bidx = INT32_MAX;
-    const uint64_t kbase = uint64_t(b) * uint64_t(a.V) + 1ull;
-    for (int64_t v = beg + threadIdx.x; v < end; v += kSampleThreads) {
-        const float x = logit_at<KIND>(row, v);
-        float s;
-        if constexpr (GREEDY) {
-            s = x;
-        } else {
-            const uint64_t h = splitmix64(a.seed, kbase + uint64_t(v));
-            const float u = static_cast<float>(static_cast<uint32_t>((h >> 40) | 1ull)) * 0x1p-24f;
-            const float y = x * a.inv_t;               // rounded product (no contraction here)
-            s = y - logf(-logf(u));
-        }
-        if (better(s, static_cast<int32_t>(v), best, bidx)) {
+    // state of logit v: seed + (b * V + v + 1) * gamma
+    const uint64_t state0 = a.seed + (uint64_t(b) * uint64_t(a.V) + 1ull) * kGamma;
+    // a thread visits its logits in increasing index order, so a strictly
+    // larger score is the only way to win (equal scores keep the lower index)
+    auto consider = [&](float x, int64_t v, uint64_t state) {
+        const float s = GREEDY ? x : gumbel_score(x, a.inv_t, state);
+        if (s > best) {
             best = s;
             bidx = static_cast<int32_t>(v);
         }
+    };
+    int64_t tail = beg;
+    if constexpr (VEC) {
+        constexpr int U = 4;                                  // vectors in flight per thread
+        const int64_t nvec = (end - beg) / W;                 // whole vectors in the chunk
+        const u32x4v_t* vp = reinterpret_cast<const u32x4v_t*>(static_cast<const uint8_t*>(row) + beg * (16 / W));
+        int64_t i = threadIdx.x;
+        for (; i + (U - 1) * kSampleThreads < nvec; i += U * kSampleThreads) {
+            u32x4v_t w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = vp[i + u * kSampleThreads];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t v0 = beg + (i + u * kSampleThreads) * W;
+                const uint64_t st = state0 + uint64_t(v0) * kGamma;
+#pragma unroll
+                for (int e = 0; e < W; ++e) consider(logit_of<KIND>(w[u], e), v0 + e, st + uint64_t(e) * kGamma);
+            }
+        }
+        for (; i < nvec; i += kSampleThreads) {
+            const u32x4v_t w0 = vp[i];
+            const int64_t v0 = beg + i * W;
+            const uint64_t st = state0 + uint64_t(v0) * kGamma;
+#pragma unroll
+            for (int e = 0; e < W; ++e) consider(logit_of<KIND>(w0, e), v0 + e, st + uint64_t(e) * kGamma);
+        }
+        tail = beg + nvec * W;
     }
+    for (int64_t v = tail + threadIdx.x; v < end; v += kSampleThreads)
+        consider(logit_at<KIND>(row, v), v, state0 + uint64_t(v) * kGamma);
+
     wave_argmax(best, bidx);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
@@ -123,14 +182,21 @@ __global__ __launch_bounds__(64) void sample_final_kernel(SampleArgs a) {
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
     if (a.B <= 0) return hipSuccess;
     const dim3 grid(a.chunks, a.B), block(kSampleThreads);
-#define PKV_SAMPLE(K)                                                                         \
-    if (a.kind == K) {                                                                        \
-        if (a.greedy) hipLaunchKernelGGL((sample_chunk_kernel<K, true>), grid, block, 0, s, a); \
-        else hipLaunchKernelGGL((sample_chunk_kernel<K, false>), grid, block, 0, s, a);        \
+    // 16-byte vectors when every row start is 16-byte aligned
+    const int esize = a.kind == kKvF32 ? 4 : 2;
+    const bool vec = reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 && (a.row_stride * esize) % 16 == 0 &&
+                     (a.chunk_len * esize) % 16 == 0;
+#define PKV_SAMPLE(K, V)                                                                           \
+    if (a.kind == K && vec == V) {                                                                 \
+        if (a.greedy) hipLaunchKernelGGL((sample_chunk_kernel<K, true, V>), grid, block, 0, s, a); \
+        else hipLaunchKernelGGL((sample_chunk_kernel<K, false, V>), grid, block, 0, s, a);        \
     }
-    PKV_SAMPLE(kKvF32)
-    PKV_SAMPLE(kKvBF16)
-    PKV_SAMPLE(kKvF16)
+    PKV_SAMPLE(kKvF32, true)
+    PKV_SAMPLE(kKvBF16, true)
+    PKV_SAMPLE(kKvF16, true)
+    PKV_SAMPLE(kKvF32, false)
+    PKV_SAMPLE(kKvBF16, false)
+    PKV_SAMPLE(kKvF16, false)
 #undef PKV_SAMPLE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
