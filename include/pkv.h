@@ -270,8 +270,9 @@ pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_p
 /* Paged INT4: K/V rows decoded in registers as (code - zero_point) * scale
  * per 32-element block ("Custom, quantized, and persistent values",
  * "Quantization examples"); never materialised.  q and out are f32
- * [B, Hq, (1,) D]; D == 128; codes/params pools as in
- * pkv_paged_cache_update_int4. */
+ * [B, Hq, (1,) D]; D == 128; Hq / Hkv in {1, 2, 4, 8}; block_size a power of
+ * two >= 16; codes/params pools as in pkv_paged_cache_update_int4, each
+ * 16-byte aligned (else PKV_E_LAYOUT). */
 pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor* k_codes,
                                            const pkv_tensor* k_params, const pkv_tensor* v_codes,
                                            const pkv_tensor* v_params,

@@ -9,12 +9,29 @@
 // attention loop, never materialised as a dense copy.
 //
 // Per (page, kv head) a token row is 64 bytes of codes + 16 bytes of
-// parameters.  Eight lanes cover one token: lane j holds dims 16j..16j+15
-// (8 code bytes, half of block j/2).  The dequantisation is folded into the
-// dot products instead of being applied per element:
-//   q . k = sum_blocks s_b * (sum_d q_d c_d - z_b * sum_d q_d)
-//   o    += p * s_b * c - p * s_b * z_b   (the second term kept per block)
-// so the codes are only converted to float (v_cvt_f32_ubyte) and fed to FMAs.
+// parameters.  A wave takes its tokens in groups of 16 (one page holds a
+// whole group: block_size is a power of two >= 16).
+//
+// Q.K on the matrix cores.  For every 32-dim block b the G query heads (rows,
+// query split into bf16 high + low parts for float32-grade products) meet the
+// raw codes of 16 tokens in v_mfma_f32_16x16x32_bf16.  A code c enters as the
+// bf16 number 128 + c, whose bit pattern is 0x4300 | c, so two codes become
+// one operand word with a shift, a mask and an or.  With qs_b = sum of q over
+// block b, the dequantised product is
+//     q . k = sum_b s_b * (S_b - (128 + z_b) * qs_b),   S_b = sum_{d in b} q_d (128 + c_d)
+// Operand layouts (checked on the device), lane l, element e = 0..7:
+//   A[i][k]: i = l % 16, k = 8 (l / 16) + e;  B[k][j]: k = 8 (l / 16) + e, j = l % 16
+//   C[i][j]: register r holds i = 4 (l / 16) + r, j = l % 16
+// so a lane ends with the scores of token l % 16 for heads 4 (l / 16) + r.
+// Within a block the dims are taken in the order the code words unpack to
+// (pair m of a word = nibbles m and m + 4); the query operand uses the same
+// order.
+//
+// P.V on the vector ALUs, the dequantisation folded in:
+//     o += p * s * c - p * s * z   (the second term kept per block)
+// with LPT lanes per token, each owning DPL dims.  The running max of every
+// head is wave-uniform (a row reduction plus v_readlane), so the lazy
+// rescale is a uniform branch and the lanes' partial outputs are plain sums.
 // The split / merge structure is that of the bf16 fast kernel.
 
 #include "device_common.h"
@@ -24,34 +41,87 @@ namespace {
 
 constexpr int kWaves4 = 4;
 constexpr int kD4 = 128;
+constexpr int kGroup = 16;       // tokens per Q.K step
 constexpr float kLazy4 = 8.0f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
-// 8 code bytes -> 16 floats in element order (even element = low nibble)
-__device__ __forceinline__ void unpack16(uint2 w, float c[16]) {
-    const uint32_t lo0 = w.x & 0x0F0F0F0Fu, hi0 = (w.x >> 4) & 0x0F0F0F0Fu;
-    const uint32_t lo1 = w.y & 0x0F0F0F0Fu, hi1 = (w.y >> 4) & 0x0F0F0F0Fu;
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+}
+
+// eight codes (one word) -> B operand: pair m = (128 + nibble m, 128 + nibble m + 4)
+__device__ __forceinline__ u32x4_t codes_operand(uint32_t w) {
+    u32x4_t r;
+    r[0] = (w & 0x000F000Fu) | 0x43004300u;
+    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    return r;
+}
+
+// all-reduce over the 16 lanes of a row
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// code bytes of one lane's dims -> floats in dim order (even dim = low nibble)
+template <int CB>
+__device__ __forceinline__ void unpack_codes(const uint32_t (&w)[(CB + 3) / 4], float (&c)[2 * CB]) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        c[2 * k] = static_cast<float>((lo0 >> (8 * k)) & 0xFFu);
-        c[2 * k + 1] = static_cast<float>((hi0 >> (8 * k)) & 0xFFu);
-        c[8 + 2 * k] = static_cast<float>((lo1 >> (8 * k)) & 0xFFu);
-        c[8 + 2 * k + 1] = static_cast<float>((hi1 >> (8 * k)) & 0xFFu);
+    for (int i = 0; i < CB / 4; ++i) {
+        const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            c[8 * i + 2 * k] = static_cast<float>((lo >> (8 * k)) & 0xFFu);
+            c[8 * i + 2 * k + 1] = static_cast<float>((hi >> (8 * k)) & 0xFFu);
+        }
     }
 }
 
 template <int G>
 __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
+    constexpr int R = G < 4 ? G : 4;            // score registers in use per lane
+    constexpr int NQ = (G + 3) / 4;             // lane quads that hold heads
+    constexpr int DPL = G <= 2 ? 32 : 64 / G;   // dims per lane in P.V
+    constexpr int LPT = kD4 / DPL;              // lanes per token in P.V
+    constexpr int TPR = 64 / LPT;               // tokens per P.V round
+    constexpr int ROUNDS = kGroup / TPR;
+    constexpr int CB = DPL / 2;                 // code bytes per lane and token
+    constexpr int CW = CB / 4;                  // code words per lane and token
+
+    __shared__ float s_p[kWaves4][kGroup][G];
     __shared__ float s_o[kWaves4][G][kD4];
     __shared__ float s_ml[kWaves4][G][2];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int grp = lane >> 3;
-    const int j = lane & 7;        // dims 16j .. 16j+15, block j/2
+    const int col = lane & 15;      // Q.K: token of the group
+    const int q4 = lane >> 4;       // Q.K: lane quad
+    const int tl = lane / LPT;      // P.V: token of the round
+    const int dc = lane % LPT;      // P.V: dims DPL * dc ..
 
     const int work = blockIdx.x;
     const int kvh = work % a.Hkv;
@@ -67,148 +137,217 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
     const int wend = min(t1, wbeg + quarter);
     const int32_t* __restrict__ pt = a.page_table + int64_t(b) * a.maxb;
 
-    float q[G][16], qsum[G];
+    // ---- query operands (rows = heads, zero rows past G), hi + lo parts
+    u32x4_t qa_hi[4], qa_lo[4];
+    {
+        const float* Q = a.q + (int64_t(b) * a.Hq + kvh * G + min(col, G - 1)) * kD4;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float* Q = a.q + (int64_t(b) * a.Hq + kvh * G + g) * kD4 + j * 16;
-        qsum[g] = 0.0f;
+        for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(Q + e);
-            q[g][e] = x.x;
-            q[g][e + 1] = x.y;
-            q[g][e + 2] = x.z;
-            q[g][e + 3] = x.w;
+            for (int m = 0; m < 4; ++m) {
+                const int d = 32 * blk + 8 * q4 + m;
+                const float x0 = col < G ? Q[d] : 0.0f, x1 = col < G ? Q[d + 4] : 0.0f;
+                const __bf16 h0 = static_cast<__bf16>(x0), h1 = static_cast<__bf16>(x1);
+                const __bf16 l0 = static_cast<__bf16>(x0 - static_cast<float>(h0));
+                const __bf16 l1 = static_cast<__bf16>(x1 - static_cast<float>(h1));
+                qa_hi[blk][m] = __builtin_bit_cast(uint32_t, bf16x2_t{h0, h1});
+                qa_lo[blk][m] = __builtin_bit_cast(uint32_t, bf16x2_t{l0, l1});
+            }
         }
+    }
+    // qs_b for the heads of this lane's score registers: the operands times ones
+    f32x4_t qs[4];
+    {
+        const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) qsum[g] += q[g][e];
+        for (int blk = 0; blk < 4; ++blk) {
+            qs[blk] = mfma16(qa_hi[blk], ones, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            qs[blk] = mfma16(qa_lo[blk], ones, qs[blk]);
+        }
     }
 
-    float m[G], l[G], o[G][16], corr[G];
+    float m[G], lp[R], o[G][DPL], corr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = -FLT_MAX;
-        l[g] = 0.0f;
         corr[g] = 0.0f;
 #pragma unroll
-        for (int d = 0; d < 16; ++d) o[g][d] = 0.0f;
+        for (int d = 0; d < DPL; ++d) o[g][d] = 0.0f;
     }
-
-    // row index (page, kvh, slot) of token t, clamped to [ts, t1)
-    auto row_of = [&](int ts, int t) -> int64_t {
-        const int tc = min(t, t1 - 1);
-        const int page = pt[ts / a.bs];
-        return (int64_t(page) * a.Hkv + kvh) * a.bs + (tc % a.bs);
-    };
-
-    struct Buf {
-        uint2 kc0, kc1, vc0, vc1;
-        uint32_t kp0, kp1, vp0, vp1;
-    };
-    auto load = [&](Buf& u, int ts) {
-        const int64_t r0 = row_of(ts, ts + grp);
-        const int64_t r1 = row_of(ts, ts + 8 + grp);
-        u.kc0 = *reinterpret_cast<const uint2*>(a.kc + r0 * 64 + j * 8);
-        u.kc1 = *reinterpret_cast<const uint2*>(a.kc + r1 * 64 + j * 8);
-        u.vc0 = *reinterpret_cast<const uint2*>(a.vc + r0 * 64 + j * 8);
-        u.vc1 = *reinterpret_cast<const uint2*>(a.vc + r1 * 64 + j * 8);
-        u.kp0 = *reinterpret_cast<const uint32_t*>(a.kp + (r0 * 4 + (j >> 1)) * 2);
-        u.kp1 = *reinterpret_cast<const uint32_t*>(a.kp + (r1 * 4 + (j >> 1)) * 2);
-        u.vp0 = *reinterpret_cast<const uint32_t*>(a.vp + (r0 * 4 + (j >> 1)) * 2);
-        u.vp1 = *reinterpret_cast<const uint32_t*>(a.vp + (r1 * 4 + (j >> 1)) * 2);
-    };
-
-    auto score = [&](uint2 codes, uint32_t par, float s[G]) {
-        float c[16];
-        unpack16(codes, c);
-        const float sc = h2f(par & 0xFFFFu), zp = h2f(par >> 16);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+    for (int i = 0; i < R; ++i) lp[i] = 0.0f;
+
+    // ---- one group's loads.  Rows past the wave's range are clamped to its
+    // last token (valid data, masked later).
+    struct Stage {
+        uint32_t kc[4];               // Q.K: code word of block b for token col
+        u32x4_t kp;                   // Q.K: (scale, zero) of the 4 blocks of token col
+        uint32_t vc[ROUNDS][CW];      // P.V: code words of this lane's dims
+        uint32_t vp[ROUNDS];          // P.V: (scale, zero) of their block
+    };
+    auto row_base = [&](int ts, int page) -> int64_t {
+        return (int64_t(page) * a.Hkv + kvh) * a.bs + (ts & (a.bs - 1));
+    };
+    auto stage_load = [&](int ts, int page) -> Stage {
+        Stage st;
+        const int64_t rb = row_base(ts, page);
+        const int last = wend - 1 - ts;
+        const int64_t rk = rb + min(col, last);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+            st.kc[blk] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.kc + rk * 64 + 16 * blk + 4 * q4));
+        st.kp = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.kp + rk * 8));
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+            const int64_t rv = rb + min(tl + TPR * rd, last);
+            const uint8_t* src = a.vc + rv * 64 + CB * dc;
+            if constexpr (CW == 4) {
+                const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st.vc[rd][i] = v[i];
+            } else if constexpr (CW == 2) {
+                const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src));
+                st.vc[rd][0] = v[0];
+                st.vc[rd][1] = v[1];
+            } else {
+                st.vc[rd][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
+            }
+            st.vp[rd] = __builtin_nontemporal_load(
+                reinterpret_cast<const uint32_t*>(a.vp + rv * 8 + 2 * ((DPL * dc) / 32)));
+        }
+        return st;
+    };
+
+    auto compute = [&](const Stage& st, int ts) {
+        // scores of token col for heads 4 q4 + i
+        f32x4_t c[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const u32x4_t kb = codes_operand(st.kc[blk]);
+            c[blk] = mfma16(qa_hi[blk], kb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            c[blk] = mfma16(qa_lo[blk], kb, c[blk]);
+        }
+        const bool live = ts + col < wend;
+        float s[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
             float acc = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc = fmaf(q[g][e], c[e], acc);
-            s[g] = group8_sum(sc * fmaf(-zp, qsum[g], acc)) * a.scale_log2;
-        }
-    };
-
-    auto compute = [&](const Buf& u, int ts) {
-        const bool live0 = ts + grp < t1;
-        const bool live1 = ts + 8 + grp < t1;
-        float s0[G], s1[G];
-        score(u.kc0, u.kp0, s0);
-        score(u.kc1, u.kp1, s1);
-        float c0[16], c1[16];
-        unpack16(u.vc0, c0);
-        unpack16(u.vc1, c1);
-        const float vs0 = h2f(u.vp0 & 0xFFFFu), vz0 = h2f(u.vp0 >> 16);
-        const float vs1 = h2f(u.vp1 & 0xFFFFu), vz1 = h2f(u.vp1 >> 16);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            s0[g] = live0 ? s0[g] : -INFINITY;
-            s1[g] = live1 ? s1[g] : -INFINITY;
-            const float mx = fmaxf(s0[g], s1[g]);
-            if (mx > m[g] + kLazy4) {
-                const float cf = exp2_fast(m[g] - mx);
-                l[g] *= cf;
-                corr[g] *= cf;
-#pragma unroll
-                for (int d = 0; d < 16; ++d) o[g][d] *= cf;
-                m[g] = mx;
+            for (int blk = 0; blk < 4; ++blk) {
+                const float sc = h2f(st.kp[blk] & 0xFFFFu);
+                const float zz = 128.0f + h2f(st.kp[blk] >> 16);
+                acc = fmaf(sc, fmaf(-zz, qs[blk][i], c[blk][i]), acc);
             }
-            const float p0 = exp2_fast(s0[g] - m[g]);
-            const float p1 = exp2_fast(s1[g] - m[g]);
-            l[g] += p0 + p1;
-            const float w0 = p0 * vs0, w1 = p1 * vs1;
-            corr[g] = fmaf(w1, vz1, fmaf(w0, vz0, corr[g]));
-#pragma unroll
-            for (int d = 0; d < 16; ++d) o[g][d] = fmaf(w1, c1[d], fmaf(w0, c0[d], o[g][d]));
+            s[i] = live ? acc * a.scale_log2 : -INFINITY;
         }
+        // group maxima per head, wave-uniform; lazy rescale
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float mx = row16_max(s[i]);
+#pragma unroll
+            for (int qq = 0; qq < NQ; ++qq) {
+                const int g = 4 * qq + i;
+                const float mg = readlane_f(mx, 16 * qq);
+                if (mg > m[g] + kLazy4) {
+                    const float cf = exp2_fast(m[g] - mg);
+                    corr[g] *= cf;
+#pragma unroll
+                    for (int d = 0; d < DPL; ++d) o[g][d] *= cf;
+                    if (q4 == qq) lp[i] *= cf;
+                    m[g] = mg;
+                }
+            }
+        }
+        // probabilities to LDS for the P.V lanes
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float mrow = (NQ > 1 && q4 == 1) ? m[(4 + i) % G] : m[i];
+            const float p = exp2_fast(s[i] - mrow);
+            lp[i] += p;
+            if (q4 < NQ) s_p[wave][col][4 * q4 + i] = p;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // P.V
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+            const int tt = tl + TPR * rd;
+            float p[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) p[g] = s_p[wave][tt][g];
+            float cv[DPL];
+            unpack_codes<CB>(st.vc[rd], cv);
+            const float vs = h2f(st.vp[rd] & 0xFFFFu), vz = h2f(st.vp[rd] >> 16);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float w = p[g] * vs;
+                corr[g] = fmaf(w, vz, corr[g]);
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(w, cv[d], o[g][d]);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
+    // Groups in pairs with two register stages (no copies between them, so a
+    // wait is only for the stage about to be used); page ids one pair ahead.
+    // Loads past the range re-read its last group; an odd group count ends
+    // with one fully masked group.
     if (wbeg < wend) {
-        Buf A, Bf;
-        load(A, wbeg);
-        for (int ts = wbeg;; ts += 2 * kSlabTokens) {
-            const bool has1 = ts + kSlabTokens < wend;
-            if (has1) load(Bf, ts + kSlabTokens);
-            compute(A, ts);
-            if (!has1) break;
-            const bool has2 = ts + 2 * kSlabTokens < wend;
-            if (has2) load(A, ts + 2 * kSlabTokens);
-            compute(Bf, ts + kSlabTokens);
-            if (!has2) break;
+        const int ng = (wend - wbeg + kGroup - 1) / kGroup;
+        auto gts = [&](int i) { return wbeg + min(i, ng - 1) * kGroup; };
+        auto page_of = [&](int i) { return pt[gts(i) >> a.log2bs]; };
+        int pgA = page_of(0), pgB = page_of(1);
+        __builtin_amdgcn_sched_barrier(0);
+        Stage A = stage_load(gts(0), pgA);
+        __builtin_amdgcn_sched_barrier(0);
+        Stage B = stage_load(gts(1), pgB);
+        __builtin_amdgcn_sched_barrier(0);
+        pgA = page_of(2);
+        pgB = page_of(3);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < ng; i += 2) {
+            compute(A, wbeg + i * kGroup);
+            A = stage_load(gts(i + 2), pgA);
+            pgA = page_of(i + 4);
+            compute(B, wbeg + (i + 1) * kGroup);
+            B = stage_load(gts(i + 3), pgB);
+            pgB = page_of(i + 5);
         }
     }
 
-    // subtract the zero-point term, then merge the eight token groups
+    // ---- finish the wave: zero-point term, sum over the token lanes, row sums of p
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int d = 0; d < 16; ++d) o[g][d] -= corr[g];
+        for (int d = 0; d < DPL; ++d) o[g][d] -= corr[g];
 #pragma unroll
-    for (int off = 8; off < 64; off <<= 1) {
+    for (int off = LPT; off < 64; off <<= 1)
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mo = __shfl_xor(m[g], off);
-            const float lo = __shfl_xor(l[g], off);
-            const float mn = fmaxf(m[g], mo);
-            const float cs = exp2_fast(m[g] - mn);
-            const float co = exp2_fast(mo - mn);
-            l[g] = l[g] * cs + lo * co;
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int d = 0; d < 16; ++d) o[g][d] = o[g][d] * cs + __shfl_xor(o[g][d], off) * co;
-            m[g] = mn;
-        }
+            for (int d = 0; d < DPL; ++d) o[g][d] += __shfl_xor(o[g][d], off);
+    float l[G];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const float rs = row16_sum(lp[i]);
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) l[4 * qq + i] = readlane_f(rs, 16 * qq);
     }
-    if (grp == 0) {
+    if (tl == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) s_o[wave][g][DPL * dc + d] = o[g][d];
+    }
+    if (lane == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int d = 0; d < 16; ++d) s_o[wave][g][j * 16 + d] = o[g][d];
-            if (j == 0) {
-                s_ml[wave][g][0] = m[g];
-                s_ml[wave][g][1] = l[g];
-            }
+            s_ml[wave][g][0] = m[g];
+            s_ml[wave][g][1] = l[g];
         }
     }
     __syncthreads();

@@ -837,6 +837,9 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
     if (block_size != bs || bs < kSlabTokens || (bs & (bs - 1)) != 0)
         return fail(PKV_E_LAYOUT, "int4 decode: block_size must equal the pool's and be a power of two >= %d", kSlabTokens);
     if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "int4 decode: max_blocks_per_seq must be positive");
+    for (const pkv_tensor* t : {k_codes, v_codes, k_params, v_params})
+        if (reinterpret_cast<uintptr_t>(t->data) % 16)
+            return fail(PKV_E_LAYOUT, "int4 decode: code and parameter pools must be 16-byte aligned");
     if (num_splits < 0) return fail(PKV_E_ARG, "num_splits must be >= 0");
     if (pool && (pool->block_size != bs || pool->num_blocks != NB || pool->maxb != max_blocks_per_seq))
         return fail(PKV_E_LAYOUT, "int4 decode: pool handle does not match the pools");

@@ -235,9 +235,11 @@ def test_generic_paths_match_oracle(kind, D, bs, G):
     assert rel_err_rows(out.double().cpu().numpy(), _paged_ref(d, lengths)) <= tol
 
 
-def test_int4_paged_decode_matches_oracle():
+@pytest.mark.parametrize("G,bs", [(1, 16), (2, 32), (4, 16), (8, 16), (4, 64)])
+def test_int4_paged_decode_matches_oracle(G, bs):
     require_gpu()
-    B, Hq, Hkv, D, bs, maxb = 4, 8, 2, 128, 16, 30
+    Hkv, D = 2, 128
+    B, Hq, maxb = 4, Hkv * G, -(-480 // bs) + 2
     lengths = np.array([1, 16, 250, 480], np.int32)
     g = synth.rng(750)
     NB = int(sum(-(-int(L) // bs) for L in lengths)) + 2
@@ -272,7 +274,6 @@ def test_int4_paged_decode_matches_oracle():
         k_log.append(oaffine.int4_dequant_rows(rows["kc"][0], rows["kp"][0]))
         v_log.append(oaffine.int4_dequant_rows(rows["vc"][0], rows["vp"][0]))
     q = synth.normal(g, (B, Hq, D))
-    G = Hq // Hkv
     ref = np.stack([np.stack([oattn.attend(q[b, h].astype(np.float64), k_log[b][h // G], v_log[b][h // G],
                                            1 / np.sqrt(D)) for h in range(Hq)]) for b in range(B)])
     kc_d, vc_d = torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV)
