@@ -31,10 +31,17 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source device flags.  The INT4 decode kernel reduces row maxima with
+# DPP; without IEEE mode (no signalling-NaN quieting) each step is a single
+# v_max_f32_dpp instead of a move plus canonicalising maxima.  Its inputs are
+# finite by construction (masked scores are -inf, never NaN).
+EXTRA = {"decode_int4.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(x for x in r.stderr.splitlines() if noise not in x)

@@ -57,13 +57,23 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                    0, 0, 0);
 }
 
-// eight codes (one word) -> B operand: pair m = (128 + nibble m, 128 + nibble m + 4)
-__device__ __forceinline__ u32x4_t codes_operand(uint32_t w) {
+// A constant in a VGPR, opaque to the optimiser, so that (x & m) | c with
+// register operands becomes one v_and_or_b32 (literal constants cannot be
+// VOP3 operands here, which would split it into an and plus an or).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "n"(c));
+    return r;
+}
+
+// eight codes (one word) -> B operand: pair m = (128 + nibble m, 128 + nibble m + 4);
+// mask = 0x000F000F, bias = 0x43004300 (128.0 in both bf16 halves)
+__device__ __forceinline__ u32x4_t codes_operand(uint32_t w, uint32_t mask, uint32_t bias) {
     u32x4_t r;
-    r[0] = (w & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = (w & mask) | bias;
+    r[1] = ((w >> 4) & mask) | bias;
+    r[2] = ((w >> 8) & mask) | bias;
+    r[3] = ((w >> 12) & mask) | bias;
     return r;
 }
 
@@ -87,16 +97,26 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// x & m, opaque to the optimiser: the byte-wise conversions below then stay
+// single v_cvt_f32_ubyte{0..3} instructions instead of a bit-field extract
+// each (the known-zero high nibbles would otherwise turn every byte into a
+// 4-bit field)
+__device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
+    uint32_t r;
+    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
+    return r;
+}
+
 // code bytes of one lane's dims -> floats in dim order (even dim = low nibble)
 template <int CB>
 __device__ __forceinline__ void unpack_codes(const uint32_t (&w)[(CB + 3) / 4], float (&c)[2 * CB]) {
 #pragma unroll
     for (int i = 0; i < CB / 4; ++i) {
-        const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t lo = and_opaque(w[i], 0x0F0F0F0Fu), hi = and_opaque(w[i] >> 4, 0x0F0F0F0Fu);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            c[8 * i + 2 * k] = static_cast<float>((lo >> (8 * k)) & 0xFFu);
-            c[8 * i + 2 * k + 1] = static_cast<float>((hi >> (8 * k)) & 0xFFu);
+            c[8 * i + 2 * k] = static_cast<float>(static_cast<uint8_t>(lo >> (8 * k)));
+            c[8 * i + 2 * k + 1] = static_cast<float>(static_cast<uint8_t>(hi >> (8 * k)));
         }
     }
 }
@@ -166,6 +186,7 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
         }
     }
 
+    const uint32_t nib_mask = vconst(0x000F000Fu), nib_bias = vconst(0x43004300u);
     float m[G], lp[R], o[G][DPL], corr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -223,7 +244,7 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
         f32x4_t c[4];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-            const u32x4_t kb = codes_operand(st.kc[blk]);
+            const u32x4_t kb = codes_operand(st.kc[blk], nib_mask, nib_bias);
             c[blk] = mfma16(qa_hi[blk], kb, f32x4_t{0.f, 0.f, 0.f, 0.f});
             c[blk] = mfma16(qa_lo[blk], kb, c[blk]);
         }
