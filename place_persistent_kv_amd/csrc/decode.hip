@@ -341,23 +341,68 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one workgroup per (row, query head).
+// Merge: one workgroup per (row, query head).  The split maxima and sums are
+// reduced across the workgroup in one pass over them; the split weights go to
+// LDS; then thread d sums dim d over the splits with eight loads in flight.
 // ---------------------------------------------------------------------------
+constexpr int kMergeLdsSplits = 1024;
+
+__device__ __forceinline__ float block_reduce(float x, bool is_max, float* scratch) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float y = __shfl_xor(x, off);
+        x = is_max ? fmaxf(x, y) : x + y;
+    }
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[w] = x;
+    __syncthreads();
+    x = scratch[0];
+    for (int i = 1; i < nw; ++i) x = is_max ? fmaxf(x, scratch[i]) : x + scratch[i];
+    return x;
+}
+
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+    __shared__ float s_w[kMergeLdsSplits];
+    __shared__ float s_red[4];
     const int bh = blockIdx.x;
     const int b = bh / a.Hq;
     const int n = a.nsplit[b];
     if (n < a.min_splits) return;
     const int64_t gbh = int64_t(b) * a.Hq + (bh % a.Hq);
     const float* ml = a.ws_ml + gbh * a.S_max * 2;
-    float mn = -FLT_MAX;
-    for (int s = 0; s < n; ++s) mn = fmaxf(mn, ml[2 * s]);
+    const float* po = a.ws_o + gbh * a.S_max * a.D;
+
+    float mx = -FLT_MAX;
+    for (int s = threadIdx.x; s < n; s += blockDim.x) mx = fmaxf(mx, ml[2 * s]);
+    const float mn = block_reduce(mx, true, s_red);
     float ls = 0.0f;
-    for (int s = 0; s < n; ++s) ls += ml[2 * s + 1] * exp2_fast(ml[2 * s] - mn);
+    for (int s = threadIdx.x; s < n; s += blockDim.x) {
+        const float w = exp2_fast(ml[2 * s] - mn);
+        ls += ml[2 * s + 1] * w;
+        if (s < kMergeLdsSplits) s_w[s] = w;
+    }
+    ls = block_reduce(ls, false, s_red);   // (its barriers also publish s_w)
     const float inv = 1.0f / ls;
     for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
-        float os = 0.0f;
-        for (int s = 0; s < n; ++s) os += a.ws_o[(gbh * a.S_max + s) * a.D + d] * exp2_fast(ml[2 * s] - mn);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int s = 0;
+        for (; s + 8 <= n; s += 8) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = po[int64_t(s + u) * a.D + d];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int su = s + u;
+                const float w = su < kMergeLdsSplits ? s_w[su] : exp2_fast(ml[2 * su] - mn);
+                acc[u] = fmaf(x[u], w, acc[u]);
+            }
+        }
+        for (; s < n; ++s) {
+            const float w = s < kMergeLdsSplits ? s_w[s] : exp2_fast(ml[2 * s] - mn);
+            acc[0] = fmaf(po[int64_t(s) * a.D + d], w, acc[0]);
+        }
+        const float os = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
         const float y = os * inv;
         const int64_t idx = gbh * a.D + d;
         if (a.out_kind == kKvF32) static_cast<float*>(a.out)[idx] = y;
