@@ -44,7 +44,7 @@ constexpr int kRowGroups = 2;   // MFMA column groups of 32 query rows per wave
 constexpr int kRows = 4 * kRowGroups * 32;  // query rows per workgroup (4 waves)
 constexpr int kKeys = 64;       // keys per tile
 constexpr int kKPad = kCD + 8;  // K row stride in LDS (bf16)
-constexpr int kVPad = kKeys + 8;  // V^T row stride in LDS (bf16)
+constexpr int kVPad = kKeys + 4;  // V^T row stride in LDS (bf16): 34 dwords, see the staging notes
 constexpr float kLazyC = 8.0f;
 
 // two floats -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32)
@@ -134,8 +134,11 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
 
     // ---- global -> register staging of one 64-key tile
     // K: thread handles 16-byte chunks c = tid + 256 i (key c / 16, dims 8 (c % 16) ..)
-    // V: thread handles dims 8 (tid % 16) .. +7 of keys 4 (tid / 16) .. +3, which
-    //    lie in one page (block_size is a power of two >= 4)
+    // V: thread handles dims 8 (tid / 16) .. +7 of keys 4 (tid % 16) .. +3, which
+    //    lie in one page (block_size is a power of two >= 4).  Transposed into
+    //    V^T rows (one per dim) of 34 dwords: the 16 lanes of a write phase
+    //    fill one row's 64 keys, and the 16 lanes of an operand read (dims
+    //    r .. r + 15) start 34 dwords apart, i.e. on distinct bank pairs.
     // Keys past the workgroup's last key are clamped to it (valid rows, masked
     // later).  The page ids a tile needs are loaded one tile ahead of its K/V
     // rows, so no K/V load waits on a page-table load issued just before it.
@@ -147,8 +150,8 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
         u32x4_t k[4];
         u32x4_t v[4];
     };
-    const int kb = 4 * (tid / 16);
-    const int d8 = 8 * (tid % 16);
+    const int kb = 4 * (tid % 16);
+    const int d8 = 8 * (tid / 16);
     auto page_load = [&](int k0) -> Pages {
         Pages pg;
 #pragma unroll
@@ -156,8 +159,11 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
         pg.v = pt[min(k0 + kb, wg_last_key) >> a.log2bs];
         return pg;
     };
-    auto row_of = [&](int page, int key) -> int64_t {
-        return ((int64_t(page) * a.Hkv + kvh) * a.bs + (min(key, wg_last_key) & (a.bs - 1))) * kCD;
+    // element offset of (page, kv head, slot of key): one 32x32->64 multiply-add
+    const uint32_t page_stride = uint32_t(a.Hkv) * uint32_t(a.bs) * kCD;
+    const uint32_t head_off = uint32_t(kvh) * uint32_t(a.bs) * kCD;
+    auto row_of = [&](int page, int key) -> uint64_t {
+        return uint64_t(uint32_t(page)) * page_stride + (head_off + uint32_t(min(key, wg_last_key) & (a.bs - 1)) * kCD);
     };
     auto stage_load = [&](int k0, const Pages& pg) -> Stage {
         Stage st;
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
             const int c = tid + 256 * i;
             *reinterpret_cast<u32x4_t*>(sK + (c / 16) * kKPad + 8 * (c % 16)) = st.k[i];
         }
-        // transpose: dim 8 (tid % 16) + 2m takes the low halves of the four keys, + 2m + 1 the high halves
+        // transpose: dim d8 + 2m takes the low halves of the four keys, d8 + 2m + 1 the high halves
         const uint32_t w[4][4] = {{st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w},
                                   {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w},
                                   {st.v[2].x, st.v[2].y, st.v[2].z, st.v[2].w},

@@ -182,7 +182,7 @@ pkv_status write_table(int32_t* table_dev, const std::vector<int32_t>& idx,
 namespace {
 
 constexpr int kTargetWorkgroups = 1024;  // 4 per CU on 256 CUs: 2 resident x 2 rounds
-constexpr int kMinAutoTps = 256;         // tokens per split, library choice
+constexpr int kMinAutoTps = 384;         // tokens per split, library choice: >= 6 steps per wave
 constexpr int kTpsQuantum = 64;          // fast kernel: 4 waves x 16 tokens
 
 struct Plan {
