@@ -22,12 +22,15 @@
 //   B[k][j]: lane l holds k = 8 (l / 32) + e, j = l % 32
 //   C[i][j]: lane l, register r holds i = 8 (r / 4) + 4 (l / 32) + r % 4, j = l % 32
 //
-// Workgroup: 4 waves, 256 query rows (256 / G positions x G heads of one kv
-// head); each wave owns two groups of 32 rows, so every K and V^T operand read
-// from LDS feeds two MFMAs.  Key tiles of 64 tokens are staged in LDS (K
-// row-major, V transposed, rows padded against bank conflicts) with the next
-// two tiles' loads in flight in registers.  Workgroups of the same (row, kv
-// head) are placed on the same XCD so they share its L2.
+// Workgroup: 8 waves, 256 query rows (256 / G positions x G heads of one kv
+// head), one 32-row MFMA column group per wave.  With about 210 VGPRs a wave,
+// two waves share each SIMD, so one wave's softmax (vector ALU) overlaps the
+// other's MFMAs.  Key tiles of 64 tokens are staged in LDS (K row-major, V
+// transposed, both laid out so that neither the staging writes nor the
+// operand reads conflict on banks) with the next two tiles' loads in flight
+// in registers.  Workgroups of the same (row, kv head) are placed on the same
+// XCD so they share its L2.  (PKV_CHUNK_WAVES=4 builds the variant with two
+// column groups per wave, each K / V^T operand read feeding two MFMAs.)
 
 #include "device_common.h"
 
@@ -40,8 +43,15 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kCD = 128;        // head size
-constexpr int kRowGroups = 2;   // MFMA column groups of 32 query rows per wave
-constexpr int kRows = 4 * kRowGroups * 32;  // query rows per workgroup (4 waves)
+#ifndef PKV_CHUNK_WAVES
+#define PKV_CHUNK_WAVES 8
+#endif
+constexpr int kWavesC = PKV_CHUNK_WAVES;          // waves per workgroup
+constexpr int kRowGroups = 8 / kWavesC;           // MFMA column groups of 32 query rows per wave
+constexpr int kThreads = 64 * kWavesC;
+constexpr int kRows = kWavesC * kRowGroups * 32;  // query rows per workgroup (256)
+constexpr int kKL = 1024 / kThreads;              // K 16-byte chunks per thread and tile
+constexpr int kVK = 1024 / kThreads;              // keys per thread in the V staging
 constexpr int kKeys = 64;       // keys per tile
 constexpr int kKPad = kCD + 8;  // K row stride in LDS (bf16)
 constexpr int kVPad = kKeys + 4;  // V^T row stride in LDS (bf16): 34 dwords, see the staging notes
@@ -67,7 +77,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 template <int G>
-__global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[kKeys * kKPad];
     __shared__ __attribute__((aligned(16))) uint16_t sVt[kCD * kVPad];
 
@@ -133,8 +143,8 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
     }
 
     // ---- global -> register staging of one 64-key tile
-    // K: thread handles 16-byte chunks c = tid + 256 i (key c / 16, dims 8 (c % 16) ..)
-    // V: thread handles dims 8 (tid / 16) .. +7 of keys 4 (tid % 16) .. +3, which
+    // K: thread handles 16-byte chunks c = tid + kThreads i (key c / 16, dims 8 (c % 16) ..)
+    // V: thread handles dims d8 .. d8 + 7 of the kVK keys kb .. kb + kVK - 1, which
     //    lie in one page (block_size is a power of two >= 4).  Transposed into
     //    V^T rows (one per dim) of 34 dwords: the 16 lanes of a write phase
     //    fill one row's 64 keys, and the 16 lanes of an operand read (dims
@@ -143,19 +153,19 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
     // later).  The page ids a tile needs are loaded one tile ahead of its K/V
     // rows, so no K/V load waits on a page-table load issued just before it.
     struct Pages {
-        i32x4_t k;
+        i32x4_t k;                    // first kKL entries used
         int v;
     };
     struct Stage {
-        u32x4_t k[4];
-        u32x4_t v[4];
+        u32x4_t k[kKL];
+        u32x4_t v[kVK];
     };
-    const int kb = 4 * (tid % 16);
-    const int d8 = 8 * (tid / 16);
+    const int kb = kVK * (tid % (64 / kVK));
+    const int d8 = 8 * (tid / (64 / kVK));
     auto page_load = [&](int k0) -> Pages {
         Pages pg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pg.k[i] = pt[min(k0 + tid / 16 + 16 * i, wg_last_key) >> a.log2bs];
+        for (int i = 0; i < kKL; ++i) pg.k[i] = pt[min(k0 + (tid + kThreads * i) / 16, wg_last_key) >> a.log2bs];
         pg.v = pt[min(k0 + kb, wg_last_key) >> a.log2bs];
         return pg;
     };
@@ -168,35 +178,38 @@ __global__ __launch_bounds__(256) void chunk_attention_kernel(ChunkArgs a) {
     auto stage_load = [&](int k0, const Pages& pg) -> Stage {
         Stage st;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
+        for (int i = 0; i < kKL; ++i) {
+            const int c = tid + kThreads * i;
             st.k[i] = *reinterpret_cast<const u32x4_t*>(a.k + row_of(pg.k[i], k0 + c / 16) + 8 * (c % 16));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kVK; ++i)
             st.v[i] = *reinterpret_cast<const u32x4_t*>(a.v + row_of(pg.v, k0 + kb + i) + d8);
         return st;
     };
     auto stage_store = [&](Stage st) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
+        for (int i = 0; i < kKL; ++i) {
+            const int c = tid + kThreads * i;
             *reinterpret_cast<u32x4_t*>(sK + (c / 16) * kKPad + 8 * (c % 16)) = st.k[i];
         }
-        // transpose: dim d8 + 2m takes the low halves of the four keys, d8 + 2m + 1 the high halves
-        const uint32_t w[4][4] = {{st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w},
-                                  {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w},
-                                  {st.v[2].x, st.v[2].y, st.v[2].z, st.v[2].w},
-                                  {st.v[3].x, st.v[3].y, st.v[3].z, st.v[3].w}};
+        // transpose: dim d8 + 2m takes the low halves of the keys' word m, d8 + 2m + 1 the high halves
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
-            u32x2_t lo, hi;
-            lo.x = __builtin_amdgcn_perm(w[1][mm], w[0][mm], 0x05040100u);
-            lo.y = __builtin_amdgcn_perm(w[3][mm], w[2][mm], 0x05040100u);
-            hi.x = __builtin_amdgcn_perm(w[1][mm], w[0][mm], 0x07060302u);
-            hi.y = __builtin_amdgcn_perm(w[3][mm], w[2][mm], 0x07060302u);
-            *reinterpret_cast<u32x2_t*>(sVt + (d8 + 2 * mm) * kVPad + kb) = lo;
-            *reinterpret_cast<u32x2_t*>(sVt + (d8 + 2 * mm + 1) * kVPad + kb) = hi;
+            if constexpr (kVK == 4) {
+                u32x2_t lo, hi;
+                lo.x = __builtin_amdgcn_perm(st.v[1][mm], st.v[0][mm], 0x05040100u);
+                lo.y = __builtin_amdgcn_perm(st.v[3][mm], st.v[2][mm], 0x05040100u);
+                hi.x = __builtin_amdgcn_perm(st.v[1][mm], st.v[0][mm], 0x07060302u);
+                hi.y = __builtin_amdgcn_perm(st.v[3][mm], st.v[2][mm], 0x07060302u);
+                *reinterpret_cast<u32x2_t*>(sVt + (d8 + 2 * mm) * kVPad + kb) = lo;
+                *reinterpret_cast<u32x2_t*>(sVt + (d8 + 2 * mm + 1) * kVPad + kb) = hi;
+            } else {
+                *reinterpret_cast<uint32_t*>(sVt + (d8 + 2 * mm) * kVPad + kb) =
+                    __builtin_amdgcn_perm(st.v[1][mm], st.v[0][mm], 0x05040100u);
+                *reinterpret_cast<uint32_t*>(sVt + (d8 + 2 * mm + 1) * kVPad + kb) =
+                    __builtin_amdgcn_perm(st.v[1][mm], st.v[0][mm], 0x07060302u);
+            }
         }
     };
 
@@ -349,10 +362,10 @@ hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s) {
     const int blocks = a.rows * a.Hkv * ((a.C + P - 1) / P);
     if (blocks <= 0) return hipSuccess;
     switch (G) {
-        case 1: hipLaunchKernelGGL(chunk_attention_kernel<1>, dim3(blocks), dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(chunk_attention_kernel<2>, dim3(blocks), dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(chunk_attention_kernel<4>, dim3(blocks), dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL(chunk_attention_kernel<8>, dim3(blocks), dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL(chunk_attention_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(chunk_attention_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(chunk_attention_kernel<4>, dim3(blocks), dim3(kThreads), 0, s, a); break;
+        case 8: hipLaunchKernelGGL(chunk_attention_kernel<8>, dim3(blocks), dim3(kThreads), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
