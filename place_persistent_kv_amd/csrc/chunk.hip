@@ -216,6 +216,8 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     // ---- one 64-key tile from LDS, as two halves of 32 keys: S^T = K Q^T,
     // online softmax, O^T += V^T P^T
     auto compute = [&](int k0) {
+        // only the diagonal tiles (reaching past the smallest causal limit of
+        // the workgroup) test keys against the limits; a uniform branch
         const bool need_mask = k0 + kKeys - 1 > wg_first_limit;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -238,17 +240,16 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
             for (int rg = 0; rg < kRowGroups; ++rg) {
                 // causal mask and max of this query row over the 32 keys, in raw
                 // score units (the scale is positive)
+                if (need_mask) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
+                        s[rg][e] = key <= limit[rg] ? s[rg][e] : -INFINITY;
+                    }
+                }
                 float mx = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float x = s[rg][e];
-                    if (need_mask) {
-                        const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
-                        x = key <= limit[rg] ? x : -INFINITY;
-                    }
-                    s[rg][e] = x;
-                    mx = fmaxf(mx, x);
-                }
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[rg][e]);
                 mx = max_halves(mx) * a.scale_log2;
                 if (mx > m[rg] + kLazyC) {
                     const float c = exp2_fast(m[rg] - mx);
