@@ -219,22 +219,31 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
         // only the diagonal tiles (reaching past the smallest causal limit of
         // the workgroup) test keys against the limits; a uniform branch
         const bool need_mask = k0 + kKeys - 1 > wg_first_limit;
+
+        // S^T for both 32-key halves, the two accumulation chains interleaved
+        f32x16_t s[2][kRowGroups];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            f32x16_t s[kRowGroups];
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
             for (int rg = 0; rg < kRowGroups; ++rg)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) s[rg][e] = 0.0f;
-            const uint16_t* krow = sK + (half * 32 + col) * kKPad + 8 * hl;
+                for (int e = 0; e < 16; ++e) s[half][rg][e] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const u32x4_t kA = *reinterpret_cast<const u32x4_t*>(krow + 16 * ks);
+        for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const u32x4_t kA = *reinterpret_cast<const u32x4_t*>(sK + (half * 32 + col) * kKPad + 8 * hl + 16 * ks);
 #pragma unroll
                 for (int rg = 0; rg < kRowGroups; ++rg)
-                    s[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kA), as_bf16x8(qB[rg][ks]), s[rg],
-                                                                   0, 0, 0);
+                    s[half][rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kA), as_bf16x8(qB[rg][ks]),
+                                                                         s[half][rg], 0, 0, 0);
             }
+        }
+
+        // per half: online softmax (the matrix cores run the other half's
+        // products meanwhile), then O^T += V^T P^T
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
             u32x4_t pB[kRowGroups][2];
 #pragma unroll
             for (int rg = 0; rg < kRowGroups; ++rg) {
@@ -244,12 +253,12 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
-                        s[rg][e] = key <= limit[rg] ? s[rg][e] : -INFINITY;
+                        s[half][rg][e] = key <= limit[rg] ? s[half][rg][e] : -INFINITY;
                     }
                 }
                 float mx = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[rg][e]);
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[half][rg][e]);
                 mx = max_halves(mx) * a.scale_log2;
                 if (mx > m[rg] + kLazyC) {
                     const float c = exp2_fast(m[rg] - mx);
@@ -268,11 +277,11 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
                     float p[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        p[e] = exp2_fast(fmaf(s[rg][8 * qq + e], a.scale_log2, neg_m));
+                        p[e] = exp2_fast(fmaf(s[half][rg][8 * qq + e], a.scale_log2, neg_m));
                         l[rg] += p[e];
                     }
                     pB[rg][qq] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+                                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
                 }
             }
             // O^T += V^T P^T: A[i = dim][k] with the keys of chunk qq taken as
