@@ -225,6 +225,63 @@ def test_paged_decode_checks_reserved_pages():
     assert status_of(pkv.paged_decode_attention, Q, kp, vp, table, 8, 16, [129, 16], OUT) == pkv.E_CAPACITY
 
 
+# --------------------------------------------------------------------------- INT4 decode and chunk attention
+def _int4_pools(bs=16, NB=32, Hkv=2, offset=0):
+    kc = R(FAKE + 0x100000 + offset, pkv.U8, [NB, Hkv, bs, 64])
+    vc = R(FAKE + 0x900000 + offset, pkv.U8, [NB, Hkv, bs, 64])
+    kp = R(FAKE + 0x1100000 + offset, pkv.F16, [NB, Hkv, bs, 4, 2])
+    vp = R(FAKE + 0x1900000 + offset, pkv.F16, [NB, Hkv, bs, 4, 2])
+    return kc, kp, vc, vp
+
+
+def test_int4_decode_layout_checks():
+    q = R(FAKE + 0x3000000, pkv.F32, [2, 8, 1, 128])
+    out = R(FAKE + 0x3100000, pkv.F32, [2, 8, 1, 128])
+    table = R(FAKE + 0x2000000, pkv.I32, [2, 8])
+    kc, kp, vc, vp = _int4_pools()
+    f = pkv.paged_decode_attention_int4
+    # block size must match the pool and be a power of two >= 16
+    assert status_of(f, q, kc, kp, vc, vp, table, 8, 32, [16, 16], out) == pkv.E_LAYOUT
+    kc8, kp8, vc8, vp8 = _int4_pools(bs=8)
+    assert status_of(f, q, kc8, kp8, vc8, vp8, table, 8, 8, [16, 16], out) == pkv.E_LAYOUT
+    # every pool 16-byte aligned
+    bad = R(kp.ptr + 4, pkv.F16, kp.shape)
+    assert status_of(f, q, kc, bad, vc, vp, table, 8, 16, [16, 16], out) == pkv.E_LAYOUT
+    # q and out f32; Hq / Hkv in {1, 2, 4, 8}
+    assert status_of(f, R(q.ptr, pkv.BF16, q.shape), kc, kp, vc, vp, table, 8, 16, [16, 16], out) == pkv.E_DTYPE
+    q6 = R(q.ptr, pkv.F32, [2, 6, 1, 128])
+    assert status_of(f, q6, kc, kp, vc, vp, table, 8, 16, [16, 16], R(out.ptr, pkv.F32, q6.shape)) == pkv.E_LAYOUT
+    # lengths within max_blocks * block_size
+    assert status_of(f, q, kc, kp, vc, vp, table, 8, 16, [129, 16], out) == pkv.E_CAPACITY
+
+
+def test_chunk_attention_checks():
+    q = R(FAKE + 0x3000000, pkv.BF16, [2, 4, 32, 128])
+    out = R(FAKE + 0x3400000, pkv.BF16, [2, 4, 32, 128])
+    kp = R(FAKE + 0x100000, pkv.BF16, [32, 2, 16, 128])
+    vp = R(FAKE + 0x900000, pkv.BF16, [32, 2, 16, 128])
+    table = R(FAKE + 0x2000000, pkv.I32, [2, 8])
+    f = pkv.chunk_attention
+    # p0 + C must fit the table's capacity, p0 >= 0
+    assert status_of(f, q, kp, vp, table, 8, 16, [97, 0], out) == pkv.E_CAPACITY
+    assert status_of(f, q, kp, vp, table, 8, 16, [-1, 0], out) == pkv.E_CAPACITY
+    # block size: equal to the pool's, a power of two, at least 4
+    kp2 = R(kp.ptr, pkv.BF16, [32, 2, 2, 128])
+    vp2 = R(vp.ptr, pkv.BF16, [32, 2, 2, 128])
+    assert status_of(f, q, kp2, vp2, table, 8, 2, [0, 0], out) == pkv.E_LAYOUT
+    kp12 = R(kp.ptr, pkv.BF16, [32, 2, 12, 128])
+    vp12 = R(vp.ptr, pkv.BF16, [32, 2, 12, 128])
+    assert status_of(f, q, kp12, vp12, table, 8, 12, [0, 0], out) == pkv.E_LAYOUT
+    assert status_of(f, q, kp, vp, table, 8, 32, [0, 0], out) == pkv.E_LAYOUT
+    # with a pool handle, every row needs ceil((p0 + C) / bs) reserved pages
+    pool = pkv.Pool(32, 16, 2, 8)
+    pool.reserve([0, 1], [48, 64])
+    assert status_of(f, q, kp, vp, table, 8, 16, [16, 40], out, pool=pool) == pkv.E_PAGE   # row 1: 72 tokens
+    # head size 128 and bf16 only
+    assert status_of(f, R(q.ptr, pkv.F32, q.shape), kp, vp, table, 8, 16, [0, 0], R(out.ptr, pkv.F32, out.shape)) \
+        == pkv.E_DTYPE
+
+
 # --------------------------------------------------------------------------- sampling
 @pytest.mark.parametrize("T", [-1.0, float("nan"), float("-inf")])
 def test_sample_rejects_bad_temperature(T):
