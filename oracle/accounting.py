@@ -36,3 +36,16 @@ def fallback_prefix_bytes(prefix_len: int, batch: int, heads: int, head_sizes, e
 def in_place_extra_cache_bytes() -> int:
     """Additional cache bytes of an in-place update (a second cache is never allocated)."""
     return 0
+
+
+def decoded_bytes(query_positions, left_window: int, head_sizes, batch: int = 1, heads: int = 1) -> int:
+    """FLOAT bytes decoded by windowed attention, counting every visible token
+    again for every query ("Persistent input/output feedback", statistics of
+    the direct call: decoded FLOAT bytes of visible tokens, repeated reads for
+    different queries included).  A query at position ``p`` sees ``[max(0,
+    p - W), p]`` for ``W = left_window >= 0`` and ``[0, p]`` for ``W = -1``."""
+    visible = 0
+    for p in query_positions:
+        lo = 0 if left_window < 0 else max(0, int(p) - left_window)
+        visible += int(p) - lo + 1
+    return visible * batch * heads * sum(int(d) for d in head_sizes) * 4

@@ -17,6 +17,12 @@ Readings (listed in the design doc): ``scale = 1/sqrt(D)`` unless given; query
 head ``h`` reads K/V head ``h // G`` with ``G = Hq / Hkv`` (contiguous
 groups); ``valid_len[b]`` counts the token appended in this step.
 
+Left window (same pages, "Versioned operator schema": ``left_window_size``
+-1 is unbounded, a non-negative value bounds the preceding tokens; "Kernel
+implementation": causal masking and the window decide the visible range): a
+query at absolute position ``p`` sees keys ``[max(0, p - W), p]``, i.e. itself
+and at most ``W`` preceding tokens.
+
 Split partials and their merge (the long-context split of the same online
 softmax): a split over token range R yields ``m = max_{j in R} s_j``,
 ``l = sum_{j in R} exp(s_j - m)`` and ``o = sum_{j in R} exp(s_j - m) v_j``
@@ -43,13 +49,18 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
     return (p @ V) / p.sum()
 
 
+def visible_begin(pos: int, left_window: int = -1) -> int:
+    """First key a query at absolute position ``pos`` sees (the last is ``pos``)."""
+    return 0 if left_window < 0 else max(0, pos - left_window)
+
+
 def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
-                     valid_len, scale=None) -> np.ndarray:
+                     valid_len, scale=None, left_window: int = -1) -> np.ndarray:
     """Single-token decode over a contiguous cache.
 
     ``q`` is ``[B, Hq, D]`` (or ``[B, Hq, 1, D]``), ``k_cache``/``v_cache`` are
-    ``[B, Hkv, capacity, D]`` (already float64), ``valid_len`` is ``[B]``.
-    Returns ``[B, Hq, D]`` float64.
+    ``[B, Hkv, capacity, D]`` (already float64), ``valid_len`` is ``[B]``; the
+    query sits at position ``valid_len - 1``.  Returns ``[B, Hq, D]`` float64.
     """
     q = np.asarray(q, dtype=np.float64)
     if q.ndim == 4:
@@ -65,9 +76,10 @@ def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         L = int(valid_len[b])
         if L < 1:
             raise ValueError("valid_len must be >= 1")
+        lo = visible_begin(L - 1, left_window)
         for h in range(Hq):
             kv = h // G
-            out[b, h] = attend(q[b, h], k_cache[b, kv, :L], v_cache[b, kv, :L], sc)
+            out[b, h] = attend(q[b, h], k_cache[b, kv, lo:L], v_cache[b, kv, lo:L], sc)
     return out
 
 
@@ -101,12 +113,13 @@ def merge_partials(parts) -> np.ndarray:
     return o / l_star
 
 
-def chunk_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, p0: int, scale=None) -> np.ndarray:
+def chunk_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, p0: int, scale=None,
+                    left_window: int = -1) -> np.ndarray:
     """Causal attention of a chunk of C queries of one row.
 
     ``q`` is ``[Hq, C, D]``; ``K``/``V`` are the row's logical ``[Hkv, p0 + C, D]``
     after the chunk was appended at position ``p0``.  Query ``t`` sits at
-    absolute position ``p0 + t`` and attends keys ``[0, p0 + t]``.
+    absolute position ``p0 + t`` and attends keys ``[visible_begin(p0 + t), p0 + t]``.
     Returns ``[Hq, C, D]`` float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -119,5 +132,6 @@ def chunk_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, p0: int, scale=
         kv = h // G
         for t in range(C):
             last = p0 + t
-            out[h, t] = attend(q[h, t], K[kv, :last + 1], V[kv, :last + 1], sc)
+            lo = visible_begin(last, left_window)
+            out[h, t] = attend(q[h, t], K[kv, lo:last + 1], V[kv, lo:last + 1], sc)
     return out
