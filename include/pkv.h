@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -245,6 +245,12 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * valid_len: host int32[B], 1 <= valid_len[b] <= capacity (includes the
  *           token appended by this step).
  * scale   : softmax scale; <= 0 means 1/sqrt(D).
+ * left_window: -1 = unbounded; W >= 0 = the query (at position
+ *           valid_len[b] - 1) sees only keys [max(0, valid_len[b] - 1 - W),
+ *           valid_len[b] - 1] ("Persistent input/output feedback", "Optional
+ *           heterogeneous paged KV", "Versioned operator schema":
+ *           left_window_size).  Pages and rows wholly before the window are
+ *           not read.  Values below -1: PKV_E_ARG.
  * out     : same shape as q; dtype of q or f32.  Query head h reads K/V head
  *           h / (Hq / Hkv).
  * workspace: device scratch of pkv_decode_workspace_size(...) bytes, 256-byte
@@ -253,7 +259,7 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *           context is cut into that many equal token ranges (at most). */
 pkv_status pkv_decode_attention(const pkv_tensor* q, const pkv_tensor* k_cache,
                                 const pkv_tensor* v_cache, const int32_t* valid_len,
-                                float scale, pkv_tensor* out, void* workspace,
+                                float scale, int32_t left_window, pkv_tensor* out, void* workspace,
                                 size_t workspace_bytes, int32_t num_splits, void* stream);
 
 /* Paged bf16/f32: k_pool, v_pool [num_blocks, Hkv, block_size, D];
@@ -264,8 +270,9 @@ pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_p
                                       const pkv_tensor* v_pool, const int32_t* page_table_dev,
                                       int32_t max_blocks_per_seq, int32_t block_size,
                                       const pkv_pool* pool, const int32_t* valid_len,
-                                      float scale, pkv_tensor* out, void* workspace,
-                                      size_t workspace_bytes, int32_t num_splits, void* stream);
+                                      float scale, int32_t left_window, pkv_tensor* out,
+                                      void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                      void* stream);
 
 /* Paged INT4: K/V rows decoded in registers as (code - zero_point) * scale
  * per 32-element block ("Custom, quantized, and persistent values",
@@ -279,15 +286,17 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
                                            const int32_t* page_table_dev,
                                            int32_t max_blocks_per_seq, int32_t block_size,
                                            const pkv_pool* pool, const int32_t* valid_len,
-                                           float scale, pkv_tensor* out, void* workspace,
-                                           size_t workspace_bytes, int32_t num_splits,
-                                           void* stream);
+                                           float scale, int32_t left_window, pkv_tensor* out,
+                                           void* workspace, size_t workspace_bytes,
+                                           int32_t num_splits, void* stream);
 
 /* Causal chunk attention after a chunk of C tokens was appended at position
  * p0[b] (host int32[B]) with pkv_paged_cache_update: query t of row b sits at
- * p0[b] + t and attends keys [0, p0[b] + t] ("Persistent input/output
- * feedback", "Optional heterogeneous paged KV", "Versioned operator schema":
- * causal by default, unbounded left window, equal new Q/K/V lengths).
+ * p0[b] + t and attends keys [lo, p0[b] + t] with lo = 0 for left_window = -1
+ * and max(0, p0[b] + t - left_window) for left_window >= 0 ("Persistent
+ * input/output feedback", "Optional heterogeneous paged KV", "Versioned
+ * operator schema": causal by default, left_window_size, equal new Q/K/V
+ * lengths); key tiles wholly before every query's window are not read.
  * q, out: bf16 [B, Hq, C, D] with D == 128 and Hq / Hkv in {1, 2, 4, 8};
  * k_pool, v_pool: bf16 [num_blocks, Hkv, block_size, D], block_size a power
  * of two >= 4 (else PKV_E_LAYOUT); page_table_dev as
@@ -299,7 +308,7 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
                                const pkv_tensor* v_pool, const int32_t* page_table_dev,
                                int32_t max_blocks_per_seq, int32_t block_size,
                                const pkv_pool* pool, const int32_t* p0, float scale,
-                               pkv_tensor* out, void* stream);
+                               int32_t left_window, pkv_tensor* out, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Sampling                                                                  */

@@ -93,12 +93,14 @@ _SIG = {
                                               C.c_int32, _P(_VP), _P(_VP), _VP]),
     "pkv_paged_gather": (C.c_int, [_T, _VP, C.c_int32, C.c_int32, C.c_int32, _T, _VP]),
     "pkv_decode_workspace_size": (C.c_size_t, [C.c_int32] * 6),
-    "pkv_decode_attention": (C.c_int, [_T, _T, _T, _I32P, C.c_float, _T, _VP, C.c_size_t, C.c_int32, _VP]),
+    "pkv_decode_attention": (C.c_int, [_T, _T, _T, _I32P, C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32,
+                                       _VP]),
     "pkv_paged_decode_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
-                                             _T, _VP, C.c_size_t, C.c_int32, _VP]),
+                                             C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_paged_decode_attention_int4": (C.c_int, [_T, _T, _T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P,
-                                                  C.c_float, _T, _VP, C.c_size_t, C.c_int32, _VP]),
-    "pkv_chunk_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float, _T, _VP]),
+                                                  C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
+    "pkv_chunk_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float, C.c_int32,
+                                      _T, _VP]),
     "pkv_sample_workspace_size": (C.c_size_t, [C.c_int32, C.c_int64]),
     "pkv_sample": (C.c_int, [_T, C.c_float, C.c_uint64, _VP, _VP, C.c_size_t, _VP]),
 }
@@ -108,6 +110,12 @@ for _name, (_res, _args) in _SIG.items():
     if _fn is not None:
         _fn.restype = _res
         _fn.argtypes = _args
+
+
+ABI_VERSION = 2      # the argument lists above follow this version of include/pkv.h
+if _lib.pkv_abi_version() != ABI_VERSION:
+    raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
+                      "rebuild it (python -m place_persistent_kv_amd.build)")
 
 
 def exported_symbols() -> list[str]:
@@ -350,41 +358,43 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, D: int, max_len: int, num_s
 
 
 def decode_attention(q, k_cache, v_cache, valid_len, out, workspace=None, scale: float = 0.0,
-                     num_splits: int = 0, stream=None) -> None:
+                     num_splits: int = 0, stream=None, left_window: int = -1) -> None:
     ws = _ptr(workspace)
     _check(_lib.pkv_decode_attention(C.byref(desc(q)), C.byref(desc(k_cache)), C.byref(desc(v_cache)),
-                                     _i32_array(valid_len), float(scale), C.byref(desc(out)), ws,
+                                     _i32_array(valid_len), float(scale), int(left_window), C.byref(desc(out)), ws,
                                      0 if workspace is None else _nbytes(workspace), int(num_splits),
                                      _stream(stream)), "pkv_decode_attention")
 
 
 def paged_decode_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, block_size: int, valid_len,
                            out, workspace=None, pool: Optional[Pool] = None, scale: float = 0.0,
-                           num_splits: int = 0, stream=None) -> None:
+                           num_splits: int = 0, stream=None, left_window: int = -1) -> None:
     _check(_lib.pkv_paged_decode_attention(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
                                            _ptr(page_table), int(max_blocks_per_seq), int(block_size),
                                            _pool_handle(pool), _i32_array(valid_len), float(scale),
-                                           C.byref(desc(out)), _ptr(workspace),
+                                           int(left_window), C.byref(desc(out)), _ptr(workspace),
                                            0 if workspace is None else _nbytes(workspace), int(num_splits),
                                            _stream(stream)), "pkv_paged_decode_attention")
 
 
 def paged_decode_attention_int4(q, k_codes, k_params, v_codes, v_params, page_table, max_blocks_per_seq: int,
                                 block_size: int, valid_len, out, workspace=None, pool: Optional[Pool] = None,
-                                scale: float = 0.0, num_splits: int = 0, stream=None) -> None:
+                                scale: float = 0.0, num_splits: int = 0, stream=None,
+                                left_window: int = -1) -> None:
     _check(_lib.pkv_paged_decode_attention_int4(
         C.byref(desc(q)), C.byref(desc(k_codes)), C.byref(desc(k_params)), C.byref(desc(v_codes)),
         C.byref(desc(v_params)), _ptr(page_table), int(max_blocks_per_seq), int(block_size), _pool_handle(pool),
-        _i32_array(valid_len), float(scale), C.byref(desc(out)), _ptr(workspace),
+        _i32_array(valid_len), float(scale), int(left_window), C.byref(desc(out)), _ptr(workspace),
         0 if workspace is None else _nbytes(workspace), int(num_splits), _stream(stream)),
         "pkv_paged_decode_attention_int4")
 
 
 def chunk_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, block_size: int, p0, out,
-                    pool: Optional[Pool] = None, scale: float = 0.0, stream=None) -> None:
+                    pool: Optional[Pool] = None, scale: float = 0.0, stream=None, left_window: int = -1) -> None:
     _check(_lib.pkv_chunk_attention(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
                                     _ptr(page_table), int(max_blocks_per_seq), int(block_size), _pool_handle(pool),
-                                    _i32_array(p0), float(scale), C.byref(desc(out)), _stream(stream)),
+                                    _i32_array(p0), float(scale), int(left_window), C.byref(desc(out)),
+                                    _stream(stream)),
            "pkv_chunk_attention")
 
 

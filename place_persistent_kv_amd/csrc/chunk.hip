@@ -5,7 +5,8 @@
 // section "Versioned operator schema": causal masking is the default, the
 // left window is unbounded, and the new Q, K and V have the same length.
 // After the chunk has been appended at position p0 (pkv_paged_cache_update),
-// query t of a row sits at p0 + t and attends keys [0, p0 + t].
+// query t of a row sits at p0 + t and attends keys [0, p0 + t], or with a left
+// window W >= 0 keys [p0 + t - W, p0 + t] (left_window_size).
 //
 // Unlike the single-token step this is a dense contraction: per (row, kv
 // head) the G * C query rows share every K/V tile, so Q.K^T and P.V run as
@@ -110,15 +111,20 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     const int32_t* pt = a.page_table + int64_t(b) * a.maxb;
     const int wg_last_key = p0 + min(t0 + P, a.C) - 1;
     const int wg_first_limit = p0 + t0;      // smallest limit in the workgroup
+    // left window: a query at position p sees keys [p - window, p]; tiles below
+    // the smallest lower limit are skipped, those below the largest are masked
+    const int wg_lo_first = a.window < 0 ? 0 : max(0, wg_first_limit - a.window);
+    const int wg_lo_last = a.window < 0 ? 0 : max(0, wg_last_key - a.window);
 
     // this lane's two query rows (row groups rg = 0, 1 of the wave)
-    int t[kRowGroups], h[kRowGroups], limit[kRowGroups];
+    int t[kRowGroups], h[kRowGroups], limit[kRowGroups], lo_lim[kRowGroups];
 #pragma unroll
     for (int rg = 0; rg < kRowGroups; ++rg) {
         const int r = (wave * kRowGroups + rg) * 32 + col;
         t[rg] = t0 + r / G;
         h[rg] = kvh * G + r % G;
         limit[rg] = p0 + min(t[rg], a.C - 1);
+        lo_lim[rg] = a.window < 0 ? 0 : max(0, limit[rg] - a.window);
     }
 
     // Q^T operand (B of S^T = K Q^T): lane holds dims 8 hl + 16 s .. +7 of its row
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     auto compute = [&](int k0) {
         // only the diagonal tiles (reaching past the smallest causal limit of
         // the workgroup) test keys against the limits; a uniform branch
-        const bool need_mask = k0 + kKeys - 1 > wg_first_limit;
+        const bool need_mask = k0 + kKeys - 1 > wg_first_limit || k0 < wg_lo_last;
 
         // S^T for both 32-key halves, the two accumulation chains interleaved
         f32x16_t s[2][kRowGroups];
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
-                        s[half][rg][e] = key <= limit[rg] ? s[half][rg][e] : -INFINITY;
+                        s[half][rg][e] = key <= limit[rg] && key >= lo_lim[rg] ? s[half][rg][e] : -INFINITY;
                     }
                 }
                 float mx = -INFINITY;
@@ -310,21 +316,22 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     // tiles ahead are requested.  Loads past the last tile re-read the last one
     // (always valid); an odd tile count ends with one fully masked tile.
     const int n_tiles = wg_last_key / kKeys + 1;
+    const int it0 = wg_lo_first / kKeys;     // first tile any query of the workgroup sees
     auto tile_key = [&](int it) { return min(it, n_tiles - 1) * kKeys; };
     // (the prologue keeps the loop's issue order, so that the waits at the
     // loop head are the same on entry as on every later pass)
-    Pages pgA = page_load(0);
-    Pages pgB = page_load(tile_key(1));
+    Pages pgA = page_load(tile_key(it0));
+    Pages pgB = page_load(tile_key(it0 + 1));
     __builtin_amdgcn_sched_barrier(0);
-    Stage A = stage_load(0, pgA);
+    Stage A = stage_load(tile_key(it0), pgA);
     __builtin_amdgcn_sched_barrier(0);
-    pgA = page_load(tile_key(2));
+    pgA = page_load(tile_key(it0 + 2));
     __builtin_amdgcn_sched_barrier(0);
-    Stage B = stage_load(tile_key(1), pgB);
+    Stage B = stage_load(tile_key(it0 + 1), pgB);
     __builtin_amdgcn_sched_barrier(0);
-    pgB = page_load(tile_key(3));
+    pgB = page_load(tile_key(it0 + 3));
     __builtin_amdgcn_sched_barrier(0);
-    for (int it = 0; it < n_tiles; it += 2) {
+    for (int it = it0; it < n_tiles; it += 2) {
         __syncthreads();               // the previous tile is consumed
         stage_store(A);
         __syncthreads();

@@ -5,8 +5,10 @@
 // What is computed -- "Persistent input/output feedback", "Optional
 // heterogeneous paged KV", sections "Versioned operator schema" and "Kernel
 // implementation": grouped-query attention (query head h reads K/V head
-// h / G), only valid tokens are read, online softmax instead of K/V
-// concatenation or a cache-length score matrix.
+// h / G), only valid and visible tokens are read (a left window W >= 0
+// limits the query at L - 1 to keys [L - 1 - W, L - 1]; splits then cover
+// only that range), online softmax instead of K/V concatenation or a
+// cache-length score matrix.
 //
 // The single-token step is a bandwidth-bound GEMV (about 4 flops per K/V
 // byte at G = 4), so it runs on the vector ALUs, not MFMA:
@@ -58,7 +60,8 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     const int split = r - a.split_begin[b];
     const int nsplit = a.split_begin[b + 1] - a.split_begin[b];
     const int L = a.len[b];
-    const int t0 = split * a.tps;
+    const int vis0 = visible_begin(L, a.window);   // first key the query sees
+    const int t0 = split_base(L, a.window) + split * a.tps;
     const int t1 = min(L, t0 + a.tps);
     const int quarter = a.tps / kWaves;
     const int wbeg = t0 + wave * quarter;
@@ -124,8 +127,8 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     };
 
     auto compute = [&](const Buf& u, int ts) {
-        const bool live0 = ts + grp < t1;
-        const bool live1 = ts + 8 + grp < t1;
+        const bool live0 = ts + grp < t1 && ts + grp >= vis0;
+        const bool live1 = ts + 8 + grp < t1 && ts + 8 + grp >= vis0;
         float s0[G], s1[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -290,7 +293,8 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     const int b = find_row(a.split_begin, a.rows, r);
     const int split = r - a.split_begin[b];
     const int L = a.len[b];
-    const int t0 = split * a.tps;
+    const int t0 = split_base(L, a.window) + split * a.tps;
+    const int ta = max(t0, visible_begin(L, a.window));   // first visible token of the split
     const int t1 = min(L, t0 + a.tps);
     const int G = a.Hq / a.Hkv;
     const int kvh = h / G;
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 
     // pass 1: scores (lanes over tokens)
     float mx = -FLT_MAX;
-    for (int t = t0 + lane; t < t1; t += 64) {
+    for (int t = ta + lane; t < t1; t += 64) {
         const int64_t off = row(t);
         float s = 0.0f;
         for (int d = 0; d < D; ++d) s = fmaf(to_f32(Q[d]), to_f32(K[off + d]), s);
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     }
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     float ls = 0.0f;
-    for (int t = t0 + lane; t < t1; t += 64) {
+    for (int t = ta + lane; t < t1; t += 64) {
         const float p = exp2_fast(s_p[t - t0] - mx);
         s_p[t - t0] = p;
         ls += p;
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     const int64_t slot = (int64_t(b) * a.Hq + h) * a.S_max + split;
     for (int d = lane; d < D; d += 64) {
         float acc = 0.0f;
-        for (int t = t0; t < t1; ++t) acc = fmaf(s_p[t - t0], to_f32(V[row(t) + d]), acc);
+        for (int t = ta; t < t1; ++t) acc = fmaf(s_p[t - t0], to_f32(V[row(t) + d]), acc);
         a.ws_o[slot * D + d] = acc;
     }
     if (lane == 0) {

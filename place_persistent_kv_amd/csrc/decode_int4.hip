@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
     const int split = r - a.split_begin[b];
     const int nsplit = a.split_begin[b + 1] - a.split_begin[b];
     const int L = a.len[b];
-    const int t0 = split * a.tps;
+    const int vis0 = visible_begin(L, a.window);   // first key the query sees
+    const int t0 = split_base(L, a.window) + split * a.tps;
     const int t1 = min(L, t0 + a.tps);
     const int quarter = a.tps / kWaves4;
     const int wbeg = t0 + wave * quarter;
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
             c[blk] = mfma16(qa_hi[blk], kb, f32x4_t{0.f, 0.f, 0.f, 0.f});
             c[blk] = mfma16(qa_lo[blk], kb, c[blk]);
         }
-        const bool live = ts + col < wend;
+        const bool live = ts + col < wend && ts + col >= vis0;
         float s[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) {

@@ -646,8 +646,8 @@ pkv_status check_q_out(const pkv_tensor* q, const pkv_tensor* out, QView* v) {
 pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_tensor* v,
                          bool paged, const int32_t* page_table, int32_t maxb, int32_t bs,
                          const pkv_pool* pool, const int32_t* valid_len, float scale,
-                         pkv_tensor* out, void* ws, size_t ws_bytes, int32_t num_splits,
-                         void* stream) {
+                         int32_t left_window, pkv_tensor* out, void* ws, size_t ws_bytes,
+                         int32_t num_splits, void* stream) {
     QView qv;
     PKV_TRY(check_q_out(q, out, &qv));
     PKV_TRY(check_tensor(k, "k", 4, 4));
@@ -688,6 +688,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
                         (long long)ceil_div(valid_len[b], bs), pool->held[b]);
     }
     if (!(scale == scale) || std::isinf(scale)) return fail(PKV_E_ARG, "scale must be finite");
+    if (left_window < -1) return fail(PKV_E_ARG, "left_window must be -1 (unbounded) or >= 0");
     const Span os = span(out);
     PKV_TRY(check_disjoint(q, "q", os, "out"));
     PKV_TRY(check_disjoint(k, "k", os, "out"));
@@ -697,7 +698,10 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
     const int G = static_cast<int>(Hq / Hkv);
     const bool fast = fast_decode_supported(kind, static_cast<int>(D), G, paged, bs);
     // size the workspace for the whole call (all row groups share it)
-    Plan full = plan_splits(valid_len, static_cast<int>(B), fast ? static_cast<int>(Hkv) : static_cast<int>(Hq),
+    // splits cover only each row's visible range (from its 64-token quantum on)
+    std::vector<int32_t> span_len(B);
+    for (int64_t b = 0; b < B; ++b) span_len[b] = valid_len[b] - split_base(valid_len[b], left_window);
+    Plan full = plan_splits(span_len.data(), static_cast<int>(B), fast ? static_cast<int>(Hkv) : static_cast<int>(Hq),
                             num_splits, fast ? 0 : kGenericMaxTps);
     const size_t need = ws_bytes_for(B, Hq, D, full.S_max);
     if (full.S_max > 1 || !fast) {
@@ -747,6 +751,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         a.rows = rows;
         const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
         a.scale_log2 = sc * 1.4426950408889634f;
+        a.window = left_window;
         int total = 0;
         bool any_split = false;
         for (int i = 0; i < rows; ++i) {
@@ -784,20 +789,21 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
 
 pkv_status pkv_decode_attention(const pkv_tensor* q, const pkv_tensor* k_cache,
                                 const pkv_tensor* v_cache, const int32_t* valid_len,
-                                float scale, pkv_tensor* out, void* workspace,
+                                float scale, int32_t left_window, pkv_tensor* out, void* workspace,
                                 size_t workspace_bytes, int32_t num_splits, void* stream) {
-    return decode_common(q, k_cache, v_cache, false, nullptr, 0, 0, nullptr, valid_len, scale, out,
-                         workspace, workspace_bytes, num_splits, stream);
+    return decode_common(q, k_cache, v_cache, false, nullptr, 0, 0, nullptr, valid_len, scale, left_window,
+                         out, workspace, workspace_bytes, num_splits, stream);
 }
 
 pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
                                       const pkv_tensor* v_pool, const int32_t* page_table_dev,
                                       int32_t max_blocks_per_seq, int32_t block_size,
                                       const pkv_pool* pool, const int32_t* valid_len,
-                                      float scale, pkv_tensor* out, void* workspace,
-                                      size_t workspace_bytes, int32_t num_splits, void* stream) {
+                                      float scale, int32_t left_window, pkv_tensor* out,
+                                      void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                      void* stream) {
     return decode_common(q, k_pool, v_pool, true, page_table_dev, max_blocks_per_seq, block_size, pool,
-                         valid_len, scale, out, workspace, workspace_bytes, num_splits, stream);
+                         valid_len, scale, left_window, out, workspace, workspace_bytes, num_splits, stream);
 }
 
 
@@ -807,7 +813,8 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
                                            const int32_t* page_table_dev,
                                            int32_t max_blocks_per_seq, int32_t block_size,
                                            const pkv_pool* pool, const int32_t* valid_len,
-                                           float scale, pkv_tensor* out, void* workspace,
+                                           float scale, int32_t left_window, pkv_tensor* out,
+                                           void* workspace,
                                            size_t workspace_bytes, int32_t num_splits,
                                            void* stream) {
     QView qv;
@@ -858,7 +865,10 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
     for (const pkv_tensor* t : {k_codes, v_codes, k_params, v_params}) PKV_TRY(check_disjoint(t, "K/V pool", os, "out"));
     if (B == 0) return ok();
 
-    Plan full = plan_splits(valid_len, static_cast<int>(B), static_cast<int>(Hkv), num_splits, 0);
+    if (left_window < -1) return fail(PKV_E_ARG, "left_window must be -1 (unbounded) or >= 0");
+    std::vector<int32_t> span_len(B);
+    for (int64_t b = 0; b < B; ++b) span_len[b] = valid_len[b] - split_base(valid_len[b], left_window);
+    Plan full = plan_splits(span_len.data(), static_cast<int>(B), static_cast<int>(Hkv), num_splits, 0);
     const size_t need = ws_bytes_for(B, Hq, D, full.S_max);
     if (full.S_max > 1) {
         if (!workspace || workspace_bytes < need)
@@ -896,6 +906,7 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
         a.rows = rows;
         const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
         a.scale_log2 = sc * 1.4426950408889634f;
+        a.window = left_window;
         int total = 0;
         bool any_split = false;
         for (int i = 0; i < rows; ++i) {
@@ -930,6 +941,7 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
                                const pkv_tensor* v_pool, const int32_t* page_table_dev,
                                int32_t max_blocks_per_seq, int32_t block_size,
                                const pkv_pool* pool, const int32_t* p0, float scale,
+                               int32_t left_window,
                                pkv_tensor* out, void* stream) {
     PKV_TRY(check_tensor(q, "q", 4, 4));
     PKV_TRY(check_tensor(out, "out", 4, 4));
@@ -952,6 +964,7 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
     if (block_size != bs) return fail(PKV_E_LAYOUT, "chunk attention: block_size != pool slot count");
     if ((bs & (bs - 1)) != 0) return fail(PKV_E_LAYOUT, "chunk attention: block_size must be a power of two");
     if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "chunk attention: max_blocks_per_seq must be positive");
+    if (left_window < -1) return fail(PKV_E_ARG, "chunk attention: left_window must be -1 (unbounded) or >= 0");
     if (pool && (pool->block_size != bs || pool->num_blocks != NB || pool->maxb != max_blocks_per_seq))
         return fail(PKV_E_LAYOUT, "chunk attention: pool handle does not match the pools");
     if (pool && B > pool->max_seqs) return fail(PKV_E_PAGE, "chunk attention: batch larger than max_seqs");
@@ -989,6 +1002,7 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
         a.row0 = static_cast<int32_t>(b0);
         const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
         a.scale_log2 = sc * 1.4426950408889634f;
+        a.window = left_window;
         for (int i = 0; i < a.rows; ++i) a.p0[i] = p0[b0 + i];
         PKV_HIP(launch_chunk(a, G, s), "chunk attention launch");
     }

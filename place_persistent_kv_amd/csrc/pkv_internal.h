@@ -90,6 +90,7 @@ struct DecodeArgs {
     int32_t S_max;               // split slots per (b, h) in the workspace
     int32_t tps;                 // tokens per split
     int32_t row0, rows;          // batch rows handled by this launch
+    int32_t window;              // left window (-1 = unbounded), see visible_begin
     float scale_log2;            // softmax scale * log2(e)
     int32_t len[kMaxRows];       // valid length per row
     int32_t split_begin[kMaxRows + 1];  // prefix sum of splits per row
@@ -107,6 +108,7 @@ struct Int4DecodeArgs {
     float* ws_ml;
     int32_t Hq, Hkv, bs, maxb, S_max, tps, row0, rows;
     int32_t log2bs;
+    int32_t window;              // left window (-1 = unbounded)
     float scale_log2;
     int32_t len[kMaxRows];
     int32_t split_begin[kMaxRows + 1];
@@ -125,6 +127,17 @@ struct MergeArgs {
 // Fast path: bf16, D == 128, G in {1, 2, 4, 8}, block_size a power of two >= 16 (or contiguous).
 bool fast_decode_supported(int kv_kind, int D, int G, bool paged, int bs);
 hipError_t launch_decode_fast(const DecodeArgs& a, int G, int total_work, hipStream_t s);
+
+// Token range of a row with valid length L under left window W: the query at
+// L - 1 sees [visible_begin, L); splits start at split_base (visible_begin
+// rounded down to whole 64-token quanta, so the fast kernels' 16-token steps
+// stay page-aligned) and tokens before visible_begin are masked.
+__host__ __device__ inline int32_t visible_begin(int32_t L, int32_t W) {
+    return W < 0 ? 0 : (L - 1 - W > 0 ? L - 1 - W : 0);
+}
+__host__ __device__ inline int32_t split_base(int32_t L, int32_t W) {
+    return visible_begin(L, W) / 64 * 64;
+}
 // Any D <= 256, f32/bf16/f16, any block size; tps <= kGenericMaxTps.
 constexpr int kGenericMaxTps = 1024;
 hipError_t launch_decode_generic(const DecodeArgs& a, int total_work, hipStream_t s);
@@ -142,6 +155,7 @@ struct ChunkArgs {
     uint16_t* out;               // [B, Hq, C, 128]
     int32_t Hq, Hkv, C, bs, maxb, row0, rows;
     int32_t log2bs;              // block_size is a power of two
+    int32_t window;              // left window (-1 = unbounded)
     float scale_log2;
     int32_t p0[kMaxRows];
 };

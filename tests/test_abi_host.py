@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if getattr(pkv._lib, n, None) is None]
     assert not missing, missing
     assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
-    assert pkv.abi_version() == 1
+    assert pkv.abi_version() == pkv.ABI_VERSION == 2
 
 
 def R(ptr, dtype, shape):
@@ -192,6 +192,17 @@ def test_decode_shape_and_dtype_errors():
     assert status_of(pkv.decode_attention, Q, KC, VC, [1, 1], R(OUT.ptr, pkv.F16, OUT.shape)) == pkv.E_DTYPE
     assert status_of(pkv.decode_attention, Q, KC, VC, [1, 1], R(OUT.ptr, pkv.BF16, [2, 8, 1, 64])) == pkv.E_LAYOUT
     assert status_of(pkv.decode_attention, Q, KC, VC, [1, 1], R(Q.ptr, pkv.BF16, Q.shape)) == pkv.E_ALIAS
+
+
+def test_left_window_must_be_minus_one_or_more():
+    assert status_of(pkv.decode_attention, Q, KC, VC, [1, 1], OUT, left_window=-2) == pkv.E_ARG
+    table = R(FAKE + 0x2000000, pkv.I32, [2, 8])
+    kp = R(FAKE + 0x100000, pkv.BF16, [32, 2, 16, 128])
+    vp = R(FAKE + 0x900000, pkv.BF16, [32, 2, 16, 128])
+    assert status_of(pkv.paged_decode_attention, Q, kp, vp, table, 8, 16, [4, 4], OUT, left_window=-5) == pkv.E_ARG
+    qc = R(FAKE + 0x3000000, pkv.BF16, [2, 4, 8, 128])
+    oc = R(FAKE + 0x3400000, pkv.BF16, [2, 4, 8, 128])
+    assert status_of(pkv.chunk_attention, qc, kp, vp, table, 8, 16, [0, 0], oc, left_window=-2) == pkv.E_ARG
 
 
 def test_decode_workspace_is_checked():

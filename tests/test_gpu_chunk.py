@@ -67,6 +67,34 @@ def test_chunk_append_and_causal_attention_match_oracle(G, C, bs):
         assert rel_err_rows(got[b], ref) <= 2e-2, b
 
 
+@pytest.mark.parametrize("W,G,C", [(0, 2, 100), (5, 2, 100), (63, 4, 40), (64, 1, 300), (150, 2, 300),
+                                   (1000, 8, 64)])
+def test_chunk_left_window_matches_oracle(W, G, C):
+    """A left window W: query t sees keys [p0 + t - W, p0 + t]; tiles before every window are skipped."""
+    require_gpu()
+    B, Hkv, D, bs = 3, 2, 128, 16
+    Hq = Hkv * G
+    p0 = np.array([0, 37, 400], np.int32)
+    maxb = -(-(int(p0.max()) + C) // bs) + 1
+    d = _setup(950 + W + C, B, Hq, Hkv, D, bs, p0, C, maxb)
+    with pkv.bind_writable(d["kd"]), pkv.bind_writable(d["vd"]):
+        pkv.paged_cache_update(d["lib_pool"], d["kd"], d["table"], bf16_dev(d["new_k"]), p0, C)
+        pkv.paged_cache_update(d["lib_pool"], d["vd"], d["table"], bf16_dev(d["new_v"]), p0, C)
+    ocache.paged_cache_update(d["kp"], d["ref_pool"].table, d["new_k"], p0, C, bs, d["ref_pool"].held)
+    ocache.paged_cache_update(d["vp"], d["ref_pool"].table, d["new_v"], p0, C, bs, d["ref_pool"].held)
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    pkv.chunk_attention(bf16_dev(d["q"]), d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"],
+                        left_window=W)
+    got = onum.bf16_to_f64(bits_host(out))
+    qh = onum.bf16_to_f64(d["q"])
+    for b in range(B):
+        L = int(p0[b]) + C
+        K = onum.bf16_to_f64(ocache.paged_gather(d["kp"], d["ref_pool"].table[b], L, bs))
+        V = onum.bf16_to_f64(ocache.paged_gather(d["vp"], d["ref_pool"].table[b], L, bs))
+        ref = oattn.chunk_attention(qh[b], K, V, int(p0[b]), left_window=W)
+        assert rel_err_rows(got[b], ref) <= 2e-2, b
+
+
 def test_last_chunk_query_equals_decode():
     require_gpu()
     B, Hkv, G, D, bs, C = 2, 2, 2, 128, 16, 48

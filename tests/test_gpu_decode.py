@@ -153,12 +153,13 @@ def _paged_inputs(seed, B, Hq, Hkv, D, bs, lengths, maxb, extra_blocks=3, order=
                 kp_host=kp, vp_host=vp)
 
 
-def _paged_ref(d, lengths):
+def _paged_ref(d, lengths, left_window=-1):
     out = []
     for b, L in enumerate(lengths):
         Hq = d["qh"].shape[1]
         G = Hq // d["k_log"][b].shape[0]
-        out.append(np.stack([oattn.attend(d["qh"][b, h], d["k_log"][b][h // G], d["v_log"][b][h // G],
+        lo = oattn.visible_begin(int(L) - 1, left_window)
+        out.append(np.stack([oattn.attend(d["qh"][b, h], d["k_log"][b][h // G][lo:], d["v_log"][b][h // G][lo:],
                                           1 / np.sqrt(d["qh"].shape[2])) for h in range(Hq)]))
     return np.stack(out)
 
@@ -235,6 +236,36 @@ def test_generic_paths_match_oracle(kind, D, bs, G):
     assert rel_err_rows(out.double().cpu().numpy(), _paged_ref(d, lengths)) <= tol
 
 
+@pytest.mark.parametrize("W", [0, 1, 63, 64, 65, 200, 5000])
+def test_left_window_matches_oracle(W):
+    """Left window W: the query at L - 1 sees keys [L - 1 - W, L - 1] (fast contiguous and paged paths,
+    the generic path, auto and forced splits)."""
+    require_gpu()
+    B, Hkv, D, cap = 4, 2, 128, 700
+    lengths = np.array([1, 70, 333, 700], np.int32)
+    for G in (4, 2):
+        Hq = Hkv * G
+        q, kc, vc, qh, kh, vh = _contig_inputs(760 + W + G, B, Hq, Hkv, D, cap, lengths)
+        ref = oattn.decode_attention(qh, kh, vh, lengths, left_window=W)
+        for S in (0, 3):
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+            ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, cap, S))
+            pkv.decode_attention(q, kc, vc, lengths, out, ws, num_splits=S, left_window=W)
+            assert rel_err_rows(_out_f64(out), ref) <= 4e-3, (G, S)
+        d = _paged_inputs(770 + W + G, B, Hq, Hkv, D, 16, lengths, 48)
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+        ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, 48 * 16))
+        pkv.paged_decode_attention(d["q"], d["kp"], d["vp"], d["table"], 48, 16, lengths, out, ws, pool=d["pool"],
+                                   left_window=W)
+        assert rel_err_rows(_out_f64(out), _paged_ref(d, lengths, W)) <= TOL["bf16"], G
+    # generic path: f32, D = 32, block size 8
+    q, kc, vc, qh, kh, vh = _contig_inputs(780 + W, B, 4, 2, 32, cap, lengths, "f32")
+    out = torch.empty((B, 4, 32), dtype=torch.float32, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, 4, 2, 32, cap))
+    pkv.decode_attention(q, kc, vc, lengths, out, ws, left_window=W)
+    assert rel_err_rows(_out_f64(out), oattn.decode_attention(qh, kh, vh, lengths, left_window=W)) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("G,bs", [(1, 16), (2, 32), (4, 16), (8, 16), (4, 64)])
 def test_int4_paged_decode_matches_oracle(G, bs):
     require_gpu()
@@ -285,3 +316,13 @@ def test_int4_paged_decode_matches_oracle(G, bs):
         pkv.paged_decode_attention_int4(torch.from_numpy(q).to(DEV), kc_d, kp_d, vc_d, vp_d, table, maxb, bs,
                                         lengths, out, ws, pool=lib_pool, num_splits=S)
         assert rel_err_rows(_out_f64(out), ref) <= TOL["int4"], S
+    for W in [0, 17, 100]:          # left window: keys [L - 1 - W, L - 1]
+        ref_w = np.stack([np.stack([oattn.attend(q[b, h].astype(np.float64),
+                                                 k_log[b][h // G][oattn.visible_begin(int(lengths[b]) - 1, W):],
+                                                 v_log[b][h // G][oattn.visible_begin(int(lengths[b]) - 1, W):],
+                                                 1 / np.sqrt(D)) for h in range(Hq)]) for b in range(B)])
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+        ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, maxb * bs))
+        pkv.paged_decode_attention_int4(torch.from_numpy(q).to(DEV), kc_d, kp_d, vc_d, vp_d, table, maxb, bs,
+                                        lengths, out, ws, pool=lib_pool, left_window=W)
+        assert rel_err_rows(_out_f64(out), ref_w) <= TOL["int4"], W
