@@ -613,8 +613,45 @@ def bench_sample(steps, warmup, cpu):
                  greedy_roofline=_hbm_roofline(nbytes, us_greedy), temperature_us=round(us_temp, 2))
 
 
+def bench_window(steps, warmup, cpu):
+    """paged32k pages (32 rows x 32768 tokens, full pool) with a left window of 4095: each query sees its
+    last 4096 tokens, and the pages before the window are not read."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    import synth
+    W = 4095
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    maxb = CTX // BS
+    kp = torch.randn((NB, HKV, BS, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    vp = torch.randn((NB, HKV, BS, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    q = torch.randn((B, HQ, 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    out = torch.empty((B, HQ, 1, D), device=dev, dtype=torch.bfloat16)
+    pool = pkv.Pool(NB, BS, B, maxb, synth.permutation(synth.rng(3, 1), NB))
+    table = torch.full((B, maxb), -1, device=dev, dtype=torch.int32)
+    pool.reserve(range(B), [CTX] * B, table)
+    ws = torch.empty(pkv.decode_workspace_size(B, HQ, HKV, D, CTX), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    us = _timed(lambda i: pkv.paged_decode_attention(q, kp, vp, table, maxb, BS, [CTX] * B, out, ws, pool=pool,
+                                                     left_window=W), steps, warmup, stream)
+    visible = W + 1
+    nbytes = B * visible * HKV * D * 2 * 2 + B * (visible // BS) * 4 + B * HQ * D * 2 * 2
+    cpu_res = None
+    if cpu:
+        rate, n, el = _oracle_decode_rows([visible], HQ, HKV, D, 10.0, 3)
+        cpu_res = {"value": round(rate, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n} rows of 32-head attention over the {visible} visible tokens in {el:.1f} s"}
+    return _line("decode tokens/s, paged bf16 GQA, 32k context with a 4096-token left window", B / (us * 1e-6),
+                 "tokens/s", steps, warmup, us, "bf16",
+                 {"workload": "window", "batch": B, "ctx": CTX, "left_window": W, "q_heads": HQ, "kv_heads": HKV,
+                  "head_dim": D, "block_size": BS, "num_blocks": NB},
+                 _hbm_roofline(nbytes, us), cpu_res, attn_us=round(us, 2), attn_algorithmic_bytes=nbytes)
+
+
 WORKLOADS = {"contig": bench_contig, "paged": bench_paged, "int4": bench_int4, "qwen-decode": bench_qwen_decode,
-             "qwen-chunk": bench_qwen_chunk, "sample": bench_sample}
+             "qwen-chunk": bench_qwen_chunk, "sample": bench_sample, "window": bench_window}
 
 
 def main():

@@ -77,7 +77,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-template <int G>
+template <int G, bool WIN>   // WIN: a left window is set (a.window >= 0)
 __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[kKeys * kKPad];
     __shared__ __attribute__((aligned(16))) uint16_t sVt[kCD * kVPad];
@@ -113,8 +113,8 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     const int wg_first_limit = p0 + t0;      // smallest limit in the workgroup
     // left window: a query at position p sees keys [p - window, p]; tiles below
     // the smallest lower limit are skipped, those below the largest are masked
-    const int wg_lo_first = a.window < 0 ? 0 : max(0, wg_first_limit - a.window);
-    const int wg_lo_last = a.window < 0 ? 0 : max(0, wg_last_key - a.window);
+    const int wg_lo_first = WIN ? max(0, wg_first_limit - a.window) : 0;
+    const int wg_lo_last = WIN ? max(0, wg_last_key - a.window) : 0;
 
     // this lane's two query rows (row groups rg = 0, 1 of the wave)
     int t[kRowGroups], h[kRowGroups], limit[kRowGroups], lo_lim[kRowGroups];
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
         t[rg] = t0 + r / G;
         h[rg] = kvh * G + r % G;
         limit[rg] = p0 + min(t[rg], a.C - 1);
-        lo_lim[rg] = a.window < 0 ? 0 : max(0, limit[rg] - a.window);
+        lo_lim[rg] = WIN ? max(0, limit[rg] - a.window) : 0;
     }
 
     // Q^T operand (B of S^T = K Q^T): lane holds dims 8 hl + 16 s .. +7 of its row
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     auto compute = [&](int k0) {
         // only the diagonal tiles (reaching past the smallest causal limit of
         // the workgroup) test keys against the limits; a uniform branch
-        const bool need_mask = k0 + kKeys - 1 > wg_first_limit || k0 < wg_lo_last;
+        const bool need_mask = k0 + kKeys - 1 > wg_first_limit || (WIN && k0 < wg_lo_last);
 
         // S^T for both 32-key halves, the two accumulation chains interleaved
         f32x16_t s[2][kRowGroups];
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
-                        s[half][rg][e] = key <= limit[rg] && key >= lo_lim[rg] ? s[half][rg][e] : -INFINITY;
+                        s[half][rg][e] = key <= limit[rg] && (!WIN || key >= lo_lim[rg]) ? s[half][rg][e] : -INFINITY;
                     }
                 }
                 float mx = -INFINITY;
@@ -379,10 +379,16 @@ hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s) {
     const int blocks = a.rows * a.Hkv * ((a.C + P - 1) / P);
     if (blocks <= 0) return hipSuccess;
     switch (G) {
-        case 1: hipLaunchKernelGGL(chunk_attention_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(chunk_attention_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(chunk_attention_kernel<4>, dim3(blocks), dim3(kThreads), 0, s, a); break;
-        case 8: hipLaunchKernelGGL(chunk_attention_kernel<8>, dim3(blocks), dim3(kThreads), 0, s, a); break;
+#define PKV_CHUNK(GG)                                                                                  \
+        case GG:                                                                                       \
+            if (a.window >= 0) hipLaunchKernelGGL((chunk_attention_kernel<GG, true>), dim3(blocks), dim3(kThreads), 0, s, a); \
+            else hipLaunchKernelGGL((chunk_attention_kernel<GG, false>), dim3(blocks), dim3(kThreads), 0, s, a); \
+            break;
+        PKV_CHUNK(1)
+        PKV_CHUNK(2)
+        PKV_CHUNK(4)
+        PKV_CHUNK(8)
+#undef PKV_CHUNK
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

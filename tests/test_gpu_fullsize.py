@@ -32,8 +32,9 @@ def _pages_host(pool_dev, ids):
     return bits_host(pool_dev.index_select(0, idx).contiguous())
 
 
-def _paged_decode_case(spec, seed, rows_to_check):
-    """Append one token per row at position L-1, attend over L tokens, check sampled rows."""
+def _paged_decode_case(spec, seed, rows_to_check, left_window=-1):
+    """Append one token per row at position L-1, attend over L tokens (or the last left_window + 1),
+    check sampled rows."""
     gen = torch.Generator(device=DEV)
     gen.manual_seed(seed)
     B, Hq, Hkv, D, bs, NB, maxb = spec.B, spec.Hq, spec.Hkv, spec.D, spec.bs, spec.NB, spec.maxb
@@ -60,7 +61,8 @@ def _paged_decode_case(spec, seed, rows_to_check):
     with pkv.bind_writable(kd), pkv.bind_writable(vd):
         pkv.paged_cache_update(lib_pool, kd, table, nk, pos, 1)
         pkv.paged_cache_update(lib_pool, vd, table, nv, pos, 1)
-    pkv.paged_decode_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, ws, pool=lib_pool)
+    pkv.paged_decode_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, ws, pool=lib_pool,
+                               left_window=left_window)
     got = onum.bf16_to_f64(bits_host(out))
     G = Hq // Hkv
     for b in rows_to_check:
@@ -72,7 +74,8 @@ def _paged_decode_case(spec, seed, rows_to_check):
         K = onum.bf16_to_f64(ocache.paged_gather(kp, local[0], int(L[b]), bs))
         V = onum.bf16_to_f64(ocache.paged_gather(vp, local[0], int(L[b]), bs))
         qb = onum.bf16_to_f64(qh[b])
-        ref = np.stack([oattn.attend(qb[h], K[h // G], V[h // G], 1 / np.sqrt(D)) for h in range(Hq)])
+        lo = oattn.visible_begin(int(L[b]) - 1, left_window)
+        ref = np.stack([oattn.attend(qb[h], K[h // G][lo:], V[h // G][lo:], 1 / np.sqrt(D)) for h in range(Hq)])
         assert rel_err_rows(got[b], ref) <= 2e-2, b
     return got
 
@@ -82,6 +85,13 @@ def test_paged32k_full_size_step():
     require_gpu()
     spec = workloads.paged32k()
     _paged_decode_case(spec, 3, [0, 13, 31])
+
+
+def test_paged32k_window_full_size():
+    """The windowed bench row: the same pool and rows, left window 4095 (the last 4096 tokens)."""
+    require_gpu()
+    spec = workloads.paged32k()
+    _paged_decode_case(spec, 3, [0, 31], left_window=4095)
 
 
 def test_paged_lognormal_full_size():
