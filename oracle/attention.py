@@ -58,9 +58,11 @@ def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                      valid_len, scale=None, left_window: int = -1) -> np.ndarray:
     """Single-token decode over a contiguous cache.
 
-    ``q`` is ``[B, Hq, D]`` (or ``[B, Hq, 1, D]``), ``k_cache``/``v_cache`` are
-    ``[B, Hkv, capacity, D]`` (already float64), ``valid_len`` is ``[B]``; the
-    query sits at position ``valid_len - 1``.  Returns ``[B, Hq, D]`` float64.
+    ``q`` is ``[B, Hq, Dk]`` (or ``[B, Hq, 1, Dk]``), ``k_cache`` is
+    ``[B, Hkv, capacity, Dk]`` and ``v_cache`` ``[B, Hkv, capacity, Dv]``
+    (already float64; K and V head sizes may differ: "Contiguous CPU
+    Attention feedback"), ``valid_len`` is ``[B]``; the query sits at position
+    ``valid_len - 1``.  Returns ``[B, Hq, Dv]`` float64.
     """
     q = np.asarray(q, dtype=np.float64)
     if q.ndim == 4:
@@ -71,7 +73,7 @@ def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         raise ValueError("query heads must be a multiple of K/V heads")
     G = Hq // Hkv
     sc = _scale(D, scale)
-    out = np.empty((B, Hq, D), dtype=np.float64)
+    out = np.empty((B, Hq, v_cache.shape[-1]), dtype=np.float64)
     for b in range(B):
         L = int(valid_len[b])
         if L < 1:

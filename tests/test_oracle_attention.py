@@ -116,3 +116,21 @@ def test_chunk_reduces_to_decode():
     assert np.array_equal(out[:, -1], last)
     one = attention.chunk_attention(q[:, :1], K[:, :p0 + 1], V[:, :p0 + 1], p0)
     assert np.array_equal(one[:, 0], attention.decode_attention(q[None, :, 0], K[None], V[None], [p0 + 1])[0])
+
+
+def test_value_head_size_may_differ_from_key_head_size():
+    """Dk != Dv: torch float64 scaled_dot_product_attention takes a value width of its own."""
+    g = synth.rng(911)
+    B, Hq, Hkv, Dk, Dv, cap = 2, 4, 2, 16, 24, 30
+    L = np.array([7, 30], np.int32)
+    q = synth.normal(g, (B, Hq, Dk)).astype(np.float64)
+    k = synth.normal(g, (B, Hkv, cap, Dk)).astype(np.float64)
+    v = synth.normal(g, (B, Hkv, cap, Dv)).astype(np.float64)
+    got = attention.decode_attention(q, k, v, L)
+    assert got.shape == (B, Hq, Dv)
+    for b in range(B):
+        for h in range(Hq):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b, h])[None, None], torch.from_numpy(k[b, h // 2, :L[b]])[None],
+                torch.from_numpy(v[b, h // 2, :L[b]])[None])[0, 0].numpy()
+            np.testing.assert_allclose(got[b, h], ref, rtol=1e-12, atol=1e-12)
