@@ -71,7 +71,8 @@ typedef enum pkv_dtype {
     PKV_F16 = 2,
     PKV_U8 = 3,
     PKV_I32 = 4,
-    PKV_I64 = 5
+    PKV_I64 = 5,
+    PKV_F64 = 6   /* sampled logits only */
 } pkv_dtype;
 
 typedef struct pkv_tensor {
@@ -235,24 +236,28 @@ pkv_status pkv_paged_gather(const pkv_tensor* pool_kv, const int32_t* page_table
 /* ------------------------------------------------------------------------ */
 
 /* Workspace (bytes) the decode entry points need for B rows, Hq query heads,
- * head size D and contexts of up to max_len tokens with `num_splits` (0 =
- * library choice, the same rule the call uses). */
+ * value head size D and contexts of up to max_len tokens with `num_splits`
+ * (0 = library choice, the same rule the call uses). */
 size_t pkv_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                  int32_t max_len, int32_t num_splits);
 
-/* q       : [B, Hq, 1, D] or [B, Hq, D], f32 or bf16.
- * k_cache, v_cache: [B, Hkv, capacity, D], same dtype as q, Hq % Hkv == 0.
+/* q       : [B, Hq, 1, Dk] or [B, Hq, Dk], f32, bf16 or f16.
+ * k_cache : [B, Hkv, capacity, Dk]; v_cache [B, Hkv, capacity, Dv] (K and V
+ *           head sizes may differ: "Persistent input/output feedback",
+ *           "Contiguous CPU Attention feedback"), Dk, Dv <= 256, same dtype
+ *           as q, Hq % Hkv == 0.  bf16 / f16 with Dk = Dv = 128 and
+ *           Hq / Hkv in {1, 2, 4, 8} takes the fast kernel.
  * valid_len: host int32[B], 1 <= valid_len[b] <= capacity (includes the
  *           token appended by this step).
- * scale   : softmax scale; <= 0 means 1/sqrt(D).
+ * scale   : softmax scale; <= 0 means 1/sqrt(Dk).
  * left_window: -1 = unbounded; W >= 0 = the query (at position
  *           valid_len[b] - 1) sees only keys [max(0, valid_len[b] - 1 - W),
  *           valid_len[b] - 1] ("Persistent input/output feedback", "Optional
  *           heterogeneous paged KV", "Versioned operator schema":
  *           left_window_size).  Pages and rows wholly before the window are
  *           not read.  Values below -1: PKV_E_ARG.
- * out     : same shape as q; dtype of q or f32.  Query head h reads K/V head
- *           h / (Hq / Hkv).
+ * out     : q's shape with Dv last; dtype of q or f32.  Query head h reads
+ *           K/V head h / (Hq / Hkv).
  * workspace: device scratch of pkv_decode_workspace_size(...) bytes, 256-byte
  *           aligned; contents need no initialisation.
  * num_splits: 0 lets the library split long contexts; otherwise each row's
@@ -262,7 +267,8 @@ pkv_status pkv_decode_attention(const pkv_tensor* q, const pkv_tensor* k_cache,
                                 float scale, int32_t left_window, pkv_tensor* out, void* workspace,
                                 size_t workspace_bytes, int32_t num_splits, void* stream);
 
-/* Paged bf16/f32: k_pool, v_pool [num_blocks, Hkv, block_size, D];
+/* Paged f32/bf16/f16: k_pool [num_blocks, Hkv, block_size, Dk], v_pool
+ * [num_blocks, Hkv, block_size, Dv];
  * page_table_dev int32[>= B, max_blocks_per_seq]; block_size must equal
  * k_pool->shape[2].  When `pool` is not NULL every row must hold
  * ceil(valid_len[b] / block_size) reserved pages (else PKV_E_PAGE). */
@@ -320,7 +326,8 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
 
 size_t pkv_sample_workspace_size(int32_t B, int64_t V);
 
-/* logits : [B, V] or [B, S, V], f32, bf16 or f16, finite.
+/* logits : [B, V] or [B, S, V], f32, f64, bf16 or f16, finite; f64 logits are
+ *          rounded to f32 (nearest even) before the draw.
  * temperature == 0: argmax, lowest index on ties.  temperature > 0: the
  * Gumbel-max draw argmax_v (fl32(x_v * fl32(1/T)) - log(-log u_v)) with
  * u_v = ((h >> 40) | 1) * 2^-24 and h output number b*V + v + 1 of

@@ -49,8 +49,8 @@ if len(_hip_runtimes_loaded()) > 1:
 # C types
 # ---------------------------------------------------------------------------
 MAX_DIMS = 6
-F32, BF16, F16, U8, I32, I64 = range(6)
-_ESIZE = {F32: 4, BF16: 2, F16: 2, U8: 1, I32: 4, I64: 8}
+F32, BF16, F16, U8, I32, I64, F64 = range(7)
+_ESIZE = {F32: 4, BF16: 2, F16: 2, U8: 1, I32: 4, I64: 8, F64: 8}
 
 OK, E_ARG, E_CAPACITY, E_READONLY, E_ALIAS, E_BUSY, E_PAGE, E_NOMEM, E_DTYPE, E_LAYOUT, E_HIP = range(11)
 STATUS_NAMES = {OK: "OK", E_ARG: "E_ARG", E_CAPACITY: "E_CAPACITY", E_READONLY: "E_READONLY",
@@ -157,7 +157,7 @@ class Raw:
 def _torch_dtype_code(t) -> int:
     import torch
     table = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.uint8: U8,
-             torch.int32: I32, torch.int64: I64}
+             torch.int32: I32, torch.int64: I64, torch.float64: F64}
     if t.dtype not in table:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return table[t.dtype]

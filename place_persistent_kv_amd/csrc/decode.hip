@@ -43,7 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kD = 128;
 constexpr float kLazy = 8.0f;  // rescale only when a score exceeds the running max by 2^8
 
-template <int G, bool PAGED>
+template <int G, bool PAGED, bool F16>   // F16: fp16 q/K/V (else bf16)
 __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     __shared__ float s_o[kWaves][G][kD];
     __shared__ float s_ml[kWaves][G][2];
@@ -52,6 +52,13 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 3;  // token within an 8-token slab
     const int j = lane & 7;     // 16-byte chunk within each half row
+    auto dot2k = [](uint32_t x, uint32_t y, float c) { return F16 ? dot2_f16(x, y, c) : dot2_bf16(x, y, c); };
+    auto cv_lo = [](uint32_t w) {
+        return F16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w))) : bf_lo(w);
+    };
+    auto cv_hi = [](uint32_t w) {
+        return F16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16))) : bf_hi(w);
+    };
 
     const int work = blockIdx.x;
     const int kvh = work % a.Hkv;
@@ -133,22 +140,22 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float x = 0.0f, y = 0.0f;
-            x = dot2_bf16(qa[g].x, u.ka0.x, x);
-            y = dot2_bf16(qa[g].x, u.ka1.x, y);
-            x = dot2_bf16(qa[g].y, u.ka0.y, x);
-            y = dot2_bf16(qa[g].y, u.ka1.y, y);
-            x = dot2_bf16(qa[g].z, u.ka0.z, x);
-            y = dot2_bf16(qa[g].z, u.ka1.z, y);
-            x = dot2_bf16(qa[g].w, u.ka0.w, x);
-            y = dot2_bf16(qa[g].w, u.ka1.w, y);
-            x = dot2_bf16(qb[g].x, u.kb0.x, x);
-            y = dot2_bf16(qb[g].x, u.kb1.x, y);
-            x = dot2_bf16(qb[g].y, u.kb0.y, x);
-            y = dot2_bf16(qb[g].y, u.kb1.y, y);
-            x = dot2_bf16(qb[g].z, u.kb0.z, x);
-            y = dot2_bf16(qb[g].z, u.kb1.z, y);
-            x = dot2_bf16(qb[g].w, u.kb0.w, x);
-            y = dot2_bf16(qb[g].w, u.kb1.w, y);
+            x = dot2k(qa[g].x, u.ka0.x, x);
+            y = dot2k(qa[g].x, u.ka1.x, y);
+            x = dot2k(qa[g].y, u.ka0.y, x);
+            y = dot2k(qa[g].y, u.ka1.y, y);
+            x = dot2k(qa[g].z, u.ka0.z, x);
+            y = dot2k(qa[g].z, u.ka1.z, y);
+            x = dot2k(qa[g].w, u.ka0.w, x);
+            y = dot2k(qa[g].w, u.ka1.w, y);
+            x = dot2k(qb[g].x, u.kb0.x, x);
+            y = dot2k(qb[g].x, u.kb1.x, y);
+            x = dot2k(qb[g].y, u.kb0.y, x);
+            y = dot2k(qb[g].y, u.kb1.y, y);
+            x = dot2k(qb[g].z, u.kb0.z, x);
+            y = dot2k(qb[g].z, u.kb1.z, y);
+            x = dot2k(qb[g].w, u.kb0.w, x);
+            y = dot2k(qb[g].w, u.kb1.w, y);
             s0[g] = group8_sum(x) * a.scale_log2;
             s1[g] = group8_sum(y) * a.scale_log2;
             s0[g] = live0 ? s0[g] : -INFINITY;
@@ -159,10 +166,10 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
         float v0[16], v1[16];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            v0[2 * k] = bf_lo(w0[k]);
-            v0[2 * k + 1] = bf_hi(w0[k]);
-            v1[2 * k] = bf_lo(w1[k]);
-            v1[2 * k + 1] = bf_hi(w1[k]);
+            v0[2 * k] = cv_lo(w0[k]);
+            v0[2 * k + 1] = cv_hi(w0[k]);
+            v1[2 * k] = cv_lo(w1[k]);
+            v1[2 * k + 1] = cv_hi(w1[k]);
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -259,6 +266,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
         if (nsplit == 1) {
             const float y = os / ls;
             if (a.out_f32) static_cast<float*>(a.out)[bh * kD + d] = y;
+            else if (F16) static_cast<_Float16*>(a.out)[bh * kD + d] = static_cast<_Float16>(y);
             else static_cast<uint16_t*>(a.out)[bh * kD + d] = f32_to_bf16_rne(y);
         } else {
             const int64_t slot = bh * a.S_max + split;
@@ -310,6 +318,14 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
         }
         return ((int64_t(b) * a.Hkv + kvh) * a.cap + t) * D;
     };
+    const int Dv = a.Dv;
+    auto vrow = [&](int t) -> int64_t {  // element offset of token t's value row
+        if (a.page_table) {
+            const int page = a.page_table[int64_t(b) * a.maxb + t / a.bs];
+            return ((int64_t(page) * a.Hkv + kvh) * a.bs + t % a.bs) * Dv;
+        }
+        return ((int64_t(b) * a.Hkv + kvh) * a.cap + t) * Dv;
+    };
 
     // pass 1: scores (lanes over tokens)
     float mx = -FLT_MAX;
@@ -333,10 +349,10 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 
     // pass 2: weighted values (lanes over dims)
     const int64_t slot = (int64_t(b) * a.Hq + h) * a.S_max + split;
-    for (int d = lane; d < D; d += 64) {
+    for (int d = lane; d < Dv; d += 64) {
         float acc = 0.0f;
-        for (int t = ta; t < t1; ++t) acc = fmaf(s_p[t - t0], to_f32(V[row(t) + d]), acc);
-        a.ws_o[slot * D + d] = acc;
+        for (int t = ta; t < t1; ++t) acc = fmaf(s_p[t - t0], to_f32(V[vrow(t) + d]), acc);
+        a.ws_o[slot * Dv + d] = acc;
     }
     if (lane == 0) {
         a.ws_ml[slot * 2 + 0] = mx;
@@ -418,7 +434,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }  // namespace
 
 bool fast_decode_supported(int kv_kind, int D, int G, bool paged, int bs) {
-    if (kv_kind != kKvBF16 || D != kD) return false;
+    if ((kv_kind != kKvBF16 && kv_kind != kKvF16) || D != kD) return false;
     if (G != 1 && G != 2 && G != 4 && G != 8) return false;
     if (paged && (bs < kSlabTokens || (bs & (bs - 1)) != 0)) return false;
     return true;
@@ -428,10 +444,16 @@ hipError_t launch_decode_fast(const DecodeArgs& a, int G, int total_work, hipStr
     if (total_work <= 0) return hipSuccess;
     const dim3 grid(total_work), block(256);
     const bool paged = a.page_table != nullptr;
+    const bool f16 = a.kv_kind == kKvF16;
 #define PKV_FAST(GG)                                                                              \
     if (G == GG) {                                                                                \
-        if (paged) hipLaunchKernelGGL((decode_fast_kernel<GG, true>), grid, block, 0, s, a);     \
-        else hipLaunchKernelGGL((decode_fast_kernel<GG, false>), grid, block, 0, s, a);          \
+        if (f16) {                                                                                \
+            if (paged) hipLaunchKernelGGL((decode_fast_kernel<GG, true, true>), grid, block, 0, s, a); \
+            else hipLaunchKernelGGL((decode_fast_kernel<GG, false, true>), grid, block, 0, s, a);    \
+        } else {                                                                                  \
+            if (paged) hipLaunchKernelGGL((decode_fast_kernel<GG, true, false>), grid, block, 0, s, a); \
+            else hipLaunchKernelGGL((decode_fast_kernel<GG, false, false>), grid, block, 0, s, a);   \
+        }                                                                                         \
         return hipGetLastError();                                                                 \
     }
     PKV_FAST(1)

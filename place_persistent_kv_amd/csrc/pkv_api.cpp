@@ -72,6 +72,7 @@ int64_t dtype_size(int32_t dt) {
         case PKV_U8: return 1;
         case PKV_I32: return 4;
         case PKV_I64: return 8;
+        case PKV_F64: return 8;
         default: return 0;
     }
 }
@@ -629,16 +630,19 @@ struct QView {
     int64_t B, Hq, D;
 };
 
-pkv_status check_q_out(const pkv_tensor* q, const pkv_tensor* out, QView* v) {
+// q [B, Hq, (1,) Dk]; out the same with the last dim dv (dv < 0: Dk)
+pkv_status check_q_out(const pkv_tensor* q, const pkv_tensor* out, QView* v, int64_t dv = -1) {
     PKV_TRY(check_tensor(q, "q", 3, 4));
     PKV_TRY(check_tensor(out, "out", 3, 4));
     if (q->ndim == 4 && q->shape[2] != 1) return fail(PKV_E_LAYOUT, "q must be [B, Hq, 1, D] or [B, Hq, D]");
     v->B = q->shape[0];
     v->Hq = q->shape[1];
     v->D = q->shape[q->ndim - 1];
-    if (out->ndim != q->ndim) return fail(PKV_E_LAYOUT, "out must have the shape of q");
+    if (dv < 0) dv = v->D;
+    if (out->ndim != q->ndim) return fail(PKV_E_LAYOUT, "out must have the shape of q (value head size last)");
     for (int i = 0; i < q->ndim; ++i)
-        if (out->shape[i] != q->shape[i]) return fail(PKV_E_LAYOUT, "out must have the shape of q");
+        if (out->shape[i] != (i == q->ndim - 1 ? dv : q->shape[i]))
+            return fail(PKV_E_LAYOUT, "out must have the shape of q (value head size last)");
     return PKV_OK;
 }
 
@@ -649,18 +653,20 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
                          int32_t left_window, pkv_tensor* out, void* ws, size_t ws_bytes,
                          int32_t num_splits, void* stream) {
     QView qv;
-    PKV_TRY(check_q_out(q, out, &qv));
     PKV_TRY(check_tensor(k, "k", 4, 4));
     PKV_TRY(check_tensor(v, "v", 4, 4));
+    const int64_t Dv = v->shape[3];                  // value head size (may differ from the key's)
+    PKV_TRY(check_q_out(q, out, &qv, Dv));
     const int64_t B = qv.B, Hq = qv.Hq, D = qv.D;
     const int64_t Hkv = k->shape[1];
     const int kind = kv_kind_of(q->dtype);
     if (kind < 0) return fail(PKV_E_DTYPE, "q must be f32, bf16 or f16");
     if (k->dtype != q->dtype || v->dtype != q->dtype) return fail(PKV_E_DTYPE, "q, k and v must share a dtype");
     if (out->dtype != q->dtype && out->dtype != PKV_F32) return fail(PKV_E_DTYPE, "out must have q's dtype or f32");
-    for (int i = 0; i < 4; ++i)
-        if (v->shape[i] != k->shape[i]) return fail(PKV_E_LAYOUT, "k and v must have the same shape");
-    if (k->shape[3] != D) return fail(PKV_E_LAYOUT, "k/v head size %lld != q head size %lld", (long long)k->shape[3], (long long)D);
+    for (int i = 0; i < 3; ++i)
+        if (v->shape[i] != k->shape[i]) return fail(PKV_E_LAYOUT, "k and v must agree in all but the head size");
+    if (k->shape[3] != D) return fail(PKV_E_LAYOUT, "k head size %lld != q head size %lld", (long long)k->shape[3], (long long)D);
+    if (Dv <= 0 || Dv > 256) return fail(PKV_E_LAYOUT, "value head size must be in [1, 256]");
     if (Hkv <= 0 || Hq % Hkv != 0) return fail(PKV_E_LAYOUT, "query heads %lld must be a multiple of K/V heads %lld", (long long)Hq, (long long)Hkv);
     if (D <= 0 || D > 256) return fail(PKV_E_LAYOUT, "head size must be in [1, 256]");
     if (num_splits < 0) return fail(PKV_E_ARG, "num_splits must be >= 0");
@@ -696,14 +702,14 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
     if (B == 0 || Hq == 0) return ok();
 
     const int G = static_cast<int>(Hq / Hkv);
-    const bool fast = fast_decode_supported(kind, static_cast<int>(D), G, paged, bs);
+    const bool fast = Dv == D && fast_decode_supported(kind, static_cast<int>(D), G, paged, bs);
     // size the workspace for the whole call (all row groups share it)
     // splits cover only each row's visible range (from its 64-token quantum on)
     std::vector<int32_t> span_len(B);
     for (int64_t b = 0; b < B; ++b) span_len[b] = valid_len[b] - split_base(valid_len[b], left_window);
     Plan full = plan_splits(span_len.data(), static_cast<int>(B), fast ? static_cast<int>(Hkv) : static_cast<int>(Hq),
                             num_splits, fast ? 0 : kGenericMaxTps);
-    const size_t need = ws_bytes_for(B, Hq, D, full.S_max);
+    const size_t need = ws_bytes_for(B, Hq, Dv, full.S_max);
     if (full.S_max > 1 || !fast) {
         if (!ws || ws_bytes < need)
             return fail(PKV_E_NOMEM, "workspace of %zu bytes needed, %zu given (pkv_decode_workspace_size)", need, ws_bytes);
@@ -712,7 +718,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
             return fail(PKV_E_ALIAS, "workspace overlaps an input or the output");
         if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(PKV_E_ARG, "workspace must be 256-byte aligned");
     }
-    const size_t o_bytes = (static_cast<size_t>(B * Hq * full.S_max * D) * 4 + 255) & ~size_t(255);
+    const size_t o_bytes = (static_cast<size_t>(B * Hq * full.S_max * Dv) * 4 + 255) & ~size_t(255);
     float* ws_o = static_cast<float*>(ws);
     float* ws_ml = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes) : nullptr;
 
@@ -729,17 +735,18 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
             a.page_table = page_table + b0 * maxb;
         } else {
             a.k = static_cast<const uint8_t*>(k->data) + b0 * Hkv * cap * D * esz;
-            a.v = static_cast<const uint8_t*>(v->data) + b0 * Hkv * cap * D * esz;
+            a.v = static_cast<const uint8_t*>(v->data) + b0 * Hkv * cap * Dv * esz;
             a.page_table = nullptr;
         }
-        a.out = static_cast<uint8_t*>(out->data) + b0 * Hq * D * out_esz;
-        a.ws_o = ws_o ? ws_o + b0 * Hq * full.S_max * D : nullptr;
+        a.out = static_cast<uint8_t*>(out->data) + b0 * Hq * Dv * out_esz;
+        a.ws_o = ws_o ? ws_o + b0 * Hq * full.S_max * Dv : nullptr;
         a.ws_ml = ws_ml ? ws_ml + b0 * Hq * full.S_max * 2 : nullptr;
         a.kv_kind = kind;
         a.out_f32 = out->dtype == PKV_F32 && q->dtype != PKV_F32;
         a.Hq = static_cast<int32_t>(Hq);
         a.Hkv = static_cast<int32_t>(Hkv);
         a.D = static_cast<int32_t>(D);
+        a.Dv = static_cast<int32_t>(Dv);
         a.cap = static_cast<int32_t>(paged ? 0 : cap);
         a.bs = paged ? bs : 0;
         a.maxb = paged ? maxb : 0;
@@ -773,7 +780,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
             m.out = a.out;
             m.out_kind = kv_kind_of(out->dtype);
             m.Hq = a.Hq;
-            m.D = a.D;
+            m.D = a.Dv;
             m.S_max = a.S_max;
             m.row0 = a.row0;
             m.rows = rows;
@@ -1037,8 +1044,8 @@ size_t pkv_sample_workspace_size(int32_t B, int64_t V) {
 pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed,
                       int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream) {
     PKV_TRY(check_tensor(logits, "logits", 2, 3));
-    const int kind = kv_kind_of(logits->dtype);
-    if (kind < 0) return fail(PKV_E_DTYPE, "sample: logits must be f32, bf16 or f16");
+    const int kind = logits->dtype == PKV_F64 ? kKvF64 : kv_kind_of(logits->dtype);
+    if (kind < 0) return fail(PKV_E_DTYPE, "sample: logits must be f32, f64, bf16 or f16");
     if (!(temperature >= 0.0f) || std::isinf(temperature))
         return fail(PKV_E_ARG, "sample: temperature must be finite and >= 0");
     if (!out_ids) return fail(PKV_E_ARG, "sample: null out_ids");

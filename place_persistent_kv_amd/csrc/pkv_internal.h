@@ -71,7 +71,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 // ---------------------------------------------------------------------------
 // Decode attention
 // ---------------------------------------------------------------------------
-enum KvKind : int32_t { kKvF32 = 0, kKvBF16 = 1, kKvF16 = 2 };
+enum KvKind : int32_t { kKvF32 = 0, kKvBF16 = 1, kKvF16 = 2, kKvF64 = 3 };   // f64: sampled logits only
 
 struct DecodeArgs {
     const void* q;               // [B, Hq, D]
@@ -83,7 +83,8 @@ struct DecodeArgs {
     float* ws_ml;                // [B, Hq, S_max, 2]  (running max (log2 units), sum)
     int32_t kv_kind;             // KvKind of q/k/v
     int32_t out_f32;             // 1: out is f32, 0: out has the KV element type
-    int32_t Hq, Hkv, D;
+    int32_t Hq, Hkv, D;          // D: query / key head size
+    int32_t Dv;                  // value (and output) head size
     int32_t cap;                 // contiguous capacity (tokens per row)
     int32_t bs, maxb;            // paged block size, page-table row length
     int32_t log2bs;              // log2(bs) (fast kernel: bs is a power of two >= 16)
@@ -124,7 +125,7 @@ struct MergeArgs {
     int32_t nsplit[kMaxRows];
 };
 
-// Fast path: bf16, D == 128, G in {1, 2, 4, 8}, block_size a power of two >= 16 (or contiguous).
+// Fast path: bf16 or f16, D == 128, G in {1, 2, 4, 8}, block_size a power of two >= 16 (or contiguous).
 bool fast_decode_supported(int kv_kind, int D, int G, bool paged, int bs);
 hipError_t launch_decode_fast(const DecodeArgs& a, int G, int total_work, hipStream_t s);
 

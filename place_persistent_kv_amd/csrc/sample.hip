@@ -34,6 +34,7 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t k) {
 template <int KIND>
 __device__ __forceinline__ float logit_at(const void* p, int64_t i) {
     if constexpr (KIND == kKvF32) return static_cast<const float*>(p)[i];
+    else if constexpr (KIND == kKvF64) return static_cast<float>(static_cast<const double*>(p)[i]);   // RNE
     else if constexpr (KIND == kKvBF16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
     else return static_cast<float>(static_cast<const _Float16*>(p)[i]);
 }
@@ -44,6 +45,8 @@ typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 template <int KIND>
 __device__ __forceinline__ float logit_of(u32x4v_t w, int e) {
     if constexpr (KIND == kKvF32) return __uint_as_float(w[e]);
+    if constexpr (KIND == kKvF64)
+        return static_cast<float>(__builtin_bit_cast(double, (uint64_t(w[2 * e + 1]) << 32) | w[2 * e]));
     const uint32_t h = (e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xFFFFu);
     if constexpr (KIND == kKvBF16) return __uint_as_float(h << 16);
     else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
@@ -93,13 +96,12 @@ template <int KIND, bool GREEDY, bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs a) {
     __shared__ float s_val[kSampleThreads / 64];
     __shared__ int32_t s_idx[kSampleThreads / 64];
-    constexpr int W = KIND == kKvF32 ? 4 : 8;   // logits per 16-byte vector
+    constexpr int W = KIND == kKvF64 ? 2 : KIND == kKvF32 ? 4 : 8;   // logits per 16-byte vector
     const int b = blockIdx.y;
     const int c = blockIdx.x;
     const int64_t beg = int64_t(c) * a.chunk_len;
     const int64_t end = min(a.V, beg + a.chunk_len);
-    const void* row = KIND == kKvF32 ? static_cast<const void*>(static_cast<const float*>(a.logits) + b * a.row_stride)
-                                     : static_cast<const void*>(static_cast<const uint16_t*>(a.logits) + b * a.row_stride);
+    const void* row = static_cast<const uint8_t*>(a.logits) + b * a.row_stride * (16 / W);
     float best = -INFINITY;
     int32_t bidx = INT32_MAX;
     // state of logit v: seed + (b * V + v + 1) * gamma
@@ -183,7 +185,7 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
     if (a.B <= 0) return hipSuccess;
     const dim3 grid(a.chunks, a.B), block(kSampleThreads);
     // 16-byte vectors when every row start is 16-byte aligned
-    const int esize = a.kind == kKvF32 ? 4 : 2;
+    const int esize = a.kind == kKvF64 ? 8 : a.kind == kKvF32 ? 4 : 2;
     const bool vec = reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 && (a.row_stride * esize) % 16 == 0 &&
                      (a.chunk_len * esize) % 16 == 0;
 #define PKV_SAMPLE(K, V)                                                                           \
@@ -194,9 +196,11 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
     PKV_SAMPLE(kKvF32, true)
     PKV_SAMPLE(kKvBF16, true)
     PKV_SAMPLE(kKvF16, true)
+    PKV_SAMPLE(kKvF64, true)
     PKV_SAMPLE(kKvF32, false)
     PKV_SAMPLE(kKvBF16, false)
     PKV_SAMPLE(kKvF16, false)
+    PKV_SAMPLE(kKvF64, false)
 #undef PKV_SAMPLE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -236,6 +236,64 @@ def test_generic_paths_match_oracle(kind, D, bs, G):
     assert rel_err_rows(out.double().cpu().numpy(), _paged_ref(d, lengths)) <= tol
 
 
+@pytest.mark.parametrize("kind,Dk,Dv,bs", [("bf16", 64, 128, 16), ("f32", 128, 48, 8), ("f16", 32, 256, 16)])
+def test_value_head_size_of_its_own(kind, Dk, Dv, bs):
+    """K and V head sizes differ (generic kernel), contiguous and paged, with and without splits."""
+    require_gpu()
+    B, Hq, Hkv, cap, maxb = 3, 8, 2, 300, 40
+    lengths = np.array([1, 150, 300], np.int32)
+    g = synth.rng(790 + Dk + Dv)
+    qf, kf, vf = (synth.normal(g, sh) for sh in [(B, Hq, Dk), (B, Hkv, cap, Dk), (B, Hkv, cap, Dv)])
+    (qs, qh), (ks, kh), (vs, vh) = (_encode(x, kind) for x in (qf, kf, vf))
+    ref = oattn.decode_attention(qh, kh, vh, lengths)
+    tol = TOL["f32"] if kind == "f32" else TOL["bf16"]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[kind]
+    for S in (0, 3):
+        out = torch.empty((B, Hq, Dv), dtype=tdt, device=DEV)
+        ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, Dv, cap, S))
+        pkv.decode_attention(_to_dev(qs, kind), _to_dev(ks, kind), _to_dev(vs, kind), lengths, out, ws, num_splits=S)
+        torch.cuda.synchronize()
+        assert rel_err_rows(out.double().cpu().numpy(), ref) <= tol, S
+    # paged: the pools take each row's logical K / V through the oracle's page layout
+    NB = int(sum(-(-int(L) // bs) for L in lengths)) + 2
+    order = synth.permutation(g, NB)
+    ref_pool = ocache.PagePool(NB, bs, B, maxb, order)
+    lib_pool = pkv.Pool(NB, bs, B, maxb, order)
+    table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+    lib_pool.reserve(range(B), lengths.tolist(), table)
+    kp = np.zeros((NB, Hkv, bs, Dk), ks.dtype)
+    vp = np.zeros((NB, Hkv, bs, Dv), vs.dtype)
+    for b in range(B):
+        L = int(lengths[b])
+        ref_pool.reserve(b, L)
+        ocache.paged_cache_update(kp, ref_pool.table[b:b + 1], ks[b:b + 1, :, :L], [0], L, bs)
+        ocache.paged_cache_update(vp, ref_pool.table[b:b + 1], vs[b:b + 1, :, :L], [0], L, bs)
+    out = torch.empty((B, Hq, Dv), dtype=tdt, device=DEV)
+    ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, Dv, maxb * bs))
+    pkv.paged_decode_attention(_to_dev(qs, kind), _to_dev(kp, kind), _to_dev(vp, kind), table, maxb, bs, lengths,
+                               out, ws, pool=lib_pool, left_window=120)
+    torch.cuda.synchronize()
+    ref_w = oattn.decode_attention(qh, kh, vh, lengths, left_window=120)
+    assert rel_err_rows(out.double().cpu().numpy(), ref_w) <= tol
+
+
+@pytest.mark.parametrize("G,bs", [(2, 16), (8, 32)])
+def test_f16_fast_paged_matches_oracle(G, bs):
+    require_gpu()
+    B, Hkv, D, maxb = 4, 2, 128, 30
+    Hq = Hkv * G
+    lengths = np.array([1, 17, 300, 30 * bs - 5], np.int32)
+    d = _paged_inputs(795 + G, B, Hq, Hkv, D, bs, lengths, maxb, kind="f16")
+    ref = _paged_ref(d, lengths)
+    for S in (0, 4):
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=DEV)
+        ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, maxb * bs, S))
+        pkv.paged_decode_attention(d["q"], d["kp"], d["vp"], d["table"], maxb, bs, lengths, out, ws,
+                                   pool=d["pool"], num_splits=S)
+        torch.cuda.synchronize()
+        assert rel_err_rows(out.double().cpu().numpy(), ref) <= 2e-3, S       # f16 output rounding is 2^-11
+
+
 @pytest.mark.parametrize("W", [0, 1, 63, 64, 65, 200, 5000])
 def test_left_window_matches_oracle(W):
     """Left window W: the query at L - 1 sees keys [L - 1 - W, L - 1] (fast contiguous and paged paths,

@@ -19,6 +19,9 @@ pytestmark = pytest.mark.gpu
 def _logits_dev(x32, kind):
     if kind == "f32":
         return torch.from_numpy(x32).to(DEV), x32
+    if kind == "f64":       # digits below float32's precision: both sides round each logit to f32 first
+        x64 = x32.astype(np.float64) * (1.0 + 1e-9 * np.sin(np.arange(x32.size)).reshape(x32.shape))
+        return torch.from_numpy(x64).to(DEV), x64.astype(np.float32)
     if kind == "bf16":
         bits = synth.f32_to_bf16_bits(x32)
         return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16), onum.bf16_to_f64(bits).astype(np.float32)
@@ -35,7 +38,7 @@ def _run(logits, T, seed):
     return ids.cpu().numpy()
 
 
-@pytest.mark.parametrize("kind", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("kind", ["f32", "bf16", "f16", "f64"])
 @pytest.mark.parametrize("B,V", [(5, 1000), (3, 151936), (130, 4097)])
 def test_greedy_is_bit_exact(kind, B, V):
     require_gpu()
@@ -55,7 +58,7 @@ def test_greedy_uses_the_last_position():
     assert np.array_equal(_run(dev, 0.0, 0), osamp.greedy(xh))
 
 
-@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["f32", "bf16", "f64"])
 def test_temperature_draws_agree_with_the_oracle(kind):
     require_gpu()
     B, V, T = 64, 151936, 0.7
