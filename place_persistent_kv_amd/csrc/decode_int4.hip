@@ -12,26 +12,26 @@
 // parameters.  A wave takes its tokens in groups of 16 (one page holds a
 // whole group: block_size is a power of two >= 16).
 //
-// Q.K on the matrix cores.  For every 32-dim block b the G query heads (rows,
-// query split into bf16 high + low parts for float32-grade products) meet the
-// raw codes of 16 tokens in v_mfma_f32_16x16x32_bf16.  A code c enters as the
-// bf16 number 128 + c, whose bit pattern is 0x4300 | c, so two codes become
-// one operand word with a shift, a mask and an or.  With qs_b = sum of q over
-// block b, the dequantised product is
+// Q.K on the matrix cores, in 4x4x4 blocks (v_mfma_f32_4x4x4bf16_1k): block
+// (token group tg of 4, 32-dim block qb) multiplies the 4 query heads (rows;
+// query split into bf16 high + low parts for float32-grade products) by the
+// raw codes of 4 tokens, 4 dims per step, 8 steps per block.  A code c enters
+// as the bf16 number 128 + c, whose bit pattern is 0x4300 | c, so two codes
+// become one operand word with one v_and_or_b32.  With qs_b = sum of q over
+// block b the dequantised product is
 //     q . k = sum_b s_b * (S_b - (128 + z_b) * qs_b),   S_b = sum_{d in b} q_d (128 + c_d)
-// Operand layouts (checked on the device), lane l, element e = 0..7:
-//   A[i][k]: i = l % 16, k = 8 (l / 16) + e;  B[k][j]: k = 8 (l / 16) + e, j = l % 16
-//   C[i][j]: register r holds i = 4 (l / 16) + r, j = l % 16
-// so a lane ends with the scores of token l % 16 for heads 4 (l / 16) + r.
-// Within a block the dims are taken in the order the code words unpack to
-// (pair m of a word = nibbles m and m + 4); the query operand uses the same
-// order.
+// Each lane loads its own token's 16 code bytes and (scale, zero) of one
+// block, applies that block's dequantisation to its 4 head results, and a
+// row rotation sums the four blocks; the lane then keeps one (token, head)
+// score, so every lane of the softmax carries a distinct score (a 16-row MFMA
+// would leave 12 of its 16 rows empty at 4 heads).
 //
 // P.V on the vector ALUs, the dequantisation folded in:
 //     o += p * s * c - p * s * z   (the second term kept per block)
 // with LPT lanes per token, each owning DPL dims.  The running max of every
-// head is wave-uniform (a row reduction plus v_readlane), so the lazy
-// rescale is a uniform branch and the lanes' partial outputs are plain sums.
+// head is wave-uniform (a reduction over the head's lanes plus v_readlane),
+// so the lazy rescale is a uniform branch and the lanes' partial outputs are
+// plain sums.
 // The split / merge structure is that of the bf16 fast kernel.
 
 #include "device_common.h"
@@ -44,7 +44,6 @@ constexpr int kD4 = 128;
 constexpr int kGroup = 16;       // tokens per Q.K step
 constexpr float kLazy4 = 8.0f;
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -52,9 +51,13 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
-__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                   0, 0, 0);
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_4x4x4bf16_1k: 16 independent 4x4x4 products; lane 4b + i holds
+// A_b[i][0..3], lane 4b + j holds B_b[0..3][j] and D_b[0..3][j] (checked on the device)
+__device__ __forceinline__ f32x4_t mfma4(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                  0, 0, 0);
 }
 
 // A constant in a VGPR, opaque to the optimiser, so that (x & m) | c with
@@ -64,33 +67,6 @@ __device__ __forceinline__ uint32_t vconst(uint32_t c) {
     uint32_t r;
     asm("v_mov_b32 %0, %1" : "=v"(r) : "n"(c));
     return r;
-}
-
-// eight codes (one word) -> B operand: pair m = (128 + nibble m, 128 + nibble m + 4);
-// mask = 0x000F000F, bias = 0x43004300 (128.0 in both bf16 halves)
-__device__ __forceinline__ u32x4_t codes_operand(uint32_t w, uint32_t mask, uint32_t bias) {
-    u32x4_t r;
-    r[0] = (w & mask) | bias;
-    r[1] = ((w >> 4) & mask) | bias;
-    r[2] = ((w >> 8) & mask) | bias;
-    r[3] = ((w >> 12) & mask) | bias;
-    return r;
-}
-
-// all-reduce over the 16 lanes of a row
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
-    return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    x += dpp<0x140>(x);
-    return x;
 }
 
 __device__ __forceinline__ float readlane_f(float x, int lane) {
@@ -123,8 +99,8 @@ __device__ __forceinline__ void unpack_codes(const uint32_t (&w)[(CB + 3) / 4], 
 
 template <int G>
 __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
-    constexpr int R = G < 4 ? G : 4;            // score registers in use per lane
-    constexpr int NQ = (G + 3) / 4;             // lane quads that hold heads
+    constexpr int HP = G < 4 ? G : 4;           // heads per Q.K pass (rows of the 4x4 blocks)
+    constexpr int NP = (G + 3) / 4;             // Q.K passes
     constexpr int DPL = G <= 2 ? 32 : 64 / G;   // dims per lane in P.V
     constexpr int LPT = kD4 / DPL;              // lanes per token in P.V
     constexpr int TPR = 64 / LPT;               // tokens per P.V round
@@ -138,8 +114,13 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int col = lane & 15;      // Q.K: token of the group
-    const int q4 = lane >> 4;       // Q.K: lane quad
+    // Q.K lanes: 16 blocks b = 4 tg + qb of 4 lanes; lane 16 tg + 4 qb + jj holds
+    // token 4 tg + jj of the group, 32-dim block qb (B operand and result), and
+    // head row jj of block qb (A operand)
+    const int qtg = lane >> 4;
+    const int qb = (lane >> 2) & 3;
+    const int jj = lane & 3;
+    const int tok = 4 * qtg + jj;
     const int tl = lane / LPT;      // P.V: token of the round
     const int dc = lane % LPT;      // P.V: dims DPL * dc ..
 
@@ -158,37 +139,51 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
     const int wend = min(t1, wbeg + quarter);
     const int32_t* __restrict__ pt = a.page_table + int64_t(b) * a.maxb;
 
-    // ---- query operands (rows = heads, zero rows past G), hi + lo parts
-    u32x4_t qa_hi[4], qa_lo[4];
-    {
-        const float* Q = a.q + (int64_t(b) * a.Hq + kvh * G + min(col, G - 1)) * kD4;
+    // ---- query operands: A rows = heads 4 p + jj (zero past G), 4 dims per
+    // step in the order the code words unpack to, hi + lo bf16 parts
+    // (step s: dims 8 (s / 2) + {0, 4, 1, 5} for even s, {2, 6, 3, 7} for odd s)
+    u32x2_t qa_hi[NP][8], qa_lo[NP][8];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
+    for (int p = 0; p < NP; ++p) {
+        const int head = 4 * p + jj;
+        const float* Q = a.q + (int64_t(b) * a.Hq + kvh * G + min(head, G - 1)) * kD4 + 32 * qb;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int d = 32 * blk + 8 * q4 + m;
-                const float x0 = col < G ? Q[d] : 0.0f, x1 = col < G ? Q[d + 4] : 0.0f;
+        for (int st = 0; st < 8; ++st) {
+            const int d0 = 8 * (st >> 1) + 2 * (st & 1);
+            const int dims[4] = {d0, d0 + 4, d0 + 1, d0 + 5};
+            uint32_t hw[2], lw[2];
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const float x0 = head < G ? Q[dims[2 * e2]] : 0.0f;
+                const float x1 = head < G ? Q[dims[2 * e2 + 1]] : 0.0f;
                 const __bf16 h0 = static_cast<__bf16>(x0), h1 = static_cast<__bf16>(x1);
                 const __bf16 l0 = static_cast<__bf16>(x0 - static_cast<float>(h0));
                 const __bf16 l1 = static_cast<__bf16>(x1 - static_cast<float>(h1));
-                qa_hi[blk][m] = __builtin_bit_cast(uint32_t, bf16x2_t{h0, h1});
-                qa_lo[blk][m] = __builtin_bit_cast(uint32_t, bf16x2_t{l0, l1});
+                hw[e2] = __builtin_bit_cast(uint32_t, bf16x2_t{h0, h1});
+                lw[e2] = __builtin_bit_cast(uint32_t, bf16x2_t{l0, l1});
             }
+            qa_hi[p][st] = u32x2_t{hw[0], hw[1]};
+            qa_lo[p][st] = u32x2_t{lw[0], lw[1]};
         }
     }
-    // qs_b for the heads of this lane's score registers: the operands times ones
-    f32x4_t qs[4];
+    // qs: sum of q over block qb for the heads 4 p + r of this lane's results
+    // (the operands times ones, accumulated over the eight steps)
+    f32x4_t qs[NP];
     {
-        const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        const u32x2_t ones = {0x3F803F80u, 0x3F803F80u};
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            qs[blk] = mfma16(qa_hi[blk], ones, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            qs[blk] = mfma16(qa_lo[blk], ones, qs[blk]);
+        for (int p = 0; p < NP; ++p) {
+            qs[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                qs[p] = mfma4(qa_hi[p][st], ones, qs[p]);
+                qs[p] = mfma4(qa_lo[p][st], ones, qs[p]);
+            }
         }
     }
 
     const uint32_t nib_mask = vconst(0x000F000Fu), nib_bias = vconst(0x43004300u);
-    float m[G], lp[R], o[G][DPL], corr[G];
+    float m[G], lp[NP], o[G][DPL], corr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = -FLT_MAX;
@@ -197,13 +192,13 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
         for (int d = 0; d < DPL; ++d) o[g][d] = 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i) lp[i] = 0.0f;
+    for (int p = 0; p < NP; ++p) lp[p] = 0.0f;
 
     // ---- one group's loads.  Rows past the wave's range are clamped to its
     // last token (valid data, masked later).
     struct Stage {
-        uint32_t kc[4];               // Q.K: code word of block b for token col
-        u32x4_t kp;                   // Q.K: (scale, zero) of the 4 blocks of token col
+        u32x4_t kc;                   // Q.K: the 32 codes of block qb of token tok
+        uint32_t kp;                  // Q.K: (scale, zero) of that block
         uint32_t vc[ROUNDS][CW];      // P.V: code words of this lane's dims
         uint32_t vp[ROUNDS];          // P.V: (scale, zero) of their block
     };
@@ -214,11 +209,9 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
         Stage st;
         const int64_t rb = row_base(ts, page);
         const int last = wend - 1 - ts;
-        const int64_t rk = rb + min(col, last);
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-            st.kc[blk] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.kc + rk * 64 + 16 * blk + 4 * q4));
-        st.kp = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.kp + rk * 8));
+        const int64_t rk = rb + min(tok, last);
+        st.kc = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.kc + rk * 64 + 16 * qb));
+        st.kp = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.kp + rk * 8 + 2 * qb));
 #pragma unroll
         for (int rd = 0; rd < ROUNDS; ++rd) {
             const int64_t rv = rb + min(tl + TPR * rd, last);
@@ -241,52 +234,70 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
     };
 
     auto compute = [&](const Stage& st, int ts) {
-        // scores of token col for heads 4 q4 + i
-        f32x4_t c[4];
+        // block-qb partial products of token tok for heads 4 p + r (hi and lo
+        // chains accumulate separately), eight steps of four dims
+        f32x4_t dh[NP], dl[NP];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const u32x4_t kb = codes_operand(st.kc[blk], nib_mask, nib_bias);
-            c[blk] = mfma16(qa_hi[blk], kb, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            c[blk] = mfma16(qa_lo[blk], kb, c[blk]);
-        }
-        const bool live = ts + col < wend && ts + col >= vis0;
-        float s[R];
+        for (int p = 0; p < NP; ++p) dh[p] = dl[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            float acc = 0.0f;
+        for (int stp = 0; stp < 8; ++stp) {
+            const uint32_t w = st.kc[stp >> 1] >> (8 * (stp & 1));
+            const u32x2_t kb = {(w & nib_mask) | nib_bias, ((w >> 4) & nib_mask) | nib_bias};
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const float sc = h2f(st.kp[blk] & 0xFFFFu);
-                const float zz = 128.0f + h2f(st.kp[blk] >> 16);
-                acc = fmaf(sc, fmaf(-zz, qs[blk][i], c[blk][i]), acc);
+            for (int p = 0; p < NP; ++p) {
+                dh[p] = mfma4(qa_hi[p][stp], kb, dh[p]);
+                dl[p] = mfma4(qa_lo[p][stp], kb, dl[p]);
             }
-            s[i] = live ? acc * a.scale_log2 : -INFINITY;
         }
-        // group maxima per head, wave-uniform; lazy rescale
+        const float sc = h2f(st.kp & 0xFFFFu);
+        const float zz = 128.0f + h2f(st.kp >> 16);
+        const bool tok_live = ts + tok < wend && ts + tok >= vis0;
+        float s[NP];
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const float mx = row16_max(s[i]);
+        for (int p = 0; p < NP; ++p) {
+            // dequantised block contribution, summed over the four blocks (lanes
+            // 4 apart in the row), then this lane keeps head 4 p + qb
+            float tot[4];
 #pragma unroll
-            for (int qq = 0; qq < NQ; ++qq) {
-                const int g = 4 * qq + i;
-                const float mg = readlane_f(mx, 16 * qq);
+            for (int r = 0; r < 4; ++r) {
+                float x = sc * fmaf(-zz, qs[p][r], dh[p][r] + dl[p][r]);
+                x += dpp<0x124>(x);   // row_ror:4
+                x += dpp<0x128>(x);   // row_ror:8
+                tot[r] = x;
+            }
+            const float mine = qb == 0 ? tot[0] : qb == 1 ? tot[1] : qb == 2 ? tot[2] : tot[3];
+            s[p] = tok_live && 4 * p + qb < G ? mine * a.scale_log2 : -INFINITY;
+        }
+        // group maxima per head (lanes with the same qb), wave-uniform; lazy rescale
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            float mx = fmaxf(s[p], dpp<0xB1>(s[p]));   // quad_perm [1,0,3,2]
+            mx = fmaxf(mx, dpp<0x4E>(mx));              // quad_perm [2,3,0,1]
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+            for (int hh = 0; hh < HP; ++hh) {
+                const int g = 4 * p + hh;
+                const float mg = readlane_f(mx, 4 * hh);
                 if (mg > m[g] + kLazy4) {
                     const float cf = exp2_fast(m[g] - mg);
                     corr[g] *= cf;
 #pragma unroll
                     for (int d = 0; d < DPL; ++d) o[g][d] *= cf;
-                    if (q4 == qq) lp[i] *= cf;
+                    if (qb == hh) lp[p] *= cf;
                     m[g] = mg;
                 }
             }
         }
         // probabilities to LDS for the P.V lanes
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const float mrow = (NQ > 1 && q4 == 1) ? m[(4 + i) % G] : m[i];
-            const float p = exp2_fast(s[i] - mrow);
-            lp[i] += p;
-            if (q4 < NQ) s_p[wave][col][4 * q4 + i] = p;
+        for (int p = 0; p < NP; ++p) {
+            float mrow = m[4 * p];
+#pragma unroll
+            for (int hh = 1; hh < HP; ++hh) mrow = qb == hh ? m[4 * p + hh] : mrow;
+            const float pr = exp2_fast(s[p] - mrow);
+            lp[p] += pr;
+            if (4 * p + qb < G) s_p[wave][tok][4 * p + qb] = pr;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -354,10 +365,13 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
             for (int d = 0; d < DPL; ++d) o[g][d] += __shfl_xor(o[g][d], off);
     float l[G];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const float rs = row16_sum(lp[i]);
+    for (int p = 0; p < NP; ++p) {
+        float rs = lp[p] + dpp<0xB1>(lp[p]);
+        rs += dpp<0x4E>(rs);
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) l[4 * qq + i] = readlane_f(rs, 16 * qq);
+        for (int hh = 0; hh < HP; ++hh) l[4 * p + hh] = readlane_f(rs, 4 * hh);
     }
     if (tl == 0) {
 #pragma unroll
