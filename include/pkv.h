@@ -8,7 +8,8 @@
  *   1. an in-place cache update whose result is the input storage
  *      (contiguous or paged; optionally quantising new rows to INT4),
  *   2. attention of the new queries over the valid cache prefix
- *      (contiguous, paged bf16, paged INT4; a causal chunk variant),
+ *      (contiguous, paged bf16, paged INT4, pages of mixed formats; a
+ *      causal chunk variant),
  *   3. greedy or seeded temperature sampling of final logits.
  *
  * Sources: the onnx-light documentation pages "Mutable execution cache"
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -315,6 +316,99 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
                                int32_t max_blocks_per_seq, int32_t block_size,
                                const pkv_pool* pool, const int32_t* p0, float scale,
                                int32_t left_window, pkv_tensor* out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Mixed-format pages                                                        */
+/* "Persistent input/output feedback", "Optional heterogeneous paged KV":
+ * every append picks the storage of the pages it creates, dense or affine
+ * INT8, UINT8, INT4, UINT4, INT2 or UINT2, K and V independently, with one
+ * scalar scale and zero point; the choice is stored with each new page, so
+ * successive appends may use different formats without converting earlier
+ * pages.  Section "Selected-block quantization": chosen pages are re-encoded
+ * from their dense or affine payload.  "Custom, quantized, and persistent
+ * values", "Struct types and byte-encodable layouts" and "Quantization
+ * examples": codes packed least-significant bits first, signed codes in two's
+ * complement, value (code - zero_point) * scale.
+ *
+ * Storage: K and V slot pools, each bf16 or f16 [num_blocks, H, block_size, D]
+ * (only the bytes matter: one slot of block_size * D * 2 bytes per (page,
+ * head)).  A page's rows are packed from the start of its slot, row t at byte
+ * t * D * bits / 8, so a pool of BF16 pages is a plain bf16 pool.  The format
+ * of every physical page lives in a descriptor table `page_desc`: u8
+ * [num_blocks, 16], one pkv_page_desc per page, owned by the caller.        */
+/* ------------------------------------------------------------------------ */
+
+typedef enum pkv_page_storage {
+    PKV_PAGE_BF16 = 0,   /* dense bfloat16 */
+    PKV_PAGE_F16 = 1,    /* dense IEEE binary16 */
+    PKV_PAGE_INT8 = 2,   /* affine codes -128..127 */
+    PKV_PAGE_UINT8 = 3,  /* affine codes 0..255 */
+    PKV_PAGE_INT4 = 4,   /* affine codes -8..7, two per byte */
+    PKV_PAGE_UINT4 = 5,  /* affine codes 0..15, two per byte */
+    PKV_PAGE_INT2 = 6,   /* affine codes -2..1, four per byte */
+    PKV_PAGE_UINT2 = 7   /* affine codes 0..3, four per byte */
+} pkv_page_storage;
+
+/* Format of the K or V rows of a page, as requested by a call.  Affine
+ * storages need a positive finite scale and an integer zero point in the code
+ * range; dense storages ignore both. */
+typedef struct pkv_page_format {
+    int32_t storage;     /* pkv_page_storage */
+    float scale;
+    int32_t zero_point;
+} pkv_page_format;
+
+/* Device descriptor of one physical page (16 bytes, written by the library). */
+typedef struct pkv_page_desc {
+    float k_scale, v_scale;
+    int16_t k_zero, v_zero;
+    uint8_t k_storage, v_storage;
+    uint8_t reserved[2];
+} pkv_page_desc;
+
+/* Append update_length new tokens of every row at position[b] (host int32[B]).
+ * k_values, v_values: bf16 [B, H, update_length, D], D a multiple of 16, no
+ * overlap with the pools or the table.  A page whose first slot this call
+ * writes gets k_format / v_format (and its descriptor); rows that continue a
+ * partly filled page are encoded in that page's stored format.  Affine codes:
+ * clamp(rint(x / scale) + zero_point) with a correctly rounded float32 divide
+ * (ties to even); F16 pages round to nearest even.  Pools, page_desc and
+ * values 16-byte aligned.  Errors as pkv_paged_cache_update, plus PKV_E_ARG
+ * for a bad format.  The pools and page_desc must be in writable bindings. */
+pkv_status pkv_mixed_cache_update(const pkv_pool* pool, const pkv_tensor* k_pool,
+                                  const pkv_tensor* v_pool, const pkv_tensor* page_desc,
+                                  const int32_t* page_table_dev, const pkv_tensor* k_values,
+                                  const pkv_tensor* v_values, const int32_t* position,
+                                  int32_t update_length, pkv_page_format k_format,
+                                  pkv_page_format v_format, void* stream);
+
+/* Re-encode pages: for i < n_pages, rows [0, valid_rows[i]) of physical page
+ * pages[i] (both host int32 arrays) are decoded ((code - zero) * scale as
+ * one float32 multiply, or the dense value) and encoded in the new format;
+ * rows [valid_rows[i], block_size) become the new format's zero.  k_format /
+ * v_format NULL keeps that tensor.  Bytes of a slot past the new rows are
+ * left as they were.  Every page must have been written by an append.
+ * Errors (nothing is written): PKV_E_ARG for duplicate pages, a valid row
+ * count outside [0, block_size] or a bad format; PKV_E_PAGE for a page id
+ * outside [0, num_blocks); PKV_E_LAYOUT when block_size * D * 2 > 65536. */
+pkv_status pkv_mixed_convert_pages(const pkv_tensor* k_pool, const pkv_tensor* v_pool,
+                                   const pkv_tensor* page_desc, const int32_t* pages,
+                                   const int32_t* valid_rows, int32_t n_pages,
+                                   const pkv_page_format* k_format,
+                                   const pkv_page_format* v_format, void* stream);
+
+/* Decode attention over mixed pages (as pkv_paged_decode_attention): q bf16
+ * [B, Hq, (1,) 128], out bf16 or f32, Hq / Hkv in {1, 2, 4, 8}, block_size a
+ * power of two >= 16.  Affine K/V are decoded in registers and never
+ * materialised; the token appended by the step is read back as stored. */
+pkv_status pkv_paged_decode_attention_mixed(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                            const pkv_tensor* v_pool, const pkv_tensor* page_desc,
+                                            const int32_t* page_table_dev,
+                                            int32_t max_blocks_per_seq, int32_t block_size,
+                                            const pkv_pool* pool, const int32_t* valid_len,
+                                            float scale, int32_t left_window, pkv_tensor* out,
+                                            void* workspace, size_t workspace_bytes,
+                                            int32_t num_splits, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Sampling                                                                  */

@@ -63,6 +63,35 @@ class PkvTensor(C.Structure):
                 ("shape", C.c_int64 * MAX_DIMS)]
 
 
+class PageFormat(C.Structure):
+    """``pkv_page_format``: storage code, scale and zero point of new or converted pages."""
+    _fields_ = [("storage", C.c_int32), ("scale", C.c_float), ("zero_point", C.c_int32)]
+
+
+PAGE_BF16, PAGE_F16, PAGE_INT8, PAGE_UINT8, PAGE_INT4, PAGE_UINT4, PAGE_INT2, PAGE_UINT2 = range(8)
+PAGE_STORAGES = {"BF16": PAGE_BF16, "F16": PAGE_F16, "INT8": PAGE_INT8, "UINT8": PAGE_UINT8,
+                 "INT4": PAGE_INT4, "UINT4": PAGE_UINT4, "INT2": PAGE_INT2, "UINT2": PAGE_UINT2}
+
+
+def page_format(storage, scale: float = 1.0, zero_point: int = 0) -> PageFormat:
+    """A :class:`PageFormat` from a storage name (``"INT8"``) or code."""
+    code = PAGE_STORAGES[storage] if isinstance(storage, str) else int(storage)
+    return PageFormat(code, float(scale), int(zero_point))
+
+
+class LengthThresholdSelector:
+    """A format selector: one (K, V) format pair while fewer than ``threshold``
+    tokens are retained, another afterwards ("Persistent input/output feedback",
+    "Optional heterogeneous paged KV": a selector picks the formats of the pages
+    an append creates from the retained length)."""
+
+    def __init__(self, threshold: int, early: tuple, late: tuple):
+        self.threshold, self.early, self.late = int(threshold), early, late
+
+    def __call__(self, retained: int) -> tuple:
+        return self.early if retained < self.threshold else self.late
+
+
 class PkvError(RuntimeError):
     """A libpkv call returned a non-zero status; ``.status`` holds it."""
 
@@ -101,6 +130,12 @@ _SIG = {
                                                   C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_chunk_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float, C.c_int32,
                                       _T, _VP]),
+    "pkv_mixed_cache_update": (C.c_int, [_VP, _T, _T, _T, _VP, _T, _T, _I32P, C.c_int32, PageFormat, PageFormat,
+                                         _VP]),
+    "pkv_mixed_convert_pages": (C.c_int, [_T, _T, _T, _I32P, _I32P, C.c_int32, _P(PageFormat), _P(PageFormat),
+                                          _VP]),
+    "pkv_paged_decode_attention_mixed": (C.c_int, [_T, _T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P,
+                                                   C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_sample_workspace_size": (C.c_size_t, [C.c_int32, C.c_int64]),
     "pkv_sample": (C.c_int, [_T, C.c_float, C.c_uint64, _VP, _VP, C.c_size_t, _VP]),
 }
@@ -112,7 +147,7 @@ for _name, (_res, _args) in _SIG.items():
         _fn.argtypes = _args
 
 
-ABI_VERSION = 2      # the argument lists above follow this version of include/pkv.h
+ABI_VERSION = 3      # the argument lists above follow this version of include/pkv.h
 if _lib.pkv_abi_version() != ABI_VERSION:
     raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
                       "rebuild it (python -m place_persistent_kv_amd.build)")
@@ -396,6 +431,44 @@ def chunk_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, bloc
                                     _i32_array(p0), float(scale), int(left_window), C.byref(desc(out)),
                                     _stream(stream)),
            "pkv_chunk_attention")
+
+
+# ---------------------------------------------------------------------------
+# Mixed-format pages
+# ---------------------------------------------------------------------------
+def mixed_page_desc(num_blocks: int, device="cuda"):
+    """A zeroed descriptor table ``u8 [num_blocks, 16]`` (every page BF16)."""
+    import torch
+    return torch.zeros((num_blocks, 16), dtype=torch.uint8, device=device)
+
+
+def mixed_cache_update(pool: Pool, k_pool, v_pool, page_desc, page_table, k_values, v_values, position,
+                       update_length: int, k_format: PageFormat, v_format: PageFormat, stream=None) -> None:
+    _check(_lib.pkv_mixed_cache_update(_pool_handle(pool), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+                                       C.byref(desc(page_desc)), _ptr(page_table), C.byref(desc(k_values)),
+                                       C.byref(desc(v_values)), _i32_array(position), int(update_length),
+                                       k_format, v_format, _stream(stream)), "pkv_mixed_cache_update")
+
+
+def mixed_convert_pages(k_pool, v_pool, page_desc, pages, valid_rows, k_format: Optional[PageFormat] = None,
+                        v_format: Optional[PageFormat] = None, stream=None) -> None:
+    pages, valid_rows = list(pages), list(valid_rows)
+    _check(_lib.pkv_mixed_convert_pages(C.byref(desc(k_pool)), C.byref(desc(v_pool)), C.byref(desc(page_desc)),
+                                        _i32_array(pages), _i32_array(valid_rows), len(pages),
+                                        None if k_format is None else C.byref(k_format),
+                                        None if v_format is None else C.byref(v_format), _stream(stream)),
+           "pkv_mixed_convert_pages")
+
+
+def paged_decode_attention_mixed(q, k_pool, v_pool, page_desc, page_table, max_blocks_per_seq: int,
+                                 block_size: int, valid_len, out, workspace=None, pool: Optional[Pool] = None,
+                                 scale: float = 0.0, num_splits: int = 0, stream=None,
+                                 left_window: int = -1) -> None:
+    _check(_lib.pkv_paged_decode_attention_mixed(
+        C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)), C.byref(desc(page_desc)), _ptr(page_table),
+        int(max_blocks_per_seq), int(block_size), _pool_handle(pool), _i32_array(valid_len), float(scale),
+        int(left_window), C.byref(desc(out)), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
+        int(num_splits), _stream(stream)), "pkv_paged_decode_attention_mixed")
 
 
 # ---------------------------------------------------------------------------

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -651,7 +652,8 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
                          bool paged, const int32_t* page_table, int32_t maxb, int32_t bs,
                          const pkv_pool* pool, const int32_t* valid_len, float scale,
                          int32_t left_window, pkv_tensor* out, void* ws, size_t ws_bytes,
-                         int32_t num_splits, void* stream) {
+                         int32_t num_splits, void* stream, const pkv_tensor* page_desc = nullptr) {
+    const bool mixed = page_desc != nullptr;
     QView qv;
     PKV_TRY(check_tensor(k, "k", 4, 4));
     PKV_TRY(check_tensor(v, "v", 4, 4));
@@ -661,7 +663,13 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
     const int64_t Hkv = k->shape[1];
     const int kind = kv_kind_of(q->dtype);
     if (kind < 0) return fail(PKV_E_DTYPE, "q must be f32, bf16 or f16");
-    if (k->dtype != q->dtype || v->dtype != q->dtype) return fail(PKV_E_DTYPE, "q, k and v must share a dtype");
+    if (mixed) {
+        if (q->dtype != PKV_BF16) return fail(PKV_E_DTYPE, "mixed pages: q must be bf16");
+        if (dtype_size(k->dtype) != 2 || dtype_size(v->dtype) != 2)
+            return fail(PKV_E_DTYPE, "mixed pages: the slot pools are described as bf16 or f16 tensors");
+    } else if (k->dtype != q->dtype || v->dtype != q->dtype) {
+        return fail(PKV_E_DTYPE, "q, k and v must share a dtype");
+    }
     if (out->dtype != q->dtype && out->dtype != PKV_F32) return fail(PKV_E_DTYPE, "out must have q's dtype or f32");
     for (int i = 0; i < 3; ++i)
         if (v->shape[i] != k->shape[i]) return fail(PKV_E_LAYOUT, "k and v must agree in all but the head size");
@@ -695,6 +703,17 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
     }
     if (!(scale == scale) || std::isinf(scale)) return fail(PKV_E_ARG, "scale must be finite");
     if (left_window < -1) return fail(PKV_E_ARG, "left_window must be -1 (unbounded) or >= 0");
+    if (mixed) {
+        PKV_TRY(check_tensor(page_desc, "page_desc", 2, 2));
+        if (page_desc->dtype != PKV_U8 || page_desc->shape[0] != k->shape[0] || page_desc->shape[1] != 16)
+            return fail(PKV_E_LAYOUT, "page_desc must be u8 [num_blocks, 16]");
+        if (!mixed_decode_supported(static_cast<int>(D), static_cast<int>(Hq / Hkv), bs) || Dv != D)
+            return fail(PKV_E_LAYOUT, "mixed pages: D = 128, Hq / Hkv in {1, 2, 4, 8}, block_size a power of two >= 16");
+        if (reinterpret_cast<uintptr_t>(k->data) % 16 || reinterpret_cast<uintptr_t>(v->data) % 16 ||
+            reinterpret_cast<uintptr_t>(page_desc->data) % 16 || reinterpret_cast<uintptr_t>(q->data) % 16)
+            return fail(PKV_E_LAYOUT, "mixed pages: pools, page_desc and q must be 16-byte aligned");
+        PKV_TRY(check_disjoint(page_desc, "page_desc", span(out), "out"));
+    }
     const Span os = span(out);
     PKV_TRY(check_disjoint(q, "q", os, "out"));
     PKV_TRY(check_disjoint(k, "k", os, "out"));
@@ -702,7 +721,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
     if (B == 0 || Hq == 0) return ok();
 
     const int G = static_cast<int>(Hq / Hkv);
-    const bool fast = Dv == D && fast_decode_supported(kind, static_cast<int>(D), G, paged, bs);
+    const bool fast = mixed || (Dv == D && fast_decode_supported(kind, static_cast<int>(D), G, paged, bs));
     // size the workspace for the whole call (all row groups share it)
     // splits cover only each row's visible range (from its 64-token quantum on)
     std::vector<int32_t> span_len(B);
@@ -759,6 +778,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
         a.scale_log2 = sc * 1.4426950408889634f;
         a.window = left_window;
+        a.page_desc = mixed ? page_desc->data : nullptr;
         int total = 0;
         bool any_split = false;
         for (int i = 0; i < rows; ++i) {
@@ -768,7 +788,9 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
             any_split |= full.nsplit[b0 + i] > 1;
         }
         a.split_begin[rows] = total;
-        if (fast) {
+        if (mixed) {
+            PKV_HIP(launch_decode_mixed(a, G, total * static_cast<int>(Hkv), s), "mixed decode launch");
+        } else if (fast) {
             PKV_HIP(launch_decode_fast(a, G, total * static_cast<int>(Hkv), s), "decode launch");
         } else {
             PKV_HIP(launch_decode_generic(a, total * static_cast<int>(Hq), s), "decode launch");
@@ -813,6 +835,212 @@ pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_p
                          valid_len, scale, left_window, out, workspace, workspace_bytes, num_splits, stream);
 }
 
+
+pkv_status pkv_paged_decode_attention_mixed(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                            const pkv_tensor* v_pool, const pkv_tensor* page_desc,
+                                            const int32_t* page_table_dev,
+                                            int32_t max_blocks_per_seq, int32_t block_size,
+                                            const pkv_pool* pool, const int32_t* valid_len,
+                                            float scale, int32_t left_window, pkv_tensor* out,
+                                            void* workspace, size_t workspace_bytes,
+                                            int32_t num_splits, void* stream) {
+    if (!page_desc) return fail(PKV_E_ARG, "decode_attention_mixed: null page_desc");
+    return decode_common(q, k_pool, v_pool, true, page_table_dev, max_blocks_per_seq, block_size, pool,
+                         valid_len, scale, left_window, out, workspace, workspace_bytes, num_splits, stream,
+                         page_desc);
+}
+
+static_assert(sizeof(pkv_page_desc) == sizeof(PageDesc) && offsetof(pkv_page_desc, v_scale) == offsetof(PageDesc, v_scale) &&
+                  offsetof(pkv_page_desc, k_zero) == offsetof(PageDesc, k_zero) &&
+                  offsetof(pkv_page_desc, k_storage) == offsetof(PageDesc, k_st) &&
+                  offsetof(pkv_page_desc, v_storage) == offsetof(PageDesc, v_st),
+              "pkv_page_desc and the kernels' descriptor share one layout");
+
+namespace {
+
+// A requested page format: storage in range; affine: positive finite scale and
+// an integer zero point inside the code range.  Dense formats are stored with
+// scale 1 and zero point 0.
+pkv_status check_page_format(const pkv_page_format& f, const char* name) {
+    if (f.storage < PKV_PAGE_BF16 || f.storage > PKV_PAGE_UINT2)
+        return fail(PKV_E_ARG, "%s: unknown page storage %d", name, f.storage);
+    if (f.storage >= PKV_PAGE_INT8) {
+        if (!(f.scale > 0.0f) || std::isinf(f.scale)) return fail(PKV_E_ARG, "%s: scale must be positive and finite", name);
+        const int nb = storage_bits(f.storage);
+        const int lo = storage_signed(f.storage) ? -(1 << (nb - 1)) : 0;
+        const int hi = storage_signed(f.storage) ? (1 << (nb - 1)) - 1 : (1 << nb) - 1;
+        if (f.zero_point < lo || f.zero_point > hi)
+            return fail(PKV_E_ARG, "%s: zero point %d outside the code range [%d, %d]", name, f.zero_point, lo, hi);
+    }
+    return PKV_OK;
+}
+
+void set_desc(PageDesc& d, const pkv_page_format& f, bool v) {
+    const bool aff = f.storage >= PKV_PAGE_INT8;
+    const float sc = aff ? f.scale : 1.0f;
+    const int16_t z = static_cast<int16_t>(aff ? f.zero_point : 0);
+    if (v) {
+        d.v_st = static_cast<uint8_t>(f.storage);
+        d.v_scale = sc;
+        d.v_zero = z;
+    } else {
+        d.k_st = static_cast<uint8_t>(f.storage);
+        d.k_scale = sc;
+        d.k_zero = z;
+    }
+}
+
+// The two slot pools and the descriptor table of a mixed pool.
+pkv_status check_mixed_pools(const pkv_tensor* k_pool, const pkv_tensor* v_pool, const pkv_tensor* page_desc,
+                             const char* who) {
+    PKV_TRY(check_tensor(k_pool, "k_pool", 4, 4));
+    PKV_TRY(check_tensor(v_pool, "v_pool", 4, 4));
+    PKV_TRY(check_tensor(page_desc, "page_desc", 2, 2));
+    if (dtype_size(k_pool->dtype) != 2 || dtype_size(v_pool->dtype) != 2)
+        return fail(PKV_E_DTYPE, "%s: the slot pools are described as bf16 or f16 tensors", who);
+    for (int i = 0; i < 4; ++i)
+        if (k_pool->shape[i] != v_pool->shape[i]) return fail(PKV_E_LAYOUT, "%s: k_pool and v_pool shapes differ", who);
+    if (page_desc->dtype != PKV_U8 || page_desc->shape[0] != k_pool->shape[0] || page_desc->shape[1] != 16)
+        return fail(PKV_E_LAYOUT, "%s: page_desc must be u8 [num_blocks, 16]", who);
+    if (k_pool->shape[3] % 16 != 0) return fail(PKV_E_LAYOUT, "%s: D must be a multiple of 16", who);
+    if (reinterpret_cast<uintptr_t>(k_pool->data) % 16 || reinterpret_cast<uintptr_t>(v_pool->data) % 16 ||
+        reinterpret_cast<uintptr_t>(page_desc->data) % 16)
+        return fail(PKV_E_LAYOUT, "%s: pools and page_desc must be 16-byte aligned", who);
+    if (overlap(span(k_pool), span(v_pool))) return fail(PKV_E_ALIAS, "%s: k_pool overlaps v_pool", who);
+    PKV_TRY(check_disjoint(page_desc, "page_desc", span(k_pool), "k_pool"));
+    PKV_TRY(check_disjoint(page_desc, "page_desc", span(v_pool), "v_pool"));
+    return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status pkv_mixed_cache_update(const pkv_pool* pool, const pkv_tensor* k_pool,
+                                  const pkv_tensor* v_pool, const pkv_tensor* page_desc,
+                                  const int32_t* page_table_dev, const pkv_tensor* k_values,
+                                  const pkv_tensor* v_values, const int32_t* position,
+                                  int32_t update_length, pkv_page_format k_format,
+                                  pkv_page_format v_format, void* stream) {
+    PKV_TRY(check_mixed_pools(k_pool, v_pool, page_desc, "mixed_cache_update"));
+    PKV_TRY(check_tensor(k_values, "k_values", 4, 4));
+    PKV_TRY(check_tensor(v_values, "v_values", 4, 4));
+    if (update_length < 0) return fail(PKV_E_ARG, "mixed_cache_update: negative update_length");
+    if (!pool) return fail(PKV_E_ARG, "mixed_cache_update: a pool handle is required");
+    PKV_TRY(check_page_format(k_format, "mixed_cache_update k_format"));
+    PKV_TRY(check_page_format(v_format, "mixed_cache_update v_format"));
+    const int64_t NB = k_pool->shape[0], H = k_pool->shape[1], bs = k_pool->shape[2], D = k_pool->shape[3];
+    const int64_t B = k_values->shape[0];
+    if (NB != pool->num_blocks || bs != pool->block_size)
+        return fail(PKV_E_LAYOUT, "mixed_cache_update: pools are [%lld, H, %lld, D] but the pool has %d blocks of %d",
+                    (long long)NB, (long long)bs, pool->num_blocks, pool->block_size);
+    if (k_values->dtype != PKV_BF16 || v_values->dtype != PKV_BF16)
+        return fail(PKV_E_DTYPE, "mixed_cache_update: values must be bf16");
+    for (const pkv_tensor* t : {k_values, v_values})
+        if (t->shape[0] != B || t->shape[1] != H || t->shape[2] != update_length || t->shape[3] != D)
+            return fail(PKV_E_LAYOUT, "mixed_cache_update: values must be [B, H, update_length, D] of the pools");
+    if (reinterpret_cast<uintptr_t>(k_values->data) % 16 || reinterpret_cast<uintptr_t>(v_values->data) % 16)
+        return fail(PKV_E_LAYOUT, "mixed_cache_update: values must be 16-byte aligned");
+    if (!page_table_dev && B > 0 && update_length > 0) return fail(PKV_E_ARG, "mixed_cache_update: null page table");
+    PKV_TRY(check_paged_positions(pool, B, position, update_length));
+    PKV_TRY(check_writable(k_pool, "k_pool"));
+    PKV_TRY(check_writable(v_pool, "v_pool"));
+    PKV_TRY(check_writable(page_desc, "page_desc"));
+    for (const pkv_tensor* t : {k_values, v_values}) {
+        PKV_TRY(check_disjoint(t, "values", span(k_pool), "k_pool"));
+        PKV_TRY(check_disjoint(t, "values", span(v_pool), "v_pool"));
+        PKV_TRY(check_disjoint(t, "values", span(page_desc), "page_desc"));
+    }
+    if (B == 0 || update_length == 0 || H == 0) return ok();
+
+    PageDesc fmt{};
+    set_desc(fmt, k_format, false);
+    set_desc(fmt, v_format, true);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        MixedAppendArgs a;
+        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
+        a.k_src = static_cast<const uint16_t*>(k_values->data) + b0 * H * update_length * D;
+        a.v_src = static_cast<const uint16_t*>(v_values->data) + b0 * H * update_length * D;
+        a.k_pool = static_cast<uint8_t*>(k_pool->data);
+        a.v_pool = static_cast<uint8_t*>(v_pool->data);
+        a.desc = static_cast<PageDesc*>(page_desc->data);
+        a.page_table = page_table_dev;
+        a.fmt = fmt;
+        a.H = static_cast<int32_t>(H);
+        a.n = update_length;
+        a.bs = static_cast<int32_t>(bs);
+        a.maxb = pool->maxb;
+        a.D = static_cast<int32_t>(D);
+        a.row0 = static_cast<int32_t>(b0);
+        for (int i = 0; i < a.rows; ++i) a.pos[i] = position[b0 + i];
+        PKV_HIP(launch_mixed_append(a, s), "mixed_cache_update launch");
+    }
+    return ok();
+}
+
+pkv_status pkv_mixed_convert_pages(const pkv_tensor* k_pool, const pkv_tensor* v_pool,
+                                   const pkv_tensor* page_desc, const int32_t* pages,
+                                   const int32_t* valid_rows, int32_t n_pages,
+                                   const pkv_page_format* k_format,
+                                   const pkv_page_format* v_format, void* stream) {
+    PKV_TRY(check_mixed_pools(k_pool, v_pool, page_desc, "mixed_convert_pages"));
+    if (n_pages < 0) return fail(PKV_E_ARG, "mixed_convert_pages: negative page count");
+    if (n_pages > 0 && (!pages || !valid_rows)) return fail(PKV_E_ARG, "mixed_convert_pages: null page list");
+    if (k_format) PKV_TRY(check_page_format(*k_format, "mixed_convert_pages k_format"));
+    if (v_format) PKV_TRY(check_page_format(*v_format, "mixed_convert_pages v_format"));
+    const int64_t NB = k_pool->shape[0], H = k_pool->shape[1], bs = k_pool->shape[2], D = k_pool->shape[3];
+    if (bs * D * 2 > 65536) return fail(PKV_E_LAYOUT, "mixed_convert_pages: block_size * D * 2 must be <= 65536");
+    std::vector<int32_t> sorted(pages, pages + n_pages);
+    for (int32_t i = 0; i < n_pages; ++i) {
+        if (pages[i] < 0 || pages[i] >= NB)
+            return fail(PKV_E_PAGE, "mixed_convert_pages: page %d outside [0, %lld)", pages[i], (long long)NB);
+        if (valid_rows[i] < 0 || valid_rows[i] > bs)
+            return fail(PKV_E_ARG, "mixed_convert_pages: valid rows %d outside [0, %lld]", valid_rows[i], (long long)bs);
+    }
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+        return fail(PKV_E_ARG, "mixed_convert_pages: page ids must be unique");
+    if (k_format) PKV_TRY(check_writable(k_pool, "k_pool"));
+    if (v_format) PKV_TRY(check_writable(v_pool, "v_pool"));
+    if (k_format || v_format) PKV_TRY(check_writable(page_desc, "page_desc"));
+    if (n_pages == 0 || (!k_format && !v_format) || H == 0) return ok();
+
+    PageDesc fmt{};
+    if (k_format) set_desc(fmt, *k_format, false);
+    if (v_format) set_desc(fmt, *v_format, true);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t i0 = 0; i0 < n_pages; i0 += kMaxConvert) {
+        const int cnt = std::min<int32_t>(kMaxConvert, n_pages - i0);
+        for (int which = 0; which < 2; ++which) {
+            const pkv_page_format* f = which ? v_format : k_format;
+            if (!f) continue;
+            MixedConvertArgs a;
+            a.pool = static_cast<uint8_t*>((which ? v_pool : k_pool)->data);
+            a.desc = static_cast<const PageDesc*>(page_desc->data);
+            a.which = which;
+            a.st = f->storage;
+            a.scale = which ? fmt.v_scale : fmt.k_scale;
+            a.zero = which ? fmt.v_zero : fmt.k_zero;
+            a.H = static_cast<int32_t>(H);
+            a.bs = static_cast<int32_t>(bs);
+            a.D = static_cast<int32_t>(D);
+            a.count = cnt;
+            for (int i = 0; i < cnt; ++i) {
+                a.page[i] = pages[i0 + i];
+                a.valid[i] = valid_rows[i0 + i];
+            }
+            PKV_HIP(launch_mixed_convert(a, s), "mixed_convert_pages launch");
+        }
+        MixedDescArgs d;
+        d.desc = static_cast<PageDesc*>(page_desc->data);
+        d.set_k = k_format != nullptr;
+        d.set_v = v_format != nullptr;
+        d.fmt = fmt;
+        d.count = cnt;
+        for (int i = 0; i < cnt; ++i) d.page[i] = pages[i0 + i];
+        PKV_HIP(launch_mixed_desc(d, s), "mixed_convert_pages descriptor launch");
+    }
+    return ok();
+}
 
 pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor* k_codes,
                                            const pkv_tensor* k_params, const pkv_tensor* v_codes,

@@ -93,6 +93,7 @@ struct DecodeArgs {
     int32_t row0, rows;          // batch rows handled by this launch
     int32_t window;              // left window (-1 = unbounded), see visible_begin
     float scale_log2;            // softmax scale * log2(e)
+    const void* page_desc;       // mixed-format pages: PageDesc[NB] (else nullptr)
     int32_t len[kMaxRows];       // valid length per row
     int32_t split_begin[kMaxRows + 1];  // prefix sum of splits per row
 };
@@ -144,6 +145,66 @@ constexpr int kGenericMaxTps = 1024;
 hipError_t launch_decode_generic(const DecodeArgs& a, int total_work, hipStream_t s);
 hipError_t launch_decode_int4(const Int4DecodeArgs& a, int G, int total_work, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Mixed-format pages
+// ---------------------------------------------------------------------------
+// Page storages (values of pkv_page_storage).
+enum PageStorage : int32_t {
+    kStBF16 = 0, kStF16 = 1, kStI8 = 2, kStU8 = 3, kStI4 = 4, kStU4 = 5, kStI2 = 6, kStU2 = 7
+};
+__host__ __device__ inline int storage_bits(int st) { return st <= kStF16 ? 16 : st <= kStU8 ? 8 : st <= kStU4 ? 4 : 2; }
+__host__ __device__ inline bool storage_signed(int st) { return st == kStI8 || st == kStI4 || st == kStI2; }
+
+// Format of one physical page (16 bytes; the layout of pkv_page_desc).
+struct PageDesc {
+    float k_scale, v_scale;      // affine scales (dense pages: unused)
+    int16_t k_zero, v_zero;      // affine zero points, in code units
+    uint8_t k_st, v_st;          // PageStorage
+    uint8_t pad[2];
+};
+static_assert(sizeof(PageDesc) == 16, "page descriptor is 16 bytes");
+
+struct MixedAppendArgs {
+    const uint16_t* k_src;       // [rows, H, n, D] bf16
+    const uint16_t* v_src;
+    uint8_t* k_pool;             // [NB, H, bs * D * 2] bytes: one slot per (page, head)
+    uint8_t* v_pool;
+    PageDesc* desc;              // [NB]
+    const int32_t* page_table;   // row (row0 + b) of [*, maxb]
+    PageDesc fmt;                // formats of the pages this append creates
+    int32_t H, n, bs, maxb, D, row0, rows;
+    int32_t pos[kMaxRows];
+};
+
+constexpr int kMaxConvert = 256; // pages per conversion launch
+struct MixedConvertArgs {
+    uint8_t* pool;               // slots of K or of V
+    const PageDesc* desc;
+    int32_t which;               // 0: K, 1: V
+    int32_t st;                  // target storage, scale and zero point
+    float scale;
+    int32_t zero;
+    int32_t H, bs, D, count;
+    int32_t page[kMaxConvert];
+    int32_t valid[kMaxConvert];  // rows [0, valid) are converted, the rest become zeros
+};
+
+struct MixedDescArgs {           // desc[page[i]] fields of the converted tensors
+    PageDesc* desc;
+    int32_t set_k, set_v;
+    PageDesc fmt;
+    int32_t count;
+    int32_t page[kMaxConvert];
+};
+
+hipError_t launch_mixed_append(const MixedAppendArgs& a, hipStream_t s);
+hipError_t launch_mixed_convert(const MixedConvertArgs& a, hipStream_t s);
+hipError_t launch_mixed_desc(const MixedDescArgs& a, hipStream_t s);
+// Decode over mixed pages: bf16 q, D == 128, G in {1, 2, 4, 8}, block_size a
+// power of two >= 16; a.k / a.v are the slot pools, a.page_desc the descriptors.
+bool mixed_decode_supported(int D, int G, int bs);
+hipError_t launch_decode_mixed(const DecodeArgs& a, int G, int total_work, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Chunk attention (MFMA)

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if getattr(pkv._lib, n, None) is None]
     assert not missing, missing
     assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
-    assert pkv.abi_version() == pkv.ABI_VERSION == 2
+    assert pkv.abi_version() == pkv.ABI_VERSION == 3
 
 
 def R(ptr, dtype, shape):
@@ -315,3 +315,116 @@ def test_one_hip_runtime_in_the_process():
     maps = open("/proc/self/maps").read()
     libs = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln and "/" in ln}
     assert len(libs) == 1, libs
+
+
+# --------------------------------------------------------------------------- mixed-format pages
+MNB, MH, MBS, MD = 8, 2, 16, 128
+MK = R(FAKE, pkv.BF16, [MNB, MH, MBS, MD])
+MV = R(FAKE + 0x200000, pkv.BF16, [MNB, MH, MBS, MD])
+MDESC = R(FAKE + 0x400000, pkv.U8, [MNB, 16])
+MTABLE = FAKE + 0x500000
+MVALS_K = R(FAKE + 0x600000, pkv.BF16, [1, MH, 4, MD])
+MVALS_V = R(FAKE + 0x700000, pkv.BF16, [1, MH, 4, MD])
+BF = pkv.page_format("BF16")
+
+
+def _mixed_bindings():
+    return [pkv.bind_writable(MK), pkv.bind_writable(MV), pkv.bind_writable(MDESC)]
+
+
+@pytest.mark.parametrize("fmt", [pkv.page_format(9), pkv.page_format("INT8", 0.0, 0),
+                                 pkv.page_format("INT8", float("inf"), 0), pkv.page_format("INT8", float("nan"), 0),
+                                 pkv.page_format("UINT4", 0.5, 16), pkv.page_format("INT2", 0.5, -3),
+                                 pkv.page_format("UINT8", 0.5, -1), pkv.page_format("INT8", 0.5, 128)])
+def test_mixed_formats_are_checked(fmt):
+    pool = pkv.Pool(MNB, MBS, 2, 4)
+    pool.reserve([0], [4])
+    bs = _mixed_bindings()
+    try:
+        assert status_of(pkv.mixed_cache_update, pool, MK, MV, MDESC, MTABLE, MVALS_K, MVALS_V, [0], 4,
+                         fmt, BF) == pkv.E_ARG
+        assert status_of(pkv.mixed_cache_update, pool, MK, MV, MDESC, MTABLE, MVALS_K, MVALS_V, [0], 4,
+                         BF, fmt) == pkv.E_ARG
+        assert status_of(pkv.mixed_convert_pages, MK, MV, MDESC, [1], [4], fmt, None) == pkv.E_ARG
+    finally:
+        for b in bs:
+            b.close()
+
+
+def test_mixed_update_errors():
+    pool = pkv.Pool(MNB, MBS, 2, 4)
+    pool.reserve([0], [4])
+    i8 = pkv.page_format("INT8", 0.01, 0)
+    # no binding: read-only
+    assert status_of(pkv.mixed_cache_update, pool, MK, MV, MDESC, MTABLE, MVALS_K, MVALS_V, [0], 4, i8, i8) \
+        == pkv.E_READONLY
+    bs = _mixed_bindings()
+    try:
+        ok = (MK, MV, MDESC, MTABLE, MVALS_K, MVALS_V)
+        assert status_of(pkv.mixed_cache_update, pool, *ok, [14], 4, i8, i8) == pkv.E_PAGE    # past the page held
+        assert status_of(pkv.mixed_cache_update, pool, *ok, [-1], 4, i8, i8) == pkv.E_CAPACITY
+        f32v = R(MVALS_K.ptr, pkv.F32, [1, MH, 4, MD])
+        assert status_of(pkv.mixed_cache_update, pool, MK, MV, MDESC, MTABLE, f32v, MVALS_V, [0], 4, i8, i8) \
+            == pkv.E_DTYPE
+        bad_desc = R(MDESC.ptr, pkv.U8, [MNB, 8])
+        assert status_of(pkv.mixed_cache_update, pool, MK, MV, bad_desc, MTABLE, MVALS_K, MVALS_V, [0], 4, i8, i8) \
+            == pkv.E_LAYOUT
+        inside = R(FAKE + 64, pkv.BF16, [1, MH, 4, MD])
+        assert status_of(pkv.mixed_cache_update, pool, MK, MV, MDESC, MTABLE, inside, MVALS_V, [0], 4, i8, i8) \
+            == pkv.E_ALIAS
+        odd = R(MVALS_K.ptr + 2, pkv.BF16, [1, MH, 4, MD])
+        assert status_of(pkv.mixed_cache_update, pool, MK, MV, MDESC, MTABLE, odd, MVALS_V, [0], 4, i8, i8) \
+            == pkv.E_LAYOUT
+    finally:
+        for b in bs:
+            b.close()
+
+
+def test_mixed_conversion_errors():
+    bs = _mixed_bindings()
+    i4 = pkv.page_format("INT4", 0.25, 0)
+    try:
+        assert status_of(pkv.mixed_convert_pages, MK, MV, MDESC, [1, 1], [4, 4], i4, None) == pkv.E_ARG
+        assert status_of(pkv.mixed_convert_pages, MK, MV, MDESC, [MNB], [4], i4, None) == pkv.E_PAGE
+        assert status_of(pkv.mixed_convert_pages, MK, MV, MDESC, [-1], [4], None, i4) == pkv.E_PAGE
+        assert status_of(pkv.mixed_convert_pages, MK, MV, MDESC, [1], [MBS + 1], i4, i4) == pkv.E_ARG
+        big_k = R(FAKE, pkv.BF16, [2, 1, 1024, 64])
+        big_v = R(FAKE + 0x200000, pkv.BF16, [2, 1, 1024, 64])
+        big_d = R(FAKE + 0x400000, pkv.U8, [2, 16])
+        assert status_of(pkv.mixed_convert_pages, big_k, big_v, big_d, [0], [4], i4, None) == pkv.E_LAYOUT
+    finally:
+        for b in bs:
+            b.close()
+    # converting needs writable pools; nothing to convert needs nothing
+    assert status_of(pkv.mixed_convert_pages, MK, MV, MDESC, [1], [4], i4, None) == pkv.E_READONLY
+    pkv.mixed_convert_pages(MK, MV, MDESC, [1], [4], None, None)
+
+
+def test_mixed_decode_errors():
+    q = R(FAKE + 0x800000, pkv.BF16, [1, 4, MD])
+    out = R(FAKE + 0x900000, pkv.BF16, [1, 4, MD])
+    ws = FAKE + 0xA00000
+
+    def call(q=q, k=MK, v=MV, d=MDESC, out=out, bs=MBS, lens=(20,), win=-1):
+        return status_of(pkv.paged_decode_attention_mixed, q, k, v, d, MTABLE, 4, bs, list(lens), out,
+                         R(ws, pkv.U8, [1 << 20]), left_window=win)
+    assert call(q=R(q.ptr, pkv.F32, [1, 4, MD]), out=R(out.ptr, pkv.F32, [1, 4, MD])) == pkv.E_DTYPE
+    assert call(q=R(q.ptr, pkv.BF16, [1, 6, MD]), out=R(out.ptr, pkv.BF16, [1, 6, MD])) == pkv.E_LAYOUT   # G = 3
+    k64 = R(FAKE, pkv.BF16, [MNB, MH, MBS, 64])
+    v64 = R(FAKE + 0x200000, pkv.BF16, [MNB, MH, MBS, 64])
+    assert call(q=R(q.ptr, pkv.BF16, [1, 4, 64]), out=R(out.ptr, pkv.BF16, [1, 4, 64]), k=k64, v=v64) \
+        == pkv.E_LAYOUT
+    k8 = R(FAKE, pkv.BF16, [MNB, MH, 8, MD])
+    v8 = R(FAKE + 0x200000, pkv.BF16, [MNB, MH, 8, MD])
+    assert call(k=k8, v=v8, bs=8) == pkv.E_LAYOUT                                                  # block < 16
+    assert call(d=R(MDESC.ptr, pkv.U8, [MNB - 1, 16])) == pkv.E_LAYOUT
+    assert call(lens=(0,)) == pkv.E_CAPACITY
+    assert call(lens=(65,)) == pkv.E_CAPACITY
+    assert call(win=-2) == pkv.E_ARG
+
+
+def test_length_threshold_selector():
+    early = (pkv.page_format("BF16"), pkv.page_format("BF16"))
+    late = (pkv.page_format("INT8", 0.01, 0), pkv.page_format("UINT4", 0.25, 8))
+    sel = pkv.LengthThresholdSelector(1024, early, late)
+    assert sel(0) is early and sel(1023) is early and sel(1024) is late
