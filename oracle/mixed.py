@@ -146,9 +146,10 @@ class MixedPool:
         self.fmt = {"k": [None] * num_blocks, "v": [None] * num_blocks}
 
     # -- rows of one page ------------------------------------------------------
-    def _rows(self, which: str, page: int, h: int, fmt: Format) -> np.ndarray:
+    def _rows(self, which: str, page: int, fmt: Format) -> np.ndarray:
+        """Rows ``[H, block_size, row_bytes]`` of a page in format ``fmt`` (a view)."""
         rb = row_bytes(fmt.storage, self.D)
-        return self.data[which][page, h, :self.bs * rb].reshape(self.bs, rb)
+        return self.data[which][page, :, :self.bs * rb].reshape(self.H, self.bs, rb)
 
     def append(self, page_table: np.ndarray, k_bf16: np.ndarray, v_bf16: np.ndarray, position,
                n: int, k_fmt: Format, v_fmt: Format) -> None:
@@ -170,12 +171,13 @@ class MixedPool:
         for which, vals in (("k", k_bf16), ("v", v_bf16)):
             x = bf16_to_f64(vals).astype(np.float32)          # exact
             for b in range(B):
-                for t in range(n):
-                    p = int(position[b]) + t
-                    page = int(page_table[b, p // self.bs])
+                p0 = int(position[b])
+                for j in range(p0 // self.bs, -(-(p0 + n) // self.bs)):
+                    page = int(page_table[b, j])
                     fmt = self.fmt[which][page]
-                    for h in range(self.H):
-                        self._rows(which, page, h, fmt)[p % self.bs] = encode_rows(x[b, h, t], fmt)
+                    lo, hi = max(p0, j * self.bs), min(p0 + n, (j + 1) * self.bs)
+                    rows = self._rows(which, page, fmt)
+                    rows[:, lo - j * self.bs:hi - j * self.bs] = encode_rows(x[b, :, lo - p0:hi - p0], fmt)
 
     def convert(self, pages, valid_rows, k_fmt: Format | None, v_fmt: Format | None) -> None:
         """Re-encode the first ``valid_rows[i]`` rows of page ``pages[i]`` (K to
@@ -203,21 +205,20 @@ class MixedPool:
             zero = encode_rows(np.zeros(self.D, np.float32), new)
             for p, nv in zip(pages, valid_rows):
                 old = self.fmt[which][p]
-                for h in range(self.H):
-                    x = decode_rows_f32(self._rows(which, p, h, old)[:nv], old, self.D)
-                    out = self._rows(which, p, h, new)
-                    out[:nv] = encode_rows(x, new)
-                    out[nv:] = zero
+                x = decode_rows_f32(self._rows(which, p, old)[:, :nv], old, self.D)
+                out = self._rows(which, p, new)
+                out[:, :nv] = encode_rows(x, new)
+                out[:, nv:] = zero
                 self.fmt[which][p] = new
 
     def gather(self, which: str, page_table_row: np.ndarray, length: int) -> np.ndarray:
         """Exact decoded logical rows ``[H, length, D]`` (float64) of one sequence."""
         out = np.empty((self.H, length, self.D), np.float64)
-        for p in range(length):
-            page = int(page_table_row[p // self.bs])
+        for j in range(-(-length // self.bs)):
+            page = int(page_table_row[j])
             fmt = self.fmt[which][page]
-            for h in range(self.H):
-                out[h, p] = decode_rows_exact(self._rows(which, page, h, fmt)[p % self.bs], fmt, self.D)
+            n = min(self.bs, length - j * self.bs)
+            out[:, j * self.bs:j * self.bs + n] = decode_rows_exact(self._rows(which, page, fmt)[:, :n], fmt, self.D)
         return out
 
 
