@@ -650,8 +650,80 @@ def bench_window(steps, warmup, cpu):
                  _hbm_roofline(nbytes, us), cpu_res, attn_us=round(us, 2), attn_algorithmic_bytes=nbytes)
 
 
+def bench_mixed(steps, warmup, cpu):
+    """Mixed-format pages at the paged32k shapes (32 rows x 32768 tokens, a full 65536-page pool), appended
+    through the library with the pages' length-threshold selector: the first 1024 tokens of a row in BF16
+    pages, the rest with INT8 keys (0.01, 0) and UINT4 values (0.25, 8).  Times the decode attention."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    w = workloads.mixed32k()
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    kp = torch.zeros((w.NB, w.Hkv, w.bs, w.D), device=dev, dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    pd = pkv.mixed_page_desc(w.NB, dev)
+    pool = pkv.Pool(w.NB, w.bs, w.B, w.maxb, w.order)
+    table = torch.full((w.B, w.maxb), -1, device=dev, dtype=torch.int32)
+    pool.reserve(range(w.B), [w.L] * w.B, table)
+    fm = lambda t: pkv.page_format(*t)
+    select = pkv.LengthThresholdSelector(w.threshold, (fm(w.early[0]), fm(w.early[1])),
+                                         (fm(w.late[0]), fm(w.late[1])))
+    binds = [pkv.bind_writable(t) for t in (kp, vp, pd)]
+    pos = 0
+    while pos < w.L:
+        n = w.threshold if pos < w.threshold else min(2048, w.L - pos)
+        kv = (torch.randn((w.B, w.Hkv, n, w.D), generator=gen, device=dev) * w.k_sigma).to(torch.bfloat16)
+        vv = (torch.randn((w.B, w.Hkv, n, w.D), generator=gen, device=dev) * w.v_sigma).to(torch.bfloat16)
+        kf, vf = select(pos)
+        pkv.mixed_cache_update(pool, kp, vp, pd, table, kv, vv, [pos] * w.B, n, kf, vf)
+        pos += n
+    del kv, vv
+    q = torch.randn((w.B, w.Hq, w.D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.D), device=dev, dtype=torch.bfloat16)
+    ws = torch.empty(pkv.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.L), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    lens = [w.L] * w.B
+    us = _timed(lambda i: pkv.paged_decode_attention_mixed(q, kp, vp, pd, table, w.maxb, w.bs, lens, out, ws,
+                                                           pool=pool), steps, warmup, stream)
+    for b in binds:
+        b.close()
+    early, late = w.threshold, w.L - w.threshold
+    row_bytes = w.D * 2 * 2 * early + (w.D * 1 + w.D // 2) * late       # K + V bytes of one (row, kv head)
+    nbytes = w.B * w.Hkv * row_bytes + w.B * w.maxb * (4 + 16) + w.B * w.Hq * w.D * 2 * 2
+    cpu_res = None
+    if cpu:
+        from oracle import mixed as om
+        import synth
+        g = synth.rng(w.seed, 9)
+        opool = om.MixedPool(w.maxb, w.Hkv, w.bs, w.D)
+        local = np.arange(w.maxb, dtype=np.int32)[None]
+        ofmt = lambda t: om.Format(*t)
+        p = 0
+        while p < w.L:                  # one row of the workload, outside the timed loop
+            n = w.threshold if p < w.threshold else min(4096, w.L - p)
+            kf, vf = (w.early if p < w.threshold else w.late)
+            kb = synth.f32_to_bf16_bits(synth.normal(g, (1, w.Hkv, n, w.D), w.k_sigma))
+            vb = synth.f32_to_bf16_bits(synth.normal(g, (1, w.Hkv, n, w.D), w.v_sigma))
+            opool.append(local, kb, vb, [p], n, ofmt(kf), ofmt(vf))
+            p += n
+        qh = synth.normal(g, (1, w.Hq, w.D)).astype(np.float64)
+        n, el = _cpu_loop(10.0, lambda i: om.decode_attention(opool, qh, local, [w.L]))
+        cpu_res = {"value": round(n / el, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n} rows of 32-head attention over one 32768-token row of the workload's mixed "
+                             f"pages (decoded exactly, float64) in {el:.1f} s"}
+    return _line("decode tokens/s, paged GQA over mixed-format pages (BF16 prefix, INT8 K / UINT4 V), 32k context",
+                 w.B / (us * 1e-6), "tokens/s", steps, warmup, us, "bf16/int8/uint4",
+                 {"workload": "mixed", "batch": w.B, "ctx": w.L, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                  "head_dim": w.D, "block_size": w.bs, "num_blocks": w.NB, "dense_prefix": w.threshold,
+                  "k_late": list(w.late[0]), "v_late": list(w.late[1])},
+                 _hbm_roofline(nbytes, us), cpu_res, attn_us=round(us, 2), attn_algorithmic_bytes=nbytes)
+
+
 WORKLOADS = {"contig": bench_contig, "paged": bench_paged, "int4": bench_int4, "qwen-decode": bench_qwen_decode,
-             "qwen-chunk": bench_qwen_chunk, "sample": bench_sample, "window": bench_window}
+             "qwen-chunk": bench_qwen_chunk, "sample": bench_sample, "window": bench_window, "mixed": bench_mixed}
 
 
 def main():

@@ -19,23 +19,32 @@
 // pool.  PageDesc[page] (16 bytes) holds the K and V storages, scales and
 // zero points.
 //
-// Decode: the structure of the bf16 fast kernel (4 waves per (row, kv head,
-// split), 16 tokens per wave step, eight lanes per row, lane j owning dims
-// 8j..8j+7 and 64+8j..64+8j+7), with the storage of each step's page read
-// from its descriptor (a wave-uniform branch).  A lane loads 2 x 2 * bits
-// bytes of each of its rows, so every load instruction still reads whole
-// row segments.  Dense BF16 pages use v_dot2_f32_bf16 with the bf16 query.
-// Every other storage is brought to fp16 pairs: F16 pages as stored, affine
-// codes as the exact integers c - z (a code u enters as the fp16 number
-// 1024 + u, bit pattern 0x6400 | u, built with v_perm_b32 / v_and_or_b32, and
-// one packed fp16 subtract of 1024 + z removes the offset exactly; signed
-// codes are offset to unsigned by flipping their top bit).  Q.K then uses
-// v_dot2_f32_f16 against the query scaled by a power of two (exact in fp16;
-// the largest |q| lands in [128, 256)), and the page's scale multiplies the
-// score; P.V multiplies the fp16 values straight into the float32 sums
-// (v_fma_mix_f32) with the value scale folded into p.
+// Decode: 4 waves per (row, kv head, split); each wave streams its quarter of
+// the split in sub-steps of 16 tokens of one page, eight lanes per row, lane j
+// owning dims 8j..8j+7 and 64+8j..64+8j+7.  A lane loads 2 x 2 * bits bytes of
+// each of its rows, so every load instruction reads whole row segments.  The
+// wave walks its sub-steps in runs of one (K bits, V bits) class: each class
+// has its own pipelined loop (V rows of a group in flight while its K rows are
+// scored, K rows of the next group while its V rows are summed), and a group
+// is two sub-steps when K and V have at most 8 bits, so narrow pages keep as
+// many bytes in flight as dense ones in the same registers.  Page ids and
+// descriptors of a group are read one group before its loads are issued.
+// Dense BF16 pages use v_dot2_f32_bf16 with the bf16 query.  Every other
+// storage is brought to fp16 pairs: F16 pages as stored, affine codes as the
+// exact integers c - z (a code u enters as the fp16 number 1024 + u, bit
+// pattern 0x6400 | u, built with v_perm_b32 / v_and_or_b32, and one packed
+// fp16 add of -(1024 + z), bit pattern 0xE400 | z, removes the offset exactly;
+// signed codes are offset to unsigned by flipping their top bit).  Q.K then
+// uses v_dot2_f32_f16 against the query scaled by a power of two (exact in
+// fp16; the largest |q| lands in [128, 256)), and the page's scale multiplies
+// the score; P.V multiplies the fp16 values straight into the float32 sums
+// (v_fma_mix_f32) with the value scale folded into p.  Both query copies live
+// in LDS and are read at each use, which keeps the kernel at two waves per
+// SIMD for four query heads per K/V head.
 
 #include "device_common.h"
+
+#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -239,6 +248,14 @@ __device__ __forceinline__ float group8_max(float x) {
     return x;
 }
 
+// lane id recomputed at the point of use (volatile: not merged with other uses,
+// so no copy of it stays live across the main loop)
+__device__ __forceinline__ int lane_now() {
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -332,10 +349,10 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     const int32_t* __restrict__ pt = a.page_table + int64_t(b) * a.maxb;
     const int64_t slot_bytes = int64_t(a.bs) * kDM * 2;
 
-    // query: bf16 (dense BF16 pages, read from LDS each such step) and fp16
-    // pairs of q * 2^e in registers (every other storage)
+    // query in LDS, read at every use: bf16 for dense BF16 pages, fp16 pairs of
+    // q * 2^e for every other storage (2^-e, per head, in a register)
     __shared__ uint4 s_q[G][2][8];          // [head][half][lane chunk j]
-    uint32_t qh[G][8];
+    __shared__ uint4 s_qh[G][2][8];
     float qinv[G];
     {
         const uint16_t* Q = static_cast<const uint16_t*>(a.q) + (int64_t(b) * a.Hq + kvh * G) * kDM;
@@ -343,10 +360,6 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
         for (int g = 0; g < G; ++g) {
             const uint4 qa = ld16(Q + g * kDM + j * 8);
             const uint4 qb = ld16(Q + g * kDM + 64 + j * 8);
-            if (threadIdx.x < 8) {
-                s_q[g][0][j] = qa;
-                s_q[g][1][j] = qb;
-            }
             const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
             float mx = 0.0f;
 #pragma unroll
@@ -354,10 +367,18 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
             mx = group8_max(mx);
             const int E = __builtin_amdgcn_readfirstlane(mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0);
             const float up = __builtin_ldexpf(1.0f, 8 - E);   // largest |q| * up in [128, 256)
-            qinv[g] = __builtin_ldexpf(1.0f, E - 8);
+            qinv[g] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                    __builtin_bit_cast(int, __builtin_ldexpf(1.0f, E - 8))));
+            uint32_t hw[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                qh[g][k] = f32_to_f16_bits(bf_lo(qw[k]) * up) | (f32_to_f16_bits(bf_hi(qw[k]) * up) << 16);
+                hw[k] = f32_to_f16_bits(bf_lo(qw[k]) * up) | (f32_to_f16_bits(bf_hi(qw[k]) * up) << 16);
+            if (threadIdx.x < 8) {
+                s_q[g][0][j] = qa;
+                s_q[g][1][j] = qb;
+                s_qh[g][0][j] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                s_qh[g][1][j] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+            }
         }
     }
     __syncthreads();
@@ -371,187 +392,300 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
         for (int d = 0; d < 16; ++d) o[g][d] = 0.0f;
     }
 
-    // Half-step pipeline: the V rows of step i are in flight while K(i) is
-    // scored, and the K rows of step i + 1 while V(i) is accumulated.  Every
-    // half-step issues four loads per lane (two rows x two halves) whatever
-    // the storage, so each wait covers exactly the older half-step.  The
-    // prefetch of the step after the last one re-reads the last step.
-    struct Rows {
-        u32x4_t r0a, r0b, r1a, r1b;
-    };
+    // Half-step pipeline over groups of sub-steps (16 tokens of one page
+    // each): the V rows of a group are in flight while its K rows are scored,
+    // and the K rows of the next group while its V rows are summed.  A group
+    // is one sub-step, or two when both sub-steps hold K and V of at most 8
+    // bits: their rows then share the 16 registers per lane that one dense
+    // sub-step uses, so narrow pages keep as many bytes in flight.  The
+    // prefetch after the last group re-reads the last sub-step.
     struct Fmt {
         int st, nb;              // storage and its bits (wave-uniform)
         float sc;                // scale (1 for dense pages)
         uint32_t flip, nz;       // signed-code offset, packed fp16 -(1024 + z')
+    };
+    struct Sub {
+        int ts, page;            // first token, page
+        Fmt kf, vf;
     };
     auto fmt_of = [&](const PageDesc& dd, bool v) {
         Fmt f;
         f.st = __builtin_amdgcn_readfirstlane((v ? dd.v_st : dd.k_st) & 7);
         f.nb = storage_bits(f.st);
         const bool aff = f.st >= kStI8;
-        f.sc = aff ? (v ? dd.v_scale : dd.k_scale) : 1.0f;
+        f.sc = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                             __builtin_bit_cast(int, aff ? (v ? dd.v_scale : dd.k_scale) : 1.0f)));
         const bool sg = storage_signed(f.st);
         f.flip = sg ? (f.nb == 8 ? 0x80808080u : f.nb == 4 ? 0x88888888u : 0xAAAAAAAAu) : 0u;
-        const int z = (v ? dd.v_zero : dd.k_zero) + (sg ? (1 << (f.nb - 1)) : 0);
-        const uint32_t h = f32_to_f16_bits(-1024.0f - float(z));
-        f.nz = h | (h << 16);
+        // -(1024 + z') in fp16 is 0xE400 | z' for 0 <= z' < 1024 (exponent 10, sign set)
+        const uint32_t z = uint32_t((v ? dd.v_zero : dd.k_zero) + (sg ? (1 << (f.nb - 1)) : 0)) & 0x3FFu;
+        f.nz = (0xE400u | z) * 0x00010001u;
         return f;
     };
-    // one row half: 2 * nb bytes
-    auto ldh = [](const uint8_t* p, int nb) -> u32x4_t {
-        if (nb == 16) return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-        if (nb == 8) {
-            const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-            return u32x4_t{v.x, v.y, 0u, 0u};
-        }
-        if (nb == 4) return u32x4_t{__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)), 0u, 0u, 0u};
-        return u32x4_t{uint32_t(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p))), 0u, 0u, 0u};
-    };
-    // rows r0 = in_page + min(grp, last), r1 = in_page + min(grp + 8, last) of one tensor
-    auto load_rows = [&](const uint8_t* head, int nb, int row0, int row1) {
-        Rows u;
-        const uint8_t* p0 = head + row0 * 16 * nb + j * nb;
-        const uint8_t* p1 = head + row1 * 16 * nb + j * nb;
-        u.r0a = ldh(p0, nb);
-        u.r0b = ldh(p0 + 8 * nb, nb);
-        u.r1a = ldh(p1, nb);
-        u.r1b = ldh(p1 + 8 * nb, nb);
-        if (nb == 2) {             // 2-bit rows: both halves in one dword (low, high)
-            u.r0a.x |= u.r0b.x << 16;
-            u.r1a.x |= u.r1b.x << 16;
-        }
+    const int nsub = wbeg < wend ? (wend - wbeg + kSlabTokens - 1) / kSlabTokens : 0;
+    auto sub_of = [&](int i) {
+        Sub u;
+        u.ts = wbeg + i * kSlabTokens;
+        u.page = pt[u.ts >> a.log2bs];
+        const PageDesc dd = desc[u.page];
+        u.kf = fmt_of(dd, false);
+        u.vf = fmt_of(dd, true);
         return u;
     };
-
-    if (wbeg < wend) {
-        const int nsteps = (wend - wbeg + kSlabTokens - 1) / kSlabTokens;
-        const int64_t kvoff = int64_t(kvh) * slot_bytes;
-        auto head_of = [&](int page) { return int64_t(page) * a.Hkv * slot_bytes + kvoff; };
-        auto rows_of = [&](int ts, int& r0, int& r1) {
-            const int in_page = ts & (a.bs - 1);
-            const int last = t1 - 1 - ts;
-            r0 = in_page + min(grp, last);
-            r1 = in_page + min(grp + 8, last);
-        };
-        int page = pt[wbeg >> a.log2bs];
-        PageDesc dd = desc[page];
-        Fmt kf = fmt_of(dd, false), vf = fmt_of(dd, true);
-        int r0, r1;
-        rows_of(wbeg, r0, r1);
-        Rows kr = load_rows(K + head_of(page), kf.nb, r0, r1);
-        for (int i = 0; i < nsteps; ++i) {
-            const int ts = wbeg + i * kSlabTokens;
-            const bool live0 = ts + grp < t1 && ts + grp >= vis0;
-            const bool live1 = ts + 8 + grp < t1 && ts + 8 + grp >= vis0;
-            // V rows of this step
-            const Rows vr = load_rows(V + head_of(page), vf.nb, r0, r1);
-            // next step's page and format (the last step prefetches itself)
-            const int tn = i + 1 < nsteps ? ts + kSlabTokens : ts;
-            const int npage = pt[tn >> a.log2bs];
-            const PageDesc nd = desc[npage];
-
-            // ---- scores of this step
-            float s0[G], s1[G];
-            if (kf.st == kStBF16) {
-                int jj = j;
-                asm volatile("" : "+v"(jj));            // keep the LDS query reads in the loop
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const uint4 qa = s_q[g][0][jj], qb = s_q[g][1][jj];
-                    float x = 0.0f, y = 0.0f;
-                    x = dot2_bf16(qa.x, kr.r0a.x, x);
-                    y = dot2_bf16(qa.x, kr.r1a.x, y);
-                    x = dot2_bf16(qa.y, kr.r0a.y, x);
-                    y = dot2_bf16(qa.y, kr.r1a.y, y);
-                    x = dot2_bf16(qa.z, kr.r0a.z, x);
-                    y = dot2_bf16(qa.z, kr.r1a.z, y);
-                    x = dot2_bf16(qa.w, kr.r0a.w, x);
-                    y = dot2_bf16(qa.w, kr.r1a.w, y);
-                    x = dot2_bf16(qb.x, kr.r0b.x, x);
-                    y = dot2_bf16(qb.x, kr.r1b.x, y);
-                    x = dot2_bf16(qb.y, kr.r0b.y, x);
-                    y = dot2_bf16(qb.y, kr.r1b.y, y);
-                    x = dot2_bf16(qb.z, kr.r0b.z, x);
-                    y = dot2_bf16(qb.z, kr.r1b.z, y);
-                    x = dot2_bf16(qb.w, kr.r0b.w, x);
-                    y = dot2_bf16(qb.w, kr.r1b.w, y);
-                    s0[g] = group8_sum(x) * a.scale_log2;
-                    s1[g] = group8_sum(y) * a.scale_log2;
-                }
-            } else {
-                uint32_t k0[8], k1[8];
-                to_f16_pairs(kr.r0a, kr.r0b, kf.nb, kf.flip, kf.nz, k0);
-                to_f16_pairs(kr.r1a, kr.r1b, kf.nb, kf.flip, kf.nz, k1);
-                const float ksc = kf.sc * a.scale_log2;
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    float x = 0.0f, y = 0.0f;
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        x = dot2_f16(qh[g][k], k0[k], x);
-                        y = dot2_f16(qh[g][k], k1[k], y);
-                    }
-                    const float sc = ksc * qinv[g];
-                    s0[g] = group8_sum(x) * sc;
-                    s1[g] = group8_sum(y) * sc;
-                }
-            }
-            float q0[G], q1[G];
+    auto narrow = [](const Sub& u) { return u.kf.nb <= 8 && u.vf.nb <= 8; };
+    const int64_t kvoff = int64_t(kvh) * slot_bytes;
+    // Rows of a sub-step into a half buffer w[4]: dense rows take all four
+    // vectors (row 0 halves, row 1 halves); narrow rows of slot s take w[2s]
+    // (row 0) and w[2s + 1] (row 1), 8-bit as (lo.xy, hi.xy), 4-bit as (lo, -, hi, -),
+    // 2-bit as one dword (lo | hi << 16).  Rows are clamped to the split's last token.
+    auto load_sub = [&](u32x4_t* w, const uint8_t* base, const Sub& u, int nb, int slot) {
+        // lane offsets are recomputed here (not hoisted: each storage would keep its own)
+        const int lane_l = lane_now();
+        const int gl = lane_l >> 3, jl = lane_l & 7;
+        const int in_page = u.ts & (a.bs - 1);
+        const int last = t1 - 1 - u.ts;
+        const int r0 = in_page + min(gl, last), r1 = in_page + min(gl + 8, last);
+        const uint8_t* head = base + int64_t(u.page) * a.Hkv * slot_bytes + kvoff;
+        const uint8_t* p0 = head + (r0 * 16 + jl) * nb;
+        const uint8_t* p1 = head + (r1 * 16 + jl) * nb;
+        if (nb == 16) {
+            w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p0));
+            w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p0 + 128));
+            w[2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p1));
+            w[3] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p1 + 128));
+        } else if (nb == 8) {
+            const u32x2_t a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p0));
+            const u32x2_t b0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p0 + 64));
+            const u32x2_t a1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p1));
+            const u32x2_t b1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p1 + 64));
+            w[2 * slot] = u32x4_t{a0.x, a0.y, b0.x, b0.y};
+            w[2 * slot + 1] = u32x4_t{a1.x, a1.y, b1.x, b1.y};
+        } else if (nb == 4) {
+            w[2 * slot].x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p0));
+            w[2 * slot].z = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p0 + 32));
+            w[2 * slot + 1].x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p1));
+            w[2 * slot + 1].z = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p1 + 32));
+        } else {
+            const uint32_t a0 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p0));
+            const uint32_t b0 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p0 + 16));
+            const uint32_t a1 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p1));
+            const uint32_t b1 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p1 + 16));
+            w[2 * slot].x = a0 | (b0 << 16);
+            w[2 * slot + 1].x = a1 | (b1 << 16);
+        }
+    };
+    // fp16 pairs (natural dim order) of a narrow row held in one vector
+    auto narrow_pairs = [](u32x4_t r, const Fmt& f, int nb, uint32_t* out) {
+        to_f16_pairs(u32x4_t{r.x, r.y, 0u, 0u}, u32x4_t{r.z, r.w, 0u, 0u}, nb, f.flip, f.nz, out);
+    };
+    // scores (log2 units) of rows 0 and 1 of a sub-step of K bits nb held in slot `slot`
+    auto scores = [&](const u32x4_t* w, const Fmt& f, int nb, int slot, float* x0, float* x1) {
+        if (nb == 16 && f.st == kStBF16) {
+            const int jj = lane_now() & 7;          // fresh: keeps the LDS query reads in the loop
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float x0 = live0 ? s0[g] : -INFINITY;
-                const float x1 = live1 ? s1[g] : -INFINITY;
-                const float mx = fmaxf(x0, x1);
-                if (mx > m[g] + kLazyM) {
-                    const float c = exp2_fast(m[g] - mx);
-                    l[g] *= c;
-#pragma unroll
-                    for (int d = 0; d < 16; ++d) o[g][d] *= c;
-                    m[g] = mx;
-                }
-                const float p0 = exp2_fast(x0 - m[g]);
-                const float p1 = exp2_fast(x1 - m[g]);
-                l[g] += p0 + p1;
-                q0[g] = p0 * vf.sc;
-                q1[g] = p1 * vf.sc;
+                const uint4 qa = s_q[g][0][jj], qb = s_q[g][1][jj];
+                float x = 0.0f, y = 0.0f;
+                x = dot2_bf16(qa.x, w[0].x, x);
+                y = dot2_bf16(qa.x, w[2].x, y);
+                x = dot2_bf16(qa.y, w[0].y, x);
+                y = dot2_bf16(qa.y, w[2].y, y);
+                x = dot2_bf16(qa.z, w[0].z, x);
+                y = dot2_bf16(qa.z, w[2].z, y);
+                x = dot2_bf16(qa.w, w[0].w, x);
+                y = dot2_bf16(qa.w, w[2].w, y);
+                x = dot2_bf16(qb.x, w[1].x, x);
+                y = dot2_bf16(qb.x, w[3].x, y);
+                x = dot2_bf16(qb.y, w[1].y, x);
+                y = dot2_bf16(qb.y, w[3].y, y);
+                x = dot2_bf16(qb.z, w[1].z, x);
+                y = dot2_bf16(qb.z, w[3].z, y);
+                x = dot2_bf16(qb.w, w[1].w, x);
+                y = dot2_bf16(qb.w, w[3].w, y);
+                x0[g] = group8_sum(x) * a.scale_log2;
+                x1[g] = group8_sum(y) * a.scale_log2;
             }
-
-            // ---- K rows of the next step in flight while this step's V is summed
-            const Fmt nkf = fmt_of(nd, false);
-            int n0, n1;
-            rows_of(tn, n0, n1);
-            kr = load_rows(K + head_of(npage), nkf.nb, n0, n1);
-
-            auto accumulate = [&](int d, float x0, float x1) {
-#pragma unroll
-                for (int g = 0; g < G; ++g) o[g][d] = fmaf(q1[g], x1, fmaf(q0[g], x0, o[g][d]));
-            };
-            if (vf.st == kStBF16) {
-                const uint32_t w0[8] = {vr.r0a.x, vr.r0a.y, vr.r0a.z, vr.r0a.w, vr.r0b.x, vr.r0b.y, vr.r0b.z, vr.r0b.w};
-                const uint32_t w1[8] = {vr.r1a.x, vr.r1a.y, vr.r1a.z, vr.r1a.w, vr.r1b.x, vr.r1b.y, vr.r1b.z, vr.r1b.w};
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    accumulate(2 * k, bf_lo(w0[k]), bf_lo(w1[k]));
-                    accumulate(2 * k + 1, bf_hi(w0[k]), bf_hi(w1[k]));
-                }
-            } else {
-                uint32_t w0[8], w1[8];
-                to_f16_pairs(vr.r0a, vr.r0b, vf.nb, vf.flip, vf.nz, w0);
-                to_f16_pairs(vr.r1a, vr.r1b, vf.nb, vf.flip, vf.nz, w1);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    accumulate(2 * k, f16_lo(w0[k]), f16_lo(w1[k]));
-                    accumulate(2 * k + 1, f16_hi(w0[k]), f16_hi(w1[k]));
-                }
-            }
-            page = npage;
-            kf = nkf;
-            vf = fmt_of(nd, true);
-            r0 = n0;
-            r1 = n1;
+            return;
         }
+        uint32_t k0[8], k1[8];
+        if (nb == 16) {
+            to_f16_pairs(w[0], w[1], 16, 0u, 0u, k0);
+            to_f16_pairs(w[2], w[3], 16, 0u, 0u, k1);
+        } else {
+            narrow_pairs(w[2 * slot], f, nb, k0);
+            narrow_pairs(w[2 * slot + 1], f, nb, k1);
+        }
+        const float ksc = f.sc * a.scale_log2;
+        const int jj = lane_now() & 7;              // fresh: keeps the LDS query reads in the loop
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint4 ha = s_qh[g][0][jj], hb = s_qh[g][1][jj];
+            const uint32_t qh[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
+            float x = 0.0f, y = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                x = dot2_f16(qh[k], k0[k], x);
+                y = dot2_f16(qh[k], k1[k], y);
+            }
+            const float sc = ksc * qinv[g];
+            x0[g] = group8_sum(x) * sc;
+            x1[g] = group8_sum(y) * sc;
+        }
+    };
+    // o += p0 * v(row 0) + p1 * v(row 1) for a sub-step of V bits nb held in slot `slot`
+    auto values = [&](const u32x4_t* w, const Fmt& f, int nb, int slot, const float* p0, const float* p1) {
+        auto accumulate = [&](int d, float x0, float x1) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) o[g][d] = fmaf(p1[g], x1, fmaf(p0[g], x0, o[g][d]));
+        };
+        if (nb == 16 && f.st == kStBF16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                accumulate(2 * k, bf_lo(w[0][k]), bf_lo(w[2][k]));
+                accumulate(2 * k + 1, bf_hi(w[0][k]), bf_hi(w[2][k]));
+                accumulate(8 + 2 * k, bf_lo(w[1][k]), bf_lo(w[3][k]));
+                accumulate(8 + 2 * k + 1, bf_hi(w[1][k]), bf_hi(w[3][k]));
+            }
+            return;
+        }
+        uint32_t w0[8], w1[8];
+        if (nb == 16) {
+            to_f16_pairs(w[0], w[1], 16, 0u, 0u, w0);
+            to_f16_pairs(w[2], w[3], 16, 0u, 0u, w1);
+        } else {
+            narrow_pairs(w[2 * slot], f, nb, w0);
+            narrow_pairs(w[2 * slot + 1], f, nb, w1);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            accumulate(2 * k, f16_lo(w0[k]), f16_lo(w1[k]));
+            accumulate(2 * k + 1, f16_hi(w0[k]), f16_hi(w1[k]));
+        }
+    };
+    // one softmax update for the (up to) four rows of a group; s[r][g] becomes
+    // p times the V scale of the row's sub-step
+    auto softmax = [&](float (*s)[G], int ts0, int np, float vs0, float vs1) {
+        const int grp = lane_now() >> 3;
+        const int ts1 = ts0 + kSlabTokens;
+        const bool live[4] = {ts0 + grp < t1 && ts0 + grp >= vis0, ts0 + 8 + grp < t1 && ts0 + 8 + grp >= vis0,
+                              np == 2 && ts1 + grp < t1 && ts1 + grp >= vis0,
+                              np == 2 && ts1 + 8 + grp < t1 && ts1 + 8 + grp >= vis0};
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[r][g] = live[r] ? s[r][g] : -INFINITY;
+            const float mx = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]));
+            if (mx > m[g] + kLazyM) {
+                const float c = exp2_fast(m[g] - mx);
+                l[g] *= c;
+#pragma unroll
+                for (int d = 0; d < 16; ++d) o[g][d] *= c;
+                m[g] = mx;
+            }
+            float ps = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[r][g] = exp2_fast(s[r][g] - m[g]);
+                ps += s[r][g];
+            }
+            l[g] += ps;
+            s[0][g] *= vs0;
+            s[1][g] *= vs0;
+            s[2][g] *= vs1;
+            s[3][g] *= vs1;
+        }
+    };
+    auto same_class = [](const Sub& u, int kb, int vb) { return u.kf.nb == kb && u.vf.nb == vb; };
+
+    // A run of groups whose sub-steps all have K bits KB and V bits VB, two
+    // sub-steps per group when both are at most 8 bits (the second may be
+    // absent at the end of the run: its rows are then masked and its loads
+    // repeat the first's), pipelined as above.  Returns the first sub-step it
+    // did not process.
+    auto run = [&](auto kbc, auto vbc, int i) -> int {
+        constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
+        constexpr int P = KB <= 8 && VB <= 8 ? 2 : 1;
+        u32x4_t kh[4], vh[4];    // components a storage does not use are never read
+        // the second sub-step of the group at c0 (or c0 again when absent)
+        auto second = [&](int at, const Sub& first, bool& has) {
+            has = false;
+            if (P == 1 || at + 1 >= nsub) return first;
+            const Sub u = sub_of(at + 1);
+            has = same_class(u, KB, VB);
+            return has ? u : first;
+        };
+        // current group (c0, c1, h1) and the next one (n0, n1, nh1), resolved
+        // one group ahead so that the page and format reads of a group are
+        // issued a whole group before its loads need them
+        Sub c0 = sub_of(i);
+        bool h1;
+        Sub c1 = second(i, c0, h1);
+        int ni = i + (h1 ? 2 : 1);
+        bool cont = ni < nsub;
+        Sub n0 = c0, n1 = c1;
+        bool nh1 = false;
+        if (cont) {
+            n0 = sub_of(ni);
+            cont = same_class(n0, KB, VB);
+            if (cont) n1 = second(ni, n0, nh1);
+        }
+        load_sub(kh, K, c0, KB, 0);
+        if (P == 2) load_sub(kh, K, c1, KB, 1);
+        for (;;) {
+            load_sub(vh, V, c0, VB, 0);
+            if (P == 2) load_sub(vh, V, c1, VB, 1);
+            float sc[4][G];
+            scores(kh, c0.kf, KB, 0, sc[0], sc[1]);
+            if (P == 2) scores(kh, c1.kf, KB, 1, sc[2], sc[3]);
+            softmax(sc, c0.ts, h1 ? 2 : 1, c0.vf.sc, c1.vf.sc);
+            if (cont) {
+                load_sub(kh, K, n0, KB, 0);
+                if (P == 2) load_sub(kh, K, n1, KB, 1);
+            }
+            // the group after next
+            const int nni = ni + (nh1 ? 2 : 1);
+            bool mcont = cont && nni < nsub;
+            Sub m0 = n0, m1 = n1;
+            bool mh1 = false;
+            if (mcont) {
+                m0 = sub_of(nni);
+                mcont = same_class(m0, KB, VB);
+                if (mcont) m1 = second(nni, m0, mh1);
+            }
+            values(vh, c0.vf, VB, 0, sc[0], sc[1]);
+            if (P == 2) values(vh, c1.vf, VB, 1, sc[2], sc[3]);
+            if (!cont) return ni;
+            i = ni;
+            c0 = n0;
+            c1 = n1;
+            h1 = nh1;
+            ni = nni;
+            n0 = m0;
+            n1 = m1;
+            nh1 = mh1;
+            cont = mcont;
+        }
+    };
+    using I16 = std::integral_constant<int, 16>;
+    using I8 = std::integral_constant<int, 8>;
+    using I4 = std::integral_constant<int, 4>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int i = 0; i < nsub;) {
+        const Sub u = sub_of(i);
+        const int kb = u.kf.nb, vb = u.vf.nb;
+#define PKV_RUN(KBV, VBV, KT, VT) \
+        if (kb == KBV && vb == VBV) { i = run(KT{}, VT{}, i); continue; }
+        PKV_RUN(16, 16, I16, I16) PKV_RUN(16, 8, I16, I8) PKV_RUN(16, 4, I16, I4) PKV_RUN(16, 2, I16, I2)
+        PKV_RUN(8, 16, I8, I16) PKV_RUN(4, 16, I4, I16) PKV_RUN(2, 16, I2, I16)
+        PKV_RUN(8, 8, I8, I8) PKV_RUN(8, 4, I8, I4) PKV_RUN(8, 2, I8, I2)
+        PKV_RUN(4, 8, I4, I8) PKV_RUN(4, 4, I4, I4) PKV_RUN(4, 2, I4, I2)
+        PKV_RUN(2, 8, I2, I8) PKV_RUN(2, 4, I2, I4)
+#undef PKV_RUN
+        i = run(I2{}, I2{}, i);      // the remaining pair, (2, 2)
     }
 
+    const int lane_e = lane_now();
+    const int grp_e = lane_e >> 3, j_e = lane_e & 7;
     // merge the eight token groups of the wave (lanes with the same j)
 #pragma unroll
     for (int off = 8; off < 64; off <<= 1) {
@@ -568,15 +702,15 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
             m[g] = mn;
         }
     }
-    if (grp == 0) {
+    if (grp_e == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
-                s_o[wave][g][j * 8 + d] = o[g][d];
-                s_o[wave][g][64 + j * 8 + d] = o[g][8 + d];
+                s_o[wave][g][j_e * 8 + d] = o[g][d];
+                s_o[wave][g][64 + j_e * 8 + d] = o[g][8 + d];
             }
-            if (j == 0) {
+            if (j_e == 0) {
                 s_ml[wave][g][0] = m[g];
                 s_ml[wave][g][1] = l[g];
             }
@@ -585,7 +719,7 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     __syncthreads();
 
     // merge the four waves; thread t handles (g, d) pairs t, t + 256, ...
-    for (int e = threadIdx.x; e < G * kDM; e += 256) {
+    for (int e = wave * 64 + lane_e; e < G * kDM; e += 256) {
         const int g = e / kDM;
         const int d = e % kDM;
         float mn = -FLT_MAX;

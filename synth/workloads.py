@@ -22,6 +22,12 @@ the tests also use scaled-down instances of the same recipes):
                   tokens, 32/8 heads, D = 128; codes ~ U{0..15}; per 32-element
                   block fp16 scale ~ U[0.01, 0.1] and zero point ~ U{0..15};
                   q ~ N(0, 1) float32.
+* ``mixed32k`` -- the paged32k shapes (32 rows x 32768 tokens, a full pool
+                  of 65536 pages of 16) appended with the pages' length-threshold
+                  format selector: the first 1024 tokens of a row in dense BF16
+                  pages, the rest with INT8 keys (scale 0.01, zero point 0) and
+                  UINT4 values (scale 0.25, zero point 8); K ~ N(0, 0.3) and
+                  V ~ N(0, 0.5) so those scales rarely saturate; q ~ N(0, 1).
 * ``qwen``     -- 128 rows, 16/8 heads, D = 128, lengths ~ U{1024..16384},
                   bf16 pages of 16 tokens; a 512-token chunk; logits
                   [128, 151936] ~ N(0, 3) float32 for sampling.
@@ -34,7 +40,7 @@ import numpy as np
 
 from . import f16_bits, f32_to_bf16_bits, lognormal_lengths, normal, permutation, rng, uniform
 
-SEEDS = {"tiny": 0, "contig": 1, "paged": 2, "paged32k": 3, "int4": 4, "qwen": 5}
+SEEDS = {"tiny": 0, "contig": 1, "paged": 2, "paged32k": 3, "int4": 4, "qwen": 5, "mixed32k": 6}
 
 
 @dataclass
@@ -150,6 +156,32 @@ def int4(seed: int = SEEDS["int4"], B: int = 32, L: int = 8192, Hq: int = 32, Hk
          bs: int = 16, NB: int = 16384) -> Int4Spec:
     lengths = np.full(B, L, dtype=np.int32)
     return Int4Spec(seed, B, Hq, Hkv, D, bs, NB, -(-L // bs), lengths, permutation(rng(seed, 1), NB))
+
+
+@dataclass
+class MixedSpec:
+    """Shapes, selector and value distributions of a mixed-format pool."""
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    bs: int
+    NB: int
+    maxb: int
+    L: int
+    threshold: int                 # tokens kept in the early formats
+    early: tuple                   # ((storage, scale, zero_point) of K, of V)
+    late: tuple
+    k_sigma: float
+    v_sigma: float
+    order: np.ndarray = field(repr=False)
+
+
+def mixed32k(seed: int = SEEDS["mixed32k"], B: int = 32, L: int = 32768, Hq: int = 32, Hkv: int = 8,
+             D: int = 128, bs: int = 16, NB: int = 65536) -> MixedSpec:
+    return MixedSpec(seed, B, Hq, Hkv, D, bs, NB, -(-L // bs), L, 1024, (("BF16", 1.0, 0), ("BF16", 1.0, 0)),
+                     (("INT8", 0.01, 0), ("UINT4", 0.25, 8)), 0.3, 0.5, permutation(rng(seed, 1), NB))
 
 
 def qwen(seed: int = SEEDS["qwen"], B: int = 128, Hq: int = 16, Hkv: int = 8, D: int = 128, bs: int = 16,

@@ -257,3 +257,55 @@ def test_qwen_shaped_layer_decode_chunk_and_sampling():
         sc = osamp.gumbel_scores(logits[b], 0.7, 5, b)
         assert abs(sc[got_ids[b]] - sc[want[b]]) <= 1e-5 * max(1.0, abs(sc[want[b]]))
     assert (got_ids == want).mean() >= 0.99
+
+
+def test_mixed32k_full_size():
+    """The mixed-format bench row: 32 x 32768 tokens in a full pool, BF16 prefix pages then INT8 K / UINT4 V
+    pages chosen by the length-threshold selector, appended in the bench's chunks; sampled rows' pages
+    bit for bit and their attention against the oracle."""
+    require_gpu()
+    from oracle import mixed as om
+    w = workloads.mixed32k()
+    rows = [0, 31]
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(w.seed)
+    kp = torch.zeros((w.NB, w.Hkv, w.bs, w.D), device=DEV, dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    pd = pkv.mixed_page_desc(w.NB, DEV)
+    pool = pkv.Pool(w.NB, w.bs, w.B, w.maxb, w.order)
+    ref_pool = ocache.PagePool(w.NB, w.bs, w.B, w.maxb, w.order)
+    table = torch.full((w.B, w.maxb), -1, device=DEV, dtype=torch.int32)
+    pool.reserve(range(w.B), [w.L] * w.B, table)
+    for b in range(w.B):
+        ref_pool.reserve(b, w.L)
+    assert np.array_equal(table.cpu().numpy(), ref_pool.table)
+    fm = lambda t: pkv.page_format(*t)
+    select = pkv.LengthThresholdSelector(w.threshold, (fm(w.early[0]), fm(w.early[1])), (fm(w.late[0]), fm(w.late[1])))
+    refs = {b: om.MixedPool(w.maxb, w.Hkv, w.bs, w.D) for b in rows}
+    local = np.arange(w.maxb, dtype=np.int32)[None]
+    with pkv.bind_writable(kp), pkv.bind_writable(vp), pkv.bind_writable(pd):
+        pos = 0
+        while pos < w.L:
+            n = w.threshold if pos < w.threshold else min(2048, w.L - pos)
+            kv = (torch.randn((w.B, w.Hkv, n, w.D), generator=gen, device=DEV) * w.k_sigma).to(torch.bfloat16)
+            vv = (torch.randn((w.B, w.Hkv, n, w.D), generator=gen, device=DEV) * w.v_sigma).to(torch.bfloat16)
+            kb, vb = bits_host(kv), bits_host(vv)
+            kf, vf = select(pos)
+            pkv.mixed_cache_update(pool, kp, vp, pd, table, kv, vv, [pos] * w.B, n, kf, vf)
+            okf, ovf = (w.early if pos < w.threshold else w.late)
+            for b in rows:
+                refs[b].append(local, kb[b:b + 1], vb[b:b + 1], [pos], n, om.Format(*okf), om.Format(*ovf))
+            pos += n
+    q = torch.randn((w.B, w.Hq, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+    qh = onum.bf16_to_f64(bits_host(q))
+    out = torch.empty((w.B, w.Hq, w.D), device=DEV, dtype=torch.bfloat16)
+    ws = workspace(pkv.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.L))
+    pkv.paged_decode_attention_mixed(q, kp, vp, pd, table, w.maxb, w.bs, [w.L] * w.B, out, ws, pool=pool)
+    got = onum.bf16_to_f64(bits_host(out))
+    for b in rows:
+        ids = torch.from_numpy(ref_pool.table[b].astype(np.int64)).to(DEV)
+        for name, t in (("k", kp), ("v", vp)):
+            gb = bytes_host(t.index_select(0, ids).contiguous()).reshape(w.maxb, w.Hkv, -1)
+            assert np.array_equal(gb, refs[b].data[name]), (b, name)
+        ref = om.decode_attention(refs[b], qh[b:b + 1], local, [w.L])
+        assert rel_err_rows(got[b], ref[0]) <= 2e-2, b
