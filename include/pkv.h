@@ -10,7 +10,8 @@
  *   2. attention of the new queries over the valid cache prefix
  *      (contiguous, paged bf16, paged INT4, pages of mixed formats; a
  *      causal chunk variant),
- *   3. greedy or seeded temperature sampling of final logits.
+ *   3. greedy or seeded temperature sampling of final logits, and the
+ *      bookkeeping of a generation loop (EOS, padding, stop).
  *
  * Sources: the onnx-light documentation pages "Mutable execution cache"
  * (in-place update contract, paged cache, runtime contract, memory planning),
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -429,6 +430,41 @@ size_t pkv_sample_workspace_size(int32_t B, int64_t V);
  * out_ids: device int64[B]. */
 pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed,
                       int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Generation loop                                                           */
+/* "Persistent input/output feedback", section "Autoregressive generation":
+ * the result holds the prompt and the generated tokens; temperature 0 is
+ * greedy, a positive one samples softmax(logits / T) and a seed makes it
+ * repeatable; generation stops at the token limit or once every row has
+ * emitted EOS; finished rows are padded with pad_token_id (EOS by default);
+ * each iteration consumes one new token.  A caller's loop runs its model,
+ * pkv_sample with pkv_generate_step_seed(seed, t, B, V), then
+ * pkv_generate_finish, and stops when *unfinished reaches 0.                */
+/* ------------------------------------------------------------------------ */
+
+/* Seed of iteration `step` of one generation: seed + step * B * V * gamma
+ * (mod 2^64, gamma the SplitMix64 increment 0x9E3779B97F4A7C15), so the
+ * draws of iteration t use SplitMix64 outputs t*B*V + b*V + v + 1 of `seed`:
+ * one counter across the whole generation, no two draws alike. */
+uint64_t pkv_generate_step_seed(uint64_t seed, int64_t step, int32_t B, int64_t V);
+
+/* sampled   : device int64[B], this iteration's draws (pkv_sample).
+ * finished  : device u8[B], 0 / 1, read and updated (zero it before the first
+ *             iteration).
+ * tokens    : device int64[B, row_stride]; column `column` receives, per
+ *             row, the sampled id, or pad_token_id if the row had already
+ *             finished.  A row finishes when the written token equals
+ *             eos_token_id (eos_token_id < 0: no EOS, rows never finish).
+ * next_ids  : device int64[B], the written tokens (the model's next input);
+ *             it may be `sampled` itself.
+ * unfinished: device int32[1], the number of rows not finished afterwards.
+ * Errors: PKV_E_ARG for null pointers, B < 0, column outside
+ * [0, row_stride); PKV_E_ALIAS when tokens overlaps another argument. */
+pkv_status pkv_generate_finish(const int64_t* sampled, uint8_t* finished, int64_t* tokens,
+                               int64_t row_stride, int32_t column, int32_t B,
+                               int64_t eos_token_id, int64_t pad_token_id, int64_t* next_ids,
+                               int32_t* unfinished, void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,7 @@ module computes nothing and never copies or converts tensors (non-contiguous
 inputs are rejected).  If ``libpkv.so`` is missing, importing this package
 raises: there is no fallback.
 
-Build the library first:  ``python -m place_persistent_kv_amd.build``.
+Build the library first:  ``python place_persistent_kv_amd/build.py``.
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m place_persistent_kv_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python place_persistent_kv_amd/build.py` "
                       "(the decode path has no CPU fallback)")
 
 # torch supplies device memory and streams and ships its own HIP runtime.  It
@@ -136,6 +136,9 @@ _SIG = {
                                           _VP]),
     "pkv_paged_decode_attention_mixed": (C.c_int, [_T, _T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P,
                                                    C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
+    "pkv_generate_step_seed": (C.c_uint64, [C.c_uint64, C.c_int64, C.c_int32, C.c_int64]),
+    "pkv_generate_finish": (C.c_int, [_VP, _VP, _VP, C.c_int64, C.c_int32, C.c_int32, C.c_int64, C.c_int64, _VP,
+                                      _VP, _VP]),
     "pkv_sample_workspace_size": (C.c_size_t, [C.c_int32, C.c_int64]),
     "pkv_sample": (C.c_int, [_T, C.c_float, C.c_uint64, _VP, _VP, C.c_size_t, _VP]),
 }
@@ -147,10 +150,10 @@ for _name, (_res, _args) in _SIG.items():
         _fn.argtypes = _args
 
 
-ABI_VERSION = 3      # the argument lists above follow this version of include/pkv.h
+ABI_VERSION = 4      # the argument lists above follow this version of include/pkv.h
 if _lib.pkv_abi_version() != ABI_VERSION:
     raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
-                      "rebuild it (python -m place_persistent_kv_amd.build)")
+                      "rebuild it (python place_persistent_kv_amd/build.py)")
 
 
 def exported_symbols() -> list[str]:
@@ -482,3 +485,60 @@ def sample(logits, temperature: float, seed: int, out_ids, workspace=None, strea
     _check(_lib.pkv_sample(C.byref(desc(logits)), float(temperature), C.c_uint64(seed & (2 ** 64 - 1)),
                            _ptr(out_ids), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
                            _stream(stream)), "pkv_sample")
+
+
+# ---------------------------------------------------------------------------
+# Generation loop
+# ---------------------------------------------------------------------------
+def generate_step_seed(seed: int, step: int, B: int, V: int) -> int:
+    return int(_lib.pkv_generate_step_seed(C.c_uint64(seed & (2 ** 64 - 1)), int(step), int(B), int(V)))
+
+
+def generate_finish(sampled, finished, tokens, column: int, eos_token_id, pad_token_id, next_ids, unfinished,
+                    stream=None) -> None:
+    """One iteration's bookkeeping (``pkv_generate_finish``); ``eos_token_id`` None means no EOS."""
+    B, row_stride = tokens.shape
+    eos = -1 if eos_token_id is None else int(eos_token_id)
+    pad = 0 if pad_token_id is None else int(pad_token_id)
+    _check(_lib.pkv_generate_finish(_ptr(sampled), _ptr(finished), _ptr(tokens), int(row_stride), int(column), int(B),
+                                    eos, pad, _ptr(next_ids), _ptr(unfinished), _stream(stream)),
+           "pkv_generate_finish")
+
+
+def generate(forward, prompt_ids, max_new_tokens: int, temperature: float = 0.0, seed: int = 0,
+             eos_token_id=None, pad_token_id=None, stream=None):
+    """Token loop ("Persistent input/output feedback", "Autoregressive generation").
+
+    ``forward(step, input_ids)`` is the caller's model: it receives the prompt
+    (device int64 ``[B, P]``) at step 0 and then the previous step's tokens
+    (device int64 ``[B]``), and returns device logits ``[B, V]`` or
+    ``[B, S, V]``.  Each iteration samples (``pkv_sample``) and books the
+    tokens (``pkv_generate_finish``) in the library; the loop stops at
+    ``max_new_tokens`` or once every row has emitted EOS (one host read of a
+    device counter per iteration).  Returns device int64 ``[B, P + generated]``.
+    """
+    import torch
+    B, P = prompt_ids.shape
+    dev = prompt_ids.device
+    pad = eos_token_id if pad_token_id is None else pad_token_id
+    tokens = torch.empty((B, P + max_new_tokens), dtype=torch.int64, device=dev)
+    tokens[:, :P].copy_(prompt_ids)
+    finished = torch.zeros(B, dtype=torch.uint8, device=dev)
+    ids = torch.empty(B, dtype=torch.int64, device=dev)
+    nxt = torch.empty(B, dtype=torch.int64, device=dev)
+    unfinished = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = None
+    inputs = prompt_ids
+    done = 0
+    for t in range(int(max_new_tokens)):
+        logits = forward(t, inputs)
+        V = logits.shape[-1]
+        if ws is None:
+            ws = torch.empty(sample_workspace_size(B, V), dtype=torch.uint8, device=dev)
+        sample(logits, temperature, generate_step_seed(seed, t, B, V), ids, ws, stream=stream)
+        generate_finish(ids, finished, tokens, P + t, eos_token_id, pad, nxt, unfinished, stream=stream)
+        done = t + 1
+        inputs = nxt
+        if eos_token_id is not None and int(unfinished.item()) == 0:
+            break
+    return tokens[:, :P + done]

@@ -1,6 +1,9 @@
 """Build libpkv.so (HIP, gfx950) in place, next to this file.
 
-    python -m place_persistent_kv_amd.build [-j N]
+    python place_persistent_kv_amd/build.py [-j N]
+
+(run it as a script: importing the package refuses a missing or stale
+library, which is what this replaces).
 
 Every ``csrc/*.hip`` and ``csrc/*.cpp`` file is compiled with hipcc for
 gfx950 and linked into ``place_persistent_kv_amd/libpkv.so``.  Packed FP32

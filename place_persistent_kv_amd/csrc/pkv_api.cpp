@@ -1309,4 +1309,38 @@ pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed
     return ok();
 }
 
+
+uint64_t pkv_generate_step_seed(uint64_t seed, int64_t step, int32_t B, int64_t V) {
+    return seed + static_cast<uint64_t>(step) * static_cast<uint64_t>(B) * static_cast<uint64_t>(V) *
+                      0x9E3779B97F4A7C15ull;
+}
+
+pkv_status pkv_generate_finish(const int64_t* sampled, uint8_t* finished, int64_t* tokens,
+                               int64_t row_stride, int32_t column, int32_t B,
+                               int64_t eos_token_id, int64_t pad_token_id, int64_t* next_ids,
+                               int32_t* unfinished, void* stream) {
+    if (B < 0) return fail(PKV_E_ARG, "generate_finish: negative batch");
+    if (!sampled || !finished || !tokens || !next_ids || !unfinished)
+        return fail(PKV_E_ARG, "generate_finish: null pointer");
+    if (row_stride <= 0 || column < 0 || column >= row_stride)
+        return fail(PKV_E_ARG, "generate_finish: column %d outside [0, %lld)", column, (long long)row_stride);
+    const Span ts = span(tokens, int64_t(B) * row_stride * 8);
+    if (overlap(ts, span(sampled, int64_t(B) * 8)) || overlap(ts, span(finished, B)) ||
+        overlap(ts, span(next_ids, int64_t(B) * 8)) || overlap(ts, span(unfinished, 4)))
+        return fail(PKV_E_ALIAS, "generate_finish: tokens overlaps another argument");
+    GenerateArgs a;
+    a.sampled = sampled;
+    a.finished = finished;
+    a.tokens = tokens;
+    a.next_ids = next_ids;
+    a.unfinished = unfinished;
+    a.row_stride = row_stride;
+    a.eos = eos_token_id;
+    a.pad = pad_token_id;
+    a.column = column;
+    a.B = B;
+    a.has_eos = eos_token_id >= 0;
+    PKV_HIP(launch_generate_finish(a, static_cast<hipStream_t>(stream)), "generate_finish launch");
+    return ok();
+}
 }  // extern "C"

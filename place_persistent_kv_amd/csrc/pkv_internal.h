@@ -225,6 +225,21 @@ bool chunk_supported(int D, int G, int bs, int C);
 hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Generation loop
+// ---------------------------------------------------------------------------
+struct GenerateArgs {
+    const int64_t* sampled;      // [B] ids drawn this iteration
+    uint8_t* finished;           // [B] 0 / 1, updated
+    int64_t* tokens;             // [B, row_stride] output, column `column` written
+    int64_t* next_ids;           // [B] the written tokens (may be `sampled`)
+    int32_t* unfinished;         // [1] rows still running after this iteration
+    int64_t row_stride;
+    int64_t eos, pad;
+    int32_t column, B, has_eos;
+};
+hipError_t launch_generate_finish(const GenerateArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Sampling
 // ---------------------------------------------------------------------------
 struct SampleArgs {

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if getattr(pkv._lib, n, None) is None]
     assert not missing, missing
     assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
-    assert pkv.abi_version() == pkv.ABI_VERSION == 3
+    assert pkv.abi_version() == pkv.ABI_VERSION == 4
 
 
 def R(ptr, dtype, shape):
@@ -428,3 +428,27 @@ def test_length_threshold_selector():
     late = (pkv.page_format("INT8", 0.01, 0), pkv.page_format("UINT4", 0.25, 8))
     sel = pkv.LengthThresholdSelector(1024, early, late)
     assert sel(0) is early and sel(1023) is early and sel(1024) is late
+
+
+# --------------------------------------------------------------------------- generation loop
+def test_generate_step_seed_matches_the_oracle():
+    from oracle import generate as ogen
+    for seed, t, B, V in [(0, 0, 1, 1), (7, 3, 128, 151936), (2 ** 64 - 1, 1000, 32, 50000)]:
+        assert pkv.generate_step_seed(seed, t, B, V) == ogen.step_seed(seed, t, B, V)
+
+
+def test_generate_finish_errors():
+    tok = R(FAKE, pkv.I64, [4, 10])
+    ids, fin, nxt, unf = FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, FAKE + 0x4000
+    with pytest.raises(pkv.PkvError) as e:
+        pkv._check(pkv._lib.pkv_generate_finish(ids, fin, tok.ptr, 10, 10, 4, 2, 2, nxt, unf, None), "x")
+    assert e.value.status == pkv.E_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv._check(pkv._lib.pkv_generate_finish(ids, fin, tok.ptr, 10, -1, 4, 2, 2, nxt, unf, None), "x")
+    assert e.value.status == pkv.E_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv._check(pkv._lib.pkv_generate_finish(None, fin, tok.ptr, 10, 0, 4, 2, 2, nxt, unf, None), "x")
+    assert e.value.status == pkv.E_ARG
+    with pytest.raises(pkv.PkvError) as e:      # next_ids inside tokens
+        pkv._check(pkv._lib.pkv_generate_finish(ids, fin, tok.ptr, 10, 0, 4, 2, 2, tok.ptr + 8, unf, None), "x")
+    assert e.value.status == pkv.E_ALIAS
