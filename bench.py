@@ -722,8 +722,85 @@ def bench_mixed(steps, warmup, cpu):
                  _hbm_roofline(nbytes, us), cpu_res, attn_us=round(us, 2), attn_algorithmic_bytes=nbytes)
 
 
+def bench_generate(steps, warmup, cpu, layers=28, new_tokens=8):
+    """The generation loop (pkv.generate) over the 28-layer Qwen-shaped paged caches: 128 rows with cached
+    prefixes of U[1024, 16384] tokens, a one-token prompt, `new_tokens` iterations.  The model is synthetic:
+    per layer q, k, v are embedding-table rows of the input token (random bf16 tables), each layer appends
+    k, v in place and runs paged decode attention, and the logits are the last layer's output times a random
+    bf16 LM head [2048, 151936]; EOS is the last vocabulary id.  `steps` timed generate calls."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    w = workloads.qwen()
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    Bq, Hq, Hkv, Dq, bs, maxb, V = w["B"], w["Hq"], w["Hkv"], w["D"], w["bs"], w["maxb"], w["vocab"]
+    runs = warmup + steps
+    ks, vs, pool, table, NBq = _qwen_pools(w, runs * new_tokens, layers, gen)
+    emb_q = torch.randn((V, Hq, Dq), generator=gen, device=dev).to(torch.bfloat16)
+    emb_k = torch.randn((V, Hkv, 1, Dq), generator=gen, device=dev).to(torch.bfloat16)
+    emb_v = torch.randn((V, Hkv, 1, Dq), generator=gen, device=dev).to(torch.bfloat16)
+    head = (torch.randn((Hq * Dq, V), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+    out = torch.empty((Bq, Hq, Dq), device=dev, dtype=torch.bfloat16)
+    L0 = w["lengths"].astype(np.int64)
+    ws = torch.empty(pkv.decode_workspace_size(Bq, Hq, Hkv, Dq, int(L0.max()) + runs * new_tokens), device=dev,
+                     dtype=torch.uint8)
+    binds = [pkv.bind_writable(t) for t in ks + vs]
+    state = {"L": L0.copy()}
+
+    def forward(step, ids):
+        tok = (ids[:, -1] if ids.dim() == 2 else ids).contiguous()
+        q = emb_q.index_select(0, tok)
+        k = emb_k.index_select(0, tok)
+        v = emb_v.index_select(0, tok)
+        pos = state["L"].tolist()
+        lens = (state["L"] + 1).tolist()
+        for layer in range(layers):
+            pkv.paged_cache_update(pool, ks[layer], table, k, pos, 1)
+            pkv.paged_cache_update(pool, vs[layer], table, v, pos, 1)
+            pkv.paged_decode_attention(q, ks[layer], vs[layer], table, maxb, bs, lens, out, ws, pool=pool)
+        state["L"] += 1
+        return out.reshape(Bq, Hq * Dq) @ head
+
+    prompt = torch.from_numpy(np.arange(Bq, dtype=np.int64)[:, None] * 7 % V).to(dev)
+    for i in range(warmup):
+        pkv.generate(forward, prompt, new_tokens, 0.7, 100 + i, V - 1)
+    torch.cuda.synchronize()
+    mean_L = float(state["L"].mean())
+    t0 = time.perf_counter()
+    produced = 0
+    for i in range(steps):
+        res = pkv.generate(forward, prompt, new_tokens, 0.7, 200 + i, V - 1)
+        produced += Bq * (res.shape[1] - 1)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    for bnd in binds:
+        bnd.close()
+    iters = produced / Bq
+    us_iter = el / iters * 1e6
+    mean_ctx = mean_L + new_tokens * steps / 2
+    nbytes = int(layers * (Bq * mean_ctx * Hkv * Dq * 4 + Bq * Hq * Dq * 4))    # attention bytes of one iteration
+    cpu_res = None
+    if cpu:
+        rate, n, el_c = _oracle_decode_rows([int(np.median(L0))], Hq, Hkv, Dq, 10.0, 5)
+        cpu_res = {"value": round(rate / layers * float(np.median(L0)) / mean_ctx, 4), "unit": "tokens/s",
+                   "cores": 1, "kind": "oracle",
+                   "sample": f"{n} median-length rows of one layer's attention in {el_c:.1f} s, scaled to {layers} "
+                             f"layers and the mean context (the LM head and sampling are not included)"}
+    return _line("generated tokens/s, 28-layer Qwen-shaped generation loop (paged bf16, T=0.7, EOS)",
+                 produced / el, "tokens/s", steps, warmup, el / steps * 1e6, "bf16",
+                 {"workload": "generate", "layers": layers, "batch": Bq, "q_heads": Hq, "kv_heads": Hkv,
+                  "head_dim": Dq, "block_size": bs, "vocab": V, "new_tokens": new_tokens,
+                  "mean_ctx": round(mean_ctx, 1), "temperature": 0.7},
+                 _hbm_roofline(nbytes, us_iter), cpu_res, us_per_iteration=round(us_iter, 1),
+                 attn_algorithmic_bytes_per_iteration=nbytes)
+
+
 WORKLOADS = {"contig": bench_contig, "paged": bench_paged, "int4": bench_int4, "qwen-decode": bench_qwen_decode,
-             "qwen-chunk": bench_qwen_chunk, "sample": bench_sample, "window": bench_window, "mixed": bench_mixed}
+             "qwen-chunk": bench_qwen_chunk, "sample": bench_sample, "window": bench_window, "mixed": bench_mixed,
+             "generate": bench_generate}
 
 
 def main():
