@@ -37,8 +37,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
 # Per-source device flags.  The INT4 decode kernel reduces row maxima with
 # DPP; without IEEE mode (no signalling-NaN quieting) each step is a single
 # v_max_f32_dpp instead of a move plus canonicalising maxima.  Its inputs are
-# finite by construction (masked scores are -inf, never NaN).
-EXTRA = {"decode_int4.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+# finite by construction (masked scores are -inf, never NaN).  Its matrix-core
+# accumulators stay in ordinary VGPRs (-amdgpu-mfma-vgpr-form): the lazy
+# softmax rescale multiplies them in place, and with AGPR accumulators the
+# compiler copies all of them out and back on every group.
+EXTRA = {"decode_int4.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -26,15 +26,24 @@
 // score, so every lane of the softmax carries a distinct score (a 16-row MFMA
 // would leave 12 of its 16 rows empty at 4 heads).
 //
-// P.V on the vector ALUs, the dequantisation folded in:
-//     o += p * s * c - p * s * z   (the second term kept per block)
-// with LPT lanes per token, each owning DPL dims.  The running max of every
-// head is wave-uniform (a reduction over the head's lanes plus v_readlane),
-// so the lazy rescale is a uniform branch and the lanes' partial outputs are
-// plain sums.
+// P.V on the matrix cores as well, in the same 4x4x4 blocks: block
+// (token quad tq, 32-dim block beta) multiplies the probabilities of 4 heads
+// times the scale of block beta (rows; bf16 high + low parts) by the raw
+// codes 128 + c of 4 tokens, each lane holding one code word (8 dims) of
+// 4 consecutive rows, so that one instruction covers 64 dims and eight cover
+// the lane's word.  With x = p * s per (head, token, block)
+//     sum_t p s (c - z) = sum_t x (128 + c) - sum_t x 128 - sum_t x z
+// the middle term is a ninth product (codes replaced by 128, so it matches
+// the first one's operands exactly) and the zero-point term a vector FMA.
+// The accumulators stay per token quad and are summed over the quads once,
+// at the end.  The running max of every head is wave-uniform (a reduction
+// over the head's lanes plus v_readlane), so the lazy rescale is a uniform
+// branch.
 // The split / merge structure is that of the bf16 fast kernel.
 
 #include "device_common.h"
+
+#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -69,60 +78,58 @@ __device__ __forceinline__ uint32_t vconst(uint32_t c) {
     return r;
 }
 
+// x * y with 0 * anything = 0 (v_mul_legacy_f32), so that a zero
+// probability cancels an arbitrary scale read from an unwritten row
+__device__ __forceinline__ float mul_legacy(float x, float y) {
+    float r;
+    asm("v_mul_legacy_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+    return r;
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-// x & m, opaque to the optimiser: the byte-wise conversions below then stay
-// single v_cvt_f32_ubyte{0..3} instructions instead of a bit-field extract
-// each (the known-zero high nibbles would otherwise turn every byte into a
-// 4-bit field)
-__device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
-    uint32_t r;
-    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
-    return r;
+// x (op) the value of lane l ^ 32 / l ^ 16, on the vector ALU (gfx950
+// v_permlane{32,16}_swap: the two results hold, per lane, the values of the
+// lane and of its partner)
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-// code bytes of one lane's dims -> floats in dim order (even dim = low nibble)
-template <int CB>
-__device__ __forceinline__ void unpack_codes(const uint32_t (&w)[(CB + 3) / 4], float (&c)[2 * CB]) {
-#pragma unroll
-    for (int i = 0; i < CB / 4; ++i) {
-        const uint32_t lo = and_opaque(w[i], 0x0F0F0F0Fu), hi = and_opaque(w[i] >> 4, 0x0F0F0F0Fu);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            c[8 * i + 2 * k] = static_cast<float>(static_cast<uint8_t>(lo >> (8 * k)));
-            c[8 * i + 2 * k + 1] = static_cast<float>(static_cast<uint8_t>(hi >> (8 * k)));
-        }
-    }
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int G>
-__global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
-    constexpr int HP = G < 4 ? G : 4;           // heads per Q.K pass (rows of the 4x4 blocks)
-    constexpr int NP = (G + 3) / 4;             // Q.K passes
-    constexpr int DPL = G <= 2 ? 32 : 64 / G;   // dims per lane in P.V
-    constexpr int LPT = kD4 / DPL;              // lanes per token in P.V
-    constexpr int TPR = 64 / LPT;               // tokens per P.V round
-    constexpr int ROUNDS = kGroup / TPR;
-    constexpr int CB = DPL / 2;                 // code bytes per lane and token
-    constexpr int CW = CB / 4;                  // code words per lane and token
+__global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4DecodeArgs a) {
+    constexpr int HP = G < 4 ? G : 4;           // heads per pass (rows of the 4x4 blocks)
+    constexpr int NP = (G + 3) / 4;             // passes
 
-    __shared__ float s_p[kWaves4][kGroup][G];
+    __shared__ float s_p[kWaves4][2][4 * NP][kGroup];   // probabilities [buffer][head][token]; rows >= G stay 0
     __shared__ float s_o[kWaves4][G][kD4];
     __shared__ float s_ml[kWaves4][G][2];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    // Q.K lanes: 16 blocks b = 4 tg + qb of 4 lanes; lane 16 tg + 4 qb + jj holds
+    // 16 blocks b = 4 tg + qb of 4 lanes.  Q.K: lane 16 tg + 4 qb + jj holds
     // token 4 tg + jj of the group, 32-dim block qb (B operand and result), and
-    // head row jj of block qb (A operand)
+    // head row jj of block qb (A operand).  P.V: the same lane holds code word
+    // 4 qb + jj (dims 32 qb + 8 jj ..) of rows 4 tg .. 4 tg + 3 (B operand and
+    // result) and head row jj for those rows and block qb (A operand).
     const int qtg = lane >> 4;
     const int qb = (lane >> 2) & 3;
     const int jj = lane & 3;
     const int tok = 4 * qtg + jj;
-    const int tl = lane / LPT;      // P.V: token of the round
-    const int dc = lane % LPT;      // P.V: dims DPL * dc ..
 
     const int work = blockIdx.x;
     const int kvh = work % a.Hkv;
@@ -138,6 +145,11 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
     const int wbeg = t0 + wave * quarter;
     const int wend = min(t1, wbeg + quarter);
     const int32_t* __restrict__ pt = a.page_table + int64_t(b) * a.maxb;
+
+    if constexpr (G < 4) {
+        for (int e = lane; e < 2 * (4 - G) * kGroup; e += 64)
+            s_p[wave][e / ((4 - G) * kGroup)][G + (e / kGroup) % (4 - G)][e % kGroup] = 0.0f;
+    }
 
     // ---- query operands: A rows = heads 4 p + jj (zero past G), 4 dims per
     // step in the order the code words unpack to, hi + lo bf16 parts
@@ -183,57 +195,50 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
     }
 
     const uint32_t nib_mask = vconst(0x000F000Fu), nib_bias = vconst(0x43004300u);
-    float m[G], lp[NP], o[G][DPL], corr[G];
+    const u32x2_t b128 = {0x43004300u, 0x43004300u};   // bf16 128 in every row and column
+    float m[G], lp[NP], offz[NP], mq[NP];   // mq[p]: m of head 4 p + qb (per lane)
+    // acc[p][i][r]: head 4 p + r, dim 32 qb + 8 jj + i, summed over this lane's token quads
+    f32x4_t acc[NP][8], off[NP];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g] = -FLT_MAX;
-        corr[g] = 0.0f;
+    for (int g = 0; g < G; ++g) m[g] = -FLT_MAX;
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) o[g][d] = 0.0f;
+    for (int p = 0; p < NP; ++p) {
+        lp[p] = 0.0f;
+        offz[p] = 0.0f;
+        mq[p] = -FLT_MAX;
+        off[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[p][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int p = 0; p < NP; ++p) lp[p] = 0.0f;
 
-    // ---- one group's loads.  Rows past the wave's range are clamped to its
-    // last token (valid data, masked later).
+    // ---- one group's loads.  Rows past the valid length (inside the same
+    // page) are read as they are: their scores become -inf, and their
+    // probabilities enter the P.V operands through multiplications that give
+    // 0 for a 0 operand whatever the other one holds.
     struct Stage {
         u32x4_t kc;                   // Q.K: the 32 codes of block qb of token tok
         uint32_t kp;                  // Q.K: (scale, zero) of that block
-        uint32_t vc[ROUNDS][CW];      // P.V: code words of this lane's dims
-        uint32_t vp[ROUNDS];          // P.V: (scale, zero) of their block
-    };
-    auto row_base = [&](int ts, int page) -> int64_t {
-        return (int64_t(page) * a.Hkv + kvh) * a.bs + (ts & (a.bs - 1));
+        uint32_t vc[4];               // P.V: code word 4 qb + jj of rows 4 qtg + k
+        uint32_t vp[4];               // P.V: (scale, zero) of block qb of those rows
     };
     auto stage_load = [&](int ts, int page) -> Stage {
         Stage st;
-        const int64_t rb = row_base(ts, page);
-        const int last = wend - 1 - ts;
-        const int64_t rk = rb + min(tok, last);
+        const int64_t rb = (int64_t(page) * a.Hkv + kvh) * a.bs + (ts & (a.bs - 1));
+        const int64_t rk = rb + tok;
         st.kc = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.kc + rk * 64 + 16 * qb));
         st.kp = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.kp + rk * 8 + 2 * qb));
+        const int64_t rv = rb + 4 * qtg;
+        const uint8_t* vsrc = a.vc + rv * 64 + 4 * (4 * qb + jj);
+        const uint16_t* psrc = a.vp + rv * 8 + 2 * qb;
 #pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-            const int64_t rv = rb + min(tl + TPR * rd, last);
-            const uint8_t* src = a.vc + rv * 64 + CB * dc;
-            if constexpr (CW == 4) {
-                const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) st.vc[rd][i] = v[i];
-            } else if constexpr (CW == 2) {
-                const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src));
-                st.vc[rd][0] = v[0];
-                st.vc[rd][1] = v[1];
-            } else {
-                st.vc[rd][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
-            }
-            st.vp[rd] = __builtin_nontemporal_load(
-                reinterpret_cast<const uint32_t*>(a.vp + rv * 8 + 2 * ((DPL * dc) / 32)));
+        for (int k = 0; k < 4; ++k) {
+            st.vc[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vsrc + 64 * k));
+            st.vp[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(psrc + 8 * k));
         }
         return st;
     };
 
-    auto compute = [&](const Stage& st, int ts) {
+    auto compute = [&](const Stage& st, int ts, auto buf) {
         // block-qb partial products of token tok for heads 4 p + r (hi and lo
         // chains accumulate separately), eight steps of four dims
         f32x4_t dh[NP], dl[NP];
@@ -273,56 +278,76 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
         for (int p = 0; p < NP; ++p) {
             float mx = fmaxf(s[p], dpp<0xB1>(s[p]));   // quad_perm [1,0,3,2]
             mx = fmaxf(mx, dpp<0x4E>(mx));              // quad_perm [2,3,0,1]
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_xor16(mx);
+            mx = max_xor32(mx);
 #pragma unroll
             for (int hh = 0; hh < HP; ++hh) {
                 const int g = 4 * p + hh;
                 const float mg = readlane_f(mx, 4 * hh);
                 if (mg > m[g] + kLazy4) {
                     const float cf = exp2_fast(m[g] - mg);
-                    corr[g] *= cf;
 #pragma unroll
-                    for (int d = 0; d < DPL; ++d) o[g][d] *= cf;
-                    if (qb == hh) lp[p] *= cf;
+                    for (int i = 0; i < 8; ++i) acc[p][i][hh] *= cf;
+                    off[p][hh] *= cf;
+                    if (jj == hh) offz[p] *= cf;
+                    if (qb == hh) {
+                        lp[p] *= cf;
+                        mq[p] = mg;
+                    }
                     m[g] = mg;
                 }
             }
         }
-        // probabilities to LDS for the P.V lanes
+        // probabilities to LDS, [head][token]
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            float mrow = m[4 * p];
-#pragma unroll
-            for (int hh = 1; hh < HP; ++hh) mrow = qb == hh ? m[4 * p + hh] : mrow;
-            const float pr = exp2_fast(s[p] - mrow);
+            const float pr = exp2_fast(s[p] - mq[p]);
             lp[p] += pr;
-            if (4 * p + qb < G) s_p[wave][tok][4 * p + qb] = pr;
+            if (4 * p + qb < G) s_p[wave][buf][4 * p + qb][tok] = pr;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // P.V
+        // P.V.  B operands: for byte m of the word, the low nibbles (dim
+        // 2 m) and the high nibbles (dim 2 m + 1) of rows (0, 1) and (2, 3),
+        // each as bf16 128 + c
+        u32x2_t vb[8];
 #pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-            const int tt = tl + TPR * rd;
-            float p[G];
+        for (int mb = 0; mb < 4; ++mb) {
+            const uint32_t sel = uint32_t(mb) | 0x0C00u | (uint32_t(4 + mb) << 16) | 0x0C000000u;
+            const uint32_t x01 = __builtin_amdgcn_perm(st.vc[1], st.vc[0], sel);
+            const uint32_t x23 = __builtin_amdgcn_perm(st.vc[3], st.vc[2], sel);
+            vb[2 * mb] = u32x2_t{(x01 & nib_mask) | nib_bias, (x23 & nib_mask) | nib_bias};
+            vb[2 * mb + 1] = u32x2_t{((x01 >> 4) & nib_mask) | nib_bias, ((x23 >> 4) & nib_mask) | nib_bias};
+        }
 #pragma unroll
-            for (int g = 0; g < G; ++g) p[g] = s_p[wave][tt][g];
-            float cv[DPL];
-            unpack_codes<CB>(st.vc[rd], cv);
-            const float vs = h2f(st.vp[rd] & 0xFFFFu), vz = h2f(st.vp[rd] >> 16);
+        for (int p = 0; p < NP; ++p) {
+            // A operand: x = p * scale of block qb for head 4 p + jj and rows
+            // 4 qtg + k (0 where p is 0), as a truncated bf16 high part plus a
+            // rounded low part
+            const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(&s_p[wave][buf][4 * p + jj][4 * qtg]);
+            float x[4], xl[4];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float w = p[g] * vs;
-                corr[g] = fmaf(w, vz, corr[g]);
-#pragma unroll
-                for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(w, cv[d], o[g][d]);
+            for (int k = 0; k < 4; ++k) {
+                x[k] = mul_legacy(pr[k], h2f(st.vp[k] & 0xFFFFu));
+                offz[p] += mul_legacy(x[k], h2f(st.vp[k] >> 16));
+                xl[k] = x[k] - __uint_as_float(__float_as_uint(x[k]) & 0xFFFF0000u);
             }
+            const u32x2_t ah = {__builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u),
+                                __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u)};
+            const u32x2_t al = {__builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(xl[0]),
+                                                                     static_cast<__bf16>(xl[1])}),
+                                __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(xl[2]),
+                                                                     static_cast<__bf16>(xl[3])})};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[p][i] = mfma4(ah, vb[i], acc[p][i]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[p][i] = mfma4(al, vb[i], acc[p][i]);
+            off[p] = mfma4(ah, b128, off[p]);
+            off[p] = mfma4(al, b128, off[p]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // no barrier here: the next group writes the other buffer, and the
+        // one after it comes after that group's barrier
     };
 
     // Groups in pairs with two register stages (no copies between them, so a
@@ -343,41 +368,49 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
         pgB = page_of(3);
         __builtin_amdgcn_sched_barrier(0);
         for (int i = 0; i < ng; i += 2) {
-            compute(A, wbeg + i * kGroup);
+            compute(A, wbeg + i * kGroup, std::integral_constant<int, 0>());
             A = stage_load(gts(i + 2), pgA);
             pgA = page_of(i + 4);
-            compute(B, wbeg + (i + 1) * kGroup);
+            compute(B, wbeg + (i + 1) * kGroup, std::integral_constant<int, 1>());
             B = stage_load(gts(i + 3), pgB);
             pgB = page_of(i + 5);
         }
     }
 
-    // ---- finish the wave: zero-point term, sum over the token lanes, row sums of p
+    // ---- finish the wave: sums over the token quads (lanes 16 apart), the
+    // 128 offset and the zero-point term, row sums of p
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int p = 0; p < NP; ++p) {
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) o[g][d] -= corr[g];
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1)
+            for (int rr = 0; rr < 4; ++rr) acc[p][i][rr] = sum_xor32(sum_xor16(acc[p][i][rr]));
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) o[g][d] += __shfl_xor(o[g][d], off);
+        for (int rr = 0; rr < 4; ++rr) off[p][rr] = sum_xor32(sum_xor16(off[p][rr]));
+        offz[p] = sum_xor32(sum_xor16(offz[p]));
+    }
     float l[G];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         float rs = lp[p] + dpp<0xB1>(lp[p]);
         rs += dpp<0x4E>(rs);
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);
+        rs = sum_xor32(sum_xor16(rs));
 #pragma unroll
         for (int hh = 0; hh < HP; ++hh) l[4 * p + hh] = readlane_f(rs, 4 * hh);
     }
-    if (tl == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+    for (int p = 0; p < NP; ++p) {
+        // zero-point sums of heads 4 p + rr for block qb: lane jj of the quad holds head jj
+        const float z0 = dpp<0x00>(offz[p]), z1 = dpp<0x55>(offz[p]);
+        const float z2 = dpp<0xAA>(offz[p]), z3 = dpp<0xFF>(offz[p]);
+        const float zr[4] = {z0, z1, z2, z3};
+        if (qtg == 0) {
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) s_o[wave][g][DPL * dc + d] = o[g][d];
+            for (int rr = 0; rr < HP; ++rr)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    s_o[wave][4 * p + rr][32 * qb + 8 * jj + i] = acc[p][i][rr] - off[p][rr] - zr[rr];
+        }
     }
     if (lane == 0) {
 #pragma unroll

@@ -326,7 +326,6 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int grp = lane >> 3;  // token within an 8-token slab
     const int j = lane & 7;     // chunk of each half row
 
     const int work = blockIdx.x;
@@ -432,7 +431,6 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
         u.vf = fmt_of(dd, true);
         return u;
     };
-    auto narrow = [](const Sub& u) { return u.kf.nb <= 8 && u.vf.nb <= 8; };
     const int64_t kvoff = int64_t(kvh) * slot_bytes;
     // Rows of a sub-step into a half buffer w[4]: dense rows take all four
     // vectors (row 0 halves, row 1 halves); narrow rows of slot s take w[2s]

@@ -337,10 +337,12 @@ def test_int4_paged_decode_matches_oracle(G, bs):
     lib_pool = pkv.Pool(NB, bs, B, maxb, order)
     table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
     lib_pool.reserve(range(B), lengths.tolist(), table)
-    kc = np.zeros((NB, Hkv, bs, D // 2), np.uint8)
-    vc = np.zeros_like(kc)
-    kp = np.zeros((NB, Hkv, bs, D // 32, 2), np.uint16)
-    vp = np.zeros_like(kp)
+    # slots no row is written to hold arbitrary codes and NaN parameters: the
+    # tail of a sequence's last page must not reach the output
+    kc = synth.rng(750, 9).integers(0, 256, size=(NB, Hkv, bs, D // 2), dtype=np.uint8)
+    vc = synth.rng(750, 10).integers(0, 256, size=(NB, Hkv, bs, D // 2), dtype=np.uint8)
+    kp = np.full((NB, Hkv, bs, D // 32, 2), 0x7E00, np.uint16)
+    vp = np.full_like(kp, 0x7E00)
     k_log, v_log = [], []
     for b in range(B):
         L = int(lengths[b])
