@@ -52,6 +52,7 @@ constexpr int kWaves4 = 4;
 constexpr int kD4 = 128;
 constexpr int kGroup = 16;       // tokens per Q.K step
 constexpr float kLazy4 = 8.0f;
+constexpr int kStages = 2;      // groups in flight per wave (register stages)
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -78,12 +79,11 @@ __device__ __forceinline__ uint32_t vconst(uint32_t c) {
     return r;
 }
 
-// x * y with 0 * anything = 0 (v_mul_legacy_f32), so that a zero
-// probability cancels an arbitrary scale read from an unwritten row
-__device__ __forceinline__ float mul_legacy(float x, float y) {
-    float r;
-    asm("v_mul_legacy_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
-    return r;
+// DPP move without an old value (every lane of the patterns used here reads
+// a lane of its own row), so that it can fold into the instruction using it
+template <int CTRL>
+__device__ __forceinline__ float dppm(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float readlane_f(float x, int lane) {
@@ -110,17 +110,27 @@ __device__ __forceinline__ float sum_xor16(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A wave-uniform 32-bit load through the scalar unit (constant address
+// space: an s_load, counted apart from the vector loads in flight)
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p));
+}
+
 template <int G>
 __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4DecodeArgs a) {
     constexpr int HP = G < 4 ? G : 4;           // heads per pass (rows of the 4x4 blocks)
     constexpr int NP = (G + 3) / 4;             // passes
 
-    __shared__ float s_p[kWaves4][2][4 * NP][kGroup];   // probabilities [buffer][head][token]; rows >= G stay 0
+    __shared__ float s_p[kWaves4][kStages][4 * NP][kGroup];   // probabilities [stage][head][token]; rows >= G stay 0
     __shared__ float s_o[kWaves4][G][kD4];
     __shared__ float s_ml[kWaves4][G][2];
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    // work-item and workgroup ids straight from the hardware registers: this
+    // file is built without IEEE mode, and the device library's id functions
+    // (built with it) would not be inlined, leaving the workgroup id in a VGPR
+    const int tid = static_cast<int>(__builtin_amdgcn_workitem_id_x());
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     // 16 blocks b = 4 tg + qb of 4 lanes.  Q.K: lane 16 tg + 4 qb + jj holds
     // token 4 tg + jj of the group, 32-dim block qb (B operand and result), and
     // head row jj of block qb (A operand).  P.V: the same lane holds code word
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
     const int jj = lane & 3;
     const int tok = 4 * qtg + jj;
 
-    const int work = blockIdx.x;
+    const int work = static_cast<int>(__builtin_amdgcn_workgroup_id_x());
     const int kvh = work % a.Hkv;
     const int r = work / a.Hkv;
     const int b = find_row(a.split_begin, a.rows, r);
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
     const int32_t* __restrict__ pt = a.page_table + int64_t(b) * a.maxb;
 
     if constexpr (G < 4) {
-        for (int e = lane; e < 2 * (4 - G) * kGroup; e += 64)
+        for (int e = lane; e < kStages * (4 - G) * kGroup; e += 64)
             s_p[wave][e / ((4 - G) * kGroup)][G + (e / kGroup) % (4 - G)][e % kGroup] = 0.0f;
     }
 
@@ -212,33 +222,42 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
     }
 
     // ---- one group's loads.  Rows past the valid length (inside the same
-    // page) are read as they are: their scores become -inf, and their
-    // probabilities enter the P.V operands through multiplications that give
-    // 0 for a 0 operand whatever the other one holds.
+    // page) are read as they are: their scores become -inf, and their V
+    // parameters are replaced by 0 before use.
     struct Stage {
         u32x4_t kc;                   // Q.K: the 32 codes of block qb of token tok
         uint32_t kp;                  // Q.K: (scale, zero) of that block
         uint32_t vc[4];               // P.V: code word 4 qb + jj of rows 4 qtg + k
         uint32_t vp[4];               // P.V: (scale, zero) of block qb of those rows
     };
+    // Per-lane byte offsets from a group's first row (the row base is
+    // wave-uniform, so each load is a scalar base plus a 32-bit lane offset)
+    const uint32_t o_kc = uint32_t(tok) * 64u + 16u * uint32_t(qb);
+    const uint32_t o_kp = uint32_t(tok) * 16u + 4u * uint32_t(qb);
+    const uint32_t o_vc = uint32_t(qtg) * 256u + 4u * uint32_t(4 * qb + jj);
+    const uint32_t o_vp = uint32_t(qtg) * 64u + 4u * uint32_t(qb);
     auto stage_load = [&](int ts, int page) -> Stage {
         Stage st;
         const int64_t rb = (int64_t(page) * a.Hkv + kvh) * a.bs + (ts & (a.bs - 1));
-        const int64_t rk = rb + tok;
-        st.kc = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.kc + rk * 64 + 16 * qb));
-        st.kp = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.kp + rk * 8 + 2 * qb));
-        const int64_t rv = rb + 4 * qtg;
-        const uint8_t* vsrc = a.vc + rv * 64 + 4 * (4 * qb + jj);
-        const uint16_t* psrc = a.vp + rv * 8 + 2 * qb;
+        const uint8_t* kc = a.kc + rb * 64;
+        const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.kp + rb * 8);
+        const uint8_t* vc = a.vc + rb * 64;
+        const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.vp + rb * 8);
+        // lane offsets made opaque here, so that they are not folded into
+        // loop-invariant 64-bit lane pointers (two VGPRs each) outside the loop
+        uint32_t okc = o_kc, okp = o_kp, ovc = o_vc, ovp = o_vp;
+        asm volatile("" : "+v"(okc), "+v"(okp), "+v"(ovc), "+v"(ovp));
+        st.kc = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc + okc));
+        st.kp = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kp + okp));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            st.vc[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vsrc + 64 * k));
-            st.vp[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(psrc + 8 * k));
+            st.vc[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vc + ovc + 64 * k));
+            st.vp[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + ovp + 16 * k));
         }
         return st;
     };
 
-    auto compute = [&](const Stage& st, int ts, auto buf) {
+    auto compute = [&](const Stage& st, int ts, int buf) {
         // block-qb partial products of token tok for heads 4 p + r (hi and lo
         // chains accumulate separately), eight steps of four dims
         f32x4_t dh[NP], dl[NP];
@@ -266,20 +285,25 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float x = sc * fmaf(-zz, qs[p][r], dh[p][r] + dl[p][r]);
-                x += dpp<0x124>(x);   // row_ror:4
-                x += dpp<0x128>(x);   // row_ror:8
+                x += dppm<0x124>(x);   // row_ror:4
+                x += dppm<0x128>(x);   // row_ror:8
                 tot[r] = x;
             }
-            const float mine = qb == 0 ? tot[0] : qb == 1 ? tot[1] : qb == 2 ? tot[2] : tot[3];
+            // all four totals exist before the lane picks one (a select, not a branch)
+            asm volatile("" : "+v"(tot[0]), "+v"(tot[1]), "+v"(tot[2]), "+v"(tot[3]));
+            const bool b0 = (lane & 4) != 0, b1 = (lane & 8) != 0;   // the bits of qb
+            const float mine = b1 ? (b0 ? tot[3] : tot[2]) : (b0 ? tot[1] : tot[0]);
             s[p] = tok_live && 4 * p + qb < G ? mine * a.scale_log2 : -INFINITY;
         }
-        // group maxima per head (lanes with the same qb), wave-uniform; lazy rescale
+        // group maxima per head (lanes with the same qb), wave-uniform; lazy
+        // rescale, checked for all heads at once
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            float mx = fmaxf(s[p], dpp<0xB1>(s[p]));   // quad_perm [1,0,3,2]
-            mx = fmaxf(mx, dpp<0x4E>(mx));              // quad_perm [2,3,0,1]
+            float mx = fmaxf(s[p], dppm<0xB1>(s[p]));   // quad_perm [1,0,3,2]
+            mx = fmaxf(mx, dppm<0x4E>(mx));              // quad_perm [2,3,0,1]
             mx = max_xor16(mx);
             mx = max_xor32(mx);
+            if (__builtin_amdgcn_ballot_w64(mx > mq[p] + kLazy4) == 0) continue;
 #pragma unroll
             for (int hh = 0; hh < HP; ++hh) {
                 const int g = 4 * p + hh;
@@ -320,17 +344,24 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
             vb[2 * mb] = u32x2_t{(x01 & nib_mask) | nib_bias, (x23 & nib_mask) | nib_bias};
             vb[2 * mb + 1] = u32x2_t{((x01 >> 4) & nib_mask) | nib_bias, ((x23 >> 4) & nib_mask) | nib_bias};
         }
+        // (scale, zero) of rows past the valid length read as 0, so that an
+        // arbitrary unwritten value cannot turn a zero probability into NaN
+        uint32_t vp[4] = {st.vp[0], st.vp[1], st.vp[2], st.vp[3]};
+        if (ts + kGroup > L) {
+            const int last = L - 1 - ts - 4 * qtg;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vp[k] = k > last ? 0u : vp[k];
+        }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             // A operand: x = p * scale of block qb for head 4 p + jj and rows
-            // 4 qtg + k (0 where p is 0), as a truncated bf16 high part plus a
-            // rounded low part
+            // 4 qtg + k, as a truncated bf16 high part plus a rounded low part
             const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(&s_p[wave][buf][4 * p + jj][4 * qtg]);
             float x[4], xl[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                x[k] = mul_legacy(pr[k], h2f(st.vp[k] & 0xFFFFu));
-                offz[p] += mul_legacy(x[k], h2f(st.vp[k] >> 16));
+                x[k] = pr[k] * h2f(vp[k] & 0xFFFFu);
+                offz[p] = fmaf(x[k], h2f(vp[k] >> 16), offz[p]);
                 xl[k] = x[k] - __uint_as_float(__float_as_uint(x[k]) & 0xFFFF0000u);
             }
             const u32x2_t ah = {__builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u),
@@ -346,34 +377,40 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
             off[p] = mfma4(ah, b128, off[p]);
             off[p] = mfma4(al, b128, off[p]);
         }
-        // no barrier here: the next group writes the other buffer, and the
-        // one after it comes after that group's barrier
+        // no barrier here: the next group writes another buffer, and the
+        // next writer of this one comes after that group's barrier
     };
 
-    // Groups in pairs with two register stages (no copies between them, so a
-    // wait is only for the stage about to be used); page ids one pair ahead.
-    // Loads past the range re-read its last group; an odd group count ends
-    // with one fully masked group.
+    // kStages register stages used in turn (no copies between them, so a
+    // wait is only for the stage about to be used); page ids one round ahead.
+    // Loads past the range re-read its last group; the last round ends with
+    // up to kStages - 1 fully masked groups.
     if (wbeg < wend) {
         const int ng = (wend - wbeg + kGroup - 1) / kGroup;
         auto gts = [&](int i) { return wbeg + min(i, ng - 1) * kGroup; };
-        auto page_of = [&](int i) { return pt[gts(i) >> a.log2bs]; };
-        int pgA = page_of(0), pgB = page_of(1);
+        auto page_of = [&](int i) { return load_uniform(pt + (gts(i) >> a.log2bs)); };
+        Stage S[kStages];
+        int pg[kStages];
+#pragma unroll
+        for (int u = 0; u < kStages; ++u) pg[u] = page_of(u);
+#pragma unroll
+        for (int u = 0; u < kStages; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+            S[u] = stage_load(gts(u), pg[u]);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        Stage A = stage_load(gts(0), pgA);
+#pragma unroll
+        for (int u = 0; u < kStages; ++u) pg[u] = page_of(kStages + u);
         __builtin_amdgcn_sched_barrier(0);
-        Stage B = stage_load(gts(1), pgB);
-        __builtin_amdgcn_sched_barrier(0);
-        pgA = page_of(2);
-        pgB = page_of(3);
-        __builtin_amdgcn_sched_barrier(0);
-        for (int i = 0; i < ng; i += 2) {
-            compute(A, wbeg + i * kGroup, std::integral_constant<int, 0>());
-            A = stage_load(gts(i + 2), pgA);
-            pgA = page_of(i + 4);
-            compute(B, wbeg + (i + 1) * kGroup, std::integral_constant<int, 1>());
-            B = stage_load(gts(i + 3), pgB);
-            pgB = page_of(i + 5);
+        for (int i = 0; i < ng; i += kStages) {
+#pragma unroll
+            for (int u = 0; u < kStages; ++u) {
+                compute(S[u], wbeg + (i + u) * kGroup, u);
+                __builtin_amdgcn_sched_barrier(0);
+                S[u] = stage_load(gts(i + u + kStages), pg[u]);
+                pg[u] = page_of(i + u + 2 * kStages);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
@@ -421,7 +458,7 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
     }
     __syncthreads();
 
-    for (int e = threadIdx.x; e < G * kD4; e += 256) {
+    for (int e = tid; e < G * kD4; e += 256) {
         const int g = e / kD4;
         const int d = e % kD4;
         float mn = -FLT_MAX;
