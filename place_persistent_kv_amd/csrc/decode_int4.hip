@@ -117,11 +117,15 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
 }
 
 template <int G>
-__global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4DecodeArgs a) {
+__global__ __launch_bounds__(256, (G <= 4 ? 4 : 2)) void decode_int4_kernel(Int4DecodeArgs a) {
     constexpr int HP = G < 4 ? G : 4;           // heads per pass (rows of the 4x4 blocks)
     constexpr int NP = (G + 3) / 4;             // passes
 
     __shared__ float s_p[kWaves4][kStages][4 * NP][kGroup];   // probabilities [stage][head][token]; rows >= G stay 0
+    // a group's V codes (row r at dword 16 (r + r / 4): the pad keeps the four
+    // rows one P.V read spans in different banks) and V parameters
+    __shared__ __align__(16) uint32_t s_vc[kWaves4][kStages][16 * 20];
+    __shared__ uint32_t s_vpar[kWaves4][kStages][64];
     __shared__ float s_o[kWaves4][G][kD4];
     __shared__ float s_ml[kWaves4][G][2];
 
@@ -164,6 +168,10 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
     // ---- query operands: A rows = heads 4 p + jj (zero past G), 4 dims per
     // step in the order the code words unpack to, hi + lo bf16 parts
     // (step s: dims 8 (s / 2) + {0, 4, 1, 5} for even s, {2, 6, 3, 7} for odd s)
+    // The query operands live in LDS (one copy per workgroup, read every
+    // group) rather than in 32 VGPRs per pass: the registers they free allow
+    // four waves per SIMD.
+    __shared__ u32x4_t s_qa[NP][8][16];   // [pass][step][4 qb + jj]: hi.xy, lo.xy
     u32x2_t qa_hi[NP][8], qa_lo[NP][8];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -187,6 +195,13 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
             qa_hi[p][st] = u32x2_t{hw[0], hw[1]};
             qa_lo[p][st] = u32x2_t{lw[0], lw[1]};
         }
+    }
+    if (wave == 0 && qtg == 0) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int st = 0; st < 8; ++st)
+                s_qa[p][st][4 * qb + jj] = u32x4_t{qa_hi[p][st].x, qa_hi[p][st].y, qa_lo[p][st].x, qa_lo[p][st].y};
     }
     // qs: sum of q over block qb for the heads 4 p + r of this lane's results
     // (the operands times ones, accumulated over the eight steps)
@@ -227,15 +242,15 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
     struct Stage {
         u32x4_t kc;                   // Q.K: the 32 codes of block qb of token tok
         uint32_t kp;                  // Q.K: (scale, zero) of that block
-        uint32_t vc[4];               // P.V: code word 4 qb + jj of rows 4 qtg + k
-        uint32_t vp[4];               // P.V: (scale, zero) of block qb of those rows
+        u32x4_t vc;                   // V codes: row lane / 4, dims 32 (lane % 4) ..
+        uint32_t vp;                  // V (scale, zero): row lane / 4, block lane % 4
     };
     // Per-lane byte offsets from a group's first row (the row base is
     // wave-uniform, so each load is a scalar base plus a 32-bit lane offset)
     const uint32_t o_kc = uint32_t(tok) * 64u + 16u * uint32_t(qb);
     const uint32_t o_kp = uint32_t(tok) * 16u + 4u * uint32_t(qb);
-    const uint32_t o_vc = uint32_t(qtg) * 256u + 4u * uint32_t(4 * qb + jj);
-    const uint32_t o_vp = uint32_t(qtg) * 64u + 4u * uint32_t(qb);
+    const uint32_t o_vc = uint32_t(lane) * 16u;
+    const uint32_t o_vp = uint32_t(lane) * 4u;
     auto stage_load = [&](int ts, int page) -> Stage {
         Stage st;
         const int64_t rb = (int64_t(page) * a.Hkv + kvh) * a.bs + (ts & (a.bs - 1));
@@ -249,13 +264,15 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
         asm volatile("" : "+v"(okc), "+v"(okp), "+v"(ovc), "+v"(ovp));
         st.kc = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc + okc));
         st.kp = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kp + okp));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            st.vc[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vc + ovc + 64 * k));
-            st.vp[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + ovp + 16 * k));
-        }
+        st.vc = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc + ovc));
+        st.vp = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + ovp));
         return st;
     };
+    // LDS word offsets: this lane's V code store, and the P.V reads (code word
+    // 4 qb + jj and block-qb parameters of rows 4 qtg + k)
+    const int w_vc = 16 * ((lane >> 2) + (lane >> 4)) + 4 * (lane & 3);
+    const int r_vc = 16 * (4 * qtg + qtg) + 4 * qb + jj;   // + 16 k for row 4 qtg + k
+    const int r_vp = 16 * qtg + qb;                        // + 4 k
 
     auto compute = [&](const Stage& st, int ts, int buf) {
         // block-qb partial products of token tok for heads 4 p + r (hi and lo
@@ -263,16 +280,22 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
         f32x4_t dh[NP], dl[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) dh[p] = dl[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        int qi = 4 * qb + jj;
+        asm volatile("" : "+v"(qi));   // re-read every group, not hoisted into registers
 #pragma unroll
         for (int stp = 0; stp < 8; ++stp) {
             const uint32_t w = st.kc[stp >> 1] >> (8 * (stp & 1));
             const u32x2_t kb = {(w & nib_mask) | nib_bias, ((w >> 4) & nib_mask) | nib_bias};
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                dh[p] = mfma4(qa_hi[p][stp], kb, dh[p]);
-                dl[p] = mfma4(qa_lo[p][stp], kb, dl[p]);
+                const u32x4_t qv = s_qa[p][stp][qi];
+                dh[p] = mfma4(u32x2_t{qv.x, qv.y}, kb, dh[p]);
+                dl[p] = mfma4(u32x2_t{qv.z, qv.w}, kb, dl[p]);
             }
         }
+        // the V tile to LDS, in the layout the P.V reads take it
+        *reinterpret_cast<u32x4_t*>(&s_vc[wave][buf][w_vc]) = st.vc;
+        s_vpar[wave][buf][lane] = st.vp;
         const float sc = h2f(st.kp & 0xFFFFu);
         const float zz = 128.0f + h2f(st.kp >> 16);
         const bool tok_live = ts + tok < wend && ts + tok >= vis0;
@@ -335,18 +358,23 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
         // P.V.  B operands: for byte m of the word, the low nibbles (dim
         // 2 m) and the high nibbles (dim 2 m + 1) of rows (0, 1) and (2, 3),
         // each as bf16 128 + c
+        uint32_t vw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vw[k] = s_vc[wave][buf][r_vc + 16 * k];
         u32x2_t vb[8];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             const uint32_t sel = uint32_t(mb) | 0x0C00u | (uint32_t(4 + mb) << 16) | 0x0C000000u;
-            const uint32_t x01 = __builtin_amdgcn_perm(st.vc[1], st.vc[0], sel);
-            const uint32_t x23 = __builtin_amdgcn_perm(st.vc[3], st.vc[2], sel);
+            const uint32_t x01 = __builtin_amdgcn_perm(vw[1], vw[0], sel);
+            const uint32_t x23 = __builtin_amdgcn_perm(vw[3], vw[2], sel);
             vb[2 * mb] = u32x2_t{(x01 & nib_mask) | nib_bias, (x23 & nib_mask) | nib_bias};
             vb[2 * mb + 1] = u32x2_t{((x01 >> 4) & nib_mask) | nib_bias, ((x23 >> 4) & nib_mask) | nib_bias};
         }
         // (scale, zero) of rows past the valid length read as 0, so that an
         // arbitrary unwritten value cannot turn a zero probability into NaN
-        uint32_t vp[4] = {st.vp[0], st.vp[1], st.vp[2], st.vp[3]};
+        uint32_t vp[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vp[k] = s_vpar[wave][buf][r_vp + 4 * k];
         if (ts + kGroup > L) {
             const int last = L - 1 - ts - 4 * qtg;
 #pragma unroll
@@ -380,6 +408,8 @@ __global__ __launch_bounds__(256, (G <= 4 ? 3 : 2)) void decode_int4_kernel(Int4
         // no barrier here: the next group writes another buffer, and the
         // next writer of this one comes after that group's barrier
     };
+
+    __syncthreads();   // the query operands in LDS
 
     // kStages register stages used in turn (no copies between them, so a
     // wait is only for the stage about to be used); page ids one round ahead.
