@@ -55,14 +55,16 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedCopyArgs a, i
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// One thread per 32-element block of one written row: 16 bytes of codes
-// (element 2k in the low nibble of byte k) and one (scale, zero point) slot.
+// One thread per 8 elements (one code word) of one written row: 8 codes in
+// one dword, element 2k in the low nibble of byte k; the thread of a block's
+// first word also writes the block's (scale, zero point) slot.  Eight
+// divisions per thread keep the latency of a short call low.
 __global__ __launch_bounds__(kThreads) void paged_int4_kernel(PagedInt4Args a, int64_t total) {
-    const int nblk = a.D / 32;
+    const int nword = a.D / 8;
     for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
          i += int64_t(gridDim.x) * kThreads) {
-        const int32_t blk = static_cast<int32_t>(i % nblk);
-        const int64_t r = i / nblk;                 // source row (b, h, t)
+        const int32_t w = static_cast<int32_t>(i % nword);
+        const int64_t r = i / nword;                // source row (b, h, t)
         const int32_t t = static_cast<int32_t>(r % a.n);
         const int64_t bh = r / a.n;
         const int32_t h = static_cast<int32_t>(bh % a.H);
@@ -71,25 +73,21 @@ __global__ __launch_bounds__(kThreads) void paged_int4_kernel(PagedInt4Args a, i
         const int32_t page = a.page_table[int64_t(a.row0 + b) * a.maxb + p / a.bs];
         const int64_t row = (int64_t(page) * a.H + h) * a.bs + p % a.bs;
 
-        uint32_t packed[4] = {0u, 0u, 0u, 0u};
+        uint32_t packed = 0u;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            const int64_t src_idx = r * a.D + blk * 32 + e;
+        for (int e = 0; e < 8; ++e) {
+            const int64_t src_idx = r * a.D + w * 8 + e;
             const float x = a.src_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.src)[src_idx])
                                        : static_cast<const float*>(a.src)[src_idx];
             // correctly rounded float32 divide, round half to even, saturate
             float c = rintf(x / a.scale) + a.zero_point;
             c = fminf(fmaxf(c, 0.0f), 15.0f);
-            packed[e / 8] |= uint32_t(c) << (4 * (e % 8));
+            packed |= uint32_t(c) << (4 * e);
         }
-        uint4 v;
-        v.x = packed[0];
-        v.y = packed[1];
-        v.z = packed[2];
-        v.w = packed[3];
-        *reinterpret_cast<uint4*>(a.codes + row * (a.D / 2) + blk * 16) = v;
-        *reinterpret_cast<uint32_t*>(a.params + (row * nblk + blk) * 2) =
-            uint32_t(a.scale_bits) | (uint32_t(a.zp_bits) << 16);
+        *reinterpret_cast<uint32_t*>(a.codes + row * (a.D / 2) + w * 4) = packed;
+        if (w % 4 == 0)
+            *reinterpret_cast<uint32_t*>(a.params + (row * (a.D / 32) + w / 4) * 2) =
+                uint32_t(a.scale_bits) | (uint32_t(a.zp_bits) << 16);
     }
 }
 
@@ -150,7 +148,7 @@ hipError_t launch_paged_copy(const PagedCopyArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_paged_int4_append(const PagedInt4Args& a, hipStream_t s) {
-    const int64_t total = int64_t(a.rows) * a.H * a.n * (a.D / 32);
+    const int64_t total = int64_t(a.rows) * a.H * a.n * (a.D / 8);
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL(paged_int4_kernel, grid_for(total), dim3(kThreads), 0, s, a, total);
     return hipGetLastError();

@@ -38,7 +38,13 @@
 // The accumulators stay per token quad and are summed over the quads once,
 // at the end.  The running max of every head is wave-uniform (a reduction
 // over the head's lanes plus v_readlane), so the lazy rescale is a uniform
-// branch.
+// branch, taken only when one ballot finds a head whose maximum rose.
+//
+// Loads: K codes as 16 bytes of one row per lane, K parameters as one dword,
+// V codes and V parameters as contiguous 16 bytes / 4 bytes per lane (the
+// whole group in one instruction each), passed through LDS to the lanes the
+// P.V blocks need them in.  The query operands sit in LDS too, which keeps
+// the kernel at four waves per SIMD; two groups are in flight per wave.
 // The split / merge structure is that of the bf16 fast kernel.
 
 #include "device_common.h"
