@@ -361,68 +361,100 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one workgroup per (row, query head).  The split maxima and sums are
-// reduced across the workgroup in one pass over them; the split weights go to
-// LDS; then thread d sums dim d over the splits with eight loads in flight.
+// Merge: one wave per (row, query head).  The partial outputs of the first
+// kMergeU splits are requested before anything else, so their latency
+// overlaps the pass over the split maxima and sums; the split weights go to
+// LDS; lane l sums dims l, l + 64, ... over the splits.
 // ---------------------------------------------------------------------------
 constexpr int kMergeLdsSplits = 1024;
+constexpr int kMergeU = 8;         // splits per batch of loads
+constexpr int kMergeMaxDPL = 4;    // dims per lane (D <= 256)
 
-__device__ __forceinline__ float block_reduce(float x, bool is_max, float* scratch) {
+__device__ __forceinline__ float wave_reduce(float x, bool is_max) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const float y = __shfl_xor(x, off);
         x = is_max ? fmaxf(x, y) : x + y;
     }
-    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[w] = x;
-    __syncthreads();
-    x = scratch[0];
-    for (int i = 1; i < nw; ++i) x = is_max ? fmaxf(x, scratch[i]) : x + scratch[i];
     return x;
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     __shared__ float s_w[kMergeLdsSplits];
-    __shared__ float s_red[4];
     const int bh = blockIdx.x;
     const int b = bh / a.Hq;
     const int n = a.nsplit[b];
     if (n < a.min_splits) return;
+    const int lane = threadIdx.x;
     const int64_t gbh = int64_t(b) * a.Hq + (bh % a.Hq);
     const float* ml = a.ws_ml + gbh * a.S_max * 2;
     const float* po = a.ws_o + gbh * a.S_max * a.D;
+    const int nd = (a.D + 63) >> 6;
+
+    // first batch of partial outputs, in flight during the weight pass
+    float x[kMergeMaxDPL][kMergeU];
+    const int n0 = min(n, kMergeU);
+#pragma unroll
+    for (int j = 0; j < kMergeMaxDPL; ++j) {
+        const int d = lane + 64 * j;
+#pragma unroll
+        for (int u = 0; u < kMergeU; ++u)
+            x[j][u] = j < nd && d < a.D && u < n0 ? po[int64_t(u) * a.D + d] : 0.0f;
+    }
 
     float mx = -FLT_MAX;
-    for (int s = threadIdx.x; s < n; s += blockDim.x) mx = fmaxf(mx, ml[2 * s]);
-    const float mn = block_reduce(mx, true, s_red);
+    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, ml[2 * s]);
+    const float mn = wave_reduce(mx, true);
     float ls = 0.0f;
-    for (int s = threadIdx.x; s < n; s += blockDim.x) {
+    for (int s = lane; s < n; s += 64) {
         const float w = exp2_fast(ml[2 * s] - mn);
         ls += ml[2 * s + 1] * w;
         if (s < kMergeLdsSplits) s_w[s] = w;
     }
-    ls = block_reduce(ls, false, s_red);   // (its barriers also publish s_w)
+    ls = wave_reduce(ls, false);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    auto weight = [&](int su) { return su < kMergeLdsSplits ? s_w[su] : exp2_fast(ml[2 * su] - mn); };
     const float inv = 1.0f / ls;
-    for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        int s = 0;
-        for (; s + 8 <= n; s += 8) {
-            float x[8];
+
+    float acc[kMergeMaxDPL][kMergeU];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) x[u] = po[int64_t(s + u) * a.D + d];
+    for (int j = 0; j < kMergeMaxDPL; ++j)
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int su = s + u;
-                const float w = su < kMergeLdsSplits ? s_w[su] : exp2_fast(ml[2 * su] - mn);
-                acc[u] = fmaf(x[u], w, acc[u]);
+        for (int u = 0; u < kMergeU; ++u) acc[j][u] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u) {
+        if (u < n0) {
+            const float w = weight(u);
+#pragma unroll
+            for (int j = 0; j < kMergeMaxDPL; ++j) acc[j][u] = x[j][u] * w;
+        }
+    }
+    for (int s = kMergeU; s < n; s += kMergeU) {
+        const int nb = min(kMergeU, n - s);
+#pragma unroll
+        for (int j = 0; j < kMergeMaxDPL; ++j) {
+            const int d = lane + 64 * j;
+#pragma unroll
+            for (int u = 0; u < kMergeU; ++u)
+                x[j][u] = j < nd && d < a.D && u < nb ? po[int64_t(s + u) * a.D + d] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeU; ++u) {
+            if (u < nb) {
+                const float w = weight(s + u);
+#pragma unroll
+                for (int j = 0; j < kMergeMaxDPL; ++j) acc[j][u] = fmaf(x[j][u], w, acc[j][u]);
             }
         }
-        for (; s < n; ++s) {
-            const float w = s < kMergeLdsSplits ? s_w[s] : exp2_fast(ml[2 * s] - mn);
-            acc[0] = fmaf(po[int64_t(s) * a.D + d], w, acc[0]);
-        }
-        const float os = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeMaxDPL; ++j) {
+        const int d = lane + 64 * j;
+        if (j >= nd || d >= a.D) continue;
+        const float os = ((acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3])) +
+                         ((acc[j][4] + acc[j][5]) + (acc[j][6] + acc[j][7]));
         const float y = os * inv;
         const int64_t idx = gbh * a.D + d;
         if (a.out_kind == kKvF32) static_cast<float*>(a.out)[idx] = y;
@@ -479,7 +511,8 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int total_work, hipStream_
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     const int blocks = a.rows * a.Hq;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(a.D <= 128 ? 128 : 256), 0, s, a);
+    if (a.D > 64 * kMergeMaxDPL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
