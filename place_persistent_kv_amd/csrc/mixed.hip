@@ -422,11 +422,17 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
         return f;
     };
     const int nsub = wbeg < wend ? (wend - wbeg + kSlabTokens - 1) / kSlabTokens : 0;
+    // page ids and descriptors are wave-uniform: read through the scalar unit
+    // (constant address space), so that waiting for them never waits for the
+    // K/V rows in flight
     auto sub_of = [&](int i) {
         Sub u;
         u.ts = wbeg + i * kSlabTokens;
-        u.page = pt[u.ts >> a.log2bs];
-        const PageDesc dd = desc[u.page];
+        u.page = *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+            reinterpret_cast<uintptr_t>(pt + (u.ts >> a.log2bs)));
+        const PageDesc dd = __builtin_bit_cast(
+            PageDesc, *reinterpret_cast<const __attribute__((address_space(4))) u32x4_t*>(
+                          reinterpret_cast<uintptr_t>(desc + u.page)));
         u.kf = fmt_of(dd, false);
         u.vf = fmt_of(dd, true);
         return u;
