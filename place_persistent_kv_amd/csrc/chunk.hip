@@ -292,11 +292,13 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
             }
             // O^T += V^T P^T: A[i = dim][k] with the keys of chunk qq taken as
             // 16 qq + 4 hl + 0..3 and 16 qq + 8 + 4 hl + 0..3 (the order of pB)
+            // (key chunk outer, dim block inner: consecutive products go to
+            // different accumulators, none waits for the one before it)
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint16_t* vrow = sVt + (32 * d + col) * kVPad + 32 * half + 4 * hl;
+            for (int qq = 0; qq < 2; ++qq) {
 #pragma unroll
-                for (int qq = 0; qq < 2; ++qq) {
+                for (int d = 0; d < 4; ++d) {
+                    const uint16_t* vrow = sVt + (32 * d + col) * kVPad + 32 * half + 4 * hl;
                     const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(vrow + 16 * qq);
                     const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(vrow + 16 * qq + 8);
                     const u32x4_t vA = u32x4_t{x0.x, x0.y, x1.x, x1.y};
