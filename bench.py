@@ -199,18 +199,21 @@ def run_cpu_baseline(budget_s: float = 12.0):
 # Other rows of the decode path, one JSON line each (python bench.py --workload X)
 # ---------------------------------------------------------------------------
 def _timed(fn, steps, warmup, stream):
-    """Average duration (us) of fn() over `steps` calls, each bracketed by HIP events."""
+    """Average duration (us) of fn() over `steps` back-to-back calls: one pair of
+    HIP events on the launch stream brackets all of them (a pair per call adds
+    the event packets' own latency to every short call), with a device
+    synchronisation before and after."""
     import torch
     for i in range(warmup):
         fn(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e0.record(stream)
     for i in range(steps):
-        evs[i][0].record(stream)
         fn(warmup + i)
-        evs[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3
+    return e0.elapsed_time(e1) / steps * 1e3
 
 
 def _line(metric, value, unit, steps, warmup, us, dtype, config, roofline, cpu=None, **extra):
