@@ -8,10 +8,17 @@ same implementation; the logits are ``[batch, vocab]`` or
 
 Readings (the pages fix only the distribution; listed in the design doc):
 
-* greedy ties go to the lowest index;
-* a draw is the Gumbel-max choice ``argmax_v (y_v - log(-log u_v))`` with
-  ``y_v = fl32(x_v * invT)``, ``invT = fl32(1 / T)``, which has exactly the
-  law ``softmax(x / T)``;
+* greedy is the argmax of the logits as given (DOUBLE logits are compared as
+  float64 values), ties to the lowest index;
+* non-finite values follow ``numpy.argmax``: NaN ranks above every number (the
+  first NaN wins) and a row of -inf values gives index 0, so every row gets an
+  index inside the vocabulary;
+* the temperature ``T`` is a float32 value (the type the library's boundary
+  takes);
+* a draw is the Gumbel-max choice ``argmax_v (y_v - log(-log u_v))``, which
+  has exactly the law ``softmax(x / T)``, with ``y_v = fl32(x_v * invT)``,
+  ``invT = fl32(1 / T)`` for FLOAT / FLOAT16 / BFLOAT16 logits and
+  ``y_v = fl64(x_v * (1 / T))`` in float64 for DOUBLE logits;
 * ``u_v`` is made from output number ``k = b * V + v + 1`` of the SplitMix64
   sequence seeded with ``seed`` (Steele, Lea and Flood, "Fast splittable
   pseudorandom number generators", OOPSLA 2014): ``u = ((h >> 40) | 1) * 2^-24``,
@@ -63,23 +70,46 @@ def last_position(logits: np.ndarray) -> np.ndarray:
     return logits
 
 
+def _values(logits: np.ndarray) -> np.ndarray:
+    """The logits as numbers: float64 arrays (DOUBLE logits) stay float64,
+    anything else is taken as float32 values (FLOAT16 / BFLOAT16 widen
+    exactly)."""
+    x = np.asarray(logits)
+    return x if x.dtype == np.float64 else x.astype(np.float32)
+
+
 def greedy(logits: np.ndarray) -> np.ndarray:
     """Index of the largest logit per row, lowest index on ties.
 
-    ``numpy.argmax`` returns the first (lowest) index among equal maxima.
+    ``numpy.argmax`` returns the first (lowest) index among equal maxima, and
+    the first NaN when a row holds one.
     """
-    x = last_position(logits)
+    x = _values(last_position(logits))
     return np.argmax(x, axis=-1).astype(np.int64)
 
 
+def temperature32(T: float) -> float:
+    """The temperature as the float32 value the boundary receives."""
+    return float(np.float32(T))
+
+
 def inv_temperature(T: float) -> np.float32:
-    return np.float32(1.0 / float(T))
+    """``fl32(1 / T)`` for the float32 temperature ``T``."""
+    return np.float32(1.0 / temperature32(T))
 
 
-def gumbel_scores(logits_f32_row: np.ndarray, T: float, seed: int, b: int) -> np.ndarray:
-    """Perturbed scores ``fl32(x * invT) - log(-log u)`` of one row, float64."""
-    x = np.asarray(logits_f32_row, dtype=np.float32)
-    y = (x * inv_temperature(T)).astype(np.float64)   # one float32 multiply, then exact widening
+def gumbel_scores(logits_row: np.ndarray, T: float, seed: int, b: int) -> np.ndarray:
+    """Perturbed scores ``y - log(-log u)`` of one row, float64.
+
+    ``y = fl32(x * fl32(1 / T))`` (one float32 multiply, then exact widening)
+    for float32 values; ``y = x * (1 / T)`` in float64 for float64 logits.
+    """
+    x = _values(logits_row)
+    with np.errstate(invalid="ignore"):
+        if x.dtype == np.float64:
+            y = x * (1.0 / temperature32(T))
+        else:
+            y = (x * inv_temperature(T)).astype(np.float64)
     u = uniforms(seed, b, x.shape[0])
     return y - np.log(-np.log(u))
 
@@ -87,11 +117,12 @@ def gumbel_scores(logits_f32_row: np.ndarray, T: float, seed: int, b: int) -> np
 def sample(logits: np.ndarray, temperature: float, seed: int) -> np.ndarray:
     """Token id per row: greedy when ``temperature == 0``, else a Gumbel-max draw.
 
-    ``logits`` must already be float32 values (bf16/fp16 inputs widen exactly).
+    ``logits`` holds the values: float64 for DOUBLE logits, float32 for the
+    others (bf16/fp16 inputs widened exactly by the caller).
     """
     if not (temperature >= 0.0):
         raise ValueError("temperature must be >= 0 and not NaN")
-    x = np.asarray(last_position(logits), dtype=np.float32)
+    x = _values(last_position(logits))
     if temperature == 0.0:
         return greedy(x)
     out = np.empty(x.shape[0], dtype=np.int64)
