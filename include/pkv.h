@@ -421,12 +421,15 @@ pkv_status pkv_paged_decode_attention_mixed(const pkv_tensor* q, const pkv_tenso
 
 size_t pkv_sample_workspace_size(int32_t B, int64_t V);
 
-/* logits : [B, V] or [B, S, V], f32, f64, bf16 or f16, finite; f64 logits are
- *          rounded to f32 (nearest even) before the draw.
- * temperature == 0: argmax, lowest index on ties.  temperature > 0: the
- * Gumbel-max draw argmax_v (fl32(x_v * fl32(1/T)) - log(-log u_v)) with
- * u_v = ((h >> 40) | 1) * 2^-24 and h output number b*V + v + 1 of
- * SplitMix64 seeded with `seed`.  Negative or NaN temperature: PKV_E_ARG.
+/* logits : [B, V] or [B, S, V], f32, f64, bf16 or f16.
+ * temperature == 0: argmax, lowest index on ties; f64 logits are compared as
+ * f64 values.  temperature > 0: the Gumbel-max draw argmax_v (y_v -
+ * log(-log u_v)) with y_v = fl32(x_v * fl32(1/T)) (f64 logits: y_v = x_v *
+ * (1/T) in f64), u_v = ((h >> 40) | 1) * 2^-24 and h output number
+ * b*V + v + 1 of SplitMix64 seeded with `seed`.  Non-finite scores follow
+ * numpy's argmax: NaN ranks above every number (the first NaN wins) and an
+ * all -inf row yields index 0, so every id lies in [0, V).  Negative, NaN or
+ * infinite temperature: PKV_E_ARG.
  * out_ids: device int64[B]. */
 pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed,
                       int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream);

@@ -1266,7 +1266,7 @@ size_t pkv_sample_workspace_size(int32_t B, int64_t V) {
     if (B <= 0 || V <= 0) return 0;
     const SamplePlan p = plan_sample(B, V);
     const size_t n = size_t(B) * p.chunks;
-    return ((n * 4 + 255) & ~size_t(255)) + ((n * 4 + 255) & ~size_t(255));
+    return ((n * 8 + 255) & ~size_t(255)) + ((n * 4 + 255) & ~size_t(255));
 }
 
 pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed,
@@ -1300,10 +1300,11 @@ pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed
     a.chunk_len = p.chunk_len;
     a.greedy = temperature == 0.0f;
     a.inv_t = a.greedy ? 0.0f : static_cast<float>(1.0 / static_cast<double>(temperature));
+    a.inv_t64 = a.greedy ? 0.0 : 1.0 / static_cast<double>(temperature);
     a.seed = seed;
     const size_t n = size_t(B) * p.chunks;
-    a.part_val = static_cast<float*>(workspace);
-    a.part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ((n * 4 + 255) & ~size_t(255)));
+    a.part_val = static_cast<double*>(workspace);
+    a.part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ((n * 8 + 255) & ~size_t(255)));
     a.out = out_ids;
     PKV_HIP(launch_sample(a, static_cast<hipStream_t>(stream)), "sample launch");
     return ok();

@@ -251,9 +251,10 @@ struct SampleArgs {
     int32_t chunks;              // vocab chunks per row
     int64_t chunk_len;           // elements per chunk (multiple of 1024)
     int32_t greedy;
-    float inv_t;
+    float inv_t;                 // fl32(1 / T): float32, bf16 and f16 logits
+    double inv_t64;              // 1 / T in float64: float64 logits
     uint64_t seed;
-    float* part_val;             // [B, chunks]
+    double* part_val;            // [B, chunks] best score per chunk (float32 scores widened)
     int32_t* part_idx;           // [B, chunks]
     int64_t* out;                // [B]
 };

@@ -10,14 +10,24 @@
 // k = b * V + v + 1 of SplitMix64 seeded with `seed` (Steele, Lea and Flood,
 // OOPSLA 2014): state = seed + k * 0x9E3779B97F4A7C15, then the SplitMix64
 // finaliser; u = ((h >> 40) | 1) * 2^-24 is exact in float32.  Greedy ties go
-// to the lowest index.  The pass is one read of the logits: each workgroup
-// reduces a vocabulary chunk of one row to (best score, index); a second
-// small kernel reduces the chunks of each row.
+// to the lowest index.  Float64 logits are compared as float64 values (greedy)
+// and scaled in float64 (y = x * (1 / T), T the float32 temperature widened).
+//
+// Non-finite scores follow numpy's argmax: NaN ranks above every number (the
+// first NaN of a row wins), and a row whose scores are all -inf yields its
+// first index, so every row gets an index inside the vocabulary.
+//
+// The pass is one read of the logits: each workgroup reduces a vocabulary
+// chunk of one row to (best score, index); a second small kernel reduces the
+// chunks of each row.  Partial scores are stored as float64 (exact for the
+// float32 scores).
 
 #include "pkv_internal.h"
 
 #include <float.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -31,10 +41,14 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t k) {
     return z ^ (z >> 31);
 }
 
+// Score type: float64 for float64 logits, float32 otherwise.
 template <int KIND>
-__device__ __forceinline__ float logit_at(const void* p, int64_t i) {
+using score_t = typename std::conditional<KIND == kKvF64, double, float>::type;
+
+template <int KIND>
+__device__ __forceinline__ score_t<KIND> logit_at(const void* p, int64_t i) {
     if constexpr (KIND == kKvF32) return static_cast<const float*>(p)[i];
-    else if constexpr (KIND == kKvF64) return static_cast<float>(static_cast<const double*>(p)[i]);   // RNE
+    else if constexpr (KIND == kKvF64) return static_cast<const double*>(p)[i];
     else if constexpr (KIND == kKvBF16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
     else return static_cast<float>(static_cast<const _Float16*>(p)[i]);
 }
@@ -43,24 +57,37 @@ typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
 // element e (a constant) of a 16-byte vector of logits
 template <int KIND>
-__device__ __forceinline__ float logit_of(u32x4v_t w, int e) {
+__device__ __forceinline__ score_t<KIND> logit_of(u32x4v_t w, int e) {
     if constexpr (KIND == kKvF32) return __uint_as_float(w[e]);
     if constexpr (KIND == kKvF64)
-        return static_cast<float>(__builtin_bit_cast(double, (uint64_t(w[2 * e + 1]) << 32) | w[2 * e]));
+        return __builtin_bit_cast(double, (uint64_t(w[2 * e + 1]) << 32) | w[2 * e]);
     const uint32_t h = (e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xFFFFu);
     if constexpr (KIND == kKvBF16) return __uint_as_float(h << 16);
     else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
-// (score, index) order: larger score wins, equal scores -> lower index
-__device__ __forceinline__ bool better(float s, int32_t i, float bs, int32_t bi) {
-    return s > bs || (s == bs && i < bi);
+// Score order: NaN above every number, otherwise numeric.  above(s, b): s
+// ranks strictly above b.
+template <typename T>
+__device__ __forceinline__ bool above(T s, T b) {
+    return !(s <= b) && b == b;
+}
+template <typename T>
+__device__ __forceinline__ bool same_rank(T s, T b) {
+    return s == b || (s != s && b != b);
 }
 
-__device__ __forceinline__ void wave_argmax(float& s, int32_t& i) {
+// (score, index) order: higher-ranked score wins, equal ranks -> lower index
+template <typename T>
+__device__ __forceinline__ bool better(T s, int32_t i, T bs, int32_t bi) {
+    return above(s, bs) || (same_rank(s, bs) && i < bi);
+}
+
+template <typename T>
+__device__ __forceinline__ void wave_argmax(T& s, int32_t& i) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-        const float so = __shfl_xor(s, off);
+        const T so = __shfl_xor(s, off);
         const int32_t io = __shfl_xor(i, off);
         if (better(so, io, s, i)) {
             s = so;
@@ -72,11 +99,10 @@ __device__ __forceinline__ void wave_argmax(float& s, int32_t& i) {
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Gumbel-perturbed score of logit x whose SplitMix64 state (seed + k * gamma)
-// is `state`: y - ln(-ln u) with y = fl32(x * invT).  Only the top 24 bits of
-// the output are used.  The logarithms are the hardware base-2 ones
-// (v_log_f32, about 1 ulp), scaled by ln 2.
-__device__ __forceinline__ float gumbel_score(float x, float inv_t, uint64_t state) {
+// Gumbel term -ln(-ln u) of the SplitMix64 state (seed + k * gamma) `state`.
+// Only the top 24 bits of the output are used.  The logarithms are the
+// hardware base-2 ones (v_log_f32, about 1 ulp), scaled by ln 2.
+__device__ __forceinline__ float gumbel_term(uint64_t state) {
 #pragma clang fp contract(off)
     uint64_t z = state;
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -84,8 +110,20 @@ __device__ __forceinline__ float gumbel_score(float x, float inv_t, uint64_t sta
     const uint32_t top = static_cast<uint32_t>((z ^ (z >> 31)) >> 40);
     const float u = static_cast<float>(top | 1u) * 0x1p-24f;
     const float e = -__builtin_amdgcn_logf(u) * kLn2;        // -ln u, an Exp(1) draw
-    const float y = x * inv_t;                                // rounded product (no contraction)
-    return y - __builtin_amdgcn_logf(e) * kLn2;
+    return -__builtin_amdgcn_logf(e) * kLn2;
+}
+
+// Perturbed score y - ln(-ln u): y = fl32(x * invT) for float32 scores (a
+// rounded product, no contraction), y = fl64(x * invT64) for float64 logits.
+__device__ __forceinline__ float gumbel_score(float x, const SampleArgs& a, uint64_t state) {
+#pragma clang fp contract(off)
+    const float y = x * a.inv_t;
+    return y + gumbel_term(state);
+}
+__device__ __forceinline__ double gumbel_score(double x, const SampleArgs& a, uint64_t state) {
+#pragma clang fp contract(off)
+    const double y = x * a.inv_t64;
+    return y + static_cast<double>(gumbel_term(state));
 }
 
 // One workgroup reduces one vocabulary chunk of one row to (best score,
@@ -94,7 +132,8 @@ __device__ __forceinline__ float gumbel_score(float x, float inv_t, uint64_t sta
 // element.
 template <int KIND, bool GREEDY, bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs a) {
-    __shared__ float s_val[kSampleThreads / 64];
+    using S = score_t<KIND>;
+    __shared__ S s_val[kSampleThreads / 64];
     __shared__ int32_t s_idx[kSampleThreads / 64];
     constexpr int W = KIND == kKvF64 ? 2 : KIND == kKvF32 ? 4 : 8;   // logits per 16-byte vector
     const int b = blockIdx.y;
@@ -102,23 +141,26 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs
     const int64_t beg = int64_t(c) * a.chunk_len;
     const int64_t end = min(a.V, beg + a.chunk_len);
     const void* row = static_cast<const uint8_t*>(a.logits) + b * a.row_stride * (16 / W);
-    float best = -INFINITY;
-    int32_t bidx = INT32_MAX;
+    const int64_t nvec = VEC ? (end - beg) / W : 0;          // whole vectors in the chunk
+    const int64_t tail = beg + nvec * W;                      // first element read singly
+    // A thread visits its logits in increasing index order.  It starts from
+    // (-inf, its first index), so an all -inf run keeps that lowest index and
+    // a later logit wins only by ranking strictly above the best so far.
+    const int64_t first = threadIdx.x < nvec ? beg + int64_t(threadIdx.x) * W
+                        : (tail + threadIdx.x < end ? tail + threadIdx.x : int64_t(INT32_MAX));
+    S best = -INFINITY;
+    int32_t bidx = static_cast<int32_t>(first);
     // state of logit v: seed + (b * V + v + 1) * gamma
     const uint64_t state0 = a.seed + (uint64_t(b) * uint64_t(a.V) + 1ull) * kGamma;
-    // a thread visits its logits in increasing index order, so a strictly
-    // larger score is the only way to win (equal scores keep the lower index)
-    auto consider = [&](float x, int64_t v, uint64_t state) {
-        const float s = GREEDY ? x : gumbel_score(x, a.inv_t, state);
-        if (s > best) {
+    auto consider = [&](S x, int64_t v, uint64_t state) {
+        const S s = GREEDY ? x : gumbel_score(x, a, state);
+        if (above(s, best)) {
             best = s;
             bidx = static_cast<int32_t>(v);
         }
     };
-    int64_t tail = beg;
     if constexpr (VEC) {
         constexpr int U = 4;                                  // vectors in flight per thread
-        const int64_t nvec = (end - beg) / W;                 // whole vectors in the chunk
         const u32x4v_t* vp = reinterpret_cast<const u32x4v_t*>(static_cast<const uint8_t*>(row) + beg * (16 / W));
         int64_t i = threadIdx.x;
         for (; i + (U - 1) * kSampleThreads < nvec; i += U * kSampleThreads) {
@@ -140,7 +182,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs
 #pragma unroll
             for (int e = 0; e < W; ++e) consider(logit_of<KIND>(w0, e), v0 + e, st + uint64_t(e) * kGamma);
         }
-        tail = beg + nvec * W;
     }
     for (int64_t v = tail + threadIdx.x; v < end; v += kSampleThreads)
         consider(logit_at<KIND>(row, v), v, state0 + uint64_t(v) * kGamma);
@@ -158,17 +199,19 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs
                 best = s_val[k];
                 bidx = s_idx[k];
             }
-        a.part_val[int64_t(b) * a.chunks + c] = best;
+        a.part_val[int64_t(b) * a.chunks + c] = static_cast<double>(best);
         a.part_idx[int64_t(b) * a.chunks + c] = bidx;
     }
 }
 
+// Every chunk holds at least one logit, so the reduction of a row ends on an
+// index inside the vocabulary.
 __global__ __launch_bounds__(64) void sample_final_kernel(SampleArgs a) {
     const int b = blockIdx.x;
-    float best = -INFINITY;
+    double best = -INFINITY;
     int32_t bidx = INT32_MAX;
     for (int c = threadIdx.x; c < a.chunks; c += 64) {
-        const float s = a.part_val[int64_t(b) * a.chunks + c];
+        const double s = a.part_val[int64_t(b) * a.chunks + c];
         const int32_t i = a.part_idx[int64_t(b) * a.chunks + c];
         if (better(s, i, best, bidx)) {
             best = s;
