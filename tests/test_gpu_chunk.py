@@ -131,3 +131,56 @@ def test_chunk_capacity_and_page_errors():
     with pytest.raises(pkv.PkvError) as e:
         pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], 2, bs, [5], out, pool=small)
     assert e.value.status == pkv.E_PAGE
+
+
+@pytest.mark.parametrize("W,G,C,bs", [(-1, 2, 300, 16), (-1, 4, 130, 32), (-1, 1, 64, 16), (37, 2, 300, 16),
+                                      (200, 8, 100, 16)])
+def test_planted_key_marks_the_causal_and_window_edges(W, G, C, bs):
+    """Every query carries 4.0 in one dimension and one key per (row, kv head) carries 128.0 there and 0
+    elsewhere, so it outscores every other key by e^40.  A query that sees that key must return its V row
+    exactly; a query that must not see it (the key lies after the query, or before its window) must return
+    bit for bit what it returned before the key was planted.  Keys sit at tile, page and diagonal edges."""
+    require_gpu()
+    B, Hkv, D, d0 = 3, 2, 128, 5
+    Hq = Hkv * G
+    p0 = np.array([0, 37, 200], np.int32)
+    maxb = -(-(int(p0.max()) + C) // bs) + 1
+    d = _setup(970 + G + C + max(W, 0), B, Hq, Hkv, D, bs, p0, C, maxb)
+    d["q"][..., d0] = synth.f32_to_bf16_bits(np.float32(4.0))
+    with pkv.bind_writable(d["kd"]), pkv.bind_writable(d["vd"]):
+        pkv.paged_cache_update(d["lib_pool"], d["kd"], d["table"], bf16_dev(d["new_k"]), p0, C)
+        pkv.paged_cache_update(d["lib_pool"], d["vd"], d["table"], bf16_dev(d["new_v"]), p0, C)
+    q = bf16_dev(d["q"])
+    base = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], maxb, bs, p0, base, pool=d["lib_pool"], left_window=W)
+    base_h = bits_host(base)
+    table = d["ref_pool"].table
+    probe = np.zeros(D, np.float32)
+    probe[d0] = 128.0
+    picks = {}
+    for b in range(B):
+        L = int(p0[b]) + C
+        cands = sorted({x for x in (0, 15, 16, 63, 64, int(p0[b]), int(p0[b]) + 1, int(p0[b]) + 31, int(p0[b]) + 32,
+                                    int(p0[b]) + 63, int(p0[b]) + 64, int(p0[b]) + C // 2, L - 1) if 0 <= x < L})
+        for kvh in range(Hkv):
+            p = cands[(b * Hkv + kvh) * 5 % len(cands)]
+            picks[(b, kvh)] = p
+            d["kd"][int(table[b, p // bs]), kvh, p % bs] = bf16_dev(synth.f32_to_bf16_bits(probe))
+    out = torch.empty_like(base)
+    pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"], left_window=W)
+    got = bits_host(out)
+    vh = bits_host(d["vd"])
+    seen = unseen = 0
+    for (b, kvh), p in picks.items():
+        vrow = vh[int(table[b, p // bs]), kvh, p % bs]
+        for t in range(C):
+            pos = int(p0[b]) + t
+            lo = oattn.visible_begin(pos, W)
+            for h in range(kvh * G, (kvh + 1) * G):
+                if lo <= p <= pos:
+                    assert np.array_equal(got[b, h, t], vrow), (b, h, t, p)
+                    seen += 1
+                else:
+                    assert np.array_equal(got[b, h, t], base_h[b, h, t]), (b, h, t, p)
+                    unseen += 1
+    assert seen and unseen

@@ -32,9 +32,67 @@ def _pages_host(pool_dev, ids):
     return bits_host(pool_dev.index_select(0, idx).contiguous())
 
 
-def _paged_decode_case(spec, seed, rows_to_check, left_window=-1):
-    """Append one token per row at position L-1, attend over L tokens (or the last left_window + 1),
-    check sampled rows."""
+F32_TOL = 1e-5          # float32 outputs: the fp32 bar (bf16 inputs are exact, accumulation is float32)
+
+
+def _bf16_round(x: torch.Tensor) -> np.ndarray:
+    return bits_host(x.to(torch.bfloat16))
+
+
+def _split_edges(L, left_window, tps):
+    """Token positions next to the edges the kernel cuts a row at (splits of tps tokens from the window's
+    64-aligned base, each split's four wave quarters, 16-token pages): the places an off-by-one would hit.
+    Only chooses where probes go; the expected output does not depend on it."""
+    lo = oattn.visible_begin(L - 1, left_window)
+    base = lo // 64 * 64
+    edges = {lo, lo + 1, L - 2, L - 1, base + 15, base + 16}
+    for cut in range(base, L, tps):
+        for q in range(4):
+            e = cut + q * (tps // 4)
+            edges.update({e - 1, e, e + 15, e + 16})
+    return sorted(e for e in edges if lo <= e < L)
+
+
+def _auto_tps(L, Hkv):
+    """Tokens per split of the library's automatic plan (about 1024 workgroups, at least 384 tokens, 64-token
+    quanta); used only to aim probes at split edges."""
+    t = -(-int(np.sum(L)) * Hkv // 1024)
+    return max(384, -(-t // 64) * 64)
+
+
+def _plant_probes(spec, kd, nk, qh, table_host, probe_rows, left_window, tps):
+    """Give one key per (probe row, kv head) a score far above every other key of the row (the query heads of
+    the group all see it), at a position next to a page, split or window edge; with a left window, a key with an
+    even larger score just before the window.  The attention output of those heads must then be that token's
+    V row.  Returns {(b, kvh): (position, outside position or None)}."""
+    G = spec.Hq // spec.Hkv
+    q32 = onum.bf16_to_f64(qh)
+    planted, k = {}, 0
+    for b in probe_rows:
+        L = int(spec.lengths[b])
+        edges = _split_edges(L, left_window, tps)
+        for kvh in range(spec.Hkv):
+            pos = edges[(k * 7) % len(edges)]
+            k += 1
+            dirn = q32[b, kvh * G:(kvh + 1) * G].sum(axis=0)
+            lo = oattn.visible_begin(L - 1, left_window)
+            out_pos = lo - 1 if lo > 0 else None
+            for p, mult in ((pos, 16.0), (out_pos, 32.0)):
+                if p is None:
+                    continue
+                row = synth.f32_to_bf16_bits((dirn * mult).astype(np.float32))
+                if p == L - 1:                                   # the token this step appends
+                    nk[b, kvh, 0] = bf16_dev(row)
+                else:
+                    kd[int(table_host[b, p // spec.bs]), kvh, p % spec.bs] = bf16_dev(row)
+            planted[(b, kvh)] = (pos, out_pos)
+    return planted
+
+
+def _paged_decode_case(spec, seed, check_rows, probe_rows, left_window=-1):
+    """Append one token per row at position L-1 and attend over L tokens (or the last left_window + 1) in the
+    bench's launch configuration.  f32 output: the checked rows against the oracle at the fp32 bar, the probe
+    rows equal to their planted token's V row.  bf16 output (what the bench times): the f32 result rounded."""
     gen = torch.Generator(device=DEV)
     gen.manual_seed(seed)
     B, Hq, Hkv, D, bs, NB, maxb = spec.B, spec.Hq, spec.Hkv, spec.D, spec.bs, spec.NB, spec.maxb
@@ -49,23 +107,32 @@ def _paged_decode_case(spec, seed, rows_to_check, left_window=-1):
     for b in range(B):
         ref_pool.reserve(b, int(L[b]))
     assert np.array_equal(table.cpu().numpy(), ref_pool.table)
+    pt = ref_pool.table
+    qh = bits_host(q)
+    planted = _plant_probes(spec, kd, nk, qh, pt, probe_rows, left_window, _auto_tps(L, Hkv))
     host = {}
-    for b in rows_to_check:
+    for b in check_rows:
         ids = ref_pool.table[b, :spec.pages(b)]
         host[b] = (ids, _pages_host(kd, ids), _pages_host(vd, ids))
-    qh, nkh, nvh = (bits_host(x) for x in (q, nk, nv))
+    nkh, nvh = bits_host(nk), bits_host(nv)
 
-    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
     ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, int(L.max())))
     pos = (L - 1).tolist()
     with pkv.bind_writable(kd), pkv.bind_writable(vd):
         pkv.paged_cache_update(lib_pool, kd, table, nk, pos, 1)
         pkv.paged_cache_update(lib_pool, vd, table, nv, pos, 1)
+    out32 = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    pkv.paged_decode_attention(q, kd, vd, table, maxb, bs, L.tolist(), out32, ws, pool=lib_pool,
+                               left_window=left_window)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
     pkv.paged_decode_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, ws, pool=lib_pool,
                                left_window=left_window)
-    got = onum.bf16_to_f64(bits_host(out))
+    assert np.array_equal(bits_host(out), _bf16_round(out32))       # one rounding of the same float32 result
+    torch.cuda.synchronize()
+    got = out32.double().cpu().numpy()
     G = Hq // Hkv
-    for b in rows_to_check:
+    worst = 0.0
+    for b in check_rows:
         ids, kp, vp = host[b]
         local = np.arange(len(ids), dtype=np.int32)[None]          # the row's pages, renumbered 0..n-1
         ocache.paged_cache_update(kp, local, nkh[b:b + 1], [int(L[b]) - 1], 1, bs)
@@ -76,30 +143,64 @@ def _paged_decode_case(spec, seed, rows_to_check, left_window=-1):
         qb = onum.bf16_to_f64(qh[b])
         lo = oattn.visible_begin(int(L[b]) - 1, left_window)
         ref = np.stack([oattn.attend(qb[h], K[h // G][lo:], V[h // G][lo:], 1 / np.sqrt(D)) for h in range(Hq)])
-        assert rel_err_rows(got[b], ref) <= 2e-2, b
+        err = rel_err_rows(got[b], ref)
+        worst = max(worst, err)
+        assert err <= F32_TOL, (b, err)
+    for (b, kvh), (p, _outside) in planted.items():
+        if p == int(L[b]) - 1:
+            want = onum.bf16_to_f64(nvh[b, kvh, 0])
+        else:
+            want = onum.bf16_to_f64(bits_host(vd[int(pt[b, p // bs]), kvh, p % bs]))
+        for h in range(kvh * G, (kvh + 1) * G):
+            assert rel_err_rows(got[b, h], want) <= F32_TOL, (b, kvh, h, p)
+    print(f"paged decode {spec.name} window {left_window}: {len(check_rows)} rows vs oracle, worst {worst:.2e}; "
+          f"{len(planted)} probes exact")
     return got
+
+
+def _rows_by_rule(L, bs, tps, want=8):
+    """Shortest, longest and median rows, plus rows ending on a page edge, one past it, one short of it, and
+    next to a split edge, up to `want` distinct rows."""
+    order = np.argsort(L, kind="stable")
+    picks = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
+    rules = [lambda x: x % bs == 0, lambda x: x % bs == 1, lambda x: x % bs == bs - 1,
+             lambda x: x % tps in (0, 1, tps - 1), lambda x: x % 64 == 0]
+    for rule in rules:
+        for b in order:
+            if rule(int(L[b])) and int(b) not in picks:
+                picks.append(int(b))
+                break
+    for b in order[::max(1, len(order) // want)]:
+        if len(picks) >= want:
+            break
+        if int(b) not in picks:
+            picks.append(int(b))
+    return sorted(picks[:max(want, len(picks))])
 
 
 def test_paged32k_full_size_step():
     """The headline workload exactly as bench.py runs it: 32 x 32768 tokens, a full 65536-page pool."""
     require_gpu()
     spec = workloads.paged32k()
-    _paged_decode_case(spec, 3, [0, 13, 31])
+    check = [0, 4, 9, 13, 18, 22, 27, 31]
+    _paged_decode_case(spec, 3, check, [b for b in range(spec.B) if b not in check])
 
 
 def test_paged32k_window_full_size():
-    """The windowed bench row: the same pool and rows, left window 4095 (the last 4096 tokens)."""
+    """The windowed bench row: the same pool and rows, left window 4095 (the last 4096 tokens); probes also put
+    a larger score just before the window, which must not be seen."""
     require_gpu()
     spec = workloads.paged32k()
-    _paged_decode_case(spec, 3, [0, 31], left_window=4095)
+    check = [0, 7, 15, 16, 23, 31, 3, 28]
+    _paged_decode_case(spec, 3, sorted(check), [b for b in range(spec.B) if b not in check], left_window=4095)
 
 
 def test_paged_lognormal_full_size():
     require_gpu()
     spec = workloads.paged()
-    order = np.argsort(spec.lengths)
-    rows = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
-    _paged_decode_case(spec, 2, rows)
+    check = _rows_by_rule(spec.lengths, spec.bs, _auto_tps(spec.lengths, spec.Hkv))
+    probes = [b for b in range(spec.B) if b not in check][::2]
+    _paged_decode_case(spec, 2, check, probes)
 
 
 def test_contiguous_full_size_32_steps():
@@ -128,13 +229,17 @@ def test_contiguous_full_size_32_steps():
             lengths = lengths + 1
             pkv.decode_attention(bf16_dev(qs).reshape(B, Hq, 1, D), kc, vc, lengths, out, ws)
             if step in (0, 17, S - 1):
-                got = onum.bf16_to_f64(bits_host(out))[:, :, 0]
+                out32 = torch.empty((B, Hq, 1, D), dtype=torch.float32, device=DEV)
+                pkv.decode_attention(bf16_dev(qs).reshape(B, Hq, 1, D), kc, vc, lengths, out32, ws)
+                assert np.array_equal(bits_host(out), _bf16_round(out32)), step
+                torch.cuda.synchronize()
+                got = out32.double().cpu().numpy()[:, :, 0]
                 qd = onum.bf16_to_f64(qs)
                 for b in range(B):
                     K = onum.bf16_to_f64(kh[b, :, :lengths[b]])
                     V = onum.bf16_to_f64(vh[b, :, :lengths[b]])
                     ref = np.stack([oattn.attend(qd[b, h], K[h // G], V[h // G], 1 / np.sqrt(D)) for h in range(Hq)])
-                    assert rel_err_rows(got[b], ref) <= 2e-2, (step, b)
+                    assert rel_err_rows(got[b], ref) <= F32_TOL, (step, b)
     assert np.array_equal(bits_host(kc), kh) and np.array_equal(bits_host(vc), vh)   # every cache byte
 
 
@@ -150,7 +255,7 @@ def test_int4_full_size():
     vc = np.zeros_like(kc)
     kp = np.zeros((NB, Hkv, bs, D // 32, 2), np.uint16)
     vp = np.zeros_like(kp)
-    check = [0, 17, 31]
+    check = [0, 4, 9, 13, 17, 22, 27, 31]
     logical = {}
     for b in range(B):
         ref_pool.reserve(b, int(spec.lengths[b]))
@@ -197,7 +302,8 @@ def test_qwen_shaped_layer_decode_chunk_and_sampling():
     for b in range(B):
         ref_pool.reserve(b, int(L[b]) + C)
     assert np.array_equal(table.cpu().numpy(), ref_pool.table)
-    check = [int(np.argmin(L)), int(np.argmax(L))]
+    order_L = np.argsort(L, kind="stable")
+    check = sorted({int(order_L[0]), int(order_L[-1])} | {int(order_L[i]) for i in (18, 37, 55, 73, 91, 110)})
     host = {}
     for b in check:
         ids = ref_pool.table[b, :-(-(int(L[b]) + C) // bs)]
@@ -232,7 +338,11 @@ def test_qwen_shaped_layer_decode_chunk_and_sampling():
     dout = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
     ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, int((L + C).max())))
     pkv.paged_decode_attention(dq, kd, vd, table, maxb, bs, (L + C).tolist(), dout, ws, pool=lib_pool)
-    dgot = onum.bf16_to_f64(bits_host(dout))
+    dout32 = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    pkv.paged_decode_attention(dq, kd, vd, table, maxb, bs, (L + C).tolist(), dout32, ws, pool=lib_pool)
+    assert np.array_equal(bits_host(dout), _bf16_round(dout32))
+    torch.cuda.synchronize()
+    dgot = dout32.double().cpu().numpy()
     dqh = onum.bf16_to_f64(bits_host(dq))
     for b in check:
         ids, kp, vp = host[b]
@@ -240,7 +350,7 @@ def test_qwen_shaped_layer_decode_chunk_and_sampling():
         K = onum.bf16_to_f64(ocache.paged_gather(kp, local, int(L[b]) + C, bs))
         V = onum.bf16_to_f64(ocache.paged_gather(vp, local, int(L[b]) + C, bs))
         ref = np.stack([oattn.attend(dqh[b, h], K[h // G], V[h // G], 1 / np.sqrt(D)) for h in range(Hq)])
-        assert rel_err_rows(dgot[b], ref) <= 2e-2, b
+        assert rel_err_rows(dgot[b], ref) <= F32_TOL, b
     # (iii) sampling of [128, 151936] logits ~ N(0, 3)
     logits = workloads.logits(w["seed"], B, w["vocab"])
     ld = torch.from_numpy(logits).to(DEV)
@@ -301,11 +411,15 @@ def test_mixed32k_full_size():
     out = torch.empty((w.B, w.Hq, w.D), device=DEV, dtype=torch.bfloat16)
     ws = workspace(pkv.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.L))
     pkv.paged_decode_attention_mixed(q, kp, vp, pd, table, w.maxb, w.bs, [w.L] * w.B, out, ws, pool=pool)
-    got = onum.bf16_to_f64(bits_host(out))
+    out32 = torch.empty((w.B, w.Hq, w.D), device=DEV, dtype=torch.float32)
+    pkv.paged_decode_attention_mixed(q, kp, vp, pd, table, w.maxb, w.bs, [w.L] * w.B, out32, ws, pool=pool)
+    assert np.array_equal(bits_host(out), _bf16_round(out32))
+    torch.cuda.synchronize()
+    got = out32.double().cpu().numpy()
     for b in rows:
         ids = torch.from_numpy(ref_pool.table[b].astype(np.int64)).to(DEV)
         for name, t in (("k", kp), ("v", vp)):
             gb = bytes_host(t.index_select(0, ids).contiguous()).reshape(w.maxb, w.Hkv, -1)
             assert np.array_equal(gb, refs[b].data[name]), (b, name)
         ref = om.decode_attention(refs[b], qh[b:b + 1], local, [w.L])
-        assert rel_err_rows(got[b], ref[0]) <= 2e-2, b
+        assert rel_err_rows(got[b], ref[0]) <= F32_TOL, b

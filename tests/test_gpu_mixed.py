@@ -18,8 +18,8 @@ from tests.gpu_util import DEV, bf16_dev, bits_host, bytes_host, rel_err_rows, r
 pytestmark = pytest.mark.gpu
 
 F = omixed.Format
-TOL_F32 = 1e-3       # float32 output, against the oracle on exactly decoded values
-TOL_BF16 = 2e-2      # bf16 output
+TOL_F32 = 1e-5       # float32 output, against the oracle on exactly decoded values
+TOL_BF16 = 2.0 ** -8 + 2e-5   # bf16 output: one rounding (unit roundoff 2^-8) of the float32 result
 AFFINE = {"INT8": (0.02, -3), "UINT8": (0.02, 130), "INT4": (0.3, 1), "UINT4": (0.3, 8), "INT2": (0.8, 0),
           "UINT2": (0.8, 2)}
 ALL = ["BF16", "F16"] + list(AFFINE)
