@@ -15,7 +15,9 @@ Inputs are synthetic (seeded, drawn on the device) and resident in HBM before
 the timed region.  Prints one JSON line.  `value` is decode tokens/s of the
 whole step (32 tokens per step); `roofline` reports the attention call, the
 dominant kernel, against the 8 TB/s HBM peak.  `cpu_baseline` times the CPU
-oracle (numpy, float64, one BLAS thread) on a bounded sample of the same step.
+oracle (numpy, float64) on a bounded sample of the same step, on one core and
+on every host core (up to 16 processes of one BLAS thread each, run before the
+GPU is touched); `value` is the all-core rate, `one_core` the single-core one.
 """
 from __future__ import annotations
 
@@ -150,22 +152,58 @@ def run_gpu(steps: int, warmup: int, profile_copy: bool):
     }
 
 
-def run_cpu_baseline(budget_s: float = 12.0):
-    """Time the oracle on whole per-sequence decode steps of the same workload:
-    append one K/V row into the row's 2048 pages, 32-head attention over 32768
-    tokens, and a T=0.7 draw over 151936 logits.  One sequence's pages are
-    generated once and reused; the oracle's work does not depend on the values."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host's cores
+# ---------------------------------------------------------------------------
+MAX_CPU_WORKERS = 16      # a host shares its cores among its GPUs: at most 16 oracle processes
 
+
+def host_cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_CPU_WORKERS))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _cpu_loop(budget_s, body):
+    """Run body(i) (which returns the units of work it did) under one BLAS thread until budget_s
+    elapses; returns (calls, units, seconds)."""
+    from threadpoolctl import threadpool_limits
+    n, units = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            units += body(n)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return n, units, el
+
+
+def _job_paged32k_step(worker=0):
+    """Whole per-sequence decode steps of the paged32k workload: append one K/V row into the row's 2048
+    pages, gather, 32-head attention over 32768 tokens, a T=0.7 draw over 151936 logits.  One token each."""
+    import numpy as np
     import synth
     from oracle import attention, cache, numeric, sampling
-
     maxb = CTX // BS
-    order = synth.permutation(synth.rng(3, 7), maxb)
+    order = synth.permutation(synth.rng(3, 7, worker), maxb)
     opool = cache.PagePool(maxb, BS, 1, maxb, order)
     opool.reserve(0, CTX)
-    g = synth.rng(3, 8)
+    g = synth.rng(3, 8, worker)
     k_pages = synth.f32_to_bf16_bits(synth.normal(g, (maxb, HKV, BS, D)))
     v_pages = synth.f32_to_bf16_bits(synth.normal(g, (maxb, HKV, BS, D)))
     q = synth.f32_to_bf16_bits(synth.normal(g, (HQ, D)))
@@ -173,26 +211,187 @@ def run_cpu_baseline(budget_s: float = 12.0):
     new_v = synth.f32_to_bf16_bits(synth.normal(g, (1, HKV, 1, D)))
     logits = synth.normal(g, (1, VOCAB), 3.0)
     G = HQ // HKV
-    rows = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            cache.paged_cache_update(k_pages, opool.table, new_k, [CTX - 1], 1, BS, opool.held)
-            cache.paged_cache_update(v_pages, opool.table, new_v, [CTX - 1], 1, BS, opool.held)
-            K = numeric.bf16_to_f64(cache.paged_gather(k_pages, opool.table[0], CTX, BS))
-            V = numeric.bf16_to_f64(cache.paged_gather(v_pages, opool.table[0], CTX, BS))
-            qh = numeric.bf16_to_f64(q)
-            for h in range(HQ):
-                attention.attend(qh[h], K[h // G], V[h // G], 1.0 / np.sqrt(D))
-            sampling.sample(logits, TEMPERATURE, rows, )
-            rows += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
-                break
-    return {"value": rows / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} whole per-sequence decode steps of the paged32k workload "
-                      f"(append K/V row, 32-head attention over 32768 tokens, T=0.7 draw over "
-                      f"{VOCAB} logits) in {el:.1f} s, numpy float64 with 1 BLAS thread"}
+
+    def body(i):
+        cache.paged_cache_update(k_pages, opool.table, new_k, [CTX - 1], 1, BS, opool.held)
+        cache.paged_cache_update(v_pages, opool.table, new_v, [CTX - 1], 1, BS, opool.held)
+        K = numeric.bf16_to_f64(cache.paged_gather(k_pages, opool.table[0], CTX, BS))
+        V = numeric.bf16_to_f64(cache.paged_gather(v_pages, opool.table[0], CTX, BS))
+        qh = numeric.bf16_to_f64(q)
+        for h in range(HQ):
+            attention.attend(qh[h], K[h // G], V[h // G], 1.0 / np.sqrt(D))
+        sampling.sample(logits, TEMPERATURE, i)
+        return 1
+    return body
+
+
+def _job_decode_rows(L_list, Hq, Hkv, D, seed, worker=0):
+    """Oracle attention of whole rows (all query heads) of the given lengths, in turn; one row each."""
+    import numpy as np
+    import synth
+    from oracle import attention
+    g = synth.rng(seed, 77, worker)
+    Lmax = max(L_list)
+    K = synth.normal(g, (Hkv, Lmax, D)).astype(np.float64)
+    V = synth.normal(g, (Hkv, Lmax, D)).astype(np.float64)
+    q = synth.normal(g, (Hq, D)).astype(np.float64)
+    G = Hq // Hkv
+
+    def body(i):
+        L = L_list[i % len(L_list)]
+        for h in range(Hq):
+            attention.attend(q[h], K[h // G, :L], V[h // G, :L], 1.0 / np.sqrt(D))
+        return 1
+    return body
+
+
+def _job_int4_rows(worker=0):
+    """INT4 rows of the int4 workload (8192 tokens, 32 heads): exact dequantisation + attention; one row each."""
+    import numpy as np
+    import synth
+    from oracle import affine, attention
+    from synth import workloads
+    spec = workloads.int4()
+    Hq, Hkv, Di = spec.Hq, spec.Hkv, spec.D
+    rows = [(spec.codes_row(b), spec.params_row(b), spec.v_codes_row(b), spec.v_params_row(b),
+             synth.normal(synth.rng(4, 6, b), (Hq, Di)).astype(np.float64)) for b in (worker % spec.B,)]
+
+    def body(i):
+        kc, kp, vc, vp, qq = rows[i % len(rows)]
+        K = affine.int4_dequant_rows(kc, kp)
+        V = affine.int4_dequant_rows(vc, vp)
+        for h in range(Hq):
+            attention.attend(qq[h], K[h // (Hq // Hkv)], V[h // (Hq // Hkv)], 1 / np.sqrt(Di))
+        return 1
+    return body
+
+
+def _job_chunk_queries(worker=0):
+    """Causal chunk queries of a median Qwen-shaped row (16 heads each); flops of each query."""
+    import numpy as np
+    import synth as sy
+    from oracle import attention
+    from synth import workloads
+    w = workloads.qwen()
+    C, Hq, Hkv, Dq = w["chunk"], w["Hq"], w["Hkv"], w["D"]
+    g = sy.rng(5, 78, worker)
+    Lr = int(np.median(w["lengths"])) + C
+    K = sy.normal(g, (Hkv, Lr, Dq)).astype(np.float64)
+    V = sy.normal(g, (Hkv, Lr, Dq)).astype(np.float64)
+    qq = sy.normal(g, (Hq, Dq)).astype(np.float64)
+    G = Hq // Hkv
+
+    def body(i):
+        t = (i * 37) % C
+        last = Lr - C + t
+        for h in range(Hq):
+            attention.attend(qq[h], K[h // G, :last + 1], V[h // G, :last + 1], 1 / np.sqrt(Dq))
+        return 4.0 * Hq * Dq * (last + 1)
+    return body
+
+
+def _job_sample_rows(worker=0):
+    """T=0.7 draws over one row of [*, 151936] N(0, 3) logits; one token each."""
+    from oracle import sampling
+    from synth import workloads
+    w = workloads.qwen()
+    x = workloads.logits(5 + worker, 4, w["vocab"])
+
+    def body(i):
+        sampling.sample(x[i % 4:i % 4 + 1], 0.7, i)
+        return 1
+    return body
+
+
+def _job_mixed_rows(worker=0):
+    """Oracle attention over one 32768-token row of the mixed32k workload's pages (decoded exactly); one row."""
+    import numpy as np
+    import synth
+    from oracle import mixed as om
+    from synth import workloads
+    w = workloads.mixed32k()
+    g = synth.rng(w.seed, 9, worker)
+    opool = om.MixedPool(w.maxb, w.Hkv, w.bs, w.D)
+    local = np.arange(w.maxb, dtype=np.int32)[None]
+    p = 0
+    while p < w.L:                  # one row of the workload, outside the timed loop
+        n = w.threshold if p < w.threshold else min(4096, w.L - p)
+        kf, vf = (w.early if p < w.threshold else w.late)
+        kb = synth.f32_to_bf16_bits(synth.normal(g, (1, w.Hkv, n, w.D), w.k_sigma))
+        vb = synth.f32_to_bf16_bits(synth.normal(g, (1, w.Hkv, n, w.D), w.v_sigma))
+        opool.append(local, kb, vb, [p], n, om.Format(*kf), om.Format(*vf))
+        p += n
+    qh = synth.normal(g, (1, w.Hq, w.D)).astype(np.float64)
+
+    def body(i):
+        om.decode_attention(opool, qh, local, [w.L])
+        return 1
+    return body
+
+
+def _job_tiny_steps(worker=0):
+    """The tiny fixture's stateful loop: prompt + 15 appends into capacity 16, attention after each; one
+    step each (a 16-step run per 16 calls)."""
+    import numpy as np
+    from oracle import attention, cache
+    from synth import workloads
+    w = workloads.tiny()
+    cap = w["capacity"]
+    q, k, v = (w[x].astype(np.float64) for x in ("q", "k", "v"))
+    kc = np.zeros((1, 1, cap, 4))
+    vc = np.zeros((1, 1, cap, 4))
+
+    def body(i):
+        t = i % cap
+        cache.cache_update(kc, k[t].reshape(1, 1, 1, 4), [t], 1)
+        cache.cache_update(vc, v[t].reshape(1, 1, 1, 4), [t], 1)
+        attention.attend(q[t, 0], kc[0, 0, :t + 1], vc[0, 0, :t + 1], 0.5)
+        return 1
+    return body
+
+
+_CPU_JOBS = {"paged32k_step": _job_paged32k_step, "decode_rows": _job_decode_rows, "int4_rows": _job_int4_rows,
+             "chunk_queries": _job_chunk_queries, "sample_rows": _job_sample_rows, "mixed_rows": _job_mixed_rows,
+             "tiny_steps": _job_tiny_steps}
+
+
+def _cpu_worker(name, kw, worker, budget_s, barrier):
+    """One oracle process: build the job, wait until every worker has built it, run it for budget_s."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    body = _CPU_JOBS[name](worker=worker, **kw)
+    body(0)
+    barrier.wait()
+    _, units, el = _cpu_loop(budget_s, body)
+    return units, el
+
+
+def oracle_baseline(name, kw, unit, what, scale=1.0, budget_one=10.0, budget_all=8.0, all_cores=True):
+    """The oracle's rate on one core and on every host core (one process per core, one BLAS thread each,
+    running together).  `scale` converts job units to `unit`.  The all-core figure is `value`."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    body = _CPU_JOBS[name](**kw)
+    body(0)
+    n1, u1, el1 = _cpu_loop(budget_one, body)
+    one = {"value": round(u1 / el1 * scale, 6), "cores": 1, "sample": f"{n1} calls in {el1:.1f} s"}
+    res = {"value": one["value"], "unit": unit, "cores": 1, "kind": "oracle", "cpu_model": cpu_model(),
+           "host_cpus": os.cpu_count(), "sample": f"{what}; 1 core: {n1} calls in {el1:.1f} s", "one_core": one}
+    cores = host_cores()
+    if not all_cores or cores < 2:
+        return res
+    ctx = mp.get_context("spawn")         # fresh interpreters: nothing of this process is inherited
+    with ctx.Manager() as mgr:
+        barrier = mgr.Barrier(cores)
+        with cf.ProcessPoolExecutor(cores, mp_context=ctx) as ex:
+            futs = [ex.submit(_cpu_worker, name, kw, wk, budget_all, barrier) for wk in range(cores)]
+            out = [f.result() for f in futs]
+    rate = sum(u / el for u, el in out) * scale
+    res.update({"value": round(rate, 6), "cores": cores,
+                "sample": f"{what}; {cores} processes together for {budget_all:.0f} s each "
+                          f"({sum(u for u, _ in out):.0f} units), one BLAS thread each; "
+                          f"1 core: {n1} calls in {el1:.1f} s"})
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -230,40 +429,6 @@ def _hbm_roofline(nbytes, us):
     achieved = nbytes / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
-
-
-def _cpu_loop(budget_s, body):
-    """Run body(i) under one BLAS thread until budget_s elapses; returns (iterations, seconds)."""
-    from threadpoolctl import threadpool_limits
-    n = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            body(n)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
-                return n, el
-
-
-def _oracle_decode_rows(L_list, Hq, Hkv, D, budget_s, seed):
-    """Oracle attention of whole rows (all heads) of the given lengths; returns rows/s."""
-    import numpy as np
-    import synth
-    from oracle import attention
-    g = synth.rng(seed, 77)
-    Lmax = max(L_list)
-    K = synth.normal(g, (Hkv, Lmax, D)).astype(np.float64)
-    V = synth.normal(g, (Hkv, Lmax, D)).astype(np.float64)
-    q = synth.normal(g, (Hq, D)).astype(np.float64)
-    G = Hq // Hkv
-
-    def body(i):
-        L = L_list[i % len(L_list)]
-        for h in range(Hq):
-            attention.attend(q[h], K[h // G, :L], V[h // G, :L], 1.0 / np.sqrt(D))
-    n, el = _cpu_loop(budget_s, body)
-    return n / el, n, el
 
 
 def bench_contig(steps, warmup, cpu):
@@ -308,11 +473,7 @@ def bench_contig(steps, warmup, cpu):
         bnd.close()
     mean_L = float(np.mean(L0 + (np.arange(steps) % S)[:, None] + 1))
     nbytes = int(mean_L * Bc * Hkv * Dc * 2 * 2 + Bc * Hq * Dc * 2 * 2)
-    cpu_res = None
-    if cpu:
-        rate, n, el = _oracle_decode_rows([int(x) for x in L0 + 16], Hq, Hkv, Dc, 10.0, 1)
-        cpu_res = {"value": round(rate, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n} rows of 32-head decode attention at the workload's lengths in {el:.1f} s"}
+    cpu_res = cpu
     return _line("decode tokens/s, contiguous bf16 GQA cache", Bc / (us_step * 1e-6), "tokens/s", steps, warmup,
                  us_step, "bf16", {"workload": "contig", "batch": Bc, "capacity": cap, "q_heads": Hq, "kv_heads": Hkv,
                                    "head_dim": Dc, "replicas_rotated": R},
@@ -357,14 +518,7 @@ def bench_paged(steps, warmup, cpu):
     bk.close()
     bv.close()
     nbytes = int(L.sum() * Hkv * Dp * 4 + sum(-(-int(x) // bs) for x in L) * 4 + Bp * Hq * Dp * 4)
-    cpu_res = None
-    if cpu:
-        order = np.argsort(L)
-        sample_L = [int(L[order[len(L) // 2]])]
-        rate, n, el = _oracle_decode_rows(sample_L, Hq, Hkv, Dp, 10.0, 2)
-        per_token = (1.0 / rate) * float(L.mean()) / sample_L[0]
-        cpu_res = {"value": round(1.0 / per_token, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n} median-length rows ({sample_L[0]} tokens) in {el:.1f} s, scaled to the mean length"}
+    cpu_res = cpu
     return _line("decode tokens/s, paged bf16 GQA, lognormal contexts", Bp / (us_step * 1e-6), "tokens/s", steps,
                  warmup, us_step, "bf16", {"workload": "paged", "batch": Bp, "num_blocks": NBp, "block_size": bs,
                                            "q_heads": Hq, "kv_heads": Hkv, "head_dim": Dp,
@@ -426,21 +580,7 @@ def bench_int4(steps, warmup, cpu):
     for bnd in binds:
         bnd.close()
     nbytes = int(L.sum() * Hkv * 160 + Bi * (int(L[0]) // bs) * 4 + Bi * Hq * Di * 4 * 2)
-    cpu_res = None
-    if cpu:
-        from oracle import affine, attention
-        import synth as sy
-
-        def body(i):
-            b = i % Bi
-            K = affine.int4_dequant_rows(spec.codes_row(b), spec.params_row(b))
-            V = affine.int4_dequant_rows(spec.v_codes_row(b), spec.v_params_row(b))
-            qq = sy.normal(sy.rng(4, 6, b), (Hq, Di)).astype(np.float64)
-            for h in range(Hq):
-                attention.attend(qq[h], K[h // (Hq // Hkv)], V[h // (Hq // Hkv)], 1 / np.sqrt(Di))
-        n, el = _cpu_loop(10.0, body)
-        cpu_res = {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n} rows (8192 tokens, 32 heads, dequantise + attention) in {el:.1f} s"}
+    cpu_res = cpu
     return _line("decode tokens/s, paged INT4 blockwise-affine GQA", Bi / (us_step * 1e-6), "tokens/s", steps, warmup,
                  us_step, "int4/f32", {"workload": "int4", "batch": Bi, "ctx": int(L[0]), "num_blocks": NBi,
                                        "block_size": bs, "q_heads": Hq, "kv_heads": Hkv, "head_dim": Di,
@@ -503,12 +643,7 @@ def bench_qwen_decode(steps, warmup, cpu, layers=28):
     for bnd in binds:
         bnd.close()
     nbytes = int(L.sum() * Hkv * Dq * 4 + sum(-(-int(x) // bs) for x in L) * 4 + Bq * Hq * Dq * 4)
-    cpu_res = None
-    if cpu:
-        rate, n, el = _oracle_decode_rows([int(np.median(L))], Hq, Hkv, Dq, 10.0, 5)
-        cpu_res = {"value": round(rate / layers * float(np.median(L)) / float(L.mean()), 4), "unit": "tokens/s",
-                   "cores": 1, "kind": "oracle",
-                   "sample": f"{n} median-length rows of one layer in {el:.1f} s, scaled to {layers} layers"}
+    cpu_res = cpu
     return _line("decode tokens/s, Qwen-shaped 28-layer paged bf16 step", Bq / (us_step * 1e-6), "tokens/s", steps,
                  warmup, us_step, "bf16", {"workload": "qwen-decode", "layers": layers, "batch": Bq, "q_heads": Hq,
                                            "kv_heads": Hkv, "head_dim": Dq, "block_size": bs,
@@ -554,26 +689,7 @@ def bench_qwen_chunk(steps, warmup, cpu):
     flops = 4.0 * Hq * Dq * float(np.sum(C * P0 + C * (C + 1) / 2))
     tflops = flops / (us_attn * 1e-6) / 1e12
     peak = 2500.0
-    cpu_res = None
-    if cpu:
-        import synth as sy
-        from oracle import attention
-        g = sy.rng(5, 78)
-        Lr = int(np.median(P0)) + C
-        K = sy.normal(g, (Hkv, Lr, Dq)).astype(np.float64)
-        V = sy.normal(g, (Hkv, Lr, Dq)).astype(np.float64)
-        qq = sy.normal(g, (Hq, Dq)).astype(np.float64)
-        done = [0.0]
-
-        def body(i):
-            t = (i * 37) % C
-            last = Lr - C + t
-            for h in range(Hq):
-                attention.attend(qq[h], K[h // 2, :last + 1], V[h // 2, :last + 1], 1 / np.sqrt(Dq))
-            done[0] += 4.0 * Hq * Dq * (last + 1)
-        n, el = _cpu_loop(10.0, body)
-        cpu_res = {"value": round(done[0] / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n} chunk queries (16 heads each) of a median row in {el:.1f} s"}
+    cpu_res = cpu
     return _line("causal chunk attention TFLOP/s (512-token chunk, MFMA bf16)", tflops, "TFLOP/s", steps, warmup,
                  us_step, "bf16", {"workload": "qwen-chunk", "batch": Bq, "chunk": C, "q_heads": Hq, "kv_heads": Hkv,
                                    "head_dim": Dq, "mean_prefix": round(float(P0.mean()), 1)},
@@ -603,13 +719,7 @@ def bench_sample(steps, warmup, cpu):
     us_greedy = _timed(lambda i: pkv.sample(lg[i % R], 0.0, i, ids, sws), steps, warmup, stream)
     us_temp = _timed(lambda i: pkv.sample(lg[i % R], 0.7, i, ids, sws), steps, warmup, stream)
     nbytes = Bs * Vs * 4
-    cpu_res = None
-    if cpu:
-        from oracle import sampling
-        x = workloads.logits(5, 4, Vs)
-        n, el = _cpu_loop(10.0, lambda i: sampling.sample(x[i % 4:i % 4 + 1], 0.7, i))
-        cpu_res = {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n} rows of T=0.7 draws over {Vs} logits in {el:.1f} s"}
+    cpu_res = cpu
     return _line("sampling tokens/s, T=0.7 over [128, 151936] logits", Bs / (us_temp * 1e-6), "tokens/s", steps,
                  warmup, us_temp, "f32", {"workload": "sample", "batch": Bs, "vocab": Vs, "replicas_rotated": R},
                  _hbm_roofline(nbytes, us_temp), cpu_res, greedy_us=round(us_greedy, 2),
@@ -641,11 +751,7 @@ def bench_window(steps, warmup, cpu):
                                                      left_window=W), steps, warmup, stream)
     visible = W + 1
     nbytes = B * visible * HKV * D * 2 * 2 + B * (visible // BS) * 4 + B * HQ * D * 2 * 2
-    cpu_res = None
-    if cpu:
-        rate, n, el = _oracle_decode_rows([visible], HQ, HKV, D, 10.0, 3)
-        cpu_res = {"value": round(rate, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n} rows of 32-head attention over the {visible} visible tokens in {el:.1f} s"}
+    cpu_res = cpu
     return _line("decode tokens/s, paged bf16 GQA, 32k context with a 4096-token left window", B / (us * 1e-6),
                  "tokens/s", steps, warmup, us, "bf16",
                  {"workload": "window", "batch": B, "ctx": CTX, "left_window": W, "q_heads": HQ, "kv_heads": HKV,
@@ -696,27 +802,7 @@ def bench_mixed(steps, warmup, cpu):
     early, late = w.threshold, w.L - w.threshold
     row_bytes = w.D * 2 * 2 * early + (w.D * 1 + w.D // 2) * late       # K + V bytes of one (row, kv head)
     nbytes = w.B * w.Hkv * row_bytes + w.B * w.maxb * (4 + 16) + w.B * w.Hq * w.D * 2 * 2
-    cpu_res = None
-    if cpu:
-        from oracle import mixed as om
-        import synth
-        g = synth.rng(w.seed, 9)
-        opool = om.MixedPool(w.maxb, w.Hkv, w.bs, w.D)
-        local = np.arange(w.maxb, dtype=np.int32)[None]
-        ofmt = lambda t: om.Format(*t)
-        p = 0
-        while p < w.L:                  # one row of the workload, outside the timed loop
-            n = w.threshold if p < w.threshold else min(4096, w.L - p)
-            kf, vf = (w.early if p < w.threshold else w.late)
-            kb = synth.f32_to_bf16_bits(synth.normal(g, (1, w.Hkv, n, w.D), w.k_sigma))
-            vb = synth.f32_to_bf16_bits(synth.normal(g, (1, w.Hkv, n, w.D), w.v_sigma))
-            opool.append(local, kb, vb, [p], n, ofmt(kf), ofmt(vf))
-            p += n
-        qh = synth.normal(g, (1, w.Hq, w.D)).astype(np.float64)
-        n, el = _cpu_loop(10.0, lambda i: om.decode_attention(opool, qh, local, [w.L]))
-        cpu_res = {"value": round(n / el, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n} rows of 32-head attention over one 32768-token row of the workload's mixed "
-                             f"pages (decoded exactly, float64) in {el:.1f} s"}
+    cpu_res = cpu
     return _line("decode tokens/s, paged GQA over mixed-format pages (BF16 prefix, INT8 K / UINT4 V), 32k context",
                  w.B / (us * 1e-6), "tokens/s", steps, warmup, us, "bf16/int8/uint4",
                  {"workload": "mixed", "batch": w.B, "ctx": w.L, "q_heads": w.Hq, "kv_heads": w.Hkv,
@@ -785,13 +871,7 @@ def bench_generate(steps, warmup, cpu, layers=28, new_tokens=8):
     us_iter = el / iters * 1e6
     mean_ctx = mean_L + new_tokens * steps / 2
     nbytes = int(layers * (Bq * mean_ctx * Hkv * Dq * 4 + Bq * Hq * Dq * 4))    # attention bytes of one iteration
-    cpu_res = None
-    if cpu:
-        rate, n, el_c = _oracle_decode_rows([int(np.median(L0))], Hq, Hkv, Dq, 10.0, 5)
-        cpu_res = {"value": round(rate / layers * float(np.median(L0)) / mean_ctx, 4), "unit": "tokens/s",
-                   "cores": 1, "kind": "oracle",
-                   "sample": f"{n} median-length rows of one layer's attention in {el_c:.1f} s, scaled to {layers} "
-                             f"layers and the mean context (the LM head and sampling are not included)"}
+    cpu_res = cpu
     return _line("generated tokens/s, 28-layer Qwen-shaped generation loop (paged bf16, T=0.7, EOS)",
                  produced / el, "tokens/s", steps, warmup, el / steps * 1e6, "bf16",
                  {"workload": "generate", "layers": layers, "batch": Bq, "q_heads": Hq, "kv_heads": Hkv,
@@ -801,9 +881,187 @@ def bench_generate(steps, warmup, cpu, layers=28, new_tokens=8):
                  attn_algorithmic_bytes_per_iteration=nbytes)
 
 
+# Context only (another machine, a CPU runtime): the pages' single four-token run of the tiny fixture on an
+# AMD EPYC 9V74, latency per token in microseconds ("Persistent input/output feedback", opening section).
+PAGES_TINY_US = {"stateful": [236.216, 34.542, 22.253, 20.891], "stateless": [358.640, 18.268, 6.079, 5.308],
+                 "host": "AMD EPYC 9V74 (CPU runtime, single observations)"}
+
+
+def bench_tiny(steps, warmup, cpu):
+    """The tiny fixture (1 row, 1 head, D = 4, float32, capacity 16): a 1-token prompt then 15 appends, each
+    step an in-place K and V append and decode attention over the valid prefix, then the append that would
+    overflow capacity and is rejected.  Each of the `steps` runs starts from an empty cache.  Reports the
+    host-observed latency of every step (issue to completion, what a caller waits per token) and its device
+    time (HIP events around the step on the launch stream), and the rejected call's host time."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    w = workloads.tiny()
+    cap = w["capacity"]
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    qd = [torch.from_numpy(w["q"][t]).reshape(1, 1, 1, 4).to(dev) for t in range(cap + 1)]
+    kd = [torch.from_numpy(w["k"][t]).reshape(1, 1, 1, 4).to(dev) for t in range(cap + 1)]
+    vd = [torch.from_numpy(w["v"][t]).reshape(1, 1, 1, 4).to(dev) for t in range(cap + 1)]
+    kc = torch.zeros((1, 1, cap, 4), device=dev)
+    vc = torch.zeros((1, 1, cap, 4), device=dev)
+    out = torch.empty((1, 1, 1, 4), device=dev)
+    ws = torch.empty(max(256, pkv.decode_workspace_size(1, 1, 1, 4, cap)), device=dev, dtype=torch.uint8)
+    bk, bv = pkv.bind_writable(kc), pkv.bind_writable(vc)
+    host = np.zeros((steps, cap))
+    devt = np.zeros((steps, cap))
+    rejected = np.zeros(steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cap)]
+
+    def run(record):
+        for t in range(cap):
+            t0 = time.perf_counter()
+            evs[t][0].record(stream)
+            assert pkv.cache_update(kc, kd[t], [t], 1) == kc.data_ptr()
+            assert pkv.cache_update(vc, vd[t], [t], 1) == vc.data_ptr()
+            pkv.decode_attention(qd[t], kc, vc, [t + 1], out, ws)
+            evs[t][1].record(stream)
+            torch.cuda.synchronize()
+            if record is not None:
+                host[record, t] = (time.perf_counter() - t0) * 1e6
+        t0 = time.perf_counter()
+        try:
+            pkv.cache_update(kc, kd[cap], [cap], 1)
+            raise RuntimeError("the append past capacity was accepted")
+        except pkv.PkvError as e:
+            assert e.status == pkv.E_CAPACITY
+        if record is not None:
+            rejected[record] = (time.perf_counter() - t0) * 1e6
+            for t in range(cap):
+                devt[record, t] = evs[t][0].elapsed_time(evs[t][1]) * 1e3
+
+    for _ in range(warmup):
+        run(None)
+    free_before = torch.cuda.mem_get_info()[0]
+    for i in range(steps):
+        run(i)
+    alloc_delta = free_before - torch.cuda.mem_get_info()[0]
+    before = (kc.clone(), vc.clone())
+    try:
+        pkv.cache_update(kc, kd[cap], [cap], 1)
+    except pkv.PkvError:
+        pass
+    torch.cuda.synchronize()
+    unchanged = bool(torch.equal(kc, before[0]) and torch.equal(vc, before[1]))
+    bk.close()
+    bv.close()
+    med_host = np.median(host, axis=0)
+    med_dev = np.median(devt, axis=0)
+    mean_us = float(med_host.mean())
+    r = _line("tiny-fixture decode step latency (append K/V + attention), us per step", mean_us, "us/step", steps,
+              warmup, mean_us * cap, "f32",
+              {"workload": "tiny", "batch": 1, "heads": 1, "head_dim": 4, "capacity": cap,
+               "steps_per_run": cap, "step": "in-place K and V append + decode attention, then a rejected append"},
+              {"bound": "latency", "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None},
+              cpu, per_step_host_us=[round(float(x), 2) for x in med_host],
+              per_step_device_us=[round(float(x), 2) for x in med_dev],
+              first_token_host_us=round(float(med_host[0]), 2), token4_host_us=round(float(med_host[3]), 2),
+              overflow_rejected_host_us=round(float(np.median(rejected)), 2),
+              overflow_leaves_cache_unchanged=unchanged,
+              device_bytes_allocated_during_steps=int(max(alloc_delta, 0)),
+              pages_cpu_runtime_us_context=PAGES_TINY_US)
+    r["higher_is_better"] = False
+    return r
+
+
+# ---------------------------------------------------------------------------
+# The oracle's baseline for each row, in the row's own unit (CPU only: run before the GPU is touched)
+# ---------------------------------------------------------------------------
+def cpu_paged32k(steps, warmup):
+    return oracle_baseline("paged32k_step", {}, "tokens/s",
+                           "whole per-sequence decode steps of the paged32k workload (append a K/V row into the "
+                           "row's 2048 pages, 32-head attention over 32768 tokens, a T=0.7 draw over 151936 "
+                           "logits), numpy float64", budget_one=12.0)
+
+
+def cpu_contig(steps, warmup):
+    from synth import workloads
+    w = workloads.contig()
+    L = [int(x) for x in w["lengths"] + 16]
+    return oracle_baseline("decode_rows", dict(L_list=L, Hq=w["Hq"], Hkv=w["Hkv"], D=w["D"], seed=1), "tokens/s",
+                           "rows of 32-head decode attention at the workload's mid-run lengths")
+
+
+def cpu_paged(steps, warmup):
+    import numpy as np
+    from synth import workloads
+    spec = workloads.paged()
+    L = spec.lengths
+    med = int(L[np.argsort(L)[len(L) // 2]])
+    return oracle_baseline("decode_rows", dict(L_list=[med], Hq=spec.Hq, Hkv=spec.Hkv, D=spec.D, seed=2),
+                           "tokens/s", f"median-length rows ({med} tokens) of 32-head attention, scaled to the "
+                           f"mean length {float(L.mean()):.0f}", scale=med / float(L.mean()))
+
+
+def cpu_int4(steps, warmup):
+    return oracle_baseline("int4_rows", {}, "tokens/s", "rows of the int4 workload (8192 tokens, 32 heads): exact "
+                           "dequantisation + attention")
+
+
+def cpu_qwen_decode(steps, warmup, layers=28):
+    import numpy as np
+    from synth import workloads
+    w = workloads.qwen()
+    L = w["lengths"].astype(np.int64) + 1
+    med = int(np.median(L))
+    return oracle_baseline("decode_rows", dict(L_list=[med], Hq=w["Hq"], Hkv=w["Hkv"], D=w["D"], seed=5),
+                           "tokens/s", f"median-length rows ({med} tokens) of one layer's 16-head attention, "
+                           f"scaled to {layers} layers and the mean length", scale=med / (layers * float(L.mean())))
+
+
+def cpu_qwen_chunk(steps, warmup):
+    return oracle_baseline("chunk_queries", {}, "TFLOP/s", "causal chunk queries (16 heads each) of a "
+                           "median-length row", scale=1e-12)
+
+
+def cpu_sample(steps, warmup):
+    return oracle_baseline("sample_rows", {}, "tokens/s", "rows of T=0.7 draws over 151936 logits")
+
+
+def cpu_window(steps, warmup):
+    visible = 4096
+    return oracle_baseline("decode_rows", dict(L_list=[visible], Hq=HQ, Hkv=HKV, D=D, seed=3), "tokens/s",
+                           f"rows of 32-head attention over the {visible} visible tokens")
+
+
+def cpu_mixed(steps, warmup):
+    return oracle_baseline("mixed_rows", {}, "tokens/s", "rows of 32-head attention over one 32768-token row of "
+                           "the workload's mixed pages (decoded exactly, float64)")
+
+
+def cpu_generate(steps, warmup, layers=28, new_tokens=8):
+    import numpy as np
+    from synth import workloads
+    w = workloads.qwen()
+    L0 = w["lengths"].astype(np.int64)
+    med = int(np.median(L0))
+    mean_ctx = float(L0.mean()) + new_tokens * (warmup + steps / 2)
+    return oracle_baseline("decode_rows", dict(L_list=[med], Hq=w["Hq"], Hkv=w["Hkv"], D=w["D"], seed=5),
+                           "tokens/s", f"median-length rows of one layer's attention, scaled to {layers} layers and "
+                           f"the mean context (the LM head and sampling are not included)",
+                           scale=med / (layers * mean_ctx))
+
+
+def cpu_tiny(steps, warmup):
+    r = oracle_baseline("tiny_steps", {}, "steps/s", "the tiny fixture's stateful steps (append K and V, attention "
+                        "over the valid prefix), numpy float64", budget_one=5.0, all_cores=False)
+    r.update({"value": round(1e6 / r["value"], 3), "unit": "us/step"})
+    r["one_core"]["value"] = r["value"]
+    return r
+
+
 WORKLOADS = {"contig": bench_contig, "paged": bench_paged, "int4": bench_int4, "qwen-decode": bench_qwen_decode,
              "qwen-chunk": bench_qwen_chunk, "sample": bench_sample, "window": bench_window, "mixed": bench_mixed,
-             "generate": bench_generate}
+             "generate": bench_generate, "tiny": bench_tiny}
+CPU_BASELINES = {"paged32k": cpu_paged32k, "contig": cpu_contig, "paged": cpu_paged, "int4": cpu_int4,
+                 "qwen-decode": cpu_qwen_decode, "qwen-chunk": cpu_qwen_chunk, "sample": cpu_sample,
+                 "window": cpu_window, "mixed": cpu_mixed, "generate": cpu_generate, "tiny": cpu_tiny}
 
 
 def main():
@@ -821,8 +1079,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the decode step would shard)", file=sys.stderr)
         sys.exit(2)
+    # the oracle's timing runs first, before this process touches the GPU (its worker processes start fresh)
+    cpu = None if args.no_cpu_baseline else CPU_BASELINES[args.workload](args.steps, args.warmup)
     if args.workload != "paged32k":
-        print(json.dumps(WORKLOADS[args.workload](args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
+        print(json.dumps(WORKLOADS[args.workload](args.steps, args.warmup, cpu)), flush=True)
         return
 
     g = run_gpu(args.steps, args.warmup, args.profile_copy)
@@ -855,8 +1115,8 @@ def main():
         "attn_algorithmic_bytes": attn_bytes,
         "device_bytes_allocated_during_steps": g["device_bytes_allocated_during_steps"],
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = run_cpu_baseline()
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
