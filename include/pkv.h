@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -281,6 +281,25 @@ pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_p
                                       float scale, int32_t left_window, pkv_tensor* out,
                                       void* workspace, size_t workspace_bytes, int32_t num_splits,
                                       void* stream);
+
+/* Variant of pkv_paged_decode_attention for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc): same arguments and results without the workspace.  The
+ * split partials live in a static device array of PKV_NOALLOC_SCRATCH_BYTES
+ * that the library keeps on every GPU it runs on until the process ends; the
+ * call allocates nothing.  A call whose partials need more than that
+ * (pkv_decode_workspace_size of the same arguments) fails with PKV_E_NOMEM
+ * before any work is enqueued.  Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (other streams, other host
+ * threads) race; calls in order on one stream do not.  Its contents need no
+ * initialisation. */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+pkv_status pkv_paged_decode_attention_noalloc(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                              const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              const pkv_pool* pool, const int32_t* valid_len,
+                                              float scale, int32_t left_window, pkv_tensor* out,
+                                              int32_t num_splits, void* stream);
 
 /* Paged INT4: K/V rows decoded in registers as (code - zero_point) * scale
  * per 32-element block ("Custom, quantized, and persistent values",

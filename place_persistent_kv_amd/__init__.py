@@ -126,6 +126,8 @@ _SIG = {
                                        _VP]),
     "pkv_paged_decode_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
                                              C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
+    "pkv_paged_decode_attention_noalloc": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
+                                                     C.c_int32, _T, C.c_int32, _VP]),
     "pkv_paged_decode_attention_int4": (C.c_int, [_T, _T, _T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P,
                                                   C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_chunk_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float, C.c_int32,
@@ -150,7 +152,7 @@ for _name, (_res, _args) in _SIG.items():
         _fn.argtypes = _args
 
 
-ABI_VERSION = 4      # the argument lists above follow this version of include/pkv.h
+ABI_VERSION = 5      # the argument lists above follow this version of include/pkv.h
 if _lib.pkv_abi_version() != ABI_VERSION:
     raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
                       "rebuild it (python place_persistent_kv_amd/build.py)")
@@ -413,6 +415,20 @@ def paged_decode_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: in
                                            int(left_window), C.byref(desc(out)), _ptr(workspace),
                                            0 if workspace is None else _nbytes(workspace), int(num_splits),
                                            _stream(stream)), "pkv_paged_decode_attention")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20      # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_decode_attention_noalloc(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, block_size: int,
+                                   valid_len, out, pool: Optional[Pool] = None, scale: float = 0.0,
+                                   num_splits: int = 0, stream=None, left_window: int = -1) -> None:
+    """``pkv_paged_decode_attention_noalloc``: the paged decode with its split partials in the library's
+    static device scratch (no workspace argument, nothing allocated)."""
+    _check(_lib.pkv_paged_decode_attention_noalloc(
+        C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)), _ptr(page_table), int(max_blocks_per_seq),
+        int(block_size), _pool_handle(pool), _i32_array(valid_len), float(scale), int(left_window),
+        C.byref(desc(out)), int(num_splits), _stream(stream)), "pkv_paged_decode_attention_noalloc")
 
 
 def paged_decode_attention_int4(q, k_codes, k_params, v_codes, v_params, page_table, max_blocks_per_seq: int,

@@ -652,7 +652,8 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
                          bool paged, const int32_t* page_table, int32_t maxb, int32_t bs,
                          const pkv_pool* pool, const int32_t* valid_len, float scale,
                          int32_t left_window, pkv_tensor* out, void* ws, size_t ws_bytes,
-                         int32_t num_splits, void* stream, const pkv_tensor* page_desc = nullptr) {
+                         int32_t num_splits, void* stream, const pkv_tensor* page_desc = nullptr,
+                         bool static_ws = false) {
     const bool mixed = page_desc != nullptr;
     QView qv;
     PKV_TRY(check_tensor(k, "k", 4, 4));
@@ -729,7 +730,14 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
     Plan full = plan_splits(span_len.data(), static_cast<int>(B), fast ? static_cast<int>(Hkv) : static_cast<int>(Hq),
                             num_splits, fast ? 0 : kGenericMaxTps);
     const size_t need = ws_bytes_for(B, Hq, Dv, full.S_max);
-    if (full.S_max > 1 || !fast) {
+    if (static_ws && (full.S_max > 1 || !fast)) {
+        // after every check: the scratch's device address is the first HIP call
+        if (need > ws_bytes)
+            return fail(PKV_E_NOMEM, "the split partials need %zu bytes, more than the %zu-byte static scratch "
+                        "(fewer splits or fewer rows per call)", need, ws_bytes);
+        const hipError_t e = noalloc_scratch(&ws);
+        if (e != hipSuccess) return fail(PKV_E_HIP, "static scratch address: %s", hipGetErrorString(e));
+    } else if (full.S_max > 1 || !fast) {
         if (!ws || ws_bytes < need)
             return fail(PKV_E_NOMEM, "workspace of %zu bytes needed, %zu given (pkv_decode_workspace_size)", need, ws_bytes);
         const Span wss = span(ws, static_cast<int64_t>(need));
@@ -835,6 +843,19 @@ pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_p
                          valid_len, scale, left_window, out, workspace, workspace_bytes, num_splits, stream);
 }
 
+
+static_assert(kNoallocScratchBytes == PKV_NOALLOC_SCRATCH_BYTES, "scratch size and its documented limit agree");
+
+pkv_status pkv_paged_decode_attention_noalloc(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                              const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              const pkv_pool* pool, const int32_t* valid_len,
+                                              float scale, int32_t left_window, pkv_tensor* out,
+                                              int32_t num_splits, void* stream) {
+    return decode_common(q, k_pool, v_pool, true, page_table_dev, max_blocks_per_seq, block_size, pool,
+                         valid_len, scale, left_window, out, nullptr, kNoallocScratchBytes, num_splits, stream,
+                         nullptr, true);
+}
 
 pkv_status pkv_paged_decode_attention_mixed(const pkv_tensor* q, const pkv_tensor* k_pool,
                                             const pkv_tensor* v_pool, const pkv_tensor* page_desc,

@@ -260,4 +260,11 @@ struct SampleArgs {
 };
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Static scratch (pkv_paged_decode_attention_noalloc)
+// ---------------------------------------------------------------------------
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;   // == PKV_NOALLOC_SCRATCH_BYTES
+// Device address of the current device's scratch array (taken once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace pkv

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if getattr(pkv._lib, n, None) is None]
     assert not missing, missing
     assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
-    assert pkv.abi_version() == pkv.ABI_VERSION == 4
+    assert pkv.abi_version() == pkv.ABI_VERSION == 5
 
 
 def R(ptr, dtype, shape):
@@ -452,3 +452,23 @@ def test_generate_finish_errors():
     with pytest.raises(pkv.PkvError) as e:      # next_ids inside tokens
         pkv._check(pkv._lib.pkv_generate_finish(ids, fin, tok.ptr, 10, 0, 4, 2, 2, tok.ptr + 8, unf, None), "x")
     assert e.value.status == pkv.E_ALIAS
+
+
+def test_noalloc_decode_validates_before_any_hip_call():
+    """The static-scratch variant fails its checks on the host, the scratch size limit included."""
+    B, Hq, Hkv, D, bs, NB, maxb = 12, 64, 8, 128, 16, 4096, 300
+    q = R(FAKE, pkv.BF16, [B, Hq, D])
+    kp = R(FAKE + (1 << 30), pkv.BF16, [NB, Hkv, bs, D])
+    vp = R(FAKE + (2 << 30), pkv.BF16, [NB, Hkv, bs, D])
+    out = R(FAKE + (3 << 30), pkv.F32, [B, Hq, D])
+    table = FAKE + (4 << 30)
+    lens = [4096] * B
+    # partials of 64 splits per row exceed the 16 MiB scratch
+    assert pkv.decode_workspace_size(B, Hq, Hkv, D, maxb * bs, 64) > pkv.NOALLOC_SCRATCH_BYTES
+    assert status_of(pkv.paged_decode_attention_noalloc, q, kp, vp, table, maxb, bs, lens, out,
+                     num_splits=64) == pkv.E_NOMEM
+    assert "static scratch" in pkv.last_error()
+    assert status_of(pkv.paged_decode_attention_noalloc, q, kp, vp, table, maxb, bs, [0] * B, out) == pkv.E_CAPACITY
+    assert status_of(pkv.paged_decode_attention_noalloc, q, kp, vp, table, maxb, 8, lens, out) == pkv.E_LAYOUT
+    assert status_of(pkv.paged_decode_attention_noalloc, R(FAKE, pkv.F16, [B, Hq, D]), kp, vp, table, maxb, bs,
+                     lens, out) == pkv.E_DTYPE
