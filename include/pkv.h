@@ -326,7 +326,8 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
  * lengths); key tiles wholly before every query's window are not read.
  * q, out: bf16 [B, Hq, C, D] with D == 128 and Hq / Hkv in {1, 2, 4, 8};
  * k_pool, v_pool: bf16 [num_blocks, Hkv, block_size, D], block_size a power
- * of two >= 4 (else PKV_E_LAYOUT); page_table_dev as
+ * of two >= 4; q, out and both pools 16-byte aligned (else PKV_E_LAYOUT);
+ * page_table_dev as
  * for pkv_paged_decode_attention.  Errors: PKV_E_CAPACITY when p0[b] < 0 or
  * p0[b] + C exceeds max_blocks_per_seq * block_size; PKV_E_PAGE when `pool` is
  * given and a row holds fewer than ceil((p0[b] + C) / block_size) pages.

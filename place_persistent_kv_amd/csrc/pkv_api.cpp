@@ -1219,6 +1219,9 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
     if (!page_table_dev) return fail(PKV_E_ARG, "chunk attention: null page table");
     if (block_size != bs) return fail(PKV_E_LAYOUT, "chunk attention: block_size != pool slot count");
     if ((bs & (bs - 1)) != 0) return fail(PKV_E_LAYOUT, "chunk attention: block_size must be a power of two");
+    if (reinterpret_cast<uintptr_t>(k_pool->data) % 16 || reinterpret_cast<uintptr_t>(v_pool->data) % 16 ||
+        reinterpret_cast<uintptr_t>(q->data) % 16 || reinterpret_cast<uintptr_t>(out->data) % 16)
+        return fail(PKV_E_LAYOUT, "chunk attention: q, out and the pools must be 16-byte aligned");
     if (max_blocks_per_seq <= 0) return fail(PKV_E_ARG, "chunk attention: max_blocks_per_seq must be positive");
     if (left_window < -1) return fail(PKV_E_ARG, "chunk attention: left_window must be -1 (unbounded) or >= 0");
     if (pool && (pool->block_size != bs || pool->num_blocks != NB || pool->maxb != max_blocks_per_seq))

@@ -291,6 +291,12 @@ def test_chunk_attention_checks():
     # head size 128 and bf16 only
     assert status_of(f, R(q.ptr, pkv.F32, q.shape), kp, vp, table, 8, 16, [0, 0], R(out.ptr, pkv.F32, out.shape)) \
         == pkv.E_DTYPE
+    # the pools, q and out are read and written in 16-byte pieces
+    for bad in ({"kp": R(kp.ptr + 8, pkv.BF16, kp.shape)}, {"vp": R(vp.ptr + 2, pkv.BF16, vp.shape)},
+                {"q": R(q.ptr + 4, pkv.BF16, q.shape)}, {"out": R(out.ptr + 8, pkv.BF16, out.shape)}):
+        args = {**dict(q=q, kp=kp, vp=vp, out=out), **bad}
+        assert status_of(f, args["q"], args["kp"], args["vp"], table, 8, 16, [0, 0], args["out"]) == pkv.E_LAYOUT
+        assert "16-byte" in pkv.last_error()
 
 
 # --------------------------------------------------------------------------- sampling
