@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -202,6 +202,53 @@ pkv_status pkv_paged_cache_update(const pkv_pool* pool, const pkv_tensor* pool_k
                                   const int32_t* position, int32_t update_length,
                                   void** out_pool, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Device-driven step (positions and lengths in device memory)               */
+/* "Mutable execution cache", section "Existing implementations": capturing a
+ * decode step in a graph needs its buffers, positions included, to be shared
+ * device state rather than values fixed at launch.  The *_dev entry points
+ * take positions, valid lengths and the sampling step from device memory, so
+ * a step enqueued once (for example captured in a HIP graph) can be replayed
+ * as the sequences grow; pkv_advance moves that state on.  Host arguments
+ * (shapes, dtypes, bindings, bounds) are checked on the host as everywhere
+ * else.  Values read from device memory are checked by the kernels: a failed
+ * check writes a non-zero pkv_status into the caller's device word
+ * *status_dev and the check's rows are left alone (see each call).  The
+ * library never clears *status_dev: zero it before the first step; a
+ * non-zero value stays until the caller clears it.                           */
+/* ------------------------------------------------------------------------ */
+
+/* K and V appended in one launch at device positions ("Mutable execution
+ * cache", "Required alias": the output is the input storage).
+ * k_cache, v_cache: [B, H, capacity, D], one dtype, each inside a writable
+ * binding; k_values, v_values: [B, H, update_length, D]; rows of D elements
+ * a multiple of 16 bytes; every tensor 16-byte aligned.
+ * position_dev: device int32[B].  update_length in [0, 64].
+ * Device check: every row has 0 <= position <= capacity - update_length;
+ * otherwise nothing is written and *status_dev = PKV_E_CAPACITY. */
+pkv_status pkv_cache_update_kv_dev(const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                                   const pkv_tensor* k_values, const pkv_tensor* v_values,
+                                   const int32_t* position_dev, int32_t update_length,
+                                   int32_t* status_dev, void* stream);
+
+/* Paged form ("Heterogeneous paged cache", "Runtime contract": existing
+ * pages are updated in place, nothing is allocated): k_pool, v_pool
+ * [num_blocks, H, block_size, D] matching `pool`; page_table_dev as for
+ * pkv_paged_cache_update.  Device checks: every row has 0 <= position and
+ * position + update_length <= max_blocks_per_seq * block_size (else
+ * PKV_E_CAPACITY), and every page the call writes has an id in
+ * [0, num_blocks) (a -1 entry is a page that was never reserved; else
+ * PKV_E_PAGE); on a failure nothing is written. */
+pkv_status pkv_paged_cache_update_kv_dev(const pkv_pool* pool, const pkv_tensor* k_pool,
+                                         const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                         const pkv_tensor* k_values, const pkv_tensor* v_values,
+                                         const int32_t* position_dev, int32_t update_length,
+                                         int32_t* status_dev, void* stream);
+
+/* values_dev[i] += delta for i < n (device int32), then *step_dev += 1 when
+ * step_dev is not NULL (the counter pkv_sample_dev reads). */
+pkv_status pkv_advance(int32_t* values_dev, int32_t n, int32_t delta, int64_t* step_dev, void* stream);
+
 /* INT4 variant: quantise the new rows on append.
  * "Persistent input/output feedback", "Optional heterogeneous paged KV":
  * affine append uses scalar parameters, rounds ties to even and saturates;
@@ -300,6 +347,29 @@ pkv_status pkv_paged_decode_attention_noalloc(const pkv_tensor* q, const pkv_ten
                                               const pkv_pool* pool, const int32_t* valid_len,
                                               float scale, int32_t left_window, pkv_tensor* out,
                                               int32_t num_splits, void* stream);
+
+/* pkv_decode_attention / pkv_paged_decode_attention with the valid lengths
+ * in device memory (valid_len_dev: device int32[B]).  max_len (host) bounds
+ * every length and sizes the split plan and the workspace
+ * (pkv_decode_workspace_size with max_len); with every row at max_len the
+ * plan and the results are those of the host-length call.  The page table
+ * is read as it stands when the kernels run.  Device checks: a row whose
+ * length is outside [1, max_len] writes nothing and sets *status_dev =
+ * PKV_E_CAPACITY; a page id outside [0, num_blocks) among a row's valid
+ * pages sets PKV_E_PAGE (the read is redirected to page 0 and the row's
+ * output is unspecified).  With a pool handle only its shape is checked. */
+pkv_status pkv_decode_attention_dev(const pkv_tensor* q, const pkv_tensor* k_cache,
+                                    const pkv_tensor* v_cache, const int32_t* valid_len_dev,
+                                    int32_t max_len, float scale, int32_t left_window, pkv_tensor* out,
+                                    void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                    int32_t* status_dev, void* stream);
+pkv_status pkv_paged_decode_attention_dev(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                          const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                          int32_t max_blocks_per_seq, int32_t block_size,
+                                          const pkv_pool* pool, const int32_t* valid_len_dev,
+                                          int32_t max_len, float scale, int32_t left_window,
+                                          pkv_tensor* out, void* workspace, size_t workspace_bytes,
+                                          int32_t num_splits, int32_t* status_dev, void* stream);
 
 /* Paged INT4: K/V rows decoded in registers as (code - zero_point) * scale
  * per 32-element block ("Custom, quantized, and persistent values",
@@ -453,6 +523,14 @@ size_t pkv_sample_workspace_size(int32_t B, int64_t V);
  * out_ids: device int64[B]. */
 pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed,
                       int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pkv_sample whose seed is that of iteration *step_dev of one generation:
+ * seed + step * B * V * 0x9E3779B97F4A7C15 (mod 2^64), i.e.
+ * pkv_generate_step_seed(seed, *step_dev, B, V), with the step counter read
+ * from device memory when the kernel runs (step_dev: device int64, advanced
+ * by pkv_advance).  step_dev NULL is pkv_sample. */
+pkv_status pkv_sample_dev(const pkv_tensor* logits, float temperature, uint64_t seed, const int64_t* step_dev,
+                          int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Generation loop                                                           */

@@ -143,6 +143,14 @@ _SIG = {
                                       _VP, _VP]),
     "pkv_sample_workspace_size": (C.c_size_t, [C.c_int32, C.c_int64]),
     "pkv_sample": (C.c_int, [_T, C.c_float, C.c_uint64, _VP, _VP, C.c_size_t, _VP]),
+    "pkv_sample_dev": (C.c_int, [_T, C.c_float, C.c_uint64, _VP, _VP, _VP, C.c_size_t, _VP]),
+    "pkv_cache_update_kv_dev": (C.c_int, [_T, _T, _T, _T, _VP, C.c_int32, _VP, _VP]),
+    "pkv_paged_cache_update_kv_dev": (C.c_int, [_VP, _T, _T, _VP, _T, _T, _VP, C.c_int32, _VP, _VP]),
+    "pkv_advance": (C.c_int, [_VP, C.c_int32, C.c_int32, _VP, _VP]),
+    "pkv_decode_attention_dev": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_float, C.c_int32, _T, _VP, C.c_size_t,
+                                           C.c_int32, _VP, _VP]),
+    "pkv_paged_decode_attention_dev": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _VP, C.c_int32,
+                                                 C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP, _VP]),
 }
 
 for _name, (_res, _args) in _SIG.items():
@@ -152,7 +160,7 @@ for _name, (_res, _args) in _SIG.items():
         _fn.argtypes = _args
 
 
-ABI_VERSION = 5      # the argument lists above follow this version of include/pkv.h
+ABI_VERSION = 6      # the argument lists above follow this version of include/pkv.h
 if _lib.pkv_abi_version() != ABI_VERSION:
     raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
                       "rebuild it (python place_persistent_kv_amd/build.py)")
@@ -501,6 +509,60 @@ def sample(logits, temperature: float, seed: int, out_ids, workspace=None, strea
     _check(_lib.pkv_sample(C.byref(desc(logits)), float(temperature), C.c_uint64(seed & (2 ** 64 - 1)),
                            _ptr(out_ids), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
                            _stream(stream)), "pkv_sample")
+
+
+def sample_dev(logits, temperature: float, seed: int, step, out_ids, workspace=None, stream=None) -> None:
+    """``pkv_sample_dev``: the seed of the iteration held in the device int64 counter ``step``."""
+    _check(_lib.pkv_sample_dev(C.byref(desc(logits)), float(temperature), C.c_uint64(seed & (2 ** 64 - 1)),
+                               _ptr(step), _ptr(out_ids), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
+                               _stream(stream)), "pkv_sample_dev")
+
+
+# ---------------------------------------------------------------------------
+# Device-driven step: positions, lengths and the sampling step in device memory
+# ---------------------------------------------------------------------------
+def cache_update_kv_dev(k_cache, v_cache, k_values, v_values, position, update_length: int, status,
+                        stream=None) -> None:
+    """``pkv_cache_update_kv_dev``: K and V appended at the device positions ``position`` (int32 [B])."""
+    _check(_lib.pkv_cache_update_kv_dev(C.byref(desc(k_cache)), C.byref(desc(v_cache)), C.byref(desc(k_values)),
+                                        C.byref(desc(v_values)), _ptr(position), int(update_length), _ptr(status),
+                                        _stream(stream)), "pkv_cache_update_kv_dev")
+
+
+def paged_cache_update_kv_dev(pool: Pool, k_pool, v_pool, page_table, k_values, v_values, position,
+                              update_length: int, status, stream=None) -> None:
+    """``pkv_paged_cache_update_kv_dev``: the paged form."""
+    _check(_lib.pkv_paged_cache_update_kv_dev(_pool_handle(pool), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+                                              _ptr(page_table), C.byref(desc(k_values)), C.byref(desc(v_values)),
+                                              _ptr(position), int(update_length), _ptr(status), _stream(stream)),
+           "pkv_paged_cache_update_kv_dev")
+
+
+def advance(values, delta: int, step=None, stream=None, n: Optional[int] = None) -> None:
+    """``pkv_advance``: ``values[:n] += delta`` (device int32) and ``step += 1`` (device int64) when given."""
+    count = int(n) if n is not None else (values.numel() if values is not None else 0)
+    _check(_lib.pkv_advance(_ptr(values), count, int(delta), _ptr(step), _stream(stream)), "pkv_advance")
+
+
+def decode_attention_dev(q, k_cache, v_cache, valid_len, max_len: int, out, status, workspace=None,
+                         scale: float = 0.0, num_splits: int = 0, stream=None, left_window: int = -1) -> None:
+    """``pkv_decode_attention_dev``: valid lengths from the device int32 tensor ``valid_len``."""
+    _check(_lib.pkv_decode_attention_dev(C.byref(desc(q)), C.byref(desc(k_cache)), C.byref(desc(v_cache)),
+                                         _ptr(valid_len), int(max_len), float(scale), int(left_window),
+                                         C.byref(desc(out)), _ptr(workspace),
+                                         0 if workspace is None else _nbytes(workspace), int(num_splits),
+                                         _ptr(status), _stream(stream)), "pkv_decode_attention_dev")
+
+
+def paged_decode_attention_dev(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, block_size: int, valid_len,
+                               max_len: int, out, status, workspace=None, pool: Optional[Pool] = None,
+                               scale: float = 0.0, num_splits: int = 0, stream=None, left_window: int = -1) -> None:
+    """``pkv_paged_decode_attention_dev``: the paged form."""
+    _check(_lib.pkv_paged_decode_attention_dev(
+        C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)), _ptr(page_table), int(max_blocks_per_seq),
+        int(block_size), _pool_handle(pool), _ptr(valid_len), int(max_len), float(scale), int(left_window),
+        C.byref(desc(out)), _ptr(workspace), 0 if workspace is None else _nbytes(workspace), int(num_splits),
+        _ptr(status), _stream(stream)), "pkv_paged_decode_attention_dev")
 
 
 # ---------------------------------------------------------------------------

@@ -11,6 +11,8 @@
 
 #include "pkv_internal.h"
 
+#include <algorithm>
+
 namespace pkv {
 namespace {
 
@@ -49,6 +51,59 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedCopyArgs a, i
         const int32_t slot = p % a.bs;
         const V* src = reinterpret_cast<const V*>(a.src + r * a.row_bytes);
         V* dst = reinterpret_cast<V*>(a.pool + ((int64_t(page) * a.H + h) * a.bs + slot) * a.row_bytes);
+        dst[c] = src[c];
+    }
+}
+
+// K and V rows at positions held in device memory.  Every workgroup first
+// checks every row of the call (position in range; paged: the pages written
+// hold ids inside the pool), so either all rows are written or none; a
+// failing check sets *status.  Then thread i copies 16-byte vector c of row
+// (tensor, b, h, t).
+__global__ __launch_bounds__(kThreads) void kv_append_dev_kernel(KvAppendDevArgs a, int64_t total) {
+    __shared__ int s_bad;
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int b = threadIdx.x; b < a.B; b += kThreads) {
+        const int32_t p = a.pos[b];
+        if (p < 0 || p > a.cap - a.n) {
+            bad = 2;                                  // PKV_E_CAPACITY
+        } else if (a.page_table != nullptr && a.n > 0) {
+            for (int32_t pg = p / a.bs; pg <= (p + a.n - 1) / a.bs; ++pg) {
+                const int32_t id = a.page_table[int64_t(b) * a.maxb + pg];
+                if (uint32_t(id) >= uint32_t(a.nb)) bad = 6;   // PKV_E_PAGE
+            }
+        }
+    }
+    if (bad) atomicMax(&s_bad, bad);
+    __syncthreads();
+    if (s_bad) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = s_bad;
+        return;
+    }
+    const int64_t vec_per_row = a.row_bytes / 16;
+    const int64_t rows_per_tensor = int64_t(a.B) * a.H * a.n;
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kThreads) {
+        const int64_t r = i / vec_per_row;            // (tensor, b, h, t)
+        const int64_t c = i - r * vec_per_row;
+        const int which = r >= rows_per_tensor;
+        const int64_t rr = r - which * rows_per_tensor;
+        const int32_t t = static_cast<int32_t>(rr % a.n);
+        const int64_t bh = rr / a.n;
+        const int32_t h = static_cast<int32_t>(bh % a.H);
+        const int32_t b = static_cast<int32_t>(bh / a.H);
+        const int32_t p = a.pos[b] + t;
+        int64_t dst_row;
+        if (a.page_table != nullptr) {
+            const int32_t page = a.page_table[int64_t(b) * a.maxb + p / a.bs];
+            dst_row = (int64_t(page) * a.H + h) * a.bs + p % a.bs;
+        } else {
+            dst_row = (int64_t(b) * a.H + h) * a.cap + p;
+        }
+        const uint4* src = reinterpret_cast<const uint4*>(a.src[which] + rr * a.row_bytes);
+        uint4* dst = reinterpret_cast<uint4*>(a.dst[which] + dst_row * a.row_bytes);
         dst[c] = src[c];
     }
 }
@@ -126,6 +181,14 @@ dim3 grid_for(int64_t total) {
 }
 
 }  // namespace
+
+hipError_t launch_kv_append_dev(const KvAppendDevArgs& a, hipStream_t s) {
+    const int64_t total = 2 * int64_t(a.B) * a.H * a.n * (a.row_bytes / 16);
+    if (total <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 4096);
+    hipLaunchKernelGGL(kv_append_dev_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a, total);
+    return hipGetLastError();
+}
 
 hipError_t launch_copy_rows(const CopyRowsArgs& a, hipStream_t s) {
     const int vb = vec_bytes(a.row_bytes, a.src, a.dst);

@@ -42,6 +42,34 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kD = 128;
 constexpr float kLazy = 8.0f;  // rescale only when a score exceeds the running max by 2^8
+constexpr int32_t kStatusCapacity = 2;   // PKV_E_CAPACITY
+constexpr int32_t kStatusPage = 6;       // PKV_E_PAGE
+
+// The (row, split) a workgroup works on.  With host lengths the split table
+// of the launch gives it; with device lengths every row has S_max split slots
+// and its split count follows from its length (a uniform load), and a length
+// outside [1, len_limit] makes the row invalid.
+struct SplitWork {
+    int b, split, nsplit, L;
+    bool ok;
+};
+__device__ __forceinline__ SplitWork split_work(const DecodeArgs& a, int r) {
+    SplitWork w;
+    if (a.len_dev == nullptr) {
+        w.b = find_row(a.split_begin, a.rows, r);
+        w.split = r - a.split_begin[w.b];
+        w.nsplit = a.split_begin[w.b + 1] - a.split_begin[w.b];
+        w.L = a.len[w.b];
+        w.ok = true;
+        return w;
+    }
+    w.b = r / a.S_max;
+    w.split = r - w.b * a.S_max;
+    w.L = a.len_dev[a.row0 + w.b];
+    w.ok = w.L >= 1 && w.L <= a.len_limit;
+    w.nsplit = w.ok ? (w.L - split_base(w.L, a.window) + a.tps - 1) / a.tps : 0;
+    return w;
+}
 
 template <int G, bool PAGED, bool F16>   // F16: fp16 q/K/V (else bf16)
 __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
@@ -62,11 +90,13 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
 
     const int work = blockIdx.x;
     const int kvh = work % a.Hkv;
-    const int r = work / a.Hkv;
-    const int b = find_row(a.split_begin, a.rows, r);
-    const int split = r - a.split_begin[b];
-    const int nsplit = a.split_begin[b + 1] - a.split_begin[b];
-    const int L = a.len[b];
+    const SplitWork sw = split_work(a, work / a.Hkv);
+    if (!sw.ok) {
+        if (sw.split == 0 && kvh == 0 && threadIdx.x == 0) *a.status = kStatusCapacity;
+        return;
+    }
+    if (sw.split >= sw.nsplit) return;
+    const int b = sw.b, split = sw.split, nsplit = sw.nsplit, L = sw.L;
     const int vis0 = visible_begin(L, a.window);   // first key the query sees
     const int t0 = split_base(L, a.window) + split * a.tps;
     const int t1 = min(L, t0 + a.tps);
@@ -101,9 +131,15 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     // Element offset of the first row of the 16-token step at ts (wave-uniform):
     // ts is a multiple of 16 and block_size a power-of-two multiple of 16, so
     // the whole step lies in one page.
+    // With device lengths a page id outside the pool is replaced by page 0
+    // (the reads stay inside the pool) and reported through *status.
     auto step_base = [&](int ts) -> int64_t {
         if constexpr (PAGED) {
-            const int page = pt[ts >> a.log2bs];
+            int page = pt[ts >> a.log2bs];
+            if (a.status != nullptr && uint32_t(page) >= uint32_t(a.nb)) {
+                if (threadIdx.x % 64 == 0) *a.status = kStatusPage;
+                page = 0;
+            }
             return ((int64_t(page) * a.Hkv + kvh) * a.bs + (ts & (a.bs - 1))) * kD;
         } else {
             return ((int64_t(b) * a.Hkv + kvh) * a.cap + ts) * kD;
@@ -297,10 +333,13 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int work = blockIdx.x;
     const int h = work % a.Hq;
-    const int r = work / a.Hq;
-    const int b = find_row(a.split_begin, a.rows, r);
-    const int split = r - a.split_begin[b];
-    const int L = a.len[b];
+    const SplitWork sw = split_work(a, work / a.Hq);
+    if (!sw.ok) {
+        if (sw.split == 0 && h == 0 && lane == 0) *a.status = kStatusCapacity;
+        return;
+    }
+    if (sw.split >= sw.nsplit) return;
+    const int b = sw.b, split = sw.split, L = sw.L;
     const int t0 = split_base(L, a.window) + split * a.tps;
     const int ta = max(t0, visible_begin(L, a.window));   // first visible token of the split
     const int t1 = min(L, t0 + a.tps);
@@ -311,19 +350,22 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     const T* K = static_cast<const T*>(a.k);
     const T* V = static_cast<const T*>(a.v);
 
-    auto row = [&](int t) -> int64_t {  // element offset of token t's row
-        if (a.page_table) {
-            const int page = a.page_table[int64_t(b) * a.maxb + t / a.bs];
-            return ((int64_t(page) * a.Hkv + kvh) * a.bs + t % a.bs) * D;
+    // with device lengths a page id outside the pool reads page 0 and sets *status
+    auto page_of = [&](int t) -> int {
+        int page = a.page_table[int64_t(b) * a.maxb + t / a.bs];
+        if (a.status != nullptr && uint32_t(page) >= uint32_t(a.nb)) {
+            *a.status = kStatusPage;
+            page = 0;
         }
+        return page;
+    };
+    auto row = [&](int t) -> int64_t {  // element offset of token t's row
+        if (a.page_table) return ((int64_t(page_of(t)) * a.Hkv + kvh) * a.bs + t % a.bs) * D;
         return ((int64_t(b) * a.Hkv + kvh) * a.cap + t) * D;
     };
     const int Dv = a.Dv;
     auto vrow = [&](int t) -> int64_t {  // element offset of token t's value row
-        if (a.page_table) {
-            const int page = a.page_table[int64_t(b) * a.maxb + t / a.bs];
-            return ((int64_t(page) * a.Hkv + kvh) * a.bs + t % a.bs) * Dv;
-        }
+        if (a.page_table) return ((int64_t(page_of(t)) * a.Hkv + kvh) * a.bs + t % a.bs) * Dv;
         return ((int64_t(b) * a.Hkv + kvh) * a.cap + t) * Dv;
     };
 
@@ -383,7 +425,14 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     __shared__ float s_w[kMergeLdsSplits];
     const int bh = blockIdx.x;
     const int b = bh / a.Hq;
-    const int n = a.nsplit[b];
+    int n;
+    if (a.len_dev != nullptr) {          // device lengths: the split count follows from the length
+        const int L = a.len_dev[a.row0 + b];
+        if (L < 1 || L > a.len_limit) return;
+        n = (L - split_base(L, a.window) + a.tps - 1) / a.tps;
+    } else {
+        n = a.nsplit[b];
+    }
     if (n < a.min_splits) return;
     const int lane = threadIdx.x;
     const int64_t gbh = int64_t(b) * a.Hq + (bh % a.Hq);

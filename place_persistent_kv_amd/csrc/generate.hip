@@ -7,7 +7,9 @@
 // the sampled id, or the pad token when the row had already finished; the
 // row finishes when the written token is EOS; the written token is also the
 // row's next input.  The rows still running are counted so that the host can
-// stop the loop.  One workgroup; B is small next to one decode step.
+// stop the loop.  One workgroup; B is small next to one decode step.  A
+// second kernel advances device-held positions and the step counter of a
+// captured decode step.
 
 #include "pkv_internal.h"
 
@@ -39,7 +41,21 @@ __global__ __launch_bounds__(kGenThreads) void generate_finish_kernel(GenerateAr
     }
 }
 
+// Positions or lengths held on the device move on by `delta` and the step
+// counter by one, so that a captured decode step can be replayed as is.
+__global__ __launch_bounds__(kGenThreads) void advance_kernel(AdvanceArgs a) {
+    for (int i = blockIdx.x * kGenThreads + threadIdx.x; i < a.n; i += gridDim.x * kGenThreads)
+        a.values[i] += a.delta;
+    if (a.step != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.step += 1;
+}
+
 }  // namespace
+
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s) {
+    const int blocks = a.n > 0 ? (a.n + kGenThreads - 1) / kGenThreads : 1;
+    hipLaunchKernelGGL(advance_kernel, dim3(blocks < 64 ? blocks : 64), dim3(kGenThreads), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_generate_finish(const GenerateArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(generate_finish_kernel, dim3(1), dim3(kGenThreads), 0, s, a);

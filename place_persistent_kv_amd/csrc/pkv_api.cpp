@@ -499,6 +499,112 @@ pkv_status pkv_paged_cache_update(const pkv_pool* pool, const pkv_tensor* pool_k
     return ok();
 }
 
+namespace {
+
+// K and V appended in one launch at positions held in device memory (the
+// contiguous form when page_table is null).
+pkv_status kv_append_dev(const char* who, const pkv_pool* pool, const pkv_tensor* k_dst,
+                         const pkv_tensor* v_dst, const int32_t* page_table_dev, const pkv_tensor* k_values,
+                         const pkv_tensor* v_values, const int32_t* position_dev, int32_t update_length,
+                         int32_t* status_dev, void* stream, bool paged) {
+    PKV_TRY(check_tensor(k_dst, "k", 4, 4));
+    PKV_TRY(check_tensor(v_dst, "v", 4, 4));
+    PKV_TRY(check_tensor(k_values, "k_values", 4, 4));
+    PKV_TRY(check_tensor(v_values, "v_values", 4, 4));
+    if (update_length < 0 || update_length > kMaxDevAppend)
+        return fail(PKV_E_ARG, "%s: update_length must be in [0, %d]", who, kMaxDevAppend);
+    if (!position_dev || !status_dev) return fail(PKV_E_ARG, "%s: null position or status", who);
+    for (int i = 0; i < 4; ++i)
+        if (k_dst->shape[i] != v_dst->shape[i]) return fail(PKV_E_LAYOUT, "%s: K and V storage shapes differ", who);
+    if (k_dst->dtype != v_dst->dtype || k_values->dtype != k_dst->dtype || v_values->dtype != k_dst->dtype)
+        return fail(PKV_E_DTYPE, "%s: values and storage must share one dtype", who);
+    const int64_t H = k_dst->shape[1], D = k_dst->shape[3];
+    const int64_t B = k_values->shape[0];
+    for (const pkv_tensor* t : {k_values, v_values})
+        if (t->shape[0] != B || t->shape[1] != H || t->shape[2] != update_length || t->shape[3] != D)
+            return fail(PKV_E_LAYOUT, "%s: values must be [B, H, update_length, D] of the storage", who);
+    const int64_t row_bytes = D * dtype_size(k_dst->dtype);
+    if (row_bytes % 16) return fail(PKV_E_LAYOUT, "%s: a row must be a multiple of 16 bytes", who);
+    for (const pkv_tensor* t : {k_dst, v_dst, k_values, v_values})
+        if (reinterpret_cast<uintptr_t>(t->data) % 16) return fail(PKV_E_LAYOUT, "%s: tensors must be 16-byte aligned", who);
+    int64_t cap;
+    if (paged) {
+        if (!pool) return fail(PKV_E_ARG, "%s: a pool handle is required", who);
+        if (k_dst->shape[0] != pool->num_blocks || k_dst->shape[2] != pool->block_size)
+            return fail(PKV_E_LAYOUT, "%s: pools do not match the pool handle", who);
+        if (B > pool->max_seqs) return fail(PKV_E_PAGE, "%s: batch larger than the pool's max_seqs", who);
+        if (!page_table_dev && B > 0) return fail(PKV_E_ARG, "%s: null page table", who);
+        cap = int64_t(pool->maxb) * pool->block_size;
+    } else {
+        if (k_dst->shape[0] != B) return fail(PKV_E_LAYOUT, "%s: cache batch != values batch", who);
+        cap = k_dst->shape[2];
+    }
+    if (cap > INT32_MAX) return fail(PKV_E_LAYOUT, "%s: capacity too large", who);
+    PKV_TRY(check_writable(k_dst, "k"));
+    PKV_TRY(check_writable(v_dst, "v"));
+    if (overlap(span(k_dst), span(v_dst))) return fail(PKV_E_ALIAS, "%s: K and V storage overlap", who);
+    for (const pkv_tensor* t : {k_values, v_values}) {
+        PKV_TRY(check_disjoint(t, "values", span(k_dst), "k"));
+        PKV_TRY(check_disjoint(t, "values", span(v_dst), "v"));
+    }
+    const Span st = span(status_dev, 4), ps = span(position_dev, B * 4);
+    if (overlap(st, span(k_dst)) || overlap(st, span(v_dst)) || overlap(ps, span(k_dst)) || overlap(ps, span(v_dst)))
+        return fail(PKV_E_ALIAS, "%s: position and status must not overlap the storage", who);
+    if (B == 0 || update_length == 0 || H == 0) return ok();
+    KvAppendDevArgs a;
+    a.src[0] = static_cast<const uint8_t*>(k_values->data);
+    a.src[1] = static_cast<const uint8_t*>(v_values->data);
+    a.dst[0] = static_cast<uint8_t*>(k_dst->data);
+    a.dst[1] = static_cast<uint8_t*>(v_dst->data);
+    a.page_table = paged ? page_table_dev : nullptr;
+    a.pos = position_dev;
+    a.status = status_dev;
+    a.row_bytes = row_bytes;
+    a.B = static_cast<int32_t>(B);
+    a.H = static_cast<int32_t>(H);
+    a.n = update_length;
+    a.cap = static_cast<int32_t>(cap);
+    a.bs = paged ? pool->block_size : 0;
+    a.maxb = paged ? pool->maxb : 0;
+    a.nb = paged ? pool->num_blocks : 0;
+    PKV_HIP(launch_kv_append_dev(a, static_cast<hipStream_t>(stream)), "kv append launch");
+    return ok();
+}
+
+}  // namespace
+
+pkv_status pkv_cache_update_kv_dev(const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                                   const pkv_tensor* k_values, const pkv_tensor* v_values,
+                                   const int32_t* position_dev, int32_t update_length, int32_t* status_dev,
+                                   void* stream) {
+    return kv_append_dev("cache_update_kv_dev", nullptr, k_cache, v_cache, nullptr, k_values, v_values,
+                         position_dev, update_length, status_dev, stream, false);
+}
+
+pkv_status pkv_paged_cache_update_kv_dev(const pkv_pool* pool, const pkv_tensor* k_pool,
+                                         const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                         const pkv_tensor* k_values, const pkv_tensor* v_values,
+                                         const int32_t* position_dev, int32_t update_length,
+                                         int32_t* status_dev, void* stream) {
+    return kv_append_dev("paged_cache_update_kv_dev", pool, k_pool, v_pool, page_table_dev, k_values, v_values,
+                         position_dev, update_length, status_dev, stream, true);
+}
+
+pkv_status pkv_advance(int32_t* values_dev, int32_t n, int32_t delta, int64_t* step_dev, void* stream) {
+    if (n < 0) return fail(PKV_E_ARG, "advance: negative count");
+    if (n > 0 && !values_dev) return fail(PKV_E_ARG, "advance: null values");
+    if (values_dev && step_dev && overlap(span(values_dev, int64_t(n) * 4), span(step_dev, 8)))
+        return fail(PKV_E_ALIAS, "advance: values overlap the step counter");
+    if (n == 0 && !step_dev) return ok();
+    AdvanceArgs a;
+    a.values = values_dev;
+    a.step = step_dev;
+    a.n = n;
+    a.delta = delta;
+    PKV_HIP(launch_advance(a, static_cast<hipStream_t>(stream)), "advance launch");
+    return ok();
+}
+
 pkv_status pkv_paged_cache_update_int4(const pkv_pool* pool, const pkv_tensor* codes_pool,
                                        const pkv_tensor* params_pool,
                                        const int32_t* page_table_dev, const pkv_tensor* values,
@@ -653,7 +759,9 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
                          const pkv_pool* pool, const int32_t* valid_len, float scale,
                          int32_t left_window, pkv_tensor* out, void* ws, size_t ws_bytes,
                          int32_t num_splits, void* stream, const pkv_tensor* page_desc = nullptr,
-                         bool static_ws = false) {
+                         bool static_ws = false, const int32_t* len_dev = nullptr, int32_t max_len = 0,
+                         int32_t* status = nullptr) {
+    const bool dev = len_dev != nullptr;   // valid lengths in device memory, bounded by max_len
     const bool mixed = page_desc != nullptr;
     QView qv;
     PKV_TRY(check_tensor(k, "k", 4, 4));
@@ -694,8 +802,15 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         if (k->shape[0] != B) return fail(PKV_E_LAYOUT, "cache batch %lld != q batch %lld", (long long)k->shape[0], (long long)B);
         cap = k->shape[2];
     }
-    if (B > 0 && !valid_len) return fail(PKV_E_ARG, "null valid_len");
-    for (int64_t b = 0; b < B; ++b) {
+    if (dev) {
+        if (!status) return fail(PKV_E_ARG, "null status");
+        if (max_len < 1 || max_len > cap)
+            return fail(PKV_E_CAPACITY, "max_len %d not in [1, %lld]", max_len, (long long)cap);
+        if (overlap(span(status, 4), span(out)) || overlap(span(len_dev, B * 4), span(out)))
+            return fail(PKV_E_ALIAS, "status and valid_len must not overlap out");
+    }
+    if (B > 0 && !valid_len && !dev) return fail(PKV_E_ARG, "null valid_len");
+    for (int64_t b = 0; b < B && !dev; ++b) {
         if (valid_len[b] < 1 || valid_len[b] > cap)
             return fail(PKV_E_CAPACITY, "row %lld: valid_len %d not in [1, %lld]", (long long)b, valid_len[b], (long long)cap);
         if (paged && pool && ceil_div(valid_len[b], bs) > pool->held[b])
@@ -725,8 +840,12 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
     const bool fast = mixed || (Dv == D && fast_decode_supported(kind, static_cast<int>(D), G, paged, bs));
     // size the workspace for the whole call (all row groups share it)
     // splits cover only each row's visible range (from its 64-token quantum on)
+    // (device lengths: every row planned at the bound max_len)
     std::vector<int32_t> span_len(B);
-    for (int64_t b = 0; b < B; ++b) span_len[b] = valid_len[b] - split_base(valid_len[b], left_window);
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t L = dev ? max_len : valid_len[b];
+        span_len[b] = L - split_base(L, left_window);
+    }
     Plan full = plan_splits(span_len.data(), static_cast<int>(B), fast ? static_cast<int>(Hkv) : static_cast<int>(Hq),
                             num_splits, fast ? 0 : kGenericMaxTps);
     const size_t need = ws_bytes_for(B, Hq, Dv, full.S_max);
@@ -789,13 +908,22 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         a.page_desc = mixed ? page_desc->data : nullptr;
         int total = 0;
         bool any_split = false;
-        for (int i = 0; i < rows; ++i) {
-            a.len[i] = valid_len[b0 + i];
-            a.split_begin[i] = total;
-            total += full.nsplit[b0 + i];
-            any_split |= full.nsplit[b0 + i] > 1;
+        if (dev) {   // S_max split slots per row; the kernels read the lengths
+            a.len_dev = len_dev;
+            a.len_limit = max_len;
+            a.nb = paged ? static_cast<int32_t>(k->shape[0]) : 0;
+            a.status = status;
+            total = rows * full.S_max;
+            any_split = full.S_max > 1;
+        } else {
+            for (int i = 0; i < rows; ++i) {
+                a.len[i] = valid_len[b0 + i];
+                a.split_begin[i] = total;
+                total += full.nsplit[b0 + i];
+                any_split |= full.nsplit[b0 + i] > 1;
+            }
+            a.split_begin[rows] = total;
         }
-        a.split_begin[rows] = total;
         if (mixed) {
             PKV_HIP(launch_decode_mixed(a, G, total * static_cast<int>(Hkv), s), "mixed decode launch");
         } else if (fast) {
@@ -815,7 +943,14 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
             m.row0 = a.row0;
             m.rows = rows;
             m.min_splits = fast ? 2 : 1;  // the fast kernel finishes single-split rows itself
-            for (int i = 0; i < rows; ++i) m.nsplit[i] = full.nsplit[b0 + i];
+            if (dev) {
+                m.len_dev = len_dev;
+                m.len_limit = max_len;
+                m.tps = full.tps;
+                m.window = left_window;
+            } else {
+                for (int i = 0; i < rows; ++i) m.nsplit[i] = full.nsplit[b0 + i];
+            }
             PKV_HIP(launch_merge(m, s), "merge launch");
         }
     }
@@ -855,6 +990,30 @@ pkv_status pkv_paged_decode_attention_noalloc(const pkv_tensor* q, const pkv_ten
     return decode_common(q, k_pool, v_pool, true, page_table_dev, max_blocks_per_seq, block_size, pool,
                          valid_len, scale, left_window, out, nullptr, kNoallocScratchBytes, num_splits, stream,
                          nullptr, true);
+}
+
+pkv_status pkv_decode_attention_dev(const pkv_tensor* q, const pkv_tensor* k_cache,
+                                    const pkv_tensor* v_cache, const int32_t* valid_len_dev,
+                                    int32_t max_len, float scale, int32_t left_window, pkv_tensor* out,
+                                    void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                    int32_t* status_dev, void* stream) {
+    if (!valid_len_dev) return fail(PKV_E_ARG, "decode_attention_dev: null valid_len");
+    return decode_common(q, k_cache, v_cache, false, nullptr, 0, 0, nullptr, nullptr, scale, left_window, out,
+                         workspace, workspace_bytes, num_splits, stream, nullptr, false, valid_len_dev, max_len,
+                         status_dev);
+}
+
+pkv_status pkv_paged_decode_attention_dev(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                          const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                          int32_t max_blocks_per_seq, int32_t block_size,
+                                          const pkv_pool* pool, const int32_t* valid_len_dev,
+                                          int32_t max_len, float scale, int32_t left_window,
+                                          pkv_tensor* out, void* workspace, size_t workspace_bytes,
+                                          int32_t num_splits, int32_t* status_dev, void* stream) {
+    if (!valid_len_dev) return fail(PKV_E_ARG, "paged_decode_attention_dev: null valid_len");
+    return decode_common(q, k_pool, v_pool, true, page_table_dev, max_blocks_per_seq, block_size, pool, nullptr,
+                         scale, left_window, out, workspace, workspace_bytes, num_splits, stream, nullptr, false,
+                         valid_len_dev, max_len, status_dev);
 }
 
 pkv_status pkv_paged_decode_attention_mixed(const pkv_tensor* q, const pkv_tensor* k_pool,
@@ -1295,6 +1454,11 @@ size_t pkv_sample_workspace_size(int32_t B, int64_t V) {
 
 pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed,
                       int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream) {
+    return pkv_sample_dev(logits, temperature, seed, nullptr, out_ids, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_sample_dev(const pkv_tensor* logits, float temperature, uint64_t seed, const int64_t* step_dev,
+                          int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream) {
     PKV_TRY(check_tensor(logits, "logits", 2, 3));
     const int kind = logits->dtype == PKV_F64 ? kKvF64 : kv_kind_of(logits->dtype);
     if (kind < 0) return fail(PKV_E_DTYPE, "sample: logits must be f32, f64, bf16 or f16");
@@ -1330,6 +1494,9 @@ pkv_status pkv_sample(const pkv_tensor* logits, float temperature, uint64_t seed
     a.part_val = static_cast<double*>(workspace);
     a.part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ((n * 8 + 255) & ~size_t(255)));
     a.out = out_ids;
+    a.step = step_dev;
+    if (step_dev && (overlap(span(step_dev, 8), wss) || overlap(span(step_dev, 8), span(out_ids, B * 8))))
+        return fail(PKV_E_ALIAS, "sample: the step counter overlaps the workspace or out_ids");
     PKV_HIP(launch_sample(a, static_cast<hipStream_t>(stream)), "sample launch");
     return ok();
 }

@@ -62,6 +62,24 @@ struct GatherArgs {              // out[h, p, :] = pool[pt[seq][p/bs], h, p%bs, 
     int32_t H, bs, length;
 };
 
+// K and V appended by one launch at positions read from device memory (a
+// captured step replays with the positions the device holds at replay time).
+// Every workgroup first checks every row of the call; if any fails, nothing
+// is written and *status receives the error.
+struct KvAppendDevArgs {
+    const uint8_t* src[2];       // K, V values [B, H, n, row_bytes]
+    uint8_t* dst[2];             // contiguous caches [B, H, cap, row_bytes] or pools [NB, H, bs, row_bytes]
+    const int32_t* page_table;   // [B, maxb] (nullptr: contiguous)
+    const int32_t* pos;          // device int32[B]
+    int32_t* status;             // device status word (sticky)
+    int64_t row_bytes;
+    int32_t B, H, n;
+    int32_t cap;                 // contiguous capacity, or maxb * bs
+    int32_t bs, maxb, nb;        // paged geometry (nb = pool blocks)
+};
+hipError_t launch_kv_append_dev(const KvAppendDevArgs& a, hipStream_t s);
+constexpr int kMaxDevAppend = 64;   // tokens per device-position append (a decode step's few tokens)
+
 hipError_t launch_copy_rows(const CopyRowsArgs& a, hipStream_t s);
 hipError_t launch_paged_copy(const PagedCopyArgs& a, hipStream_t s);
 hipError_t launch_paged_int4_append(const PagedInt4Args& a, hipStream_t s);
@@ -94,6 +112,14 @@ struct DecodeArgs {
     int32_t window;              // left window (-1 = unbounded), see visible_begin
     float scale_log2;            // softmax scale * log2(e)
     const void* page_desc;       // mixed-format pages: PageDesc[NB] (else nullptr)
+    // Device lengths (else nullptr): row row0 + i has length len_dev[row0 + i],
+    // S_max split slots, splits past its own count exit at once; rows whose
+    // length is outside [1, len_limit] and rows that meet a page id outside
+    // [0, nb) set *status and write nothing.  len[] and split_begin[] unused.
+    const int32_t* len_dev = nullptr;
+    int32_t len_limit = 0;
+    int32_t nb = 0;
+    int32_t* status = nullptr;
     int32_t len[kMaxRows];       // valid length per row
     int32_t split_begin[kMaxRows + 1];  // prefix sum of splits per row
 };
@@ -123,6 +149,10 @@ struct MergeArgs {
     int32_t out_kind;            // KvKind of out
     int32_t Hq, D, S_max, row0, rows;
     int32_t min_splits;          // rows with fewer partials were finished by the attention kernel
+    // device lengths (else nullptr): the split count of a row comes from its
+    // length as in DecodeArgs; invalid rows are skipped
+    const int32_t* len_dev = nullptr;
+    int32_t len_limit = 0, tps = 0, window = -1;
     int32_t nsplit[kMaxRows];
 };
 
@@ -239,6 +269,13 @@ struct GenerateArgs {
 };
 hipError_t launch_generate_finish(const GenerateArgs& a, hipStream_t s);
 
+struct AdvanceArgs {             // values[i] += delta for i < n; ++*step
+    int32_t* values;
+    int64_t* step;
+    int32_t n, delta;
+};
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Sampling
 // ---------------------------------------------------------------------------
@@ -254,6 +291,7 @@ struct SampleArgs {
     float inv_t;                 // fl32(1 / T): float32, bf16 and f16 logits
     double inv_t64;              // 1 / T in float64: float64 logits
     uint64_t seed;
+    const int64_t* step = nullptr;   // device step counter: seed + step * B * V * gamma
     double* part_val;            // [B, chunks] best score per chunk (float32 scores widened)
     int32_t* part_idx;           // [B, chunks]
     int64_t* out;                // [B]

@@ -150,8 +150,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs
                         : (tail + threadIdx.x < end ? tail + threadIdx.x : int64_t(INT32_MAX));
     S best = -INFINITY;
     int32_t bidx = static_cast<int32_t>(first);
-    // state of logit v: seed + (b * V + v + 1) * gamma
-    const uint64_t state0 = a.seed + (uint64_t(b) * uint64_t(a.V) + 1ull) * kGamma;
+    // state of logit v: seed + (b * V + v + 1) * gamma; with a device step
+    // counter the seed is that of iteration *step (seed + step * B * V * gamma)
+    uint64_t seed = a.seed;
+    if (a.step != nullptr) seed += uint64_t(*a.step) * uint64_t(a.B) * uint64_t(a.V) * kGamma;
+    const uint64_t state0 = seed + (uint64_t(b) * uint64_t(a.V) + 1ull) * kGamma;
     auto consider = [&](S x, int64_t v, uint64_t state) {
         const S s = GREEDY ? x : gumbel_score(x, a, state);
         if (above(s, best)) {

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if getattr(pkv._lib, n, None) is None]
     assert not missing, missing
     assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
-    assert pkv.abi_version() == pkv.ABI_VERSION == 5
+    assert pkv.abi_version() == pkv.ABI_VERSION == 6
 
 
 def R(ptr, dtype, shape):
@@ -478,3 +478,50 @@ def test_noalloc_decode_validates_before_any_hip_call():
     assert status_of(pkv.paged_decode_attention_noalloc, q, kp, vp, table, maxb, 8, lens, out) == pkv.E_LAYOUT
     assert status_of(pkv.paged_decode_attention_noalloc, R(FAKE, pkv.F16, [B, Hq, D]), kp, vp, table, maxb, bs,
                      lens, out) == pkv.E_DTYPE
+
+
+# --------------------------------------------------------------------------- device-driven step
+def test_device_step_entry_points_validate_host_arguments():
+    """Shapes, dtypes, bounds, bindings and aliasing of the *_dev calls are checked on the host."""
+    B, H, cap, D = 2, 2, 64, 128
+    kc = R(FAKE, pkv.BF16, [B, H, cap, D])
+    vc = R(FAKE + (1 << 24), pkv.BF16, [B, H, cap, D])
+    kv = R(FAKE + (2 << 24), pkv.BF16, [B, H, 1, D])
+    vv = R(FAKE + (3 << 24), pkv.BF16, [B, H, 1, D])
+    pos, st = FAKE + (4 << 24), FAKE + (5 << 24)
+    f = pkv.cache_update_kv_dev
+    with pkv.bind_writable(kc), pkv.bind_writable(vc):
+        assert status_of(f, kc, vc, kv, vv, pos, 1, None) == pkv.E_ARG                    # status required
+        assert status_of(f, kc, vc, kv, vv, None, 1, st) == pkv.E_ARG                     # position required
+        assert status_of(f, kc, vc, R(kv.ptr, pkv.BF16, [B, H, 65, D]), R(vv.ptr, pkv.BF16, [B, H, 65, D]),
+                         pos, 65, st) == pkv.E_ARG                                        # at most 64 tokens
+        assert status_of(f, kc, vc, kv, R(vv.ptr, pkv.F16, vv.shape), pos, 1, st) == pkv.E_DTYPE
+        assert status_of(f, kc, R(vc.ptr, pkv.BF16, [B, H, cap - 1, D]), kv, vv, pos, 1, st) == pkv.E_LAYOUT
+        assert status_of(f, kc, vc, R(kv.ptr + 2, pkv.BF16, kv.shape), vv, pos, 1, st) == pkv.E_LAYOUT
+        assert status_of(f, kc, vc, kv, vv, kc.ptr + 64, 1, st) == pkv.E_ALIAS            # position inside the cache
+        assert status_of(f, kc, vc, R(kc.ptr, pkv.BF16, kv.shape), vv, pos, 1, st) == pkv.E_ALIAS
+    assert status_of(f, kc, vc, kv, vv, pos, 1, st) == pkv.E_READONLY                     # no writable binding
+    # paged: a pool handle matching the pools
+    kp = R(FAKE, pkv.BF16, [32, H, 16, D])
+    vp = R(FAKE + (1 << 24), pkv.BF16, [32, H, 16, D])
+    with pkv.bind_writable(kp), pkv.bind_writable(vp):
+        pool = pkv.Pool(32, 16, B, 4)
+        assert status_of(pkv.paged_cache_update_kv_dev, None, kp, vp, FAKE + (6 << 24), kv, vv, pos, 1, st) \
+            == pkv.E_ARG
+        assert status_of(pkv.paged_cache_update_kv_dev, pkv.Pool(16, 16, B, 4), kp, vp, FAKE + (6 << 24), kv, vv,
+                         pos, 1, st) == pkv.E_LAYOUT
+    # attention: max_len within the capacity, status required
+    q = R(FAKE + (7 << 24), pkv.BF16, [B, 4, D])
+    out = R(FAKE + (8 << 24), pkv.BF16, [B, 4, D])
+    ws = R(FAKE + (9 << 24), pkv.U8, [1 << 20])
+    g = pkv.decode_attention_dev
+    assert status_of(g, q, kc, vc, pos, cap + 1, out, st, ws) == pkv.E_CAPACITY
+    assert status_of(g, q, kc, vc, pos, 0, out, st, ws) == pkv.E_CAPACITY
+    assert status_of(g, q, kc, vc, pos, cap, out, None, ws) == pkv.E_ARG
+    assert status_of(g, q, kc, vc, None, cap, out, st, ws) == pkv.E_ARG
+    assert status_of(g, q, kc, vc, pos, cap, out, out.ptr, ws) == pkv.E_ALIAS
+    assert status_of(pkv.paged_decode_attention_dev, q, kp, vp, FAKE + (6 << 24), 4, 16, pos, 65, out, st, ws) \
+        == pkv.E_CAPACITY
+    assert status_of(pkv.advance, None, 1, n=1) == pkv.E_ARG
+    assert status_of(pkv.sample_dev, R(FAKE, pkv.F32, [2, 100]), 0.5, 0, FAKE + 512,
+                     FAKE + (1 << 24), R(FAKE + 256, pkv.U8, [1 << 16])) == pkv.E_ALIAS
