@@ -126,9 +126,36 @@ def run_gpu(steps: int, warmup: int, profile_copy: bool):
         if ev:
             ev[3].record(stream)
 
+    # the same step as a captured HIP graph on the device-driven entry points: one fused K+V append at the
+    # device positions, attention over the device lengths, a draw seeded from the device step counter
+    pos_dev = torch.full((B,), CTX - 1, dtype=torch.int32, device=dev)
+    len_dev = torch.full((B,), CTX, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    step_ctr = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def step_dev():
+        pkv.paged_cache_update_kv_dev(pool, k_pool, v_pool, table, new_k, new_v, pos_dev, 1, status)
+        pkv.paged_decode_attention_dev(q, k_pool, v_pool, table, maxb, BS, len_dev, CTX, out, status, ws, pool=pool)
+        pkv.sample_dev(logits, TEMPERATURE, 1000, step_ctr, ids, sws)
+        pkv.advance(None, 0, step_ctr)
+
     for i in range(warmup):
         step(i, None)
     torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step_dev()
+    for i in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / steps
+    assert int(status.item()) == 0
     free_before = torch.cuda.mem_get_info()[0]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -148,6 +175,7 @@ def run_gpu(steps: int, warmup: int, profile_copy: bool):
         "update_us": acc[0] / steps * 1e3,
         "attn_us": acc[1] / steps * 1e3,
         "sample_us": acc[2] / steps * 1e3,
+        "graph_step_us": graph_ms * 1e3,
         "device_bytes_allocated_during_steps": int(max(alloc_delta, 0)),
     }
 
@@ -469,6 +497,22 @@ def bench_contig(steps, warmup, cpu):
     us_step = _timed(step, steps, warmup, stream)
     us_attn = _timed(attn_only, steps, warmup, stream)
     us_warm = _timed(lambda i: attn_only(i, False), steps, warmup, stream)
+    # captured step per replica: fused K+V append at the replica's device lengths, lengths + 1, attention
+    lens = [torch.from_numpy(L0.astype(np.int32)).to(dev) for _ in range(R)]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    graphs = []
+    for r in range(R):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            pkv.cache_update_kv_dev(kc[r], vc[r], nk, nv, lens[r], 1, status)
+            pkv.advance(lens[r], 1)
+            pkv.decode_attention_dev(q, kc[r], vc[r], lens[r], cap, out, status, ws)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    for r in range(R):
+        lens[r].copy_(torch.from_numpy(L0.astype(np.int32)))
+    us_graph = _timed(lambda i: graphs[i % R].replay(), steps, min(warmup, R), stream)
+    assert int(status.item()) == 0
     for bnd in binds:
         bnd.close()
     mean_L = float(np.mean(L0 + (np.arange(steps) % S)[:, None] + 1))
@@ -478,7 +522,8 @@ def bench_contig(steps, warmup, cpu):
                  us_step, "bf16", {"workload": "contig", "batch": Bc, "capacity": cap, "q_heads": Hq, "kv_heads": Hkv,
                                    "head_dim": Dc, "replicas_rotated": R},
                  _hbm_roofline(nbytes, us_attn), cpu_res, attn_us=round(us_attn, 2),
-                 attn_us_warm=round(us_warm, 2), attn_algorithmic_bytes=nbytes)
+                 attn_us_warm=round(us_warm, 2), attn_algorithmic_bytes=nbytes,
+                 graph_step_us=round(us_graph, 2), graph_tokens_per_s=round(Bc / (us_graph * 1e-6), 1))
 
 
 def bench_paged(steps, warmup, cpu):
@@ -640,6 +685,22 @@ def bench_qwen_decode(steps, warmup, cpu, layers=28):
     us_step = _timed(step, steps, warmup, stream)
     us_attn = _timed(lambda i: pkv.paged_decode_attention(q, ks[i % layers], vs[i % layers], table, maxb, bs, lens,
                                                           out, ws, pool=pool), steps * 4, warmup, stream)
+    # the 28-layer step as one captured graph on the device-driven calls (positions and lengths on the device;
+    # they stay at the same token, as the eager step's do).  Device lengths are planned from their bound (the
+    # longest row), so the split count is given: the number the host plan gives the longest rows.
+    graph_splits = -(-int(L.max()) // max(384, -(-(-(-int(L.sum()) * Hkv // 1024)) // 64) * 64))
+    pos_dev = torch.from_numpy((L - 1).astype(np.int32)).to(dev)
+    len_dev = torch.from_numpy(L.astype(np.int32)).to(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for layer in range(layers):
+            pkv.paged_cache_update_kv_dev(pool, ks[layer], vs[layer], table, nk, nk, pos_dev, 1, status)
+            pkv.paged_decode_attention_dev(q, ks[layer], vs[layer], table, maxb, bs, len_dev, int(L.max()), out,
+                                           status, ws, pool=pool, num_splits=graph_splits)
+    torch.cuda.synchronize()
+    us_graph = _timed(lambda i: gr.replay(), steps, warmup, stream)
+    assert int(status.item()) == 0
     for bnd in binds:
         bnd.close()
     nbytes = int(L.sum() * Hkv * Dq * 4 + sum(-(-int(x) // bs) for x in L) * 4 + Bq * Hq * Dq * 4)
@@ -649,7 +710,8 @@ def bench_qwen_decode(steps, warmup, cpu, layers=28):
                                            "kv_heads": Hkv, "head_dim": Dq, "block_size": bs,
                                            "blocks_per_layer": NBq, "mean_ctx": round(float(L.mean()), 1)},
                  _hbm_roofline(nbytes, us_attn), cpu_res, attn_us_per_layer=round(us_attn, 2),
-                 attn_algorithmic_bytes_per_layer=nbytes)
+                 attn_algorithmic_bytes_per_layer=nbytes, graph_step_us=round(us_graph, 2),
+                 graph_tokens_per_s=round(Bq / (us_graph * 1e-6), 1))
 
 
 def bench_qwen_chunk(steps, warmup, cpu):
@@ -949,6 +1011,38 @@ def bench_tiny(steps, warmup, cpu):
         pass
     torch.cuda.synchronize()
     unchanged = bool(torch.equal(kc, before[0]) and torch.equal(vc, before[1]))
+    # the same run as captured steps: one graph per step (its own inputs), positions and lengths held on the
+    # device (fused K+V append at the length, length + 1, attention over the length)
+    kc2 = torch.zeros((1, 1, cap, 4), device=dev)
+    vc2 = torch.zeros((1, 1, cap, 4), device=dev)
+    bk2, bv2 = pkv.bind_writable(kc2), pkv.bind_writable(vc2)
+    lens = torch.zeros(1, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out2 = torch.empty_like(out)
+    graphs = []
+    for t in range(cap):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            pkv.cache_update_kv_dev(kc2, vc2, kd[t], vd[t], lens, 1, status)
+            pkv.advance(lens, 1)
+            pkv.decode_attention_dev(qd[t], kc2, vc2, lens, cap, out2, status, ws)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    ghost = np.zeros((steps, cap))
+    for i in range(-warmup, steps):
+        lens.zero_()
+        torch.cuda.synchronize()
+        for t in range(cap):
+            t0 = time.perf_counter()
+            graphs[t].replay()
+            torch.cuda.synchronize()
+            if i >= 0:
+                ghost[i, t] = (time.perf_counter() - t0) * 1e6
+    graph_matches = bool(torch.equal(kc2, kc) and torch.equal(vc2, vc) and torch.equal(out2, out)) and \
+        int(status.item()) == 0
+    bk2.close()
+    bv2.close()
+    med_graph = np.median(ghost, axis=0)
     bk.close()
     bv.close()
     med_host = np.median(host, axis=0)
@@ -963,6 +1057,9 @@ def bench_tiny(steps, warmup, cpu):
               per_step_device_us=[round(float(x), 2) for x in med_dev],
               first_token_host_us=round(float(med_host[0]), 2), token4_host_us=round(float(med_host[3]), 2),
               overflow_rejected_host_us=round(float(np.median(rejected)), 2),
+              graph_per_step_host_us=[round(float(x), 2) for x in med_graph],
+              graph_mean_host_us=round(float(med_graph.mean()), 2),
+              graph_run_equals_eager_run=graph_matches,
               overflow_leaves_cache_unchanged=unchanged,
               device_bytes_allocated_during_steps=int(max(alloc_delta, 0)),
               pages_cpu_runtime_us_context=PAGES_TINY_US)
@@ -1112,6 +1209,8 @@ def main():
         "attn_tokens_per_s": round(B / (g["attn_us"] * 1e-6), 1),
         "update_us": round(g["update_us"], 2),
         "sample_us": round(g["sample_us"], 2),
+        "graph_step_us": round(g["graph_step_us"], 2),
+        "graph_tokens_per_s": round(B / (g["graph_step_us"] * 1e-6), 1),
         "attn_algorithmic_bytes": attn_bytes,
         "device_bytes_allocated_during_steps": g["device_bytes_allocated_during_steps"],
     }

@@ -45,6 +45,12 @@ constexpr float kLazy = 8.0f;  // rescale only when a score exceeds the running 
 constexpr int32_t kStatusCapacity = 2;   // PKV_E_CAPACITY
 constexpr int32_t kStatusPage = 6;       // PKV_E_PAGE
 
+// A wave-uniform 32-bit load through the scalar unit (constant address
+// space: an s_load, which never waits behind the vector loads in flight)
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p));
+}
+
 // The (row, split) a workgroup works on.  With host lengths the split table
 // of the launch gives it; with device lengths every row has S_max split slots
 // and its split count follows from its length (a uniform load), and a length
@@ -65,7 +71,7 @@ __device__ __forceinline__ SplitWork split_work(const DecodeArgs& a, int r) {
     }
     w.b = r / a.S_max;
     w.split = r - w.b * a.S_max;
-    w.L = a.len_dev[a.row0 + w.b];
+    w.L = load_uniform(a.len_dev + a.row0 + w.b);
     w.ok = w.L >= 1 && w.L <= a.len_limit;
     w.nsplit = w.ok ? (w.L - split_base(w.L, a.window) + a.tps - 1) / a.tps : 0;
     return w;
@@ -131,13 +137,15 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     // Element offset of the first row of the 16-token step at ts (wave-uniform):
     // ts is a multiple of 16 and block_size a power-of-two multiple of 16, so
     // the whole step lies in one page.
-    // With device lengths a page id outside the pool is replaced by page 0
-    // (the reads stay inside the pool) and reported through *status.
+    // Page ids are wave-uniform scalar loads.  With device lengths a page id
+    // outside the pool is replaced by page 0 (the reads stay inside the
+    // pool) and reported through *status once the wave is done.
+    bool bad_page = false;
     auto step_base = [&](int ts) -> int64_t {
         if constexpr (PAGED) {
-            int page = pt[ts >> a.log2bs];
+            int page = load_uniform(pt + (ts >> a.log2bs));
             if (a.status != nullptr && uint32_t(page) >= uint32_t(a.nb)) {
-                if (threadIdx.x % 64 == 0) *a.status = kStatusPage;
+                bad_page = true;
                 page = 0;
             }
             return ((int64_t(page) * a.Hkv + kvh) * a.bs + (ts & (a.bs - 1))) * kD;
@@ -250,6 +258,8 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
             compute(A, ts);
         }
     }
+
+    if (bad_page && lane == 0) *a.status = kStatusPage;
 
     // merge the eight token groups of the wave (lanes with the same j)
 #pragma unroll
