@@ -68,13 +68,14 @@ __device__ __forceinline__ score_t<KIND> logit_of(u32x4v_t w, int e) {
 
 // Score order: NaN above every number, otherwise numeric.  above(s, b): s
 // ranks strictly above b.
+// (bitwise, not short-circuit: two compares and one scalar AND, no branch)
 template <typename T>
 __device__ __forceinline__ bool above(T s, T b) {
-    return !(s <= b) && b == b;
+    return !(s <= b) & (b == b);
 }
 template <typename T>
 __device__ __forceinline__ bool same_rank(T s, T b) {
-    return s == b || (s != s && b != b);
+    return (s == b) | ((s != s) & (b != b));
 }
 
 // (score, index) order: higher-ranked score wins, equal ranks -> lower index
@@ -157,10 +158,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(SampleArgs
     const uint64_t state0 = seed + (uint64_t(b) * uint64_t(a.V) + 1ull) * kGamma;
     auto consider = [&](S x, int64_t v, uint64_t state) {
         const S s = GREEDY ? x : gumbel_score(x, a, state);
-        if (above(s, best)) {
-            best = s;
-            bidx = static_cast<int32_t>(v);
-        }
+        const bool take = above(s, best);
+        best = take ? s : best;
+        bidx = take ? static_cast<int32_t>(v) : bidx;
     };
     if constexpr (VEC) {
         constexpr int U = 4;                                  // vectors in flight per thread
