@@ -178,6 +178,23 @@ pkv_status pkv_pool_free_count(const pkv_pool* pool, int32_t* free_pages);
 /* Copy the host page table int32[max_seqs, max_blocks_per_seq] (-1 = none). */
 pkv_status pkv_pool_table(const pkv_pool* pool, int32_t* out_host);
 
+/* Page-id trust contract.  The device page table is caller-owned memory and
+ * the library never copies it back to the host.  The calls that take host
+ * positions or host lengths (pkv_paged_cache_update and its INT4 and mixed
+ * forms, pkv_paged_gather, the paged decode calls, pkv_chunk_attention)
+ * therefore check a row against the pool's host mirror by counting: with
+ * `pool` given, each row must hold enough reserved pages for
+ * the positions it writes or reads (else PKV_E_PAGE, nothing launched).  The
+ * ids themselves are read from the device table inside the kernels and are
+ * trusted there: a table that disagrees with what pkv_pool_reserve wrote
+ * (edited by the caller, or a table of another pool) makes those kernels
+ * read or write the pages it names, and with `pool == NULL` the counts are
+ * not checked either.  Keep the table as pkv_pool_reserve / _release leave
+ * it.  The device-driven calls (the *_dev entry points below) do range-check
+ * every id they read against [0, num_blocks): an id outside it is never
+ * dereferenced for a write, reads page 0 instead, and sets *status to
+ * PKV_E_PAGE. */
+
 /* ------------------------------------------------------------------------ */
 /* Paged in-place cache update                                               */
 /* "Mutable execution cache", sections "Heterogeneous paged cache" and
