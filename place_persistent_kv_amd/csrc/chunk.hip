@@ -34,10 +34,15 @@
 // store instructions), two tile buffers, the next tile's loads in flight
 // while the current one is computed, one barrier per tile.  K and V keep the
 // pages' row-major [key][dim] layout in LDS, each 256-byte row's sixteen
-// 16-byte chunks permuted by chunk ^ 2 (key % 8) (the loading lane fetches
-// the chunk its slot holds).  The K operand of S^T is one 16-byte read per
-// lane (8 consecutive rows of one read phase hit 8 distinct chunk columns);
-// the V^T operand of O^T comes from the row-major V rows through the
+// 16-byte chunks permuted by chunk ^ swz(key % 16) (the loading lane fetches
+// the chunk its slot holds).  The LDS serves 256 bytes per cycle: 16 lanes of
+// a 16-byte read or 32 lanes of an 8-byte read.  swz is a bijection of the 16
+// rows (the 16 rows a K read phase touches use 16 distinct chunk columns), and
+// within each aligned group of 4 rows it takes 4 distinct values of bits 2-3
+// (a V read phase touches 4 chunks 4 d .. 4 d + 3 of 4 such rows, which then
+// also land on 16 distinct columns); it also keeps both read kinds apart on
+// 128-byte bank windows.  The K operand of S^T is one 16-byte read per
+// lane; the V^T operand of O^T comes from the row-major V rows through the
 // transposing LDS read ds_read_b64_tr_b16, which hands lane i of a 16-lane
 // group element i % 4 of the 8-byte pieces read by lanes 4 k + i / 4
 // (k = 0..3) -- so lanes that read 4 dims of 4 consecutive keys deliver each
@@ -45,6 +50,8 @@
 // scalar loads, one tile ahead.
 
 #include "device_common.h"
+
+#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -84,13 +91,81 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// chunk-column permutation of tile row `key`: for i = key % 4 the values
+// 0, 6, 12, 10 (distinct in bits 2-3 and in bits 1-2), bit 1 flipped for rows
+// 8..15 of 16, bit 0 set for rows 4..7 of 8
+__device__ __forceinline__ int swz(int key) {
+    const int i = key & 3;
+    return ((i << 2) ^ (i << 1)) ^ (((key >> 3) & 1) << 1) ^ ((key >> 2) & 1);
+}
+
 // element offset of (key, chunk) in a tile: row-major rows of 128 bf16, chunk
-// c of row `key` stored at chunk column c ^ 2 (key % 8)
-__device__ __forceinline__ int tile_off(int key, int chunk) { return key * kCD + 8 * (chunk ^ (2 * (key & 7))); }
+// c of row `key` stored at chunk column c ^ swz(key)
+__device__ __forceinline__ int tile_off(int key, int chunk) { return key * kCD + 8 * (chunk ^ swz(key)); }
 
 // 8 bytes read through the transposing LDS path
 __device__ __forceinline__ u32x2_t read_tr(const lds_u16* p) {
     const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+// 16-byte global-to-LDS load (global_load_lds_dwordx4): lane L's 16 bytes at
+// base + voff land at LDS byte address lds + 16 L (M0 holds lds; one wait
+// state between the M0 write and the load).  Issued as inline assembly so
+// that the compiler does not make the LDS operand reads of the other tile
+// buffers wait for it: each wave waits for its own loads (vmcnt) before the
+// barrier that hands the tile to the workgroup.
+// M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory");
+}
+
+// Four such loads of consecutive 1 KB blocks: load i reads base + (voff0 ^
+// 16 i) + 1024 i and writes LDS lds + 1024 i + 16 L (instruction offset 1024 i,
+// which applies to both the global and the LDS address).
+__device__ __forceinline__ void dma16x4(const void* base, uint32_t voff0, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %5\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %6\n\t"
+        "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, %6 offset:2048\n\t"
+        "global_load_lds_dwordx4 %4, %6 offset:3072\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff0), "v"(voff0 ^ 16u), "v"(voff0 ^ 32u), "v"(voff0 ^ 48u), "s"(lds), "s"(base)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_u16* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Pin a value to this point of the program: the compiler must have computed it
+// here and cannot sink its computation past the barrier that follows (which
+// would move a phase's work into the next phase)
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+
+// A value the compiler must treat as unknown (so that it adds constants to it
+// as instruction offsets instead of folding them into new registers)
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// LDS reads at a byte address
+__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) u32x4_t*)(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ u32x2_t lds_read_tr(uint32_t addr) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(static_cast<uintptr_t>(addr)));
     return __builtin_bit_cast(u32x2_t, v);
 }
 
@@ -99,11 +174,14 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
     return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p));
 }
 
-template <int G, bool WIN>   // WIN: a left window is set (a.window >= 0)
+// WIN: a left window is set (a.window >= 0); FAST: block_size >= 16
+template <int G, bool WIN, bool FAST>
 __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) {
-    // two tile buffers, K and V each [64 keys][128 dims] (chunk-permuted rows)
-    __shared__ __attribute__((aligned(16))) uint16_t sK0[kTileElems], sV0[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sK1[kTileElems], sV1[kTileElems];
+    // LDS (160 KB): three K and three V tile buffers (each [64 keys][128
+    // dims], chunk-permuted rows), then the workgroup's 256 query rows, [row]
+    // [128 dims], permuted like the tiles (wave w only touches rows 32 w ..
+    // 32 w + 31)
+    __shared__ __attribute__((aligned(16))) uint16_t smem[6 * kTileElems + kRows * kCD];
 
     constexpr int P = kRows / G;  // positions per workgroup
     const int tid = threadIdx.x;
@@ -146,13 +224,6 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     const int limit = p0 + min(t, a.C - 1);
     const int lo_lim = WIN ? max(0, limit - a.window) : 0;
 
-    // Q^T operand (B of S^T = K Q^T): lane holds dims 8 hl + 16 s .. +7 of its row
-    u32x4_t qB[8];
-    {
-        const uint16_t* Q = a.q + ((int64_t(b) * a.Hq + h) * a.C + min(t, a.C - 1)) * kCD;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) qB[s] = *reinterpret_cast<const u32x4_t*>(Q + 16 * s + 8 * hl);
-    }
 
     f32x16_t o[4];
     float m = -FLT_MAX, l = 0.0f;
@@ -161,37 +232,44 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
 
-    // ---- global -> LDS loads of one tile.  Wave w fills rows 8 w .. 8 w + 7
-    // of the K and V tiles with two 1 KB loads each (rows 8 w + 4 i .. + 3 for
-    // i = 0, 1); lane L writes slot L of such a load, i.e. row 8 w + 4 i + L / 16,
-    // chunk column L % 16, so it fetches chunk (L % 16) ^ 2 (row % 8) of its
-    // row.  Keys past the workgroup's last key are clamped to it (valid rows,
-    // masked later); an aligned 4-row group lies in one page (block_size >= 4).
+    // ---- global -> LDS loads of one tile, by the four waves of one group
+    // (see below): wave w or w + 4 fills rows 16 w .. 16 w + 15 of a tile with
+    // four 1 KB loads (rows 16 w + 4 i .. + 3); lane L writes slot L of such a
+    // load, i.e. row 16 w + 4 i + L / 16, chunk column L % 16, so it fetches
+    // chunk (L % 16) ^ swz(row) of its row.
     const uint32_t page_bytes = uint32_t(a.Hkv) * uint32_t(a.bs) * kCD * 2;
     const uint32_t head_bytes = uint32_t(kvh) * uint32_t(a.bs) * kCD * 2;
     const int lrow = lane >> 4;                              // row within a 1 KB load
-    struct Pages {
-        int32_t p[2];
+    const int wr = 16 * (wave & 3);                          // first tile row of this wave's loads
+
+    // block_size >= 16: the wave's 16 rows lie in one page, the page of key
+    // min(k0 + wr, last key) (so no page past the row's last is touched); the
+    // rows are not clamped: those past the last key hold whatever that page
+    // holds there, K ones are masked out of the scores and V ones are zeroed
+    // in LDS before they are read.  Row 16 w' + 4 i + L / 16 of load i sits
+    // at in-page row (k0 % bs rounded down to 64) + (16 w' + 4 i + L / 16) %
+    // bs, and swz(16 w' + 4 i + L / 16) = swz(L / 16) ^ i, so load i fetches
+    // byte offset (voff0 ^ 16 i) + 1024 i and writes LDS at M0 + 1024 i +
+    // 16 L, where the 1024 i is the instruction's offset (added to both).
+    const uint32_t voff0 = head_bytes + uint32_t((wr + lrow) & (a.bs - 1)) * (kCD * 2) +
+                           16u * uint32_t((lane & 15) ^ swz(lrow));
+    auto page_fast = [&](int k0) -> int32_t { return load_uniform(pt + (min(k0 + wr, wg_last_key) >> a.log2bs)); };
+    auto base_fast = [&](const uint16_t* src, int k0, int32_t page) -> const uint8_t* {
+        return reinterpret_cast<const uint8_t*>(src) + uint64_t(uint32_t(page)) * page_bytes +
+               uint32_t(k0 & (a.bs - 1) & ~(kKeys - 1)) * (kCD * 2);
     };
-    auto page_load = [&](int k0) -> Pages {
-        Pages pg;
+    // any block_size >= 4: rows past the last key clamped to it (valid rows,
+    // masked later); an aligned 4-row group lies in one page
+    auto load_general = [&](const uint16_t* src, int k0, lds_u16* dst) {
+        const uint32_t lds = lds_addr(dst + wr * kCD);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            pg.p[i] = load_uniform(pt + (min(k0 + 8 * wave + 4 * i, wg_last_key) >> a.log2bs));
-        return pg;
-    };
-    auto tile_load = [&](int k0, const Pages& pg, lds_u16* dK, lds_u16* dV) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = 8 * wave + 4 * i + lrow;           // row of the tile
+        for (int i = 0; i < 4; ++i) {
+            const int page = load_uniform(pt + (min(k0 + wr + 4 * i, wg_last_key) >> a.log2bs));
+            const int row = wr + 4 * i + lrow;                   // row of the tile
             const int key = min(k0 + row, wg_last_key);
-            const int chunk = (lane & 15) ^ (2 * (row & 7));
+            const int chunk = (lane & 15) ^ swz(row);
             const uint32_t off = head_bytes + uint32_t(key & (a.bs - 1)) * (kCD * 2) + 16u * uint32_t(chunk);
-            const uint64_t page_off = uint64_t(uint32_t(pg.p[i])) * page_bytes;
-            gbl_u8* gk = (gbl_u8*)(reinterpret_cast<const uint8_t*>(a.k) + page_off) + off;
-            gbl_u8* gv = (gbl_u8*)(reinterpret_cast<const uint8_t*>(a.v) + page_off) + off;
-            __builtin_amdgcn_global_load_lds(gk, dK + (8 * wave + 4 * i) * kCD, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gv, dV + (8 * wave + 4 * i) * kCD, 16, 0, 0);
+            dma16(reinterpret_cast<const uint8_t*>(src) + uint64_t(uint32_t(page)) * page_bytes, off, lds + 1024u * i);
         }
     };
 
@@ -204,116 +282,256 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     const int vkey = 4 * (g16 >> 1) + ((lane & 15) >> 2);
     const int vchunk = 2 * (g16 & 1) + ((lane & 3) >> 1);
     const int vsub = 4 * (lane & 1);
-
-    // ---- one 64-key tile from LDS, as two halves of 32 keys: S^T = K Q^T,
-    // online softmax, O^T += V^T P^T
-    auto compute = [&](int k0, const lds_u16* tK, const lds_u16* tV) {
-        // only the diagonal tiles (reaching past the smallest causal limit of
-        // the workgroup) test keys against the limits; a uniform branch
-        const bool need_mask = k0 + kKeys - 1 > wg_first_limit || (WIN && k0 < wg_lo_last);
-
-        // S^T for both 32-key halves, the two accumulation chains interleaved
-        f32x16_t s[2];
+    // Per-lane LDS byte addresses of the operand reads, each the address of
+    // the read in tile buffer 0 / at key block 0 (the rest are instruction
+    // offsets: 16 KB per buffer, 8 KB per 32-key half, 4 KB per 16-key block):
+    //   kaddr[ks]  K (A of S^T): key col, chunk hl + 2 ks (swz(key) = swz(col))
+    //   vaddr[dv]  V^T (A of O^T), d = dv / 2, second read = dv % 2
+    //   qaddr[ks]  Q^T (B of S^T): row r of this wave, chunk hl + 2 ks
+    // Made opaque so that the three K and three V buffers share them.
+    uint32_t kaddr[8], vaddr[8], qaddr[8];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8; ++ks) {
+        kaddr[ks] = opaque(lds_addr((lds_u16*)(smem) + tile_off(col, hl + 2 * ks)));
+        qaddr[ks] = opaque(lds_addr((lds_u16*)(smem) + 6 * kTileElems + tile_off(r, hl + 2 * ks)));
+    }
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int key = half * 32 + col;
-                const u32x4_t kA = *(const __attribute__((address_space(3))) u32x4_t*)(tK + tile_off(key, hl + 2 * ks));
-                const f32x16_t acc = ks == 0 ? f32x16_t{} : s[half];
-                s[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kA), as_bf16x8(qB[ks]), acc, 0, 0, 0);
+    for (int dv = 0; dv < 8; ++dv)
+        vaddr[dv] = opaque(lds_addr((lds_u16*)(smem) + 3 * kTileElems + tile_off(vkey + 8 * (dv % 2), 4 * (dv / 2) + vchunk) + vsub));
+
+    // Q rows of this wave into LDS (same 16-byte global-to-LDS loads: row
+    // 32 wave + 4 i + L / 16, chunk column L % 16 for lane L of load i)
+    lds_u16* const Qs = (lds_u16*)(smem) + 6 * kTileElems;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 32 * wave + 4 * i + lrow;
+        const int qt_ = t0 + row / G;
+        const int qh = kvh * G + row % G;
+        const uint32_t qoff = uint32_t(((uint32_t(qh) * uint32_t(a.C) + uint32_t(min(qt_, a.C - 1))) * kCD) * 2u)
+                              + 16u * uint32_t((lane & 15) ^ swz(row));
+        dma16(a.q + int64_t(b) * a.Hq * a.C * kCD, qoff, lds_addr(Qs + (32 * wave + 4 * i) * kCD));
+    }
+
+    // O^T += V^T P^T of one tile; p[2 half + qq] covers keys 32 half + 16 qq ..
+    // + 15, taken as 4 hl + 0..3 and 8 + 4 hl + 0..3 (the order the lanes hold
+    // the scores in); the V^T operand reads use the same key order
+    auto accumulate = [&](auto vbuf, const u32x4_t (&p)[4]) {
+        constexpr uint32_t VB = decltype(vbuf)::value * kTileElems * 2;
+#pragma unroll
+        for (int hq = 0; hq < 4; ++hq) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const u32x2_t x0 = lds_read_tr(vaddr[2 * d] + VB + hq * 4096);
+                const u32x2_t x1 = lds_read_tr(vaddr[2 * d + 1] + VB + hq * 4096);
+                const u32x4_t vA = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vA), as_bf16x8(p[hq]), o[d], 0, 0, 0);
             }
         }
+    };
 
-        // per half: online softmax (the matrix cores run the other half's
-        // products meanwhile), then O^T += V^T P^T
+    // Online softmax of one tile's scores (raw units; the scale is positive):
+    // causal / window mask on the diagonal tiles, lazy running max (moved only
+    // when the tile's max exceeds it by kLazyC, in log2 units), P as bf16 B
+    // operands, running sum.  Returns the factor the running output must be
+    // multiplied by before this tile's P V is added (1 unless the max moved).
+    auto softmax = [&](auto masked, int k0, f32x16_t (&s)[2], u32x4_t (&p)[4]) -> float {
+        if constexpr (decltype(masked)::value) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            u32x4_t pB[2];
-            // causal mask and max of this query row over the 32 keys, in raw
-            // score units (the scale is positive)
-            if (need_mask) {
+            for (int half = 0; half < 2; ++half)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int key = k0 + half * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
                     s[half][e] = key <= limit && (!WIN || key >= lo_lim) ? s[half][e] : -INFINITY;
                 }
-            }
-            float mx = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[half][e]);
-            mx = max_halves(mx) * a.scale_log2;
-            if (mx > m + kLazyC) {
-                const float c = exp2_fast(m - mx);
-                l *= c;
+        mx = max_halves(mx) * a.scale_log2;
+        const float m_new = mx > m + kLazyC ? mx : m;
+        const float c = exp2_fast(m - m_new);
+        const float neg_m = -m_new;
+        float psum = 0.0f;
 #pragma unroll
-                for (int d = 0; d < 4; ++d)
+        for (int hq = 0; hq < 4; ++hq) {
+            float x[8];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) o[d][e] *= c;
-                m = mx;
+            for (int e = 0; e < 8; ++e) {
+                x[e] = exp2_fast(fmaf(s[hq / 2][8 * (hq % 2) + e], a.scale_log2, neg_m));
+                psum += x[e];
             }
-            const float neg_m = -m;
-            // P^T as B operands: chunk qq covers keys 16 qq .. 16 qq + 15 of
-            // the half, element e of this lane = register 8 qq + e of s
+            p[hq] = u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                            pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+        }
+        l = l * c + psum;
+        m = m_new;
+        return c;
+    };
+
+    // Two groups of waves in ping-pong.  Waves w and w + 4 share a SIMD;
+    // each runs, per key tile j, a matrix phase M_j (O += V_{j-1} P_{j-1},
+    // then S_j = K_j Q^T: 32 products) and a softmax phase V_j (vector ALU:
+    // S_j -> P_j, running max / sum, output rescale), with a workgroup
+    // barrier after every phase; M_n only adds the last tile's P V.  Group 1
+    // (waves 4-7) passes one barrier first and so runs one phase behind group
+    // 0: while one wave of a SIMD is in a softmax phase, the other feeds the
+    // matrix core.  Interval i (between two barriers) holds phase i of group
+    // 0 (M_j for i = 2 j, V_j for i = 2 j + 1) and phase i - 1 of group 1.
+    // Tiles: K_j in K buffer j % 3, V_j in V buffer j % 3.  Group 0 loads
+    // K_{j+2} during its M_j (interval 2 j), group 1 loads V_{j+1} during its
+    // M_j (interval 2 j + 1), the loads interleaved with the products so
+    // that the matrix core hides their issue; each wave waits for them at
+    // the end of its V_j.  The buffers overwritten then held K_{j-1} and
+    // V_{j-2}, last read in intervals 2 j - 1; each tile is in place at
+    // least an interval before it is first read.  K_0, K_1 and V_0 are loaded
+    // before the loop.  Page ids for a wave's next loads are read during its
+    // softmax phase and waited for at its end: no scalar load is in flight in
+    // a matrix phase, where a wait on an LDS read would also wait for it.
+    // Loads past the last tile re-read it (harmless).
+    const int grp = wave >> 2;
+    const int n_tiles = wg_last_key / kKeys + 1;
+    const int it0 = wg_lo_first / kKeys;     // first tile any query of the workgroup sees
+    const int n = n_tiles - it0;             // tiles this workgroup visits
+    auto tile_key = [&](int j) { return min(it0 + j, n_tiles - 1) * kKeys; };
+    auto need_mask = [&](int j) {
+        const int k0 = (it0 + j) * kKeys;
+        return k0 + kKeys - 1 > wg_first_limit || (WIN && k0 < wg_lo_last);
+    };
+    lds_u16* const Kb = (lds_u16*)(smem);                    // K buffers 0, 1, 2
+    lds_u16* const Vb = Kb + 3 * kTileElems;                 // V buffers 0, 1, 2
+    constexpr bool fast = FAST;
+
+    f32x16_t sc[2];             // S of the current tile
+    u32x4_t pb[4];              // P of the current tile
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                float p[8];
+    for (int q = 0; q < 4; ++q) pb[q] = u32x4_t{0u, 0u, 0u, 0u};
+    {   // V buffer 2 is read by M_0 (times P = 0): zero it so that no stale
+        // LDS bits (a NaN pattern) can reach the accumulators
+        u32x4_t* z = (u32x4_t*)(Vb + 2 * kTileElems);
+        for (int e = tid; e < kTileElems / 8; e += kThreads) z[e] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    // the tile this wave loads during M_j is tile j + 2 of K (group 0) or
+    // tile j + 1 of V (group 1); pgL: its page (fast path)
+    const uint16_t* const lsrc = grp ? a.v : a.k;
+    const int lahead = grp ? 1 : 2;
+    int32_t pgL = 0;
+    if constexpr (FAST) {
+        if (grp == 1) {
+            dma16x4(base_fast(a.k, tile_key(0), page_fast(tile_key(0))), voff0, lds_addr(Kb + wr * kCD));
+            dma16x4(base_fast(a.k, tile_key(1), page_fast(tile_key(1))), voff0, lds_addr(Kb + (kTileElems + wr * kCD)));
+        } else {
+            dma16x4(base_fast(a.v, tile_key(0), page_fast(tile_key(0))), voff0, lds_addr(Vb + wr * kCD));
+        }
+        pgL = page_fast(tile_key(lahead));
+    } else {
+        if (grp == 1) {
+            load_general(a.k, tile_key(0), Kb);
+            load_general(a.k, tile_key(1), Kb + kTileElems);
+        } else {
+            load_general(a.v, tile_key(0), Vb);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);      // vmcnt(0) lgkmcnt(0): K_0, K_1, V_0, Q, page ids
+    __syncthreads();
+    if (grp == 1) __syncthreads();
+
+    // M_j: the 16 products of O += V_{j-1} P_{j-1} (A operand V^T through
+    // the transposing read) alternate with the 16 of S_j = K_j Q^T, the
+    // operand reads about two products ahead of their use (one wave per SIMD
+    // is in this phase, so nothing else hides the LDS latency); with DMA,
+    // this wave's four tile loads go out after the first eight products
+    auto matrix_phase = [&](auto dma, auto vbuf, auto kbuf, const uint8_t* lbase, uint32_t llds) {
+        constexpr uint32_t VB = decltype(vbuf)::value * kTileElems * 2;
+        constexpr uint32_t KB = decltype(kbuf)::value * kTileElems * 2;
+        u32x4_t va[16], ka[16], qa[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = exp2_fast(fmaf(s[half][8 * qq + e], a.scale_log2, neg_m));
-                    l += p[e];
-                }
-                pB[qq] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        for (int i = 0; i < 16; ++i) {
+            const int hq = i / 4, d = i % 4;
+            const u32x2_t x0 = lds_read_tr(vaddr[2 * d] + VB + hq * 4096);
+            const u32x2_t x1 = lds_read_tr(vaddr[2 * d + 1] + VB + hq * 4096);
+            va[i] = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+            const int ks = i / 2, half = i % 2;
+            if (half == 0) qa[ks] = lds_read16(qaddr[ks]);
+            ka[i] = lds_read16(kaddr[ks] + KB + half * 8192);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int hq = i / 4, d = i % 4;
+            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[i]), as_bf16x8(pb[hq]), o[d], 0, 0, 0);
+            const int ks = i / 2, half = i % 2;
+            const f32x16_t acc = ks == 0 ? f32x16_t{} : sc[half];
+            sc[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i]), as_bf16x8(qa[ks]), acc, 0, 0, 0);
+            if constexpr (decltype(dma)::value) {
+                if (i == 3) dma16x4(lbase, voff0, llds);
             }
-            // O^T += V^T P^T: A[i = dim][k] with the keys of chunk qq taken as
-            // 16 qq + 4 hl + 0..3 and 16 qq + 8 + 4 hl + 0..3 (the order of pB)
-            // (key chunk outer, dim block inner: consecutive products go to
-            // different accumulators, none waits for the one before it)
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);          // operand reads of the first products
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const int key = half * 32 + 16 * qq + vkey;
-                    const u32x2_t x0 = read_tr(tV + tile_off(key, 4 * d + vchunk) + vsub);
-                    const u32x2_t x1 = read_tr(tV + tile_off(key + 8, 4 * d + vchunk) + vsub);
-                    const u32x4_t vA = u32x4_t{x0.x, x0.y, x1.x, x1.y};
-                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vA), as_bf16x8(pB[qq]), o[d], 0, 0, 0);
-                }
-            }
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // O product
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // S product
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // reads
         }
     };
 
-    // Tiles alternate between the two buffers (the loop is unrolled by two, so
-    // each buffer is a fixed LDS array).  At a tile: wait for this wave's loads
-    // of it, barrier (every wave's loads have landed, and every wave is done
-    // with the other buffer), start the next tile's loads into the other
-    // buffer, request the page ids of the tile after that, compute.  Loads
-    // past the last tile re-read the last one (always valid); an odd tile
-    // count ends with one fully masked tile.
-    const int n_tiles = wg_last_key / kKeys + 1;
-    const int it0 = wg_lo_first / kKeys;     // first tile any query of the workgroup sees
-    auto tile_key = [&](int it) { return min(it, n_tiles - 1) * kKeys; };
-    lds_u16* const K0 = (lds_u16*)(sK0);
-    lds_u16* const V0 = (lds_u16*)(sV0);
-    lds_u16* const K1 = (lds_u16*)(sK1);
-    lds_u16* const V1 = (lds_u16*)(sV1);
-    Pages pg = page_load(tile_key(it0));
-    tile_load(tile_key(it0), pg, K0, V0);
-    pg = page_load(tile_key(it0 + 1));
-    for (int it = it0; it < n_tiles; it += 2) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of the tile
+    // one tile j (PAR = j % 3): M_j, barrier, V_j, barrier
+    auto tile = [&](auto par, int j) {
+        constexpr int PAR = decltype(par)::value;
+        using VBUF = std::integral_constant<int, (PAR + 2) % 3>;        // V_{j-1}
+        using KBUF = std::integral_constant<int, PAR>;                  // K_j
+        lds_u16* const ldst = grp ? Vb + ((PAR + 1) % 3) * kTileElems : Kb + ((PAR + 2) % 3) * kTileElems;
+        const int lkey = tile_key(j + lahead);
+        if constexpr (FAST) {
+            matrix_phase(std::true_type{}, VBUF{}, KBUF{}, base_fast(lsrc, lkey, pgL), lds_addr(ldst + wr * kCD));
+        } else {
+            load_general(lsrc, lkey, ldst);
+            matrix_phase(std::false_type{}, VBUF{}, KBUF{}, nullptr, 0u);
+        }
+        pin(sc[0]);
+        pin(sc[1]);
         __syncthreads();
-        tile_load(tile_key(it + 1), pg, K1, V1);
-        pg = page_load(tile_key(it + 2));
-        compute(it * kKeys, K0, V0);
-
-        __builtin_amdgcn_s_waitcnt(0x0f70);
+        if constexpr (FAST) pgL = page_fast(tile_key(j + lahead + 1));
+        const int k0 = (it0 + j) * kKeys;
+        const float c = need_mask(j) ? softmax(std::true_type{}, k0, sc, pb)
+                                     : softmax(std::false_type{}, k0, sc, pb);
+        if (c < 1.0f) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[d][e] *= c;
+        }
+        if (FAST && grp == 0 && j == n - 1) {
+            // V_{n-1} (landed, group 1 waited for it at the end of V_{n-2}):
+            // zero its rows past the workgroup's last key before M_n reads them
+            const int first = wg_last_key - k0 + 1;
+            u32x4_t* z = (u32x4_t*)(Vb + PAR * kTileElems);
+            for (int e = first * 16 + tid; e < kKeys * 16; e += 256) z[e] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pin(pb[q]);
+        __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0): this wave's loads, page ids
         __syncthreads();
-        tile_load(tile_key(it + 2), pg, K0, V0);
-        pg = page_load(tile_key(it + 3));
-        compute((it + 1) * kKeys, K1, V1);
+    };
+    int j = 0;
+    for (; j + 3 <= n; j += 3) {
+        tile(std::integral_constant<int, 0>{}, j);
+        tile(std::integral_constant<int, 1>{}, j + 1);
+        tile(std::integral_constant<int, 2>{}, j + 2);
     }
+    if (j < n) tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n) tile(std::integral_constant<int, 1>{}, j + 1);
+    // M_n: the last tile's P V (tile n - 1, in V buffer (n - 1) % 3)
+    {
+        const int lb = (n - 1) % 3;
+        if (lb == 0) accumulate(std::integral_constant<int, 0>{}, pb);
+        else if (lb == 1) accumulate(std::integral_constant<int, 1>{}, pb);
+        else accumulate(std::integral_constant<int, 2>{}, pb);
+    }
+    __syncthreads();
+    if (grp == 0) __syncthreads();
 
     // ---- normalise and store: lane holds dims 32 d + 8 (e / 4) + 4 hl + e % 4 of its row
     const float lt = sum_halves(l);
@@ -346,8 +564,13 @@ hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s) {
     switch (G) {
 #define PKV_CHUNK(GG)                                                                                  \
         case GG:                                                                                       \
-            if (a.window >= 0) hipLaunchKernelGGL((chunk_attention_kernel<GG, true>), dim3(blocks), dim3(kThreads), 0, s, a); \
-            else hipLaunchKernelGGL((chunk_attention_kernel<GG, false>), dim3(blocks), dim3(kThreads), 0, s, a); \
+            if (a.bs >= 16) {                                                                          \
+                if (a.window >= 0) hipLaunchKernelGGL((chunk_attention_kernel<GG, true, true>), dim3(blocks), dim3(kThreads), 0, s, a); \
+                else hipLaunchKernelGGL((chunk_attention_kernel<GG, false, true>), dim3(blocks), dim3(kThreads), 0, s, a); \
+            } else {                                                                                   \
+                if (a.window >= 0) hipLaunchKernelGGL((chunk_attention_kernel<GG, true, false>), dim3(blocks), dim3(kThreads), 0, s, a); \
+                else hipLaunchKernelGGL((chunk_attention_kernel<GG, false, false>), dim3(blocks), dim3(kThreads), 0, s, a); \
+            }                                                                                          \
             break;
         PKV_CHUNK(1)
         PKV_CHUNK(2)
