@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
             bkv = id / n_qt;
         }
     }
-    const int b = bkv / a.Hkv;
+    const int b = a.order[bkv / a.Hkv];
     const int kvh = bkv % a.Hkv;
     const int t0 = qt * P;
     const int p0 = a.p0[b];

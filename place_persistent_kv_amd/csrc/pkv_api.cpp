@@ -1421,7 +1421,12 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
         const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
         a.scale_log2 = sc * 1.4426950408889634f;
         a.window = left_window;
-        for (int i = 0; i < a.rows; ++i) a.p0[i] = p0[b0 + i];
+        for (int i = 0; i < a.rows; ++i) {
+            a.p0[i] = p0[b0 + i];
+            a.order[i] = static_cast<uint16_t>(i);
+        }
+        // longest rows first, so that the short ones fill the end of the launch
+        std::stable_sort(a.order, a.order + a.rows, [&](uint16_t x, uint16_t y) { return a.p0[x] > a.p0[y]; });
         PKV_HIP(launch_chunk(a, G, s), "chunk attention launch");
     }
     return ok();

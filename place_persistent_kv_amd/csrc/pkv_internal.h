@@ -250,6 +250,7 @@ struct ChunkArgs {
     int32_t window;              // left window (-1 = unbounded)
     float scale_log2;
     int32_t p0[kMaxRows];
+    uint16_t order[kMaxRows];    // rows by descending prefix: the longest go out first
 };
 bool chunk_supported(int D, int G, int bs, int C);
 hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s);
