@@ -49,3 +49,21 @@ def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
 
 def workspace(nbytes: int) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=DEV)
+
+
+U_BF16 = 2.0 ** -8      # bf16 unit roundoff (8 significant bits, round to nearest even)
+
+
+def assert_bf16_pv_bound(got: np.ndarray, ref: np.ndarray, s: np.ndarray, V: np.ndarray):
+    """Elementwise error bound of an attention output whose probabilities enter P.V as bf16 and whose result
+    is rounded to bf16 (the MFMA chunk kernel).  s: [..., n] scaled scores (-inf where a key is not
+    visible), V: [..., n, D] the values, ref / got: [..., D].  Rounding each p_k to bf16 (relative error
+    <= u) while the denominator sums the unrounded p gives |o~ - o| <= u * w, w = sum_k p_k |v_k| /
+    sum_k p_k; the bf16 output adds u * |o~|.  So |got - ref| <= u (1 + u) (w + |ref|), plus float32
+    noise.  A key dropped or counted twice moves an element by p_k |v_k - o| / sum p, which this catches
+    on short rows; the planted-key tests catch it on long ones."""
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    w = np.einsum("...k,...kd->...d", p, np.abs(V)) / p.sum(axis=-1)[..., None]
+    bound = U_BF16 * (1 + U_BF16) * (w + np.abs(ref)) + 1e-6 * np.abs(ref).max()
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), float((err / bound).max())

@@ -9,21 +9,39 @@ import synth
 from oracle import attention as oattn
 from oracle import cache as ocache
 from oracle import numeric as onum
-from tests.gpu_util import DEV, bf16_dev, bits_host, rel_err_rows, require_gpu, workspace
+from tests.gpu_util import (DEV, assert_bf16_pv_bound, bf16_dev, bits_host, rel_err_rows, require_gpu,
+                            workspace)
 
 pytestmark = pytest.mark.gpu
 
 
-def _setup(seed, B, Hq, Hkv, D, bs, p0, C, maxb):
-    """Prefix of p0[b] tokens already in the pages; returns device state and the host mirror."""
+BF16_NAN = 0x7FC0
+def _assert_chunk_bound(got, ref, qh, K, V, p0, left_window=-1):
+    """The bf16 P.V bound (`assert_bf16_pv_bound`) for every query of a chunk: query t at p0 + t sees keys
+    [p0 + t - W, p0 + t] (all earlier ones without a window)."""
+    Hq, C, D = got.shape
+    G = Hq // K.shape[0]
+    pos = p0 + np.arange(C)
+    keys = np.arange(K.shape[1])
+    vis = keys[None, :] <= pos[:, None]
+    if left_window >= 0:
+        vis &= keys[None, :] >= (pos - left_window)[:, None]
+    for h in range(Hq):
+        s = np.where(vis, qh[h] @ K[h // G].T / np.sqrt(D), -np.inf)
+        assert_bf16_pv_bound(got[h], ref[h], s, np.broadcast_to(V[h // G], (C,) + V[h // G].shape))
+
+
+def _setup(seed, B, Hq, Hkv, D, bs, p0, C, maxb, fill=0):
+    """Prefix of p0[b] tokens already in the pages; returns device state and the host mirror.  Slots no
+    append writes (past a row's length, and unreserved pages) hold the bf16 bits `fill`."""
     g = synth.rng(seed)
     NB = int(sum(-(-(int(x) + C) // bs) for x in p0)) + 2
     order = synth.permutation(g, NB)
     ref_pool = ocache.PagePool(NB, bs, B, maxb, order)
     lib_pool = pkv.Pool(NB, bs, B, maxb, order)
     table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
-    kp = np.zeros((NB, Hkv, bs, D), np.uint16)
-    vp = np.zeros_like(kp)
+    kp = np.full((NB, Hkv, bs, D), fill, np.uint16)
+    vp = np.full_like(kp, fill)
     for b in range(B):
         ref_pool.reserve(b, int(p0[b]) + C)
         L = int(p0[b])
@@ -64,7 +82,7 @@ def test_chunk_append_and_causal_attention_match_oracle(G, C, bs):
         K = onum.bf16_to_f64(ocache.paged_gather(d["kp"], d["ref_pool"].table[b], L, bs))
         V = onum.bf16_to_f64(ocache.paged_gather(d["vp"], d["ref_pool"].table[b], L, bs))
         ref = oattn.chunk_attention(qh[b], K, V, int(p0[b]))
-        assert rel_err_rows(got[b], ref) <= 2e-2, b
+        _assert_chunk_bound(got[b], ref, qh[b], K, V, int(p0[b]))
 
 
 @pytest.mark.parametrize("W,G,C", [(0, 2, 100), (5, 2, 100), (63, 4, 40), (64, 1, 300), (150, 2, 300),
@@ -92,7 +110,7 @@ def test_chunk_left_window_matches_oracle(W, G, C):
         K = onum.bf16_to_f64(ocache.paged_gather(d["kp"], d["ref_pool"].table[b], L, bs))
         V = onum.bf16_to_f64(ocache.paged_gather(d["vp"], d["ref_pool"].table[b], L, bs))
         ref = oattn.chunk_attention(qh[b], K, V, int(p0[b]), left_window=W)
-        assert rel_err_rows(got[b], ref) <= 2e-2, b
+        _assert_chunk_bound(got[b], ref, qh[b], K, V, int(p0[b]), W)
 
 
 def test_last_chunk_query_equals_decode():
@@ -184,3 +202,38 @@ def test_planted_key_marks_the_causal_and_window_edges(W, G, C, bs):
                     assert np.array_equal(got[b, h, t], base_h[b, h, t]), (b, h, t, p)
                     unseen += 1
     assert seen and unseen
+
+
+@pytest.mark.parametrize("G,C,bs,W", [(2, 100, 16, -1), (4, 70, 32, -1), (2, 300, 8, -1), (1, 5, 16, -1),
+                                      (2, 129, 64, -1), (2, 100, 16, 40)])
+def test_unwritten_slots_are_never_used(G, C, bs, W):
+    """Every slot no append writes holds a bf16 NaN: the rows past each row's length in its last page, and
+    the pages no row holds.  Lengths end inside a page and inside a 64-key tile.  The outputs must be finite
+    and match the oracle, which only sees the written rows (a NaN key past the last one is masked; a NaN
+    value row times a zero probability would still poison the products, so it must never be read as is)."""
+    require_gpu()
+    B, Hkv, D = 3, 2, 128
+    Hq = Hkv * G
+    p0 = np.array([3, 41, 190], np.int32)
+    maxb = -(-(int(p0.max()) + C) // bs) + 1
+    d = _setup(990 + G + C + bs, B, Hq, Hkv, D, bs, p0, C, maxb, fill=BF16_NAN)
+    with pkv.bind_writable(d["kd"]), pkv.bind_writable(d["vd"]):
+        pkv.paged_cache_update(d["lib_pool"], d["kd"], d["table"], bf16_dev(d["new_k"]), p0, C)
+        pkv.paged_cache_update(d["lib_pool"], d["vd"], d["table"], bf16_dev(d["new_v"]), p0, C)
+    ocache.paged_cache_update(d["kp"], d["ref_pool"].table, d["new_k"], p0, C, bs, d["ref_pool"].held)
+    ocache.paged_cache_update(d["vp"], d["ref_pool"].table, d["new_v"], p0, C, bs, d["ref_pool"].held)
+    assert np.array_equal(bits_host(d["kd"]), d["kp"]) and np.array_equal(bits_host(d["vd"]), d["vp"])
+    assert any((int(x) + C) % bs for x in p0)                     # some row ends inside a page
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    pkv.chunk_attention(bf16_dev(d["q"]), d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"],
+                        left_window=W)
+    got = onum.bf16_to_f64(bits_host(out))
+    assert np.isfinite(got).all()
+    qh = onum.bf16_to_f64(d["q"])
+    for b in range(B):
+        L = int(p0[b]) + C
+        K = onum.bf16_to_f64(ocache.paged_gather(d["kp"], d["ref_pool"].table[b], L, bs))
+        V = onum.bf16_to_f64(ocache.paged_gather(d["vp"], d["ref_pool"].table[b], L, bs))
+        assert np.isfinite(K).all() and np.isfinite(V).all()
+        ref = oattn.chunk_attention(qh[b], K, V, int(p0[b]), left_window=W)
+        _assert_chunk_bound(got[b], ref, qh[b], K, V, int(p0[b]), W)
