@@ -31,8 +31,9 @@
 //
 // Key tiles of 64 tokens go from the pages straight into LDS with 16-byte
 // global-to-LDS loads (global_load_lds_dwordx4: no staging registers, no LDS
-// store instructions), two tile buffers, the next tile's loads in flight
-// while the current one is computed, one barrier per tile.  K and V keep the
+// store instructions), three K and three V tile buffers, the loads of the
+// next tiles in flight while the current one is computed, one barrier per
+// tile.  K and V keep the
 // pages' row-major [key][dim] layout in LDS, each 256-byte row's sixteen
 // 16-byte chunks permuted by chunk ^ swz(key % 16) (the loading lane fetches
 // the chunk its slot holds).  The LDS serves 256 bytes per cycle: 16 lanes of
@@ -68,6 +69,7 @@ constexpr int kRows = kWavesC * 32;  // query rows per workgroup (256)
 constexpr int kKeys = 64;       // keys per tile
 constexpr int kTileElems = kKeys * kCD;   // one K or V tile (bf16 elements, 16 KB)
 constexpr float kLazyC = 8.0f;
+constexpr float kLazyP = 256.0f;   // 2^kLazyC
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(1))) const uint8_t gbl_u8;
@@ -335,6 +337,33 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     // operands, running sum.  Returns the factor the running output must be
     // multiplied by before this tile's P V is added (1 unless the max moved).
     auto softmax = [&](auto masked, int k0, f32x16_t (&s)[2], u32x4_t (&p)[4]) -> float {
+        if constexpr (!decltype(masked)::value) {
+            // First try the running max as it stands: if no P of the wave
+            // exceeds 2^kLazyC (every lane's sum of its 32 P is at most that),
+            // no row's max moves by the lazy rule below, and these are its P
+            // bit for bit.  Otherwise (the first tile of a row, a max that
+            // jumped, a NaN) the general path recomputes the tile.
+            const float neg_m = -m;
+            float psum = 0.0f;
+            u32x4_t pt[4];
+#pragma unroll
+            for (int hq = 0; hq < 4; ++hq) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    x[e] = exp2_fast(fmaf(s[hq / 2][8 * (hq % 2) + e], a.scale_log2, neg_m));
+                    psum += x[e];
+                }
+                pt[hq] = u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                 pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+            }
+            if (__builtin_amdgcn_ballot_w64(!(psum <= kLazyP)) == 0) {
+#pragma unroll
+                for (int hq = 0; hq < 4; ++hq) p[hq] = pt[hq];
+                l += psum;
+                return 1.0f;
+            }
+        }
         if constexpr (decltype(masked)::value) {
 #pragma unroll
             for (int half = 0; half < 2; ++half)
@@ -373,23 +402,25 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     // Two groups of waves in ping-pong.  Waves w and w + 4 share a SIMD;
     // each runs, per key tile j, a matrix phase M_j (O += V_{j-1} P_{j-1},
     // then S_j = K_j Q^T: 32 products) and a softmax phase V_j (vector ALU:
-    // S_j -> P_j, running max / sum, output rescale), with a workgroup
-    // barrier after every phase; M_n only adds the last tile's P V.  Group 1
-    // (waves 4-7) passes one barrier first and so runs one phase behind group
-    // 0: while one wave of a SIMD is in a softmax phase, the other feeds the
-    // matrix core.  Interval i (between two barriers) holds phase i of group
-    // 0 (M_j for i = 2 j, V_j for i = 2 j + 1) and phase i - 1 of group 1.
-    // Tiles: K_j in K buffer j % 3, V_j in V buffer j % 3.  Group 0 loads
-    // K_{j+2} during its M_j (interval 2 j), group 1 loads V_{j+1} during its
-    // M_j (interval 2 j + 1), the loads interleaved with the products so
-    // that the matrix core hides their issue; each wave waits for them at
-    // the end of its V_j.  The buffers overwritten then held K_{j-1} and
-    // V_{j-2}, last read in intervals 2 j - 1; each tile is in place at
-    // least an interval before it is first read.  K_0, K_1 and V_0 are loaded
-    // before the loop.  Page ids for a wave's next loads are read during its
-    // softmax phase and waited for at its end: no scalar load is in flight in
-    // a matrix phase, where a wait on an LDS read would also wait for it.
-    // Loads past the last tile re-read it (harmless).
+    // S_j -> P_j, running max / sum, output rescale); a final step adds the
+    // last tile's P V.  Interval j ends with the one workgroup barrier of
+    // tile j: in it group 0 (waves 0-3) runs M_j then V_j, group 1 (waves
+    // 4-7) runs V_{j-1} then M_j, so that while one wave of a SIMD is in a
+    // softmax phase the other feeds the matrix core.
+    // Tiles: K_j in K buffer j % 3, V_j in V buffer j % 3.  In interval j
+    // group 0 loads K_{j+2} and group 1 loads V_{j+1}, the loads interleaved
+    // with the products of M_j so that the matrix core hides their issue;
+    // each wave waits for its loads of interval j - 1 at the end of interval
+    // j, so a tile loaded in interval j - 2 is in place after barrier j - 1,
+    // before interval j reads it.  The buffers overwritten in interval j
+    // held K_{j-1} and V_{j-2}, last read by M_{j-1} before barrier j - 1.
+    // K_0, K_1 and V_0 are loaded before the loop.  Page ids for a wave's
+    // next loads are requested where no LDS wait of a matrix phase follows
+    // before their own wait (group 0: at the start of its V_j; group 1: at
+    // the end of its M_j) and waited for at the end of the wave's next
+    // softmax phase, since a wait on an LDS read would also wait for an
+    // outstanding scalar load.  Loads past the last tile re-read it
+    // (harmless).
     const int grp = wave >> 2;
     const int n_tiles = wg_last_key / kKeys + 1;
     const int it0 = wg_lo_first / kKeys;     // first tile any query of the workgroup sees
@@ -419,23 +450,21 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     int32_t pgL = 0;
     if constexpr (FAST) {
         if (grp == 1) {
-            dma16x4(base_fast(a.k, tile_key(0), page_fast(tile_key(0))), voff0, lds_addr(Kb + wr * kCD));
+            const int32_t p0g = page_fast(tile_key(0));
+            dma16x4(base_fast(a.k, tile_key(0), p0g), voff0, lds_addr(Kb + wr * kCD));
             dma16x4(base_fast(a.k, tile_key(1), page_fast(tile_key(1))), voff0, lds_addr(Kb + (kTileElems + wr * kCD)));
-        } else {
-            dma16x4(base_fast(a.v, tile_key(0), page_fast(tile_key(0))), voff0, lds_addr(Vb + wr * kCD));
+            dma16x4(base_fast(a.v, tile_key(0), p0g), voff0, lds_addr(Vb + wr * kCD));
         }
         pgL = page_fast(tile_key(lahead));
     } else {
         if (grp == 1) {
             load_general(a.k, tile_key(0), Kb);
             load_general(a.k, tile_key(1), Kb + kTileElems);
-        } else {
             load_general(a.v, tile_key(0), Vb);
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0070);      // vmcnt(0) lgkmcnt(0): K_0, K_1, V_0, Q, page ids
     __syncthreads();
-    if (grp == 1) __syncthreads();
 
     // M_j: the 16 products of O += V_{j-1} P_{j-1} (A operand V^T through
     // the transposing read) alternate with the 16 of S_j = K_j Q^T, the
@@ -477,11 +506,30 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
         }
     };
 
-    // one tile j (PAR = j % 3): M_j, barrier, V_j, barrier
-    auto tile = [&](auto par, int j) {
+    // softmax phase V_jt of this wave (its scores S_jt -> P_jt); group 0 also
+    // requests the page ids of its next tile loads (waited for at the end)
+    auto softmax_phase = [&](int jt) __attribute__((always_inline)) {
+        if (FAST && grp == 0) pgL = page_fast(tile_key(jt + lahead + 1));
+        const int k0 = (it0 + jt) * kKeys;
+        const float c = need_mask(jt) ? softmax(std::true_type{}, k0, sc, pb)
+                                      : softmax(std::false_type{}, k0, sc, pb);
+        if (c < 1.0f) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[d][e] *= c;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pin(pb[q]);
+        __builtin_amdgcn_s_waitcnt(0xc07f);                       // lgkmcnt(0): the page ids
+    };
+    // interval j < n (PAR = j % 3): group 0 runs M_j then V_j, group 1 runs
+    // V_{j-1} then M_j, then one barrier
+    auto interval = [&](auto par, int j) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par)::value;
         using VBUF = std::integral_constant<int, (PAR + 2) % 3>;        // V_{j-1}
         using KBUF = std::integral_constant<int, PAR>;                  // K_j
+        if (grp == 1 && j > 0) softmax_phase(j - 1);
         lds_u16* const ldst = grp ? Vb + ((PAR + 1) % 3) * kTileElems : Kb + ((PAR + 2) % 3) * kTileElems;
         const int lkey = tile_key(j + lahead);
         if constexpr (FAST) {
@@ -492,46 +540,42 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
         }
         pin(sc[0]);
         pin(sc[1]);
-        __syncthreads();
-        if constexpr (FAST) pgL = page_fast(tile_key(j + lahead + 1));
-        const int k0 = (it0 + j) * kKeys;
-        const float c = need_mask(j) ? softmax(std::true_type{}, k0, sc, pb)
-                                     : softmax(std::false_type{}, k0, sc, pb);
-        if (c < 1.0f) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[d][e] *= c;
+        // group 1's page ids for M_{j+1}: requested now, after this phase's
+        // LDS reads, waited for at the end of its V_j
+        if (FAST && grp == 1) pgL = page_fast(tile_key(j + lahead + 1));
+        if (grp == 0) softmax_phase(j);
+        // this wave's loads of interval j - 1 (first read in interval j + 1);
+        // those of interval j may stay in flight
+        __builtin_amdgcn_s_waitcnt(0x0f74);                       // vmcnt(4)
+        if (FAST && grp == 1 && j == n - 1) {
+            // V_{n-1} (loaded by this wave's group in interval n - 2, or before
+            // the loop): zero this wave's rows of it past the workgroup's last
+            // key before M_n reads them
+            const int first = wg_last_key - (it0 + j) * kKeys + 1;
+            uint32_t* zb = (uint32_t*)(Vb + PAR * kTileElems);
+            for (int rr = max(first, wr); rr < wr + 16; ++rr)
+                for (int e = lane; e < kCD / 2; e += 64) zb[rr * (kCD / 2) + e] = 0u;
         }
-        if (FAST && grp == 0 && j == n - 1) {
-            // V_{n-1} (landed, group 1 waited for it at the end of V_{n-2}):
-            // zero its rows past the workgroup's last key before M_n reads them
-            const int first = wg_last_key - k0 + 1;
-            u32x4_t* z = (u32x4_t*)(Vb + PAR * kTileElems);
-            for (int e = first * 16 + tid; e < kKeys * 16; e += 256) z[e] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pin(pb[q]);
-        __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0): this wave's loads, page ids
         __syncthreads();
     };
     int j = 0;
     for (; j + 3 <= n; j += 3) {
-        tile(std::integral_constant<int, 0>{}, j);
-        tile(std::integral_constant<int, 1>{}, j + 1);
-        tile(std::integral_constant<int, 2>{}, j + 2);
+        interval(std::integral_constant<int, 0>{}, j);
+        interval(std::integral_constant<int, 1>{}, j + 1);
+        interval(std::integral_constant<int, 2>{}, j + 2);
     }
-    if (j < n) tile(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < n) tile(std::integral_constant<int, 1>{}, j + 1);
-    // M_n: the last tile's P V (tile n - 1, in V buffer (n - 1) % 3)
+    if (j < n) interval(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n) interval(std::integral_constant<int, 1>{}, j + 1);
+    // interval n: group 1's V_{n-1}, then every wave's last P V (tile n - 1,
+    // in V buffer (n - 1) % 3)
+    if (grp == 1) softmax_phase(n - 1);
     {
         const int lb = (n - 1) % 3;
         if (lb == 0) accumulate(std::integral_constant<int, 0>{}, pb);
         else if (lb == 1) accumulate(std::integral_constant<int, 1>{}, pb);
         else accumulate(std::integral_constant<int, 2>{}, pb);
     }
-    __syncthreads();
-    if (grp == 0) __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): no load may outlive the kernel
 
     // ---- normalise and store: lane holds dims 32 d + 8 (e / 4) + 4 hl + e % 4 of its row
     const float lt = sum_halves(l);

@@ -113,6 +113,44 @@ def test_chunk_left_window_matches_oracle(W, G, C):
         _assert_chunk_bound(got[b], ref, qh[b], K, V, int(p0[b]), W)
 
 
+@pytest.mark.parametrize("rise", [10.0, 14.0])
+def test_running_max_rise_in_a_later_tile(rise):
+    """One prefix key in a later, unmasked tile outscores the rest by about `rise` log2 units (the typical
+    maximum of the other keys is about 3.6).  At 10 the rise above the running max stays mostly inside the
+    lazy margin of 8, so probabilities up to about 2^8 are accumulated under the old max; at 14 it passes
+    the margin and the max moves, rescaling the output.  Both must match the oracle."""
+    require_gpu()
+    B, Hkv, D, bs, G, C, d0 = 2, 2, 128, 16, 2, 64, 7
+    Hq = Hkv * G
+    p0 = np.array([300, 700], np.int32)
+    maxb = -(-(int(p0.max()) + C) // bs) + 1
+    d = _setup(1010 + int(rise), B, Hq, Hkv, D, bs, p0, C, maxb)
+    d["q"][..., d0] = synth.f32_to_bf16_bits(np.float32(4.0))
+    d["new_k"][..., d0] = 0
+    table = d["ref_pool"].table
+    lift = synth.f32_to_bf16_bits(np.float32(rise * np.sqrt(D) / (4.0 * np.log2(np.e))))
+    for b, p in ((0, 150), (1, 400)):
+        for pos in range(int(p0[b])):
+            d["kp"][int(table[b, pos // bs]), :, pos % bs, d0] = 0
+        d["kp"][int(table[b, p // bs]), :, p % bs, d0] = lift
+    d["kd"] = bf16_dev(d["kp"])
+    with pkv.bind_writable(d["kd"]), pkv.bind_writable(d["vd"]):
+        pkv.paged_cache_update(d["lib_pool"], d["kd"], d["table"], bf16_dev(d["new_k"]), p0, C)
+        pkv.paged_cache_update(d["lib_pool"], d["vd"], d["table"], bf16_dev(d["new_v"]), p0, C)
+    ocache.paged_cache_update(d["kp"], table, d["new_k"], p0, C, bs, d["ref_pool"].held)
+    ocache.paged_cache_update(d["vp"], table, d["new_v"], p0, C, bs, d["ref_pool"].held)
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    pkv.chunk_attention(bf16_dev(d["q"]), d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"])
+    got = onum.bf16_to_f64(bits_host(out))
+    qh = onum.bf16_to_f64(d["q"])
+    for b in range(B):
+        L = int(p0[b]) + C
+        K = onum.bf16_to_f64(ocache.paged_gather(d["kp"], table[b], L, bs))
+        V = onum.bf16_to_f64(ocache.paged_gather(d["vp"], table[b], L, bs))
+        ref = oattn.chunk_attention(qh[b], K, V, int(p0[b]))
+        _assert_chunk_bound(got[b], ref, qh[b], K, V, int(p0[b]))
+
+
 def test_last_chunk_query_equals_decode():
     require_gpu()
     B, Hkv, G, D, bs, C = 2, 2, 2, 128, 16, 48
