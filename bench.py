@@ -714,9 +714,10 @@ def bench_qwen_decode(steps, warmup, cpu, layers=28):
                  graph_tokens_per_s=round(Bq / (us_graph * 1e-6), 1))
 
 
-def bench_qwen_chunk(steps, warmup, cpu):
+def bench_qwen_chunk(steps, warmup, cpu, constant=None):
     """One layer: a 512-token chunk appended in place to 128 paged rows (prefix U[1024, 16384]) and the
-    causal chunk attention on the bf16 matrix cores."""
+    causal chunk attention on the bf16 matrix cores.  `constant` (a float) replaces every input value with
+    it: the calibration of the data-dependent clock only."""
     import numpy as np
     import torch
     import place_persistent_kv_amd as pkv
@@ -732,6 +733,9 @@ def bench_qwen_chunk(steps, warmup, cpu):
     q = torch.randn((Bq, Hq, C, Dq), generator=gen, device=dev, dtype=torch.bfloat16)
     nk = torch.randn((Bq, Hkv, C, Dq), generator=gen, device=dev, dtype=torch.bfloat16)
     out = torch.empty((Bq, Hq, C, Dq), device=dev, dtype=torch.bfloat16)
+    if constant is not None:
+        for t in ks + vs + [q, nk]:
+            t.fill_(constant)
     binds = [pkv.bind_writable(t) for t in ks + vs]
     stream = torch.cuda.current_stream()
     p0 = P0.tolist()
@@ -759,6 +763,38 @@ def bench_qwen_chunk(steps, warmup, cpu):
                   "frac": round(tflops / peak, 4), "traffic": None}, cpu_res,
                  attn_us=round(us_attn, 2), step_us=round(us_step, 2), attn_flops=flops,
                  chunk_tokens_per_s=round(Bq * C / (us_step * 1e-6), 1))
+
+
+def bench_mfma_ceiling(steps, warmup, cpu):
+    """What the matrix cores deliver on this board for the data the benchmarks use.  Dense bf16 MFMA work
+    is limited by power before the published rate is reached, and the limit depends on the operands'
+    bit activity: a plain 8192^3 bf16 GEMM (torch.matmul, the vendor library) is timed on N(0, 1)
+    operands and on constant ones, and so is the Qwen-shaped chunk attention launch."""
+    import torch
+    n = 8192
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    a = torch.randn((n, n), generator=gen, device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), generator=gen, device=dev, dtype=torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    flops = 2.0 * n ** 3
+    us_normal = _timed(lambda i: torch.matmul(a, b, out=c), steps, warmup, stream)
+    a.fill_(0.0115)
+    b.fill_(0.0115)
+    us_const = _timed(lambda i: torch.matmul(a, b, out=c), steps, warmup, stream)
+    del a, b, c
+    torch.cuda.empty_cache()
+    chunk_normal = bench_qwen_chunk(steps, warmup, None)
+    chunk_const = bench_qwen_chunk(steps, warmup, None, constant=0.0115)
+    tf = flops / (us_normal * 1e-6) / 1e12
+    return _line("bf16 dense GEMM TFLOP/s (8192^3, torch.matmul) on N(0, 1) operands", tf, "TFLOP/s", steps,
+                 warmup, us_normal, "bf16", {"workload": "mfma-ceiling", "m": n, "n": n, "k": n},
+                 {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                  "frac": round(tf / 2500.0, 4), "traffic": None}, cpu,
+                 gemm_constant_tflops=round(flops / (us_const * 1e-6) / 1e12, 1),
+                 chunk_normal_tflops=chunk_normal["value"], chunk_constant_tflops=chunk_const["value"])
 
 
 def bench_sample(steps, warmup, cpu):
@@ -1155,7 +1191,7 @@ def cpu_tiny(steps, warmup):
 
 WORKLOADS = {"contig": bench_contig, "paged": bench_paged, "int4": bench_int4, "qwen-decode": bench_qwen_decode,
              "qwen-chunk": bench_qwen_chunk, "sample": bench_sample, "window": bench_window, "mixed": bench_mixed,
-             "generate": bench_generate, "tiny": bench_tiny}
+             "generate": bench_generate, "tiny": bench_tiny, "mfma-ceiling": bench_mfma_ceiling}
 CPU_BASELINES = {"paged32k": cpu_paged32k, "contig": cpu_contig, "paged": cpu_paged, "int4": cpu_int4,
                  "qwen-decode": cpu_qwen_decode, "qwen-chunk": cpu_qwen_chunk, "sample": cpu_sample,
                  "window": cpu_window, "mixed": cpu_mixed, "generate": cpu_generate, "tiny": cpu_tiny}
@@ -1177,7 +1213,8 @@ def main():
               "(see DESIGN.md for how the decode step would shard)", file=sys.stderr)
         sys.exit(2)
     # the oracle's timing runs first, before this process touches the GPU (its worker processes start fresh)
-    cpu = None if args.no_cpu_baseline else CPU_BASELINES[args.workload](args.steps, args.warmup)
+    cpu = None if args.no_cpu_baseline or args.workload not in CPU_BASELINES else \
+        CPU_BASELINES[args.workload](args.steps, args.warmup)
     if args.workload != "paged32k":
         print(json.dumps(WORKLOADS[args.workload](args.steps, args.warmup, cpu)), flush=True)
         return
