@@ -59,7 +59,8 @@ def _setup(seed, B, Hq, Hkv, D, bs, p0, C, maxb, fill=0):
                 ref_pool=ref_pool, new_k=new_k, new_v=new_v, q=q)
 
 
-@pytest.mark.parametrize("G,C,bs", [(2, 100, 16), (1, 64, 16), (4, 7, 16), (8, 130, 32), (2, 1, 16), (2, 300, 8)])
+@pytest.mark.parametrize("G,C,bs", [(2, 100, 16), (1, 64, 16), (4, 7, 16), (8, 130, 32), (2, 1, 16), (2, 300, 8),
+                                    (2, 100, 4)])
 def test_chunk_append_and_causal_attention_match_oracle(G, C, bs):
     require_gpu()
     B, Hkv, D = 3, 2, 128
@@ -243,7 +244,7 @@ def test_planted_key_marks_the_causal_and_window_edges(W, G, C, bs):
 
 
 @pytest.mark.parametrize("G,C,bs,W", [(2, 100, 16, -1), (4, 70, 32, -1), (2, 300, 8, -1), (1, 5, 16, -1),
-                                      (2, 129, 64, -1), (2, 100, 16, 40)])
+                                      (2, 129, 64, -1), (2, 100, 16, 40), (4, 90, 4, -1)])
 def test_unwritten_slots_are_never_used(G, C, bs, W):
     """Every slot no append writes holds a bf16 NaN: the rows past each row's length in its last page, and
     the pages no row holds.  Lengths end inside a page and inside a 64-key tile.  The outputs must be finite
