@@ -72,7 +72,6 @@ constexpr float kLazyC = 8.0f;
 constexpr float kLazyP = 256.0f;   // 2^kLazyC
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
-typedef __attribute__((address_space(1))) const uint8_t gbl_u8;
 
 // two floats -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -104,12 +103,6 @@ __device__ __forceinline__ int swz(int key) {
 // element offset of (key, chunk) in a tile: row-major rows of 128 bf16, chunk
 // c of row `key` stored at chunk column c ^ swz(key)
 __device__ __forceinline__ int tile_off(int key, int chunk) { return key * kCD + 8 * (chunk ^ swz(key)); }
-
-// 8 bytes read through the transposing LDS path
-__device__ __forceinline__ u32x2_t read_tr(const lds_u16* p) {
-    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-    return __builtin_bit_cast(u32x2_t, v);
-}
 
 // 16-byte global-to-LDS load (global_load_lds_dwordx4): lane L's 16 bytes at
 // base + voff land at LDS byte address lds + 16 L (M0 holds lds; one wait
@@ -162,7 +155,7 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
     return x;
 }
 
-// LDS reads at a byte address
+// LDS reads at a byte address (16 bytes; 8 bytes through the transposing path)
 __device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
     return *(const __attribute__((address_space(3))) u32x4_t*)(static_cast<uintptr_t>(addr));
 }
@@ -432,7 +425,6 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     };
     lds_u16* const Kb = (lds_u16*)(smem);                    // K buffers 0, 1, 2
     lds_u16* const Vb = Kb + 3 * kTileElems;                 // V buffers 0, 1, 2
-    constexpr bool fast = FAST;
 
     f32x16_t sc[2];             // S of the current tile
     u32x4_t pb[4];              // P of the current tile

@@ -34,13 +34,6 @@ namespace {
 
 constexpr int kSampleThreads = 256;
 
-__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t k) {
-    uint64_t z = seed + k * 0x9E3779B97F4A7C15ull;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    return z ^ (z >> 31);
-}
-
 // Score type: float64 for float64 logits, float32 otherwise.
 template <int KIND>
 using score_t = typename std::conditional<KIND == kKvF64, double, float>::type;
