@@ -12,7 +12,7 @@ import place_persistent_kv_amd as pkv
 import synth
 from oracle import generate as ogen
 from oracle import sampling as osamp
-from tests.gpu_util import DEV, bf16_dev, require_gpu
+from tests.gpu_util import DEV, require_gpu
 
 pytestmark = pytest.mark.gpu
 
