@@ -31,6 +31,8 @@
 
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace pkv {
 namespace {
 
@@ -399,14 +401,25 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
     __syncthreads();
 
-    // pass 2: weighted values (lanes over dims)
-    const int64_t slot = (int64_t(b) * a.Hq + h) * a.S_max + split;
+    // pass 2: weighted values (lanes over dims).  A row with one split is
+    // finished here (the merge would scale it by exactly 1 and then by 1 / ls,
+    // which is what is done here); otherwise the partials go to the workspace.
+    const int64_t bh = int64_t(b) * a.Hq + h;
+    const int64_t slot = bh * a.S_max + split;
+    const float inv = 1.0f / ls;
     for (int d = lane; d < Dv; d += 64) {
         float acc = 0.0f;
         for (int t = ta; t < t1; ++t) acc = fmaf(s_p[t - t0], to_f32(V[vrow(t) + d]), acc);
-        a.ws_o[slot * Dv + d] = acc;
+        if (sw.nsplit == 1) {
+            const float y = acc * inv;
+            if (a.out_f32 || std::is_same<T, float>::value) static_cast<float*>(a.out)[bh * Dv + d] = y;
+            else if (std::is_same<T, _Float16>::value) static_cast<_Float16*>(a.out)[bh * Dv + d] = static_cast<_Float16>(y);
+            else static_cast<uint16_t*>(a.out)[bh * Dv + d] = f32_to_bf16_rne(y);
+        } else {
+            a.ws_o[slot * Dv + d] = acc;
+        }
     }
-    if (lane == 0) {
+    if (sw.nsplit > 1 && lane == 0) {
         a.ws_ml[slot * 2 + 0] = mx;
         a.ws_ml[slot * 2 + 1] = ls;
     }

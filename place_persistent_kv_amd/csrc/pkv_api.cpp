@@ -931,7 +931,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         } else {
             PKV_HIP(launch_decode_generic(a, total * static_cast<int>(Hq), s), "decode launch");
         }
-        if (any_split || !fast) {
+        if (any_split) {
             MergeArgs m;
             m.ws_o = a.ws_o;
             m.ws_ml = a.ws_ml;
@@ -942,7 +942,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
             m.S_max = a.S_max;
             m.row0 = a.row0;
             m.rows = rows;
-            m.min_splits = fast ? 2 : 1;  // the fast kernel finishes single-split rows itself
+            m.min_splits = 2;  // every attention kernel finishes single-split rows itself
             if (dev) {
                 m.len_dev = len_dev;
                 m.len_limit = max_len;
