@@ -115,8 +115,7 @@ def run_gpu(steps: int, warmup: int, profile_copy: bool):
     def step(i, ev):
         if ev:
             ev[0].record(stream)
-        pkv.paged_cache_update(pool, k_pool, table, new_k, pos, 1)
-        pkv.paged_cache_update(pool, v_pool, table, new_v, pos, 1)
+        pkv.paged_cache_update_kv(pool, k_pool, v_pool, table, new_k, new_v, pos, 1)
         if ev:
             ev[1].record(stream)
         pkv.paged_decode_attention(q, k_pool, v_pool, table, maxb, BS, lens, out, ws, pool=pool)
@@ -553,8 +552,7 @@ def bench_paged(steps, warmup, cpu):
     pos = (L - 1).tolist()
 
     def step(i):
-        pkv.paged_cache_update(pool, kd, table, nk, pos, 1)
-        pkv.paged_cache_update(pool, vd, table, nv, pos, 1)
+        pkv.paged_cache_update_kv(pool, kd, vd, table, nk, nv, pos, 1)
         pkv.paged_decode_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, ws, pool=pool)
 
     us_step = _timed(step, steps, warmup, stream)
@@ -678,8 +676,7 @@ def bench_qwen_decode(steps, warmup, cpu, layers=28):
 
     def step(i):
         for layer in range(layers):
-            pkv.paged_cache_update(pool, ks[layer], table, nk, pos, 1)
-            pkv.paged_cache_update(pool, vs[layer], table, nk, pos, 1)
+            pkv.paged_cache_update_kv(pool, ks[layer], vs[layer], table, nk, nk, pos, 1)
             pkv.paged_decode_attention(q, ks[layer], vs[layer], table, maxb, bs, lens, out, ws, pool=pool)
 
     us_step = _timed(step, steps, warmup, stream)
@@ -744,8 +741,7 @@ def bench_qwen_chunk(steps, warmup, cpu, constant=None):
         pkv.chunk_attention(q, ks[0], vs[0], table, maxb, bs, p0, out, pool=pool)
 
     def step(i):
-        pkv.paged_cache_update(pool, ks[0], table, nk, p0, C)
-        pkv.paged_cache_update(pool, vs[0], table, nk, p0, C)
+        pkv.paged_cache_update_kv(pool, ks[0], vs[0], table, nk, nk, p0, C)
         attn(i)
 
     us_step = _timed(step, steps, warmup, stream)
@@ -945,8 +941,7 @@ def bench_generate(steps, warmup, cpu, layers=28, new_tokens=8):
         pos = state["L"].tolist()
         lens = (state["L"] + 1).tolist()
         for layer in range(layers):
-            pkv.paged_cache_update(pool, ks[layer], table, k, pos, 1)
-            pkv.paged_cache_update(pool, vs[layer], table, v, pos, 1)
+            pkv.paged_cache_update_kv(pool, ks[layer], vs[layer], table, k, v, pos, 1)
             pkv.paged_decode_attention(q, ks[layer], vs[layer], table, maxb, bs, lens, out, ws, pool=pool)
         state["L"] += 1
         return out.reshape(Bq, Hq * Dq) @ head

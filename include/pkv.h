@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 6
+#define PKV_ABI_VERSION 7
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -218,6 +218,21 @@ pkv_status pkv_paged_cache_update(const pkv_pool* pool, const pkv_tensor* pool_k
                                   const int32_t* page_table_dev, const pkv_tensor* values,
                                   const int32_t* position, int32_t update_length,
                                   void** out_pool, void* stream);
+
+/* The same update for the K and the V pool of one page table in one launch
+ * (a decode step appends both): the result equals pkv_paged_cache_update of
+ * k_values into k_pool followed by v_values into v_pool.  Every check of both
+ * runs before anything is launched, so either both pools are written or
+ * neither.  k_pool and v_pool: same shape and dtype, disjoint, each inside a
+ * writable binding; k_values and v_values: same shape [B, H, update_length,
+ * D], neither overlapping either pool.  Errors as pkv_paged_cache_update,
+ * plus PKV_E_LAYOUT / PKV_E_DTYPE when K and V differ in shape or dtype and
+ * PKV_E_ALIAS when the pools overlap.  The storage of each pool is its input
+ * (no separate output pointers). */
+pkv_status pkv_paged_cache_update_kv(const pkv_pool* pool, const pkv_tensor* k_pool,
+                                     const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                     const pkv_tensor* k_values, const pkv_tensor* v_values,
+                                     const int32_t* position, int32_t update_length, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Device-driven step (positions and lengths in device memory)               */

@@ -118,6 +118,7 @@ _SIG = {
     "pkv_pool_free_count": (C.c_int, [_VP, _I32P]),
     "pkv_pool_table": (C.c_int, [_VP, _I32P]),
     "pkv_paged_cache_update": (C.c_int, [_VP, _T, _VP, _T, _I32P, C.c_int32, _P(_VP), _VP]),
+    "pkv_paged_cache_update_kv": (C.c_int, [_VP, _T, _T, _VP, _T, _T, _I32P, C.c_int32, _VP]),
     "pkv_paged_cache_update_int4": (C.c_int, [_VP, _T, _T, _VP, _T, C.c_uint16, C.c_uint16, _I32P,
                                               C.c_int32, _P(_VP), _P(_VP), _VP]),
     "pkv_paged_gather": (C.c_int, [_T, _VP, C.c_int32, C.c_int32, C.c_int32, _T, _VP]),
@@ -160,7 +161,7 @@ for _name, (_res, _args) in _SIG.items():
         _fn.argtypes = _args
 
 
-ABI_VERSION = 6      # the argument lists above follow this version of include/pkv.h
+ABI_VERSION = 7      # the argument lists above follow this version of include/pkv.h
 if _lib.pkv_abi_version() != ABI_VERSION:
     raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
                       "rebuild it (python place_persistent_kv_amd/build.py)")
@@ -380,6 +381,15 @@ def paged_cache_update(pool: Pool, pool_kv, page_table, values, position, update
                                        C.byref(desc(values)), _i32_array(position), int(update_length),
                                        C.byref(out), _stream(stream)), "pkv_paged_cache_update")
     return out.value
+
+
+def paged_cache_update_kv(pool: Pool, k_pool, v_pool, page_table, k_values, v_values, position,
+                          update_length: int, stream=None) -> None:
+    """``pkv_paged_cache_update_kv``: K and V appended at host positions in one launch."""
+    _check(_lib.pkv_paged_cache_update_kv(_pool_handle(pool), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+                                          _ptr(page_table), C.byref(desc(k_values)), C.byref(desc(v_values)),
+                                          _i32_array(position), int(update_length), _stream(stream)),
+           "pkv_paged_cache_update_kv")
 
 
 def paged_cache_update_int4(pool: Pool, codes_pool, params_pool, page_table, values, scale_f16_bits: int,

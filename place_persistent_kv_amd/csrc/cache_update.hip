@@ -35,11 +35,15 @@ __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyRowsArgs a, int
     }
 }
 
-template <typename V>
+// PAIR: indices [total / 2, total) copy the second (src2, pool2) pair
+template <typename V, bool PAIR>
 __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedCopyArgs a, int64_t total) {
     const int64_t vec_per_row = a.row_bytes / int64_t(sizeof(V));
-    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
-         i += int64_t(gridDim.x) * kThreads) {
+    const int64_t per_pair = PAIR ? total / 2 : total;
+    for (int64_t j = int64_t(blockIdx.x) * kThreads + threadIdx.x; j < total;
+         j += int64_t(gridDim.x) * kThreads) {
+        const bool second = PAIR && j >= per_pair;
+        const int64_t i = second ? j - per_pair : j;
         const int64_t r = i / vec_per_row;          // source row index (b, h, t)
         const int64_t c = i - r * vec_per_row;
         const int32_t t = static_cast<int32_t>(r % a.n);
@@ -49,8 +53,8 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedCopyArgs a, i
         const int32_t p = a.pos[b] + t;
         const int32_t page = a.page_table[int64_t(a.row0 + b) * a.maxb + p / a.bs];
         const int32_t slot = p % a.bs;
-        const V* src = reinterpret_cast<const V*>(a.src + r * a.row_bytes);
-        V* dst = reinterpret_cast<V*>(a.pool + ((int64_t(page) * a.H + h) * a.bs + slot) * a.row_bytes);
+        const V* src = reinterpret_cast<const V*>((second ? a.src2 : a.src) + r * a.row_bytes);
+        V* dst = reinterpret_cast<V*>((second ? a.pool2 : a.pool) + ((int64_t(page) * a.H + h) * a.bs + slot) * a.row_bytes);
         dst[c] = src[c];
     }
 }
@@ -201,12 +205,18 @@ hipError_t launch_copy_rows(const CopyRowsArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_paged_copy(const PagedCopyArgs& a, hipStream_t s) {
-    const int vb = vec_bytes(a.row_bytes, a.src, a.pool);
-    const int64_t total = int64_t(a.rows) * a.H * a.n * a.row_bytes / vb;
+    const bool pair = a.src2 != nullptr;
+    int vb = vec_bytes(a.row_bytes, a.src, a.pool);
+    if (pair) vb = std::min(vb, vec_bytes(a.row_bytes, a.src2, a.pool2));
+    const int64_t total = (pair ? 2 : 1) * (int64_t(a.rows) * a.H * a.n * a.row_bytes / vb);
     if (total == 0) return hipSuccess;
-    if (vb == 16) hipLaunchKernelGGL(paged_copy_kernel<uint4>, grid_for(total), dim3(kThreads), 0, s, a, total);
-    else if (vb == 4) hipLaunchKernelGGL(paged_copy_kernel<uint32_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
-    else hipLaunchKernelGGL(paged_copy_kernel<uint8_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
+#define PKV_PAGED_COPY(V)                                                                           \
+    if (pair) hipLaunchKernelGGL((paged_copy_kernel<V, true>), grid_for(total), dim3(kThreads), 0, s, a, total); \
+    else hipLaunchKernelGGL((paged_copy_kernel<V, false>), grid_for(total), dim3(kThreads), 0, s, a, total);
+    if (vb == 16) { PKV_PAGED_COPY(uint4) }
+    else if (vb == 4) { PKV_PAGED_COPY(uint32_t) }
+    else { PKV_PAGED_COPY(uint8_t) }
+#undef PKV_PAGED_COPY
     return hipGetLastError();
 }
 

@@ -453,6 +453,64 @@ pkv_status check_paged_positions(const pkv_pool* pool, int64_t B, const int32_t*
     return PKV_OK;
 }
 
+// Everything a host-position paged append of `values` into `pool_kv` checks
+// before it launches (the launch itself is the caller's)
+pkv_status paged_update_checks(const char* who, const pkv_pool* pool, const pkv_tensor* pool_kv,
+                               const int32_t* page_table_dev, const pkv_tensor* values,
+                               const int32_t* position, int32_t update_length) {
+    PKV_TRY(check_tensor(pool_kv, "pool_kv", 4, 4));
+    PKV_TRY(check_tensor(values, "values", 4, 4));
+    if (update_length < 0) return fail(PKV_E_ARG, "%s: negative update_length", who);
+    if (!pool) return fail(PKV_E_ARG, "%s: a pool handle is required", who);
+    const int64_t NB = pool_kv->shape[0], H = pool_kv->shape[1], bs = pool_kv->shape[2], D = pool_kv->shape[3];
+    const int64_t B = values->shape[0];
+    if (NB != pool->num_blocks || bs != pool->block_size)
+        return fail(PKV_E_LAYOUT, "%s: pool_kv is [%lld, H, %lld, D] but the pool has %d blocks of %d", who,
+                    (long long)NB, (long long)bs, pool->num_blocks, pool->block_size);
+    if (values->dtype != pool_kv->dtype) return fail(PKV_E_DTYPE, "%s: values dtype != pool dtype", who);
+    if (values->shape[1] != H || values->shape[2] != update_length || values->shape[3] != D)
+        return fail(PKV_E_LAYOUT, "%s: values must be [B, H, update_length, D] of the pool", who);
+    if (!page_table_dev && B > 0 && update_length > 0) return fail(PKV_E_ARG, "%s: null page table", who);
+    PKV_TRY(check_paged_positions(pool, B, position, update_length));
+    PKV_TRY(check_writable(pool_kv, "pool_kv"));
+    PKV_TRY(check_disjoint(values, "values", span(pool_kv), "pool_kv"));
+    return PKV_OK;
+}
+
+// One launch per kMaxRows rows; a second (values, pool) pair, when given,
+// is written by the same launches
+pkv_status paged_update_launch(const char* who, const pkv_pool* pool, const pkv_tensor* pool_kv,
+                               const pkv_tensor* pool2, const int32_t* page_table_dev, const pkv_tensor* values,
+                               const pkv_tensor* values2, const int32_t* position, int32_t update_length,
+                               void* stream) {
+    const int64_t H = pool_kv->shape[1], bs = pool_kv->shape[2], D = pool_kv->shape[3];
+    const int64_t B = values->shape[0];
+    const int64_t row_bytes = D * dtype_size(pool_kv->dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        PagedCopyArgs a;
+        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
+        const int64_t src_off = b0 * H * update_length * row_bytes;
+        a.src = static_cast<const uint8_t*>(values->data) + src_off;
+        a.pool = static_cast<uint8_t*>(pool_kv->data);
+        if (pool2) {
+            a.src2 = static_cast<const uint8_t*>(values2->data) + src_off;
+            a.pool2 = static_cast<uint8_t*>(pool2->data);
+        }
+        a.page_table = page_table_dev;
+        a.row_bytes = row_bytes;
+        a.H = static_cast<int32_t>(H);
+        a.n = update_length;
+        a.bs = static_cast<int32_t>(bs);
+        a.maxb = pool->maxb;
+        a.row0 = static_cast<int32_t>(b0);
+        for (int i = 0; i < a.rows; ++i) a.pos[i] = position[b0 + i];
+        const hipError_t e = launch_paged_copy(a, s);
+        if (e != hipSuccess) return fail(PKV_E_HIP, "%s launch: %s", who, hipGetErrorString(e));
+    }
+    return ok();
+}
+
 }  // namespace
 
 pkv_status pkv_paged_cache_update(const pkv_pool* pool, const pkv_tensor* pool_kv,
@@ -462,41 +520,30 @@ pkv_status pkv_paged_cache_update(const pkv_pool* pool, const pkv_tensor* pool_k
     PKV_TRY(check_tensor(pool_kv, "pool_kv", 4, 4));
     PKV_TRY(check_tensor(values, "values", 4, 4));
     if (!out_pool) return fail(PKV_E_ARG, "paged_cache_update: null out_pool");
-    if (update_length < 0) return fail(PKV_E_ARG, "paged_cache_update: negative update_length");
-    if (!pool) return fail(PKV_E_ARG, "paged_cache_update: a pool handle is required");
-    const int64_t NB = pool_kv->shape[0], H = pool_kv->shape[1], bs = pool_kv->shape[2], D = pool_kv->shape[3];
-    const int64_t B = values->shape[0];
-    if (NB != pool->num_blocks || bs != pool->block_size)
-        return fail(PKV_E_LAYOUT, "paged_cache_update: pool_kv is [%lld, H, %lld, D] but the pool has %d blocks of %d",
-                    (long long)NB, (long long)bs, pool->num_blocks, pool->block_size);
-    if (values->dtype != pool_kv->dtype) return fail(PKV_E_DTYPE, "paged_cache_update: values dtype != pool dtype");
-    if (values->shape[1] != H || values->shape[2] != update_length || values->shape[3] != D)
-        return fail(PKV_E_LAYOUT, "paged_cache_update: values must be [B, H, update_length, D] of the pool");
-    if (!page_table_dev && B > 0 && update_length > 0) return fail(PKV_E_ARG, "paged_cache_update: null page table");
-    PKV_TRY(check_paged_positions(pool, B, position, update_length));
-    PKV_TRY(check_writable(pool_kv, "pool_kv"));
-    PKV_TRY(check_disjoint(values, "values", span(pool_kv), "pool_kv"));
+    PKV_TRY(paged_update_checks("paged_cache_update", pool, pool_kv, page_table_dev, values, position, update_length));
     *out_pool = pool_kv->data;
     if (numel(values) == 0) return ok();
+    return paged_update_launch("paged_cache_update", pool, pool_kv, nullptr, page_table_dev, values, nullptr,
+                               position, update_length, stream);
+}
 
-    const int64_t row_bytes = D * dtype_size(pool_kv->dtype);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
-        PagedCopyArgs a;
-        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
-        a.src = static_cast<const uint8_t*>(values->data) + b0 * H * update_length * row_bytes;
-        a.pool = static_cast<uint8_t*>(pool_kv->data);
-        a.page_table = page_table_dev;
-        a.row_bytes = row_bytes;
-        a.H = static_cast<int32_t>(H);
-        a.n = update_length;
-        a.bs = static_cast<int32_t>(bs);
-        a.maxb = pool->maxb;
-        a.row0 = static_cast<int32_t>(b0);
-        for (int i = 0; i < a.rows; ++i) a.pos[i] = position[b0 + i];
-        PKV_HIP(launch_paged_copy(a, s), "paged_cache_update launch");
-    }
-    return ok();
+pkv_status pkv_paged_cache_update_kv(const pkv_pool* pool, const pkv_tensor* k_pool, const pkv_tensor* v_pool,
+                                     const int32_t* page_table_dev, const pkv_tensor* k_values,
+                                     const pkv_tensor* v_values, const int32_t* position, int32_t update_length,
+                                     void* stream) {
+    const char* who = "paged_cache_update_kv";
+    PKV_TRY(paged_update_checks(who, pool, k_pool, page_table_dev, k_values, position, update_length));
+    PKV_TRY(paged_update_checks(who, pool, v_pool, page_table_dev, v_values, position, update_length));
+    for (int i = 0; i < 4; ++i)
+        if (k_pool->shape[i] != v_pool->shape[i] || k_values->shape[i] != v_values->shape[i])
+            return fail(PKV_E_LAYOUT, "%s: K and V pools, and K and V values, must have the same shapes", who);
+    if (k_pool->dtype != v_pool->dtype) return fail(PKV_E_DTYPE, "%s: K and V pools differ in dtype", who);
+    if (overlap(span(k_pool), span(v_pool))) return fail(PKV_E_ALIAS, "%s: k_pool overlaps v_pool", who);
+    PKV_TRY(check_disjoint(k_values, "k_values", span(v_pool), "v_pool"));
+    PKV_TRY(check_disjoint(v_values, "v_values", span(k_pool), "k_pool"));
+    if (numel(k_values) == 0) return ok();
+    return paged_update_launch(who, pool, k_pool, v_pool, page_table_dev, k_values, v_values, position,
+                               update_length, stream);
 }
 
 namespace {

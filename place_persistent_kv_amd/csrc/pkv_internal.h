@@ -28,6 +28,8 @@ struct CopyRowsArgs {            // contiguous: dst[b,h,pos_b+t,:] = src[b,h,t,:
 struct PagedCopyArgs {           // paged: pool[pt[b][p/bs], h, p%bs, :] = src[b,h,t,:]
     const uint8_t* src;          // [rows, H, n, row_bytes]
     uint8_t* pool;               // [NB, H, bs, row_bytes]
+    const uint8_t* src2 = nullptr;   // a second (values, pool) pair written by the same
+    uint8_t* pool2 = nullptr;        // launch at the same positions (K and V), or nullptr
     const int32_t* page_table;   // row (row0 + b) of [*, maxb]
     int64_t row_bytes;
     int32_t H, n, bs, maxb, row0, rows;

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if getattr(pkv._lib, n, None) is None]
     assert not missing, missing
     assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
-    assert pkv.abi_version() == pkv.ABI_VERSION == 6
+    assert pkv.abi_version() == pkv.ABI_VERSION == 7
 
 
 def R(ptr, dtype, shape):
@@ -149,6 +149,35 @@ def test_paged_update_needs_reserved_pages_and_capacity():
     assert status_of(pkv.paged_cache_update, pool, kv, table, vals, [0, 0], 1) == pkv.E_READONLY
     with pkv.bind_writable(bad):
         assert status_of(pkv.paged_cache_update, pool, bad, table, vals, [0, 0], 1) == pkv.E_LAYOUT
+
+
+def test_paired_kv_update_checks_both_tensors_before_any_write():
+    """pkv_paged_cache_update_kv: every check of the K update and of the V update, plus K/V agreement."""
+    pool = pkv.Pool(16, 4, 2, 4)
+    pool.reserve([0, 1], [5, 4])
+    kp = R(FAKE, pkv.BF16, [16, 2, 4, 8])
+    vp = R(FAKE + 0x40000, pkv.BF16, [16, 2, 4, 8])
+    kv = R(FAKE + 0x100000, pkv.BF16, [2, 2, 1, 8])
+    vv = R(FAKE + 0x140000, pkv.BF16, [2, 2, 1, 8])
+    table = R(FAKE + 0x200000, pkv.I32, [2, 4])
+    f = pkv.paged_cache_update_kv
+    with pkv.bind_writable(kp):
+        assert status_of(f, pool, kp, vp, table, kv, vv, [0, 0], 1) == pkv.E_READONLY   # V pool not writable
+    with pkv.bind_writable(kp), pkv.bind_writable(vp):
+        assert status_of(f, pool, kp, vp, table, kv, vv, [7, 4], 1) == pkv.E_PAGE       # row 1, page 1
+        assert status_of(f, pool, kp, vp, table, kv, vv, [16, 0], 1) == pkv.E_CAPACITY
+        assert status_of(f, None, kp, vp, table, kv, vv, [0, 0], 1) == pkv.E_ARG
+        assert status_of(f, pool, kp, vp, None, kv, vv, [0, 0], 1) == pkv.E_ARG          # page table required
+        assert status_of(f, pool, kp, vp, table, kv, R(vv.ptr, pkv.F16, vv.shape), [0, 0], 1) == pkv.E_DTYPE
+        assert status_of(f, pool, kp, vp, table, kv, R(vv.ptr, pkv.BF16, [2, 2, 2, 8]), [0, 0], 1) \
+            == pkv.E_LAYOUT                                                              # V values of another length
+        assert status_of(f, pool, kp, vp, table, kv, R(kp.ptr + 64, pkv.BF16, vv.shape), [0, 0], 1) \
+            == pkv.E_ALIAS                                                               # V values inside the K pool
+        assert status_of(f, pool, kp, kp, table, kv, vv, [0, 0], 1) == pkv.E_ALIAS       # one pool for K and V
+    big = R(FAKE + 0x400000, pkv.BF16, [16, 2, 4, 16])
+    with pkv.bind_writable(kp), pkv.bind_writable(big):
+        assert status_of(f, pool, kp, big, table, kv, R(vv.ptr, pkv.BF16, [2, 2, 1, 16]), [0, 0], 1) \
+            == pkv.E_LAYOUT                                                              # pools of two head sizes
 
 
 def test_int4_update_parameter_checks():

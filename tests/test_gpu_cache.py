@@ -107,6 +107,43 @@ def test_paged_update_and_gather_are_bit_exact(bs, D):
         assert np.array_equal(bits_host(out), ocache.paged_gather(host, ref_pool.table[b], int(lengths[b]), bs))
 
 
+@pytest.mark.parametrize("bs,D,kind", [(16, 128, "bf16"), (4, 8, "f32"), (32, 6, "f16")])
+def test_paired_kv_update_equals_two_single_updates(bs, D, kind):
+    """pkv_paged_cache_update_kv writes both pools exactly as the oracle's K update and V update would
+    (every byte of both pools, sentinels included), across page boundaries and for rows whose byte size
+    forces the narrower copy widths; a failing call writes neither pool."""
+    require_gpu()
+    g = synth.rng(611, bs, D)
+    B, H, maxb = 3, 2, 10
+    NB = B * maxb + 3
+    lib_pool, ref_pool, table, kp, khost = _paged_setup(g, NB, H, bs, D, B, maxb, kind)
+    vp = sentinel_dev((NB, H, bs, D), DTYPES[kind][0])
+    vhost = bytes_host(vp).view(DTYPES[kind][1]).reshape(NB, H, bs, D).copy()
+    lengths = np.zeros(B, np.int32)
+    with pkv.bind_writable(kp), pkv.bind_writable(vp):
+        for n in [1, bs + 3, 2 * bs - 1, 1]:
+            kvals, vvals = _values(g, (B, H, n, D), kind), _values(g, (B, H, n, D), kind)
+            new = (lengths + n).tolist()
+            lib_pool.reserve(range(B), new, table)
+            for b in range(B):
+                ref_pool.reserve(b, new[b])
+            pkv.paged_cache_update_kv(lib_pool, kp, vp, table, _dev(kvals, kind), _dev(vvals, kind), lengths, n)
+            ocache.paged_cache_update(khost, ref_pool.table, kvals, lengths, n, bs, held_pages=ref_pool.held)
+            ocache.paged_cache_update(vhost, ref_pool.table, vvals, lengths, n, bs, held_pages=ref_pool.held)
+            lengths += n
+            assert same_bytes(kp, khost) and same_bytes(vp, vhost)
+        # past the reserved pages: rejected before any write, both pools unchanged
+        vals = _dev(_values(g, (B, H, bs, D), kind), kind)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.paged_cache_update_kv(lib_pool, kp, vp, table, vals, vals, lengths, bs)
+        assert e.value.status == pkv.E_PAGE
+        assert same_bytes(kp, khost) and same_bytes(vp, vhost)
+
+
+def same_bytes(dev, host):
+    return np.array_equal(bytes_host(dev), np.ascontiguousarray(host).view(np.uint8).reshape(-1))
+
+
 def test_paged_update_past_reserved_pages_fails_without_writing():
     require_gpu()
     g = synth.rng(602)
