@@ -485,8 +485,7 @@ def bench_contig(steps, warmup, cpu):
     def step(i, rot=True):
         r = i % R if rot else 0
         pos = (L0 + i % S).tolist()
-        pkv.cache_update(kc[r], nk, pos, 1)
-        pkv.cache_update(vc[r], nv, pos, 1)
+        pkv.cache_update_kv(kc[r], vc[r], nk, nv, pos, 1)
         pkv.decode_attention(q, kc[r], vc[r], [p + 1 for p in pos], out, ws)
 
     def attn_only(i, rot=True):
@@ -1011,8 +1010,7 @@ def bench_tiny(steps, warmup, cpu):
         for t in range(cap):
             t0 = time.perf_counter()
             evs[t][0].record(stream)
-            assert pkv.cache_update(kc, kd[t], [t], 1) == kc.data_ptr()
-            assert pkv.cache_update(vc, vd[t], [t], 1) == vc.data_ptr()
+            pkv.cache_update_kv(kc, vc, kd[t], vd[t], [t], 1)
             pkv.decode_attention(qd[t], kc, vc, [t + 1], out, ws)
             evs[t][1].record(stream)
             torch.cuda.synchronize()
@@ -1020,7 +1018,7 @@ def bench_tiny(steps, warmup, cpu):
                 host[record, t] = (time.perf_counter() - t0) * 1e6
         t0 = time.perf_counter()
         try:
-            pkv.cache_update(kc, kd[cap], [cap], 1)
+            pkv.cache_update_kv(kc, vc, kd[cap], vd[cap], [cap], 1)
             raise RuntimeError("the append past capacity was accepted")
         except pkv.PkvError as e:
             assert e.status == pkv.E_CAPACITY

@@ -135,6 +135,19 @@ pkv_status pkv_cache_update(const pkv_tensor* cache, const pkv_tensor* values,
                             const int32_t* position, int32_t update_length,
                             void** out_cache, void* stream);
 
+/* The same update for a K and a V cache in one launch (a decode step appends
+ * both): the result equals pkv_cache_update of k_values into k_cache
+ * followed by v_values into v_cache.  Every check of both runs before
+ * anything is launched, so either both caches are written or neither.
+ * k_cache and v_cache: same shape and dtype, disjoint, each inside a writable
+ * binding; k_values and v_values: [B, H, update_length, D] of the caches,
+ * neither overlapping either cache.  Errors as pkv_cache_update, plus
+ * PKV_E_LAYOUT / PKV_E_DTYPE when K and V differ in shape or dtype and
+ * PKV_E_ALIAS when the caches overlap. */
+pkv_status pkv_cache_update_kv(const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                               const pkv_tensor* k_values, const pkv_tensor* v_values,
+                               const int32_t* position, int32_t update_length, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Fixed page pool (host metadata)                                           */
 /* "Mutable execution cache", sections "Heterogeneous paged cache",

@@ -119,6 +119,7 @@ _SIG = {
     "pkv_pool_table": (C.c_int, [_VP, _I32P]),
     "pkv_paged_cache_update": (C.c_int, [_VP, _T, _VP, _T, _I32P, C.c_int32, _P(_VP), _VP]),
     "pkv_paged_cache_update_kv": (C.c_int, [_VP, _T, _T, _VP, _T, _T, _I32P, C.c_int32, _VP]),
+    "pkv_cache_update_kv": (C.c_int, [_T, _T, _T, _T, _I32P, C.c_int32, _VP]),
     "pkv_paged_cache_update_int4": (C.c_int, [_VP, _T, _T, _VP, _T, C.c_uint16, C.c_uint16, _I32P,
                                               C.c_int32, _P(_VP), _P(_VP), _VP]),
     "pkv_paged_gather": (C.c_int, [_T, _VP, C.c_int32, C.c_int32, C.c_int32, _T, _VP]),
@@ -381,6 +382,13 @@ def paged_cache_update(pool: Pool, pool_kv, page_table, values, position, update
                                        C.byref(desc(values)), _i32_array(position), int(update_length),
                                        C.byref(out), _stream(stream)), "pkv_paged_cache_update")
     return out.value
+
+
+def cache_update_kv(k_cache, v_cache, k_values, v_values, position, update_length: int, stream=None) -> None:
+    """``pkv_cache_update_kv``: K and V appended to contiguous caches at host positions in one launch."""
+    _check(_lib.pkv_cache_update_kv(C.byref(desc(k_cache)), C.byref(desc(v_cache)), C.byref(desc(k_values)),
+                                    C.byref(desc(v_values)), _i32_array(position), int(update_length),
+                                    _stream(stream)), "pkv_cache_update_kv")
 
 
 def paged_cache_update_kv(pool: Pool, k_pool, v_pool, page_table, k_values, v_values, position,

@@ -18,19 +18,24 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename V>
+// PAIR: indices [total / 2, total) copy the second (src2, dst2) pair
+template <typename V, bool PAIR>
 __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyRowsArgs a, int64_t total) {
     // thread i copies vector c of row-slab (b, h): the n rows written for (b, h)
     // are contiguous both in `values` and at `position` in the cache.
     const int64_t vec_per_bh = a.n * a.row_bytes / int64_t(sizeof(V));
-    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
-         i += int64_t(gridDim.x) * kThreads) {
+    const int64_t per_pair = PAIR ? total / 2 : total;
+    for (int64_t j = int64_t(blockIdx.x) * kThreads + threadIdx.x; j < total;
+         j += int64_t(gridDim.x) * kThreads) {
+        const bool second = PAIR && j >= per_pair;
+        const int64_t i = second ? j - per_pair : j;
         const int64_t bh = i / vec_per_bh;
         const int64_t c = i - bh * vec_per_bh;
         const int32_t b = static_cast<int32_t>(bh / a.H);
         const int32_t h = static_cast<int32_t>(bh - int64_t(b) * a.H);
-        const V* src = reinterpret_cast<const V*>(a.src + bh * a.n * a.row_bytes);
-        V* dst = reinterpret_cast<V*>(a.dst + ((int64_t(b) * a.H + h) * a.cap + a.pos[b]) * a.row_bytes);
+        const V* src = reinterpret_cast<const V*>((second ? a.src2 : a.src) + bh * a.n * a.row_bytes);
+        V* dst = reinterpret_cast<V*>((second ? a.dst2 : a.dst) +
+                                      ((int64_t(b) * a.H + h) * a.cap + a.pos[b]) * a.row_bytes);
         dst[c] = src[c];
     }
 }
@@ -195,12 +200,18 @@ hipError_t launch_kv_append_dev(const KvAppendDevArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_copy_rows(const CopyRowsArgs& a, hipStream_t s) {
-    const int vb = vec_bytes(a.row_bytes, a.src, a.dst);
-    const int64_t total = int64_t(a.rows) * a.H * a.n * a.row_bytes / vb;
+    const bool pair = a.src2 != nullptr;
+    int vb = vec_bytes(a.row_bytes, a.src, a.dst);
+    if (pair) vb = std::min(vb, vec_bytes(a.row_bytes, a.src2, a.dst2));
+    const int64_t total = (pair ? 2 : 1) * (int64_t(a.rows) * a.H * a.n * a.row_bytes / vb);
     if (total == 0) return hipSuccess;
-    if (vb == 16) hipLaunchKernelGGL(copy_rows_kernel<uint4>, grid_for(total), dim3(kThreads), 0, s, a, total);
-    else if (vb == 4) hipLaunchKernelGGL(copy_rows_kernel<uint32_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
-    else hipLaunchKernelGGL(copy_rows_kernel<uint8_t>, grid_for(total), dim3(kThreads), 0, s, a, total);
+#define PKV_COPY_ROWS(V)                                                                            \
+    if (pair) hipLaunchKernelGGL((copy_rows_kernel<V, true>), grid_for(total), dim3(kThreads), 0, s, a, total); \
+    else hipLaunchKernelGGL((copy_rows_kernel<V, false>), grid_for(total), dim3(kThreads), 0, s, a, total);
+    if (vb == 16) { PKV_COPY_ROWS(uint4) }
+    else if (vb == 4) { PKV_COPY_ROWS(uint32_t) }
+    else { PKV_COPY_ROWS(uint8_t) }
+#undef PKV_COPY_ROWS
     return hipGetLastError();
 }
 

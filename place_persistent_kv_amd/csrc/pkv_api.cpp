@@ -271,43 +271,88 @@ pkv_status pkv_unbind(pkv_binding* binding) {
 }
 
 // ---------------------------------------------------------------------------
+namespace {
+
+// Everything a contiguous append of `values` into `cache` checks before it
+// launches (the launch itself is the caller's)
+pkv_status cache_update_checks(const char* who, const pkv_tensor* cache, const pkv_tensor* values,
+                               const int32_t* position, int32_t update_length) {
+    PKV_TRY(check_tensor(cache, "cache", 4, 4));
+    PKV_TRY(check_tensor(values, "values", 4, 4));
+    if (update_length < 0) return fail(PKV_E_ARG, "%s: negative update_length", who);
+    const int64_t B = cache->shape[0], H = cache->shape[1], cap = cache->shape[2], D = cache->shape[3];
+    if (values->dtype != cache->dtype) return fail(PKV_E_DTYPE, "%s: values dtype != cache dtype", who);
+    if (values->shape[0] != B || values->shape[1] != H || values->shape[2] != update_length ||
+        values->shape[3] != D)
+        return fail(PKV_E_LAYOUT, "%s: values must be [B, H, update_length, D] of the cache", who);
+    if (B > 0 && !position) return fail(PKV_E_ARG, "%s: null position", who);
+    for (int64_t b = 0; b < B; ++b)
+        if (position[b] < 0 || int64_t(position[b]) + update_length > cap)
+            return fail(PKV_E_CAPACITY, "%s: row %lld: position %d + update_length %d > capacity %lld", who,
+                        (long long)b, position[b], update_length, (long long)cap);
+    PKV_TRY(check_writable(cache, "cache"));
+    PKV_TRY(check_disjoint(values, "values", span(cache), "cache"));
+    return PKV_OK;
+}
+
+// One launch per kMaxRows rows; a second (values, cache) pair, when given,
+// is written by the same launches
+pkv_status cache_update_launch(const char* who, const pkv_tensor* cache, const pkv_tensor* cache2,
+                               const pkv_tensor* values, const pkv_tensor* values2, const int32_t* position,
+                               int32_t update_length, void* stream) {
+    const int64_t B = cache->shape[0], H = cache->shape[1], cap = cache->shape[2], D = cache->shape[3];
+    const int64_t row_bytes = D * dtype_size(cache->dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
+        CopyRowsArgs a;
+        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
+        const int64_t src_off = b0 * H * update_length * row_bytes, dst_off = b0 * H * cap * row_bytes;
+        a.src = static_cast<const uint8_t*>(values->data) + src_off;
+        a.dst = static_cast<uint8_t*>(cache->data) + dst_off;
+        if (cache2) {
+            a.src2 = static_cast<const uint8_t*>(values2->data) + src_off;
+            a.dst2 = static_cast<uint8_t*>(cache2->data) + dst_off;
+        }
+        a.row_bytes = row_bytes;
+        a.H = static_cast<int32_t>(H);
+        a.n = update_length;
+        a.cap = static_cast<int32_t>(cap);
+        for (int i = 0; i < a.rows; ++i) a.pos[i] = position[b0 + i];
+        const hipError_t e = launch_copy_rows(a, s);
+        if (e != hipSuccess) return fail(PKV_E_HIP, "%s launch: %s", who, hipGetErrorString(e));
+    }
+    return ok();
+}
+
+}  // namespace
+
 pkv_status pkv_cache_update(const pkv_tensor* cache, const pkv_tensor* values,
                             const int32_t* position, int32_t update_length,
                             void** out_cache, void* stream) {
     PKV_TRY(check_tensor(cache, "cache", 4, 4));
     PKV_TRY(check_tensor(values, "values", 4, 4));
     if (!out_cache) return fail(PKV_E_ARG, "cache_update: null out_cache");
-    if (update_length < 0) return fail(PKV_E_ARG, "cache_update: negative update_length");
-    const int64_t B = cache->shape[0], H = cache->shape[1], cap = cache->shape[2], D = cache->shape[3];
-    if (values->dtype != cache->dtype) return fail(PKV_E_DTYPE, "cache_update: values dtype != cache dtype");
-    if (values->shape[0] != B || values->shape[1] != H || values->shape[2] != update_length ||
-        values->shape[3] != D)
-        return fail(PKV_E_LAYOUT, "cache_update: values must be [B, H, update_length, D] of the cache");
-    if (B > 0 && !position) return fail(PKV_E_ARG, "cache_update: null position");
-    for (int64_t b = 0; b < B; ++b)
-        if (position[b] < 0 || int64_t(position[b]) + update_length > cap)
-            return fail(PKV_E_CAPACITY, "cache_update: row %lld: position %d + update_length %d > capacity %lld",
-                        (long long)b, position[b], update_length, (long long)cap);
-    PKV_TRY(check_writable(cache, "cache"));
-    PKV_TRY(check_disjoint(values, "values", span(cache), "cache"));
+    PKV_TRY(cache_update_checks("cache_update", cache, values, position, update_length));
     *out_cache = cache->data;
     if (numel(values) == 0) return ok();
+    return cache_update_launch("cache_update", cache, nullptr, values, nullptr, position, update_length, stream);
+}
 
-    const int64_t row_bytes = D * dtype_size(cache->dtype);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
-        CopyRowsArgs a;
-        a.rows = static_cast<int32_t>(std::min<int64_t>(kMaxRows, B - b0));
-        a.src = static_cast<const uint8_t*>(values->data) + b0 * H * update_length * row_bytes;
-        a.dst = static_cast<uint8_t*>(cache->data) + b0 * H * cap * row_bytes;
-        a.row_bytes = row_bytes;
-        a.H = static_cast<int32_t>(H);
-        a.n = update_length;
-        a.cap = static_cast<int32_t>(cap);
-        for (int i = 0; i < a.rows; ++i) a.pos[i] = position[b0 + i];
-        PKV_HIP(launch_copy_rows(a, s), "cache_update launch");
-    }
-    return ok();
+pkv_status pkv_cache_update_kv(const pkv_tensor* k_cache, const pkv_tensor* v_cache, const pkv_tensor* k_values,
+                               const pkv_tensor* v_values, const int32_t* position, int32_t update_length,
+                               void* stream) {
+    const char* who = "cache_update_kv";
+    PKV_TRY(cache_update_checks(who, k_cache, k_values, position, update_length));
+    PKV_TRY(cache_update_checks(who, v_cache, v_values, position, update_length));
+    for (int i = 0; i < 4; ++i)
+        if (k_cache->shape[i] != v_cache->shape[i])
+            return fail(PKV_E_LAYOUT, "%s: K and V caches must have the same shape", who);
+    if (k_cache->dtype != v_cache->dtype) return fail(PKV_E_DTYPE, "%s: K and V caches differ in dtype", who);
+    if (overlap(span(k_cache), span(v_cache))) return fail(PKV_E_ALIAS, "%s: k_cache overlaps v_cache", who);
+    PKV_TRY(check_disjoint(k_values, "k_values", span(v_cache), "v_cache"));
+    PKV_TRY(check_disjoint(v_values, "v_values", span(k_cache), "k_cache"));
+    if (numel(k_values) == 0) return ok();
+    return cache_update_launch(who, k_cache, v_cache, k_values, v_values, position, update_length, stream);
 }
 
 // ---------------------------------------------------------------------------

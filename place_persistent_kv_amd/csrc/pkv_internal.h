@@ -20,6 +20,8 @@ constexpr int kFastD = 128;          // head size of the fast bf16 / INT4 decode
 struct CopyRowsArgs {            // contiguous: dst[b,h,pos_b+t,:] = src[b,h,t,:]
     const uint8_t* src;          // [rows, H, n, row_bytes]
     uint8_t* dst;                // [rows, H, cap, row_bytes]
+    const uint8_t* src2 = nullptr;   // a second (values, cache) pair written by the same
+    uint8_t* dst2 = nullptr;         // launch at the same positions (K and V), or nullptr
     int64_t row_bytes;
     int32_t H, n, cap, rows;
     int32_t pos[kMaxRows];

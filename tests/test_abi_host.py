@@ -90,6 +90,26 @@ def test_cache_update_shape_and_dtype_errors():
         assert status_of(pkv.cache_update, CACHE, VALS, [0, 0], -1) == pkv.E_ARG
 
 
+def test_paired_contiguous_update_checks_both_tensors():
+    """pkv_cache_update_kv: every check of the K update and of the V update, plus K/V agreement."""
+    vcache = R(FAKE + 0x40000, pkv.BF16, [2, 3, 16, 8])
+    vvals = R(FAKE + 0x140000, pkv.BF16, [2, 3, 4, 8])
+    f = pkv.cache_update_kv
+    with pkv.bind_writable(CACHE):
+        assert status_of(f, CACHE, vcache, VALS, vvals, [0, 0], 4) == pkv.E_READONLY   # V cache not writable
+    with pkv.bind_writable(CACHE), pkv.bind_writable(vcache):
+        assert status_of(f, CACHE, vcache, VALS, vvals, [13, 0], 4) == pkv.E_CAPACITY
+        assert status_of(f, CACHE, vcache, VALS, vvals, [0, 0], -1) == pkv.E_ARG
+        assert status_of(f, CACHE, vcache, VALS, R(vvals.ptr, pkv.F16, vvals.shape), [0, 0], 4) == pkv.E_DTYPE
+        assert status_of(f, CACHE, vcache, VALS, R(vvals.ptr, pkv.BF16, [2, 3, 4, 4]), [0, 0], 4) == pkv.E_LAYOUT
+        assert status_of(f, CACHE, vcache, VALS, R(CACHE.ptr + 64, pkv.BF16, vvals.shape), [0, 0], 4) \
+            == pkv.E_ALIAS                                                               # V values inside the K cache
+        assert status_of(f, CACHE, CACHE, VALS, vvals, [0, 0], 4) == pkv.E_ALIAS         # one cache for K and V
+    other = R(FAKE + 0x80000, pkv.BF16, [2, 3, 20, 8])
+    with pkv.bind_writable(CACHE), pkv.bind_writable(other):
+        assert status_of(f, CACHE, other, VALS, vvals, [0, 0], 4) == pkv.E_LAYOUT       # capacities differ
+
+
 # --------------------------------------------------------------------------- pool
 def test_pool_matches_the_oracle_pool():
     g = synth.rng(500)

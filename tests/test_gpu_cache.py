@@ -52,6 +52,32 @@ def test_contiguous_update_is_bit_exact_in_place(kind, D, n):
             assert np.array_equal(bytes_host(cache), host.view(np.uint8).reshape(-1))
 
 
+@pytest.mark.parametrize("kind,D,n", [("bf16", 128, 1), ("f32", 4, 3), ("f16", 6, 2), ("u8", 7, 5)])
+def test_paired_contiguous_update_equals_two_single_updates(kind, D, n):
+    """pkv_cache_update_kv writes both caches exactly as the oracle's K update and V update would (every
+    byte, sentinels included; row sizes that force the 16-, 4- and 1-byte copy widths); a failing call
+    writes neither cache."""
+    require_gpu()
+    g = synth.rng(612, D, n)
+    B, H, cap = 3, 2, 37
+    kc, vc = sentinel_dev((B, H, cap, D), DTYPES[kind][0]), sentinel_dev((B, H, cap, D), DTYPES[kind][0])
+    kh = bytes_host(kc).view(DTYPES[kind][1]).reshape(B, H, cap, D).copy()
+    vh = kh.copy()
+    with pkv.bind_writable(kc), pkv.bind_writable(vc):
+        for step in range(3):
+            pos = g.integers(0, cap - n + 1, size=B).astype(np.int32)
+            kvals, vvals = _values(g, (B, H, n, D), kind), _values(g, (B, H, n, D), kind)
+            pkv.cache_update_kv(kc, vc, _dev(kvals, kind), _dev(vvals, kind), pos, n)
+            ocache.cache_update(kh, kvals, pos, n)
+            ocache.cache_update(vh, vvals, pos, n)
+            assert same_bytes(kc, kh) and same_bytes(vc, vh)
+        vals = _dev(_values(g, (B, H, n, D), kind), kind)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.cache_update_kv(kc, vc, vals, vals, [0, cap - n + 1, 0], n)
+        assert e.value.status == pkv.E_CAPACITY
+        assert same_bytes(kc, kh) and same_bytes(vc, vh)
+
+
 def test_overflow_and_readonly_leave_the_cache_untouched():
     require_gpu()
     cache = sentinel_dev((1, 1, 16, 4), torch.float32)
