@@ -204,30 +204,34 @@ class Raw:
         return n * _ESIZE[self.dtype]
 
 
+_DTYPE_CODES = None
+_SHAPE_T = C.c_int64 * MAX_DIMS
+
+
 def _torch_dtype_code(t) -> int:
-    import torch
-    table = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.uint8: U8,
-             torch.int32: I32, torch.int64: I64, torch.float64: F64}
-    if t.dtype not in table:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.uint8: U8,
+                        torch.int32: I32, torch.int64: I64, torch.float64: F64}
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return table[t.dtype]
+    return code
 
 
 def desc(x) -> PkvTensor:
     """``pkv_tensor`` for a torch tensor (contiguous, any device) or a :class:`Raw`."""
-    d = PkvTensor()
     if isinstance(x, Raw):
-        d.data, d.dtype, shape = x.ptr, x.dtype, list(x.shape)
+        ptr, code, shape = x.ptr, x.dtype, tuple(int(s) for s in x.shape)
     else:
         if not x.is_contiguous():
             raise ValueError("tensor must be contiguous (libpkv never copies inputs)")
-        d.data, d.dtype, shape = x.data_ptr(), _torch_dtype_code(x), list(x.shape)
-    if not 1 <= len(shape) <= MAX_DIMS:
-        raise ValueError(f"rank {len(shape)} not supported")
-    d.ndim = len(shape)
-    for i, s in enumerate(shape):
-        d.shape[i] = int(s)
-    return d
+        ptr, code, shape = x.data_ptr(), _torch_dtype_code(x), x.shape
+    n = len(shape)
+    if not 1 <= n <= MAX_DIMS:
+        raise ValueError(f"rank {n} not supported")
+    return PkvTensor(ptr, code, n, _SHAPE_T(*shape))
 
 
 def _ptr(x) -> Optional[int]:
@@ -248,13 +252,19 @@ def _nbytes(x) -> int:
 
 def _i32_array(values) -> C.Array:
     vals = [int(v) for v in values]
-    return (C.c_int32 * max(1, len(vals)))(*vals)
+    return (C.c_int32 * (len(vals) or 1))(*vals)
+
+
+_GPU = None
 
 
 def current_stream() -> Optional[int]:
     """Handle of torch's current HIP stream (None when no GPU is visible)."""
+    global _GPU
     import torch
-    if not torch.cuda.is_available():
+    if _GPU is None:
+        _GPU = torch.cuda.is_available()
+    if not _GPU:
         return None
     return torch.cuda.current_stream().cuda_stream
 
