@@ -760,6 +760,58 @@ def bench_qwen_chunk(steps, warmup, cpu, constant=None):
                  chunk_tokens_per_s=round(Bq * C / (us_step * 1e-6), 1))
 
 
+def bench_qwen_chunk_1row(steps, warmup, cpu):
+    """One request of the qwen-chunk shape: a 512-token chunk after a 16384-token prefix.  Its launch has
+    one workgroup per (K/V head, 128-token query tile), 32 in all, so the library splits every workgroup's
+    key range and merges the parts; the unsplit launch and a sweep of split counts are reported beside it."""
+    import numpy as np
+    import torch
+    import place_persistent_kv_amd as pkv
+    from synth import workloads
+    w = workloads.qwen(B=1, lo=16384, hi=16384)
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    C = w["chunk"]
+    ks, vs, pool, table, NBq = _qwen_pools(w, C, 1, gen)
+    Bq, Hq, Hkv, Dq, bs, maxb = w["B"], w["Hq"], w["Hkv"], w["D"], w["bs"], w["maxb"]
+    P0 = w["lengths"].astype(np.int64)
+    q = torch.randn((Bq, Hq, C, Dq), generator=gen, device=dev, dtype=torch.bfloat16)
+    nk = torch.randn((Bq, Hkv, C, Dq), generator=gen, device=dev, dtype=torch.bfloat16)
+    out = torch.empty((Bq, Hq, C, Dq), device=dev, dtype=torch.bfloat16)
+    binds = [pkv.bind_writable(t) for t in ks + vs]
+    stream = torch.cuda.current_stream()
+    p0 = P0.tolist()
+    sweep = [1, 2, 4, 8, 16]
+    ws = torch.empty(max(pkv.chunk_workspace_size(Bq, Hq, Hkv, C, S) for S in sweep + [0]), dtype=torch.uint8,
+                     device=dev)
+
+    def attn(S):
+        return lambda i: pkv.chunk_attention(q, ks[0], vs[0], table, maxb, bs, p0, out, pool=pool, workspace=ws,
+                                             num_splits=S)
+
+    def step(i):
+        pkv.paged_cache_update_kv(pool, ks[0], vs[0], table, nk, nk, p0, C)
+        attn(0)(i)
+
+    us_step = _timed(step, steps, warmup, stream)
+    us_auto = _timed(attn(0), steps, warmup, stream)
+    us_sweep = {str(S): round(_timed(attn(S), steps, warmup, stream), 2) for S in sweep}
+    for bnd in binds:
+        bnd.close()
+    flops = 4.0 * Hq * Dq * float(np.sum(C * P0 + C * (C + 1) / 2))
+    tflops = flops / (us_auto * 1e-6) / 1e12
+    peak = 2500.0
+    return _line("causal chunk attention TFLOP/s (one request, 512-token chunk, MFMA bf16)", tflops, "TFLOP/s",
+                 steps, warmup, us_step, "bf16",
+                 {"workload": "qwen-chunk-1row", "batch": Bq, "chunk": C, "q_heads": Hq, "kv_heads": Hkv,
+                  "head_dim": Dq, "prefix": int(P0[0])},
+                 {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                  "frac": round(tflops / peak, 4), "traffic": None}, cpu,
+                 attn_us=round(us_auto, 2), step_us=round(us_step, 2), attn_flops=flops,
+                 attn_us_by_splits=us_sweep)
+
+
 def bench_mfma_ceiling(steps, warmup, cpu):
     """What the matrix cores deliver on this board for the data the benchmarks use.  Dense bf16 MFMA work
     is limited by power before the published rate is reached, and the limit depends on the operands'
@@ -1183,8 +1235,9 @@ def cpu_tiny(steps, warmup):
 
 
 WORKLOADS = {"contig": bench_contig, "paged": bench_paged, "int4": bench_int4, "qwen-decode": bench_qwen_decode,
-             "qwen-chunk": bench_qwen_chunk, "sample": bench_sample, "window": bench_window, "mixed": bench_mixed,
-             "generate": bench_generate, "tiny": bench_tiny, "mfma-ceiling": bench_mfma_ceiling}
+             "qwen-chunk": bench_qwen_chunk, "qwen-chunk-1row": bench_qwen_chunk_1row, "sample": bench_sample,
+             "window": bench_window, "mixed": bench_mixed, "generate": bench_generate, "tiny": bench_tiny,
+             "mfma-ceiling": bench_mfma_ceiling}
 CPU_BASELINES = {"paged32k": cpu_paged32k, "contig": cpu_contig, "paged": cpu_paged, "int4": cpu_int4,
                  "qwen-decode": cpu_qwen_decode, "qwen-chunk": cpu_qwen_chunk, "sample": cpu_sample,
                  "window": cpu_window, "mixed": cpu_mixed, "generate": cpu_generate, "tiny": cpu_tiny}

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 7
+#define PKV_ABI_VERSION 8
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -452,6 +452,36 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
                                int32_t max_blocks_per_seq, int32_t block_size,
                                const pkv_pool* pool, const int32_t* p0, float scale,
                                int32_t left_window, pkv_tensor* out, void* stream);
+
+/* Workspace (bytes) pkv_chunk_attention_split needs for B rows, Hq query
+ * heads, Hkv K/V heads and C chunk tokens with `num_splits` parts (0 = the
+ * most the library picks by itself on the current device); 0 when no
+ * workspace is needed or the arguments are invalid. */
+size_t pkv_chunk_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t C, int32_t num_splits);
+
+/* pkv_chunk_attention with the key range of every workgroup (256 query rows
+ * of one K/V head) cut into num_splits near-equal parts, each part its own
+ * workgroup, and the parts' partial results combined by the log-sum-exp
+ * merge of the decode calls: the online softmax of "Kernel implementation"
+ * taken over a partition of the keys.  For small batches, whose launch
+ * would leave compute units idle.  Arguments and results as for
+ * pkv_chunk_attention, plus:
+ * num_splits: 1 = no split (the pkv_chunk_attention launch, workspace
+ *           unused); 2 .. 64 = that many parts (parts with no key tile write
+ *           an empty partial); 0 = library choice from the launch size and
+ *           the longest key range.  Other values: PKV_E_ARG.
+ * workspace: device scratch of at least pkv_chunk_workspace_size(B, Hq,
+ *           Hkv, C, num_splits) bytes, 256-byte aligned, disjoint from q,
+ *           out and the pools (PKV_E_NOMEM when smaller, PKV_E_ARG when
+ *           misaligned, PKV_E_ALIAS when overlapping); only read when more
+ *           than one part is used.  Stream-ordered: the next call on the
+ *           stream may reuse it. */
+pkv_status pkv_chunk_attention_split(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                     const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                     int32_t max_blocks_per_seq, int32_t block_size,
+                                     const pkv_pool* pool, const int32_t* p0, float scale,
+                                     int32_t left_window, pkv_tensor* out, void* workspace,
+                                     size_t workspace_bytes, int32_t num_splits, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Mixed-format pages                                                        */

@@ -134,6 +134,9 @@ _SIG = {
                                                   C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_chunk_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float, C.c_int32,
                                       _T, _VP]),
+    "pkv_chunk_workspace_size": (C.c_size_t, [C.c_int32] * 5),
+    "pkv_chunk_attention_split": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
+                                            C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_mixed_cache_update": (C.c_int, [_VP, _T, _T, _T, _VP, _T, _T, _I32P, C.c_int32, PageFormat, PageFormat,
                                          _VP]),
     "pkv_mixed_convert_pages": (C.c_int, [_T, _T, _T, _I32P, _I32P, C.c_int32, _P(PageFormat), _P(PageFormat),
@@ -162,7 +165,7 @@ for _name, (_res, _args) in _SIG.items():
         _fn.argtypes = _args
 
 
-ABI_VERSION = 7      # the argument lists above follow this version of include/pkv.h
+ABI_VERSION = 8      # the argument lists above follow this version of include/pkv.h
 if _lib.pkv_abi_version() != ABI_VERSION:
     raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
                       "rebuild it (python place_persistent_kv_amd/build.py)")
@@ -479,13 +482,29 @@ def paged_decode_attention_int4(q, k_codes, k_params, v_codes, v_params, page_ta
         "pkv_paged_decode_attention_int4")
 
 
+def chunk_workspace_size(B: int, Hq: int, Hkv: int, C: int, num_splits: int = 0) -> int:
+    return int(_lib.pkv_chunk_workspace_size(B, Hq, Hkv, C, num_splits))
+
+
 def chunk_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, block_size: int, p0, out,
-                    pool: Optional[Pool] = None, scale: float = 0.0, stream=None, left_window: int = -1) -> None:
-    _check(_lib.pkv_chunk_attention(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
-                                    _ptr(page_table), int(max_blocks_per_seq), int(block_size), _pool_handle(pool),
-                                    _i32_array(p0), float(scale), int(left_window), C.byref(desc(out)),
-                                    _stream(stream)),
-           "pkv_chunk_attention")
+                    pool: Optional[Pool] = None, scale: float = 0.0, stream=None, left_window: int = -1,
+                    workspace=None, num_splits: int = 1) -> None:
+    """Causal chunk attention; with ``num_splits`` other than 1 (0 = library choice) the key range of every
+    workgroup is split into parts whose partials ``workspace`` (``chunk_workspace_size`` bytes) holds."""
+    if num_splits == 1 and workspace is None:
+        _check(_lib.pkv_chunk_attention(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+                                        _ptr(page_table), int(max_blocks_per_seq), int(block_size),
+                                        _pool_handle(pool), _i32_array(p0), float(scale), int(left_window),
+                                        C.byref(desc(out)), _stream(stream)),
+               "pkv_chunk_attention")
+        return
+    _check(_lib.pkv_chunk_attention_split(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+                                          _ptr(page_table), int(max_blocks_per_seq), int(block_size),
+                                          _pool_handle(pool), _i32_array(p0), float(scale), int(left_window),
+                                          C.byref(desc(out)), _ptr(workspace),
+                                          0 if workspace is None else _nbytes(workspace), int(num_splits),
+                                          _stream(stream)),
+           "pkv_chunk_attention_split")
 
 
 # ---------------------------------------------------------------------------

@@ -59,6 +59,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -68,6 +70,7 @@ constexpr int kThreads = 64 * kWavesC;
 constexpr int kRows = kWavesC * 32;  // query rows per workgroup (256)
 constexpr int kKeys = 64;       // keys per tile
 constexpr int kTileElems = kKeys * kCD;   // one K or V tile (bf16 elements, 16 KB)
+static_assert(kRows == kChunkQueryRows && kKeys == kChunkKeys, "host and kernel tile shapes differ");
 constexpr float kLazyC = 8.0f;
 constexpr float kLazyP = 256.0f;   // 2^kLazyC
 
@@ -185,19 +188,26 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     const int hl = lane >> 5;     // which half of the wave
     const int col = lane & 31;    // MFMA column = query row within the wave's row group
 
-    // ---- work item: (row b, kv head, query tile), XCD-grouped when possible
+    // ---- work item: (row b, kv head, query tile, key range), XCD-grouped
+    // when possible (the query tiles of one (row, kv head, key range) share
+    // its K/V tiles in that XCD's L2)
     const int n_qt = (a.C + P - 1) / P;
     const int n_bkv = a.rows * a.Hkv;
-    int bkv, qt;
+    const int S = a.kv_splits;
+    int bkv, qt, ks;
     {
         const int id = blockIdx.x;
         if (n_bkv % 8 == 0) {
             const int xcd = id % 8, local = id / 8;
             qt = local % n_qt;
-            bkv = (local / n_qt) * 8 + xcd;
+            const int rest = local / n_qt;
+            ks = rest % S;
+            bkv = (rest / S) * 8 + xcd;
         } else {
             qt = id % n_qt;
-            bkv = id / n_qt;
+            const int rest = id / n_qt;
+            ks = rest % S;
+            bkv = rest / S;
         }
     }
     const int b = a.order[bkv / a.Hkv];
@@ -226,6 +236,38 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
+
+    // key tiles this workgroup visits: [it0, n_tiles), from the first tile
+    // any of its queries sees to the tile of its last key, or (split over the
+    // keys) part ks of S near-equal parts of that range
+    int it0, n_tiles;
+    {
+        const int first = wg_lo_first / kKeys, end = wg_last_key / kKeys + 1;
+        const int per = (end - first + S - 1) / S;
+        it0 = first + ks * per;
+        n_tiles = min(end, it0 + per);
+    }
+    const int n = n_tiles - it0;
+
+    // split partial of this lane's query row: the unnormalised output (this
+    // lane's dims), and from the lane of the first half the running max (log2
+    // units) and the sum over both halves
+    auto store_partial = [&](float lt) {
+        if (t >= a.C) return;
+        const int64_t row = ((int64_t(b) * a.Hq + h) * a.C + t) * S + ks;
+        float* wo = a.ws_o + row * kCD;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                *reinterpret_cast<f32x4_t*>(wo + 32 * d + 8 * e4 + 4 * hl) =
+                    f32x4_t{o[d][4 * e4], o[d][4 * e4 + 1], o[d][4 * e4 + 2], o[d][4 * e4 + 3]};
+        if (hl == 0) *reinterpret_cast<f32x2_t*>(a.ws_ml + row * 2) = f32x2_t{m, lt};
+    };
+    if (n <= 0) {        // a part with no key tile (more parts than tiles): empty partial
+        store_partial(0.0f);
+        return;
+    }
 
     // ---- global -> LDS loads of one tile, by the four waves of one group
     // (see below): wave w or w + 4 fills rows 16 w .. 16 w + 15 of a tile with
@@ -415,9 +457,6 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
     // outstanding scalar load.  Loads past the last tile re-read it
     // (harmless).
     const int grp = wave >> 2;
-    const int n_tiles = wg_last_key / kKeys + 1;
-    const int it0 = wg_lo_first / kKeys;     // first tile any query of the workgroup sees
-    const int n = n_tiles - it0;             // tiles this workgroup visits
     auto tile_key = [&](int j) { return min(it0 + j, n_tiles - 1) * kKeys; };
     auto need_mask = [&](int j) {
         const int k0 = (it0 + j) * kKeys;
@@ -571,7 +610,9 @@ __global__ __launch_bounds__(kThreads) void chunk_attention_kernel(ChunkArgs a) 
 
     // ---- normalise and store: lane holds dims 32 d + 8 (e / 4) + 4 hl + e % 4 of its row
     const float lt = sum_halves(l);
-    if (t < a.C) {
+    if (S > 1) {
+        store_partial(lt);
+    } else if (t < a.C) {
         const float inv = 1.0f / lt;
         uint16_t* O = a.out + ((int64_t(b) * a.Hq + h) * a.C + t) * kCD;
 #pragma unroll
@@ -595,7 +636,7 @@ bool chunk_supported(int D, int G, int bs, int C) {
 
 hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s) {
     const int P = kRows / G;
-    const int blocks = a.rows * a.Hkv * ((a.C + P - 1) / P);
+    const int blocks = a.rows * a.Hkv * ((a.C + P - 1) / P) * a.kv_splits;
     if (blocks <= 0) return hipSuccess;
     switch (G) {
 #define PKV_CHUNK(GG)                                                                                  \

@@ -12,6 +12,7 @@
 #include "pkv_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdarg>
@@ -1444,12 +1445,66 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
 }
 
 // ---------------------------------------------------------------------------
-pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
-                               const pkv_tensor* v_pool, const int32_t* page_table_dev,
-                               int32_t max_blocks_per_seq, int32_t block_size,
-                               const pkv_pool* pool, const int32_t* p0, float scale,
-                               int32_t left_window,
-                               pkv_tensor* out, void* stream) {
+namespace {
+
+// Compute units of the current device (256 on a whole gfx950 part, fewer in
+// a partitioned mode); 256 when no device answers.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+// Workgroups of one chunk launch of `rows` rows without a split.
+int64_t chunk_workgroups(int64_t rows, int64_t Hkv, int G, int64_t C) {
+    return rows * Hkv * ceil_div(C, kChunkQueryRows / G);
+}
+
+// Most parts the library picks by itself: at most four workgroups per CU in
+// total (one workgroup fills a CU's LDS) and kChunkMaxAutoSplits.
+constexpr int kChunkMaxAutoSplits = 16;
+int chunk_auto_cap(int64_t base, int cus) {
+    if (base >= cus) return 1;
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kChunkMaxAutoSplits, 4 * cus / base)));
+}
+
+// Parts per key range when the caller leaves the choice to the library.  A
+// workgroup occupies a CU alone, so a launch of fewer workgroups than CUs
+// leaves CUs idle; S parts multiply the workgroups by S and cost the partials
+// (written by the attention, read by the merge) and a merge launch.  Modelled
+// time of S parts: rounds of the grid over the CUs x (tiles / S + 2) tile
+// times of about 1.9 us (256 query rows x 64 keys x 128 dims, both products,
+// at the measured matrix rate per CU), plus 3 us and the partial bytes at
+// 4 TB/s for the merge; the cheapest S up to the cap wins.
+int chunk_auto_splits(int64_t base, int cus, int64_t max_tiles, int64_t query_rows) {
+    const int cap = chunk_auto_cap(base, cus);
+    int best = 1;
+    double best_us = 0.0;
+    for (int S = 1; S <= cap; ++S) {
+        const double rounds = double(ceil_div(base * S, cus));
+        double us = rounds * (double(ceil_div(max_tiles, S)) + 2.0) * 1.9;
+        if (S > 1) us += 3.0 + 2.0 * double(S) * double(query_rows) * (kChunkD + 2) * 4.0 / 4.0e6;
+        if (S == 1 || us < best_us) {
+            best = S;
+            best_us = us;
+        }
+    }
+    return best;
+}
+
+pkv_status chunk_attention_impl(const pkv_tensor* q, const pkv_tensor* k_pool, const pkv_tensor* v_pool,
+                                const int32_t* page_table_dev, int32_t max_blocks_per_seq, int32_t block_size,
+                                const pkv_pool* pool, const int32_t* p0, float scale, int32_t left_window,
+                                pkv_tensor* out, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                void* stream) {
     PKV_TRY(check_tensor(q, "q", 4, 4));
     PKV_TRY(check_tensor(out, "out", 4, 4));
     PKV_TRY(check_tensor(k_pool, "k_pool", 4, 4));
@@ -1492,7 +1547,36 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
     PKV_TRY(check_disjoint(q, "q", os, "out"));
     PKV_TRY(check_disjoint(k_pool, "k_pool", os, "out"));
     PKV_TRY(check_disjoint(v_pool, "v_pool", os, "out"));
+    if (num_splits < 0 || num_splits > kChunkMaxSplits)
+        return fail(PKV_E_ARG, "chunk attention: num_splits must be 0 (library choice) .. %d", kChunkMaxSplits);
     if (B == 0) return ok();
+    const int64_t rows_max = std::min<int64_t>(B, kMaxRows);
+    int S = num_splits;
+    if (S == 0) {
+        // longest key range of a workgroup: the last query tile of the longest row
+        int64_t p0_max = 0;
+        for (int64_t b = 0; b < B; ++b) p0_max = std::max<int64_t>(p0_max, p0[b]);
+        const int64_t last = p0_max + C - 1;
+        const int64_t first = left_window >= 0 ? std::max<int64_t>(0, last - (kChunkQueryRows / G) + 1 - left_window) : 0;
+        S = chunk_auto_splits(chunk_workgroups(rows_max, Hkv, G, C), device_cus(),
+                              last / kChunkKeys - first / kChunkKeys + 1, rows_max * Hq * C);
+    }
+    float* ws_o = nullptr;
+    float* ws_ml = nullptr;
+    if (S > 1) {
+        const size_t need = ws_bytes_for(rows_max, Hq * C, kChunkD, S);
+        if (!workspace || workspace_bytes < need)
+            return fail(PKV_E_NOMEM, "chunk attention: workspace of %zu bytes needed, %zu given (pkv_chunk_workspace_size)",
+                        need, workspace_bytes);
+        if (reinterpret_cast<uintptr_t>(workspace) % 256)
+            return fail(PKV_E_ARG, "chunk attention: workspace must be 256-byte aligned");
+        const Span wss = span(workspace, static_cast<int64_t>(need));
+        if (overlap(wss, os) || overlap(wss, span(q)) || overlap(wss, span(k_pool)) || overlap(wss, span(v_pool)))
+            return fail(PKV_E_ALIAS, "chunk attention: workspace overlaps q, out or a pool");
+        const size_t o_bytes = (static_cast<size_t>(rows_max * Hq * C * S * kChunkD) * 4 + 255) & ~size_t(255);
+        ws_o = static_cast<float*>(workspace);
+        ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int64_t b0 = 0; b0 < B; b0 += kMaxRows) {
         ChunkArgs a;
@@ -1519,10 +1603,63 @@ pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
         }
         // longest rows first, so that the short ones fill the end of the launch
         std::stable_sort(a.order, a.order + a.rows, [&](uint16_t x, uint16_t y) { return a.p0[x] > a.p0[y]; });
+        a.kv_splits = S;
+        a.ws_o = ws_o;
+        a.ws_ml = ws_ml;
         PKV_HIP(launch_chunk(a, G, s), "chunk attention launch");
+        if (S > 1) {
+            // the partials of query (row, head, token) sit where the merge
+            // expects those of row `row` and "head" head * C + token
+            MergeArgs m;
+            m.ws_o = ws_o;
+            m.ws_ml = ws_ml;
+            m.out = a.out;
+            m.out_kind = kKvBF16;
+            m.Hq = static_cast<int32_t>(Hq * C);
+            m.D = kChunkD;
+            m.S_max = S;
+            m.row0 = 0;
+            m.rows = a.rows;
+            m.min_splits = 1;
+            for (int i = 0; i < a.rows; ++i) m.nsplit[i] = S;
+            PKV_HIP(launch_merge(m, s), "chunk attention merge launch");
+        }
     }
     return ok();
 }
+
+}  // namespace
+
+size_t pkv_chunk_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t C, int32_t num_splits) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || C <= 0 || Hq % Hkv != 0 || num_splits < 0 || num_splits > kChunkMaxSplits)
+        return 0;
+    const int G = Hq / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return 0;
+    const int64_t rows_max = std::min<int64_t>(B, kMaxRows);
+    const int S = num_splits > 0 ? num_splits : chunk_auto_cap(chunk_workgroups(rows_max, Hkv, G, C), device_cus());
+    return S > 1 ? ws_bytes_for(rows_max, int64_t(Hq) * C, kChunkD, S) : 0;
+}
+
+pkv_status pkv_chunk_attention(const pkv_tensor* q, const pkv_tensor* k_pool,
+                               const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                               int32_t max_blocks_per_seq, int32_t block_size,
+                               const pkv_pool* pool, const int32_t* p0, float scale,
+                               int32_t left_window,
+                               pkv_tensor* out, void* stream) {
+    return chunk_attention_impl(q, k_pool, v_pool, page_table_dev, max_blocks_per_seq, block_size, pool, p0, scale,
+                                left_window, out, nullptr, 0, 1, stream);
+}
+
+pkv_status pkv_chunk_attention_split(const pkv_tensor* q, const pkv_tensor* k_pool,
+                                     const pkv_tensor* v_pool, const int32_t* page_table_dev,
+                                     int32_t max_blocks_per_seq, int32_t block_size,
+                                     const pkv_pool* pool, const int32_t* p0, float scale,
+                                     int32_t left_window, pkv_tensor* out, void* workspace,
+                                     size_t workspace_bytes, int32_t num_splits, void* stream) {
+    return chunk_attention_impl(q, k_pool, v_pool, page_table_dev, max_blocks_per_seq, block_size, pool, p0, scale,
+                                left_window, out, workspace, workspace_bytes, num_splits, stream);
+}
+
 
 // ---------------------------------------------------------------------------
 namespace {

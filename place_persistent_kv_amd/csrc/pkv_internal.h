@@ -255,7 +255,19 @@ struct ChunkArgs {
     float scale_log2;
     int32_t p0[kMaxRows];
     uint16_t order[kMaxRows];    // rows by descending prefix: the longest go out first
+    // Split over the keys (kv_splits > 1): workgroup (row, kv head, query
+    // tile, part s) takes part s of kv_splits near-equal parts of its query
+    // tile's key-tile range and writes, per query row, the unnormalised output
+    // and (max in log2 units, sum) to the workspace for the merge; with
+    // kv_splits == 1 the output is written directly.
+    int32_t kv_splits = 1;
+    float* ws_o = nullptr;       // [rows, Hq, C, kv_splits, 128]
+    float* ws_ml = nullptr;      // [rows, Hq, C, kv_splits, 2]
 };
+constexpr int kChunkQueryRows = 256;   // query rows (token x head pairs of one K/V head) per workgroup
+constexpr int kChunkKeys = 64;         // keys per tile
+constexpr int kChunkD = 128;           // head size
+constexpr int kChunkMaxSplits = 64;    // parts of a workgroup's key range
 bool chunk_supported(int D, int G, int bs, int C);
 hipError_t launch_chunk(const ChunkArgs& a, int G, hipStream_t s);
 

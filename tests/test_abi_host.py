@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if getattr(pkv._lib, n, None) is None]
     assert not missing, missing
     assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
-    assert pkv.abi_version() == pkv.ABI_VERSION == 7
+    assert pkv.abi_version() == pkv.ABI_VERSION == 8
 
 
 def R(ptr, dtype, shape):
@@ -346,6 +346,40 @@ def test_chunk_attention_checks():
         args = {**dict(q=q, kp=kp, vp=vp, out=out), **bad}
         assert status_of(f, args["q"], args["kp"], args["vp"], table, 8, 16, [0, 0], args["out"]) == pkv.E_LAYOUT
         assert "16-byte" in pkv.last_error()
+
+
+def test_chunk_split_workspace_is_checked():
+    q = R(FAKE + 0x3000000, pkv.BF16, [2, 4, 32, 128])
+    out = R(FAKE + 0x3400000, pkv.BF16, [2, 4, 32, 128])
+    kp = R(FAKE + 0x100000, pkv.BF16, [32, 2, 16, 128])
+    vp = R(FAKE + 0x900000, pkv.BF16, [32, 2, 16, 128])
+    table = R(FAKE + 0x2000000, pkv.I32, [2, 8])
+    f = pkv.chunk_attention
+    need = pkv.chunk_workspace_size(2, 4, 2, 32, 4)
+    for S in (-1, 65):
+        assert status_of(f, q, kp, vp, table, 8, 16, [40, 0], out, workspace=R(FAKE + 0x4000000, pkv.U8, [need]),
+                         num_splits=S) == pkv.E_ARG
+    assert status_of(f, q, kp, vp, table, 8, 16, [40, 0], out, num_splits=4) == pkv.E_NOMEM
+    small = R(FAKE + 0x4000000, pkv.U8, [need - 256])
+    assert status_of(f, q, kp, vp, table, 8, 16, [40, 0], out, workspace=small, num_splits=4) == pkv.E_NOMEM
+    skew = R(FAKE + 0x4000000 + 128, pkv.U8, [need])
+    assert status_of(f, q, kp, vp, table, 8, 16, [40, 0], out, workspace=skew, num_splits=4) == pkv.E_ARG
+    for inside in (out.ptr, kp.ptr, q.ptr):
+        ws = R(inside, pkv.U8, [need])
+        assert status_of(f, q, kp, vp, table, 8, 16, [40, 0], out, workspace=ws, num_splits=4) == pkv.E_ALIAS
+
+
+def test_chunk_workspace_size():
+    up = lambda x: -(-x // 256) * 256
+    for B, Hq, Hkv, C, S in [(2, 4, 2, 32, 4), (1, 16, 8, 512, 8), (3, 8, 8, 7, 64), (300, 2, 1, 5, 2)]:
+        rows = min(B, 256)
+        assert pkv.chunk_workspace_size(B, Hq, Hkv, C, S) == up(rows * Hq * C * S * 128 * 4) + \
+            up(rows * Hq * C * S * 2 * 4)
+    assert pkv.chunk_workspace_size(2, 4, 2, 32, 1) == 0                  # no split, no workspace
+    assert pkv.chunk_workspace_size(128, 16, 8, 512, 0) == 0              # a launch that fills the device
+    assert pkv.chunk_workspace_size(1, 16, 8, 512, 0) > 0                 # one row leaves CUs idle
+    for bad in [(0, 4, 2, 32, 2), (2, 6, 4, 32, 2), (2, 4, 2, 0, 2), (2, 4, 2, 32, 65), (2, 32, 2, 32, 2)]:
+        assert pkv.chunk_workspace_size(*bad) == 0
 
 
 # --------------------------------------------------------------------------- sampling

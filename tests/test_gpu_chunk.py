@@ -31,6 +31,15 @@ def _assert_chunk_bound(got, ref, qh, K, V, p0, left_window=-1):
         assert_bf16_pv_bound(got[h], ref[h], s, np.broadcast_to(V[h // G], (C,) + V[h // G].shape))
 
 
+def _chunk(d, q, out, maxb, bs, p0, W=-1, S=1):
+    """Chunk attention on `d`'s pools; S != 1 splits every workgroup's key range (0: library choice)."""
+    B, Hq, C, _ = out.shape
+    Hkv = d["kd"].shape[1]
+    ws = None if S == 1 else workspace(pkv.chunk_workspace_size(B, Hq, Hkv, C, S))
+    pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"], left_window=W,
+                        workspace=ws, num_splits=S)
+
+
 def _setup(seed, B, Hq, Hkv, D, bs, p0, C, maxb, fill=0):
     """Prefix of p0[b] tokens already in the pages; returns device state and the host mirror.  Slots no
     append writes (past a row's length, and unreserved pages) hold the bf16 bits `fill`."""
@@ -114,6 +123,65 @@ def test_chunk_left_window_matches_oracle(W, G, C):
         _assert_chunk_bound(got[b], ref, qh[b], K, V, int(p0[b]), W)
 
 
+@pytest.mark.parametrize("S,G,C,bs,W", [(2, 2, 100, 16, -1), (3, 1, 64, 16, -1), (5, 4, 130, 32, -1),
+                                       (64, 2, 100, 16, -1), (3, 2, 300, 8, 150), (4, 8, 64, 16, 1000),
+                                       (7, 2, 1, 16, -1), (2, 2, 90, 4, 63), (0, 2, 256, 16, -1)])
+def test_split_over_keys_matches_oracle(S, G, C, bs, W):
+    """The key range of every workgroup cut into S parts whose partials the log-sum-exp merge combines
+    (S = 0: the library's choice, which splits this small batch).  Parts hold whole tiles, a part may hold
+    none (S = 64 against rows of two tiles), and a query may see no key of a part (the diagonal tiles and
+    the window's first tiles)."""
+    require_gpu()
+    B, Hkv, D = 3, 2, 128
+    Hq = Hkv * G
+    p0 = np.array([0, 37, 1200], np.int32)
+    maxb = -(-(int(p0.max()) + C) // bs) + 1
+    d = _setup(1040 + S + G + C, B, Hq, Hkv, D, bs, p0, C, maxb)
+    with pkv.bind_writable(d["kd"]), pkv.bind_writable(d["vd"]):
+        pkv.paged_cache_update_kv(d["lib_pool"], d["kd"], d["vd"], d["table"], bf16_dev(d["new_k"]),
+                                  bf16_dev(d["new_v"]), p0, C)
+    ocache.paged_cache_update(d["kp"], d["ref_pool"].table, d["new_k"], p0, C, bs, d["ref_pool"].held)
+    ocache.paged_cache_update(d["vp"], d["ref_pool"].table, d["new_v"], p0, C, bs, d["ref_pool"].held)
+    if S == 0:
+        assert pkv.chunk_workspace_size(B, Hq, Hkv, C, 0) > 0
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    _chunk(d, bf16_dev(d["q"]), out, maxb, bs, p0, W, S)
+    got = onum.bf16_to_f64(bits_host(out))
+    qh = onum.bf16_to_f64(d["q"])
+    for b in range(B):
+        L = int(p0[b]) + C
+        K = onum.bf16_to_f64(ocache.paged_gather(d["kp"], d["ref_pool"].table[b], L, bs))
+        V = onum.bf16_to_f64(ocache.paged_gather(d["vp"], d["ref_pool"].table[b], L, bs))
+        ref = oattn.chunk_attention(qh[b], K, V, int(p0[b]), left_window=W)
+        _assert_chunk_bound(got[b], ref, qh[b], K, V, int(p0[b]), W)
+
+
+def test_split_workspace_errors():
+    require_gpu()
+    B, Hkv, G, D, bs, C = 1, 2, 2, 128, 16, 64
+    Hq = Hkv * G
+    p0 = np.array([500], np.int32)
+    maxb = -(-(int(p0[0]) + C) // bs) + 1
+    d = _setup(1060, B, Hq, Hkv, D, bs, p0, C, maxb)
+    q = bf16_dev(d["q"])
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    need = pkv.chunk_workspace_size(B, Hq, Hkv, C, 4)
+    ws = workspace(need + 512)
+    cases = [(None, 4, pkv.E_NOMEM), (ws[:need - 256], 4, pkv.E_NOMEM), (ws[128:need + 128], 4, pkv.E_ARG),
+             (ws, 65, pkv.E_ARG), (ws, -1, pkv.E_ARG)]
+    for w, S, status in cases:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"],
+                                workspace=w, num_splits=S)
+        assert e.value.status == status, (S, status)
+    big = workspace(need + out.numel() * 2)       # the workspace may not overlap the output
+    inner = big[:out.numel() * 2].view(torch.bfloat16).view(out.shape)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], maxb, bs, p0, inner, pool=d["lib_pool"],
+                            workspace=big, num_splits=4)
+    assert e.value.status == pkv.E_ALIAS
+
+
 @pytest.mark.parametrize("rise", [10.0, 14.0])
 def test_running_max_rise_in_a_later_tile(rise):
     """One prefix key in a later, unmasked tile outscores the rest by about `rise` log2 units (the typical
@@ -190,9 +258,10 @@ def test_chunk_capacity_and_page_errors():
     assert e.value.status == pkv.E_PAGE
 
 
-@pytest.mark.parametrize("W,G,C,bs", [(-1, 2, 300, 16), (-1, 4, 130, 32), (-1, 1, 64, 16), (37, 2, 300, 16),
-                                      (200, 8, 100, 16)])
-def test_planted_key_marks_the_causal_and_window_edges(W, G, C, bs):
+@pytest.mark.parametrize("W,G,C,bs,S", [(-1, 2, 300, 16, 1), (-1, 4, 130, 32, 1), (-1, 1, 64, 16, 1),
+                                        (37, 2, 300, 16, 1), (200, 8, 100, 16, 1), (-1, 2, 300, 16, 3),
+                                        (37, 2, 300, 16, 2)])
+def test_planted_key_marks_the_causal_and_window_edges(W, G, C, bs, S):
     """Every query carries 4.0 in one dimension and one key per (row, kv head) carries 128.0 there and 0
     elsewhere, so it outscores every other key by e^40.  A query that sees that key must return its V row
     exactly; a query that must not see it (the key lies after the query, or before its window) must return
@@ -209,7 +278,7 @@ def test_planted_key_marks_the_causal_and_window_edges(W, G, C, bs):
         pkv.paged_cache_update(d["lib_pool"], d["vd"], d["table"], bf16_dev(d["new_v"]), p0, C)
     q = bf16_dev(d["q"])
     base = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
-    pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], maxb, bs, p0, base, pool=d["lib_pool"], left_window=W)
+    _chunk(d, q, base, maxb, bs, p0, W, S)
     base_h = bits_host(base)
     table = d["ref_pool"].table
     probe = np.zeros(D, np.float32)
@@ -224,7 +293,7 @@ def test_planted_key_marks_the_causal_and_window_edges(W, G, C, bs):
             picks[(b, kvh)] = p
             d["kd"][int(table[b, p // bs]), kvh, p % bs] = bf16_dev(synth.f32_to_bf16_bits(probe))
     out = torch.empty_like(base)
-    pkv.chunk_attention(q, d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"], left_window=W)
+    _chunk(d, q, out, maxb, bs, p0, W, S)
     got = bits_host(out)
     vh = bits_host(d["vd"])
     seen = unseen = 0
@@ -243,9 +312,10 @@ def test_planted_key_marks_the_causal_and_window_edges(W, G, C, bs):
     assert seen and unseen
 
 
-@pytest.mark.parametrize("G,C,bs,W", [(2, 100, 16, -1), (4, 70, 32, -1), (2, 300, 8, -1), (1, 5, 16, -1),
-                                      (2, 129, 64, -1), (2, 100, 16, 40), (4, 90, 4, -1)])
-def test_unwritten_slots_are_never_used(G, C, bs, W):
+@pytest.mark.parametrize("G,C,bs,W,S", [(2, 100, 16, -1, 1), (4, 70, 32, -1, 1), (2, 300, 8, -1, 1),
+                                        (1, 5, 16, -1, 1), (2, 129, 64, -1, 1), (2, 100, 16, 40, 1),
+                                        (4, 90, 4, -1, 1), (2, 100, 16, -1, 3), (4, 90, 4, -1, 2)])
+def test_unwritten_slots_are_never_used(G, C, bs, W, S):
     """Every slot no append writes holds a bf16 NaN: the rows past each row's length in its last page, and
     the pages no row holds.  Lengths end inside a page and inside a 64-key tile.  The outputs must be finite
     and match the oracle, which only sees the written rows (a NaN key past the last one is masked; a NaN
@@ -264,8 +334,7 @@ def test_unwritten_slots_are_never_used(G, C, bs, W):
     assert np.array_equal(bits_host(d["kd"]), d["kp"]) and np.array_equal(bits_host(d["vd"]), d["vp"])
     assert any((int(x) + C) % bs for x in p0)                     # some row ends inside a page
     out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
-    pkv.chunk_attention(bf16_dev(d["q"]), d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"],
-                        left_window=W)
+    _chunk(d, bf16_dev(d["q"]), out, maxb, bs, p0, W, S)
     got = onum.bf16_to_f64(bits_host(out))
     assert np.isfinite(got).all()
     qh = onum.bf16_to_f64(d["q"])

@@ -1,7 +1,7 @@
 """Batches larger than the 256 rows one launch takes: the host splits them into launches whose row,
 page-table, query and output offsets must line up.  Every row of a 300-row batch is checked against
 the oracle for the paired paged append, paged decode (with and without splits), contiguous decode
-(fast and generic kernels), INT4 decode and chunk attention."""
+(fast and generic kernels), INT4 decode and chunk attention (with and without a split over the keys)."""
 import numpy as np
 import pytest
 import torch
@@ -49,7 +49,8 @@ def test_decode_and_paired_append_over_300_rows():
     assert np.array_equal(bits_host(d["kp"]), d["kp_host"]) and np.array_equal(bits_host(d["vp"]), d["vp_host"])
 
 
-def test_chunk_attention_over_300_rows():
+@pytest.mark.parametrize("S", [1, 2])         # without and with a split over the keys
+def test_chunk_attention_over_300_rows(S):
     require_gpu()
     Hkv, G, D, bs, C = 2, 2, 128, 16, 3
     Hq = Hkv * G
@@ -63,7 +64,9 @@ def test_chunk_attention_over_300_rows():
     ocache.paged_cache_update(d["vp"], d["ref_pool"].table, d["new_v"], p0, C, bs, d["ref_pool"].held)
     assert np.array_equal(bits_host(d["kd"]), d["kp"]) and np.array_equal(bits_host(d["vd"]), d["vp"])
     out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
-    pkv.chunk_attention(bf16_dev(d["q"]), d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"])
+    ws = None if S == 1 else workspace(pkv.chunk_workspace_size(B, Hq, Hkv, C, S))
+    pkv.chunk_attention(bf16_dev(d["q"]), d["kd"], d["vd"], d["table"], maxb, bs, p0, out, pool=d["lib_pool"],
+                        workspace=ws, num_splits=S)
     got = onum.bf16_to_f64(bits_host(out))
     qh = onum.bf16_to_f64(d["q"])
     for b in range(B):
