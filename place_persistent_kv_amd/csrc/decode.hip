@@ -427,9 +427,10 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge: one wave per (row, query head).  The partial outputs of the first
-// kMergeU splits are requested before anything else, so their latency
-// overlaps the pass over the split maxima and sums; the split weights go to
-// LDS; lane l sums dims l, l + 64, ... over the splits.
+// kMergeU splits and the (max, sum) pairs of the first 64 splits are
+// requested before anything else, so that one memory latency covers the
+// weights and the first batch; weights are read across lanes (splits 64 and
+// up: through LDS); lane l sums dims l, l + 64, ... over the splits.
 // ---------------------------------------------------------------------------
 constexpr int kMergeLdsSplits = 1024;
 constexpr int kMergeU = 8;         // splits per batch of loads
@@ -474,20 +475,36 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
             x[j][u] = j < nd && d < a.D && u < n0 ? po[int64_t(u) * a.D + d] : 0.0f;
     }
 
-    float mx = -FLT_MAX;
-    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, ml[2 * s]);
+    // (max, sum) of split `lane` in registers, requested with the outputs:
+    // one memory round trip covers the common case of at most 64 splits;
+    // splits 64 and up take further passes and keep their weights in LDS
+    float m_l = -FLT_MAX, l_l = 0.0f;
+    if (lane < n) {
+        const float2 v = *reinterpret_cast<const float2*>(ml + 2 * lane);
+        m_l = v.x;
+        l_l = v.y;
+    }
+    float mx = m_l;
+    for (int s = lane + 64; s < n; s += 64) mx = fmaxf(mx, ml[2 * s]);
     const float mn = wave_reduce(mx, true);
-    float ls = 0.0f;
-    for (int s = lane; s < n; s += 64) {
+    const float w_l = lane < n ? exp2_fast(m_l - mn) : 0.0f;
+    float ls = l_l * w_l;
+    for (int s = lane + 64; s < n; s += 64) {
         const float w = exp2_fast(ml[2 * s] - mn);
         ls += ml[2 * s + 1] * w;
         if (s < kMergeLdsSplits) s_w[s] = w;
     }
     ls = wave_reduce(ls, false);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    auto weight = [&](int su) { return su < kMergeLdsSplits ? s_w[su] : exp2_fast(ml[2 * su] - mn); };
+    if (n > 64) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    // weight of split su (uniform across the wave)
+    auto weight = [&](int su) {
+        if (su < 64) return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), su));
+        return su < kMergeLdsSplits ? s_w[su] : exp2_fast(ml[2 * su] - mn);
+    };
     const float inv = 1.0f / ls;
 
     float acc[kMergeMaxDPL][kMergeU];
