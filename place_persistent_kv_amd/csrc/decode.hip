@@ -64,10 +64,9 @@ struct SplitWork {
 __device__ __forceinline__ SplitWork split_work(const DecodeArgs& a, int r) {
     SplitWork w;
     if (a.len_dev == nullptr) {
-        w.b = find_row(a.split_begin, a.rows, r);
-        w.split = r - a.split_begin[w.b];
-        w.nsplit = a.split_begin[w.b + 1] - a.split_begin[w.b];
+        split_item(a.full_begin, a.tail_row, a.rows, r, w.b, w.split);
         w.L = a.len[w.b];
+        w.nsplit = (w.L - split_base(w.L, a.window) + a.tps - 1) / a.tps;
         w.ok = true;
         return w;
     }

@@ -67,5 +67,25 @@ __device__ __forceinline__ int find_row(const int32_t* split_begin, int rows, in
     return lo;
 }
 
+// Row and split of work item r of a launch over host lengths.  The splits
+// that hold a whole tps tokens come first, row by row (full_begin: prefix
+// sums of their per-row counts, full_begin[rows] their total), then each
+// row's shorter last split, longest first (tail_row), so that the largest
+// workgroups are dispatched first and the short ones fill the end of the
+// grid.  A row with r in its full range has full_begin[b] <= r <
+// full_begin[b + 1]; its last split is split number full_begin[b + 1] -
+// full_begin[b].
+__device__ __forceinline__ void split_item(const int32_t* full_begin, const uint16_t* tail_row, int rows, int r,
+                                           int& b, int& split) {
+    const int n_full = full_begin[rows];
+    if (r < n_full) {
+        b = find_row(full_begin, rows, r);
+        split = r - full_begin[b];
+    } else {
+        b = tail_row[r - n_full];
+        split = full_begin[b + 1] - full_begin[b];
+    }
+}
+
 }  // namespace
 }  // namespace pkv

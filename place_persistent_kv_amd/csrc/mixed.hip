@@ -331,10 +331,10 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     const int work = blockIdx.x;
     const int kvh = work % a.Hkv;
     const int r = work / a.Hkv;
-    const int b = find_row(a.split_begin, a.rows, r);
-    const int split = r - a.split_begin[b];
-    const int nsplit = a.split_begin[b + 1] - a.split_begin[b];
+    int b, split;
+    split_item(a.full_begin, a.tail_row, a.rows, r, b, split);
     const int L = a.len[b];
+    const int nsplit = (L - split_base(L, a.window) + a.tps - 1) / a.tps;
     const int vis0 = visible_begin(L, a.window);
     const int t0 = split_base(L, a.window) + split * a.tps;
     const int t1 = min(L, t0 + a.tps);

@@ -228,6 +228,25 @@ int64_t split_bound(int32_t max_len, int32_t num_splits) {
     return std::max(s_auto, s_gen);
 }
 
+// Work order of a launch over host lengths (the kernels' split_item): the
+// splits of a whole tps tokens first, row by row, then each row's shorter
+// last split, longest first.  span: the rows' split ranges (nsplit = ceil(span
+// / tps) each); returns the number of work items, sum of nsplit.
+int work_order(const int32_t* span, int rows, int32_t tps, int32_t* full_begin, uint16_t* tail_row) {
+    int n_full = 0;
+    for (int i = 0; i < rows; ++i) {
+        full_begin[i] = n_full;
+        n_full += span[i] / tps;
+    }
+    full_begin[rows] = n_full;
+    int n_tail = 0;
+    for (int i = 0; i < rows; ++i)
+        if (span[i] % tps) tail_row[n_tail++] = static_cast<uint16_t>(i);
+    std::stable_sort(tail_row, tail_row + n_tail,
+                     [&](uint16_t x, uint16_t y) { return span[x] % tps > span[y] % tps; });
+    return n_full + n_tail;
+}
+
 size_t ws_bytes_for(int64_t B, int64_t Hq, int64_t D, int64_t S) {
     // [B, Hq, S, D] partial outputs + [B, Hq, S, 2] (max, sum), each 256-aligned
     size_t o = static_cast<size_t>(B * Hq * S * D) * 4;
@@ -1011,11 +1030,9 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         } else {
             for (int i = 0; i < rows; ++i) {
                 a.len[i] = valid_len[b0 + i];
-                a.split_begin[i] = total;
-                total += full.nsplit[b0 + i];
                 any_split |= full.nsplit[b0 + i] > 1;
             }
-            a.split_begin[rows] = total;
+            total = work_order(span_len.data() + b0, rows, full.tps, a.full_begin, a.tail_row);
         }
         if (mixed) {
             PKV_HIP(launch_decode_mixed(a, G, total * static_cast<int>(Hkv), s), "mixed decode launch");
@@ -1419,11 +1436,9 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
         bool any_split = false;
         for (int i = 0; i < rows; ++i) {
             a.len[i] = valid_len[b0 + i];
-            a.split_begin[i] = total;
-            total += full.nsplit[b0 + i];
             any_split |= full.nsplit[b0 + i] > 1;
         }
-        a.split_begin[rows] = total;
+        total = work_order(span_len.data() + b0, rows, full.tps, a.full_begin, a.tail_row);
         PKV_HIP(launch_decode_int4(a, G, total * static_cast<int>(Hkv), s), "int4 decode launch");
         if (any_split) {
             MergeArgs m;

@@ -119,13 +119,17 @@ struct DecodeArgs {
     // Device lengths (else nullptr): row row0 + i has length len_dev[row0 + i],
     // S_max split slots, splits past its own count exit at once; rows whose
     // length is outside [1, len_limit] and rows that meet a page id outside
-    // [0, nb) set *status and write nothing.  len[] and split_begin[] unused.
+    // [0, nb) set *status and write nothing.  len[], full_begin[] and
+    // tail_row[] unused.
     const int32_t* len_dev = nullptr;
     int32_t len_limit = 0;
     int32_t nb = 0;
     int32_t* status = nullptr;
     int32_t len[kMaxRows];       // valid length per row
-    int32_t split_begin[kMaxRows + 1];  // prefix sum of splits per row
+    // work order (split_item): prefix sums of the rows' whole-tps splits, and
+    // the rows whose last split is shorter, by that split's size, longest first
+    int32_t full_begin[kMaxRows + 1];
+    uint16_t tail_row[kMaxRows];
 };
 
 struct Int4DecodeArgs {
@@ -143,7 +147,8 @@ struct Int4DecodeArgs {
     int32_t window;              // left window (-1 = unbounded)
     float scale_log2;
     int32_t len[kMaxRows];
-    int32_t split_begin[kMaxRows + 1];
+    int32_t full_begin[kMaxRows + 1];   // work order as in DecodeArgs
+    uint16_t tail_row[kMaxRows];
 };
 
 struct MergeArgs {
