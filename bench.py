@@ -459,7 +459,8 @@ def _hbm_roofline(nbytes, us):
 
 
 def bench_contig(steps, warmup, cpu):
-    """Contiguous bf16 cache [8, 8, 4096, 128]: append one K/V row + decode attention per step.
+    """Contiguous bf16 cache [8, 8, 4096, 128]: append one K/V row + decode attention per step (one fused call;
+    the two-call step is reported beside it).
     Six cache replicas are rotated so that each step reads K/V from HBM, not from the 256 MB MALL."""
     import numpy as np
     import torch
@@ -482,8 +483,13 @@ def bench_contig(steps, warmup, cpu):
     binds = [pkv.bind_writable(t) for t in kc + vc]
     stream = torch.cuda.current_stream()
 
-    def step(i, rot=True):
+    def step(i, rot=True):          # the append fused into the attention launch
         r = i % R if rot else 0
+        pos = (L0 + i % S).tolist()
+        pkv.decode_step(kc[r], vc[r], nk, nv, pos, 1, q, out, ws)
+
+    def step_two_calls(i):          # the K+V append and the attention as two calls
+        r = i % R
         pos = (L0 + i % S).tolist()
         pkv.cache_update_kv(kc[r], vc[r], nk, nv, pos, 1)
         pkv.decode_attention(q, kc[r], vc[r], [p + 1 for p in pos], out, ws)
@@ -493,6 +499,7 @@ def bench_contig(steps, warmup, cpu):
         pkv.decode_attention(q, kc[r], vc[r], (L0 + i % S + 1).tolist(), out, ws)
 
     us_step = _timed(step, steps, warmup, stream)
+    us_two = _timed(step_two_calls, steps, warmup, stream)
     us_attn = _timed(attn_only, steps, warmup, stream)
     us_warm = _timed(lambda i: attn_only(i, False), steps, warmup, stream)
     # captured step per replica: fused K+V append at the replica's device lengths, lengths + 1, attention
@@ -520,7 +527,7 @@ def bench_contig(steps, warmup, cpu):
                  us_step, "bf16", {"workload": "contig", "batch": Bc, "capacity": cap, "q_heads": Hq, "kv_heads": Hkv,
                                    "head_dim": Dc, "replicas_rotated": R},
                  _hbm_roofline(nbytes, us_attn), cpu_res, attn_us=round(us_attn, 2),
-                 attn_us_warm=round(us_warm, 2), attn_algorithmic_bytes=nbytes,
+                 attn_us_warm=round(us_warm, 2), attn_algorithmic_bytes=nbytes, step_two_call_us=round(us_two, 2),
                  graph_step_us=round(us_graph, 2), graph_tokens_per_s=round(Bc / (us_graph * 1e-6), 1))
 
 
@@ -1054,23 +1061,31 @@ def bench_tiny(steps, warmup, cpu):
     ws = torch.empty(max(256, pkv.decode_workspace_size(1, 1, 1, 4, cap)), device=dev, dtype=torch.uint8)
     bk, bv = pkv.bind_writable(kc), pkv.bind_writable(vc)
     host = np.zeros((steps, cap))
+    host2 = np.zeros((steps, cap))
     devt = np.zeros((steps, cap))
     rejected = np.zeros(steps)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cap)]
 
-    def run(record):
+    def run(record, fused=True):
+        # a step: the fused append + attention call (one launch); fused=False: the K+V append and the
+        # attention as two calls
         for t in range(cap):
             t0 = time.perf_counter()
             evs[t][0].record(stream)
-            pkv.cache_update_kv(kc, vc, kd[t], vd[t], [t], 1)
-            pkv.decode_attention(qd[t], kc, vc, [t + 1], out, ws)
+            if fused:
+                pkv.decode_step(kc, vc, kd[t], vd[t], [t], 1, qd[t], out, ws)
+            else:
+                pkv.cache_update_kv(kc, vc, kd[t], vd[t], [t], 1)
+                pkv.decode_attention(qd[t], kc, vc, [t + 1], out, ws)
             evs[t][1].record(stream)
             torch.cuda.synchronize()
             if record is not None:
-                host[record, t] = (time.perf_counter() - t0) * 1e6
+                (host if fused else host2)[record, t] = (time.perf_counter() - t0) * 1e6
+        if not fused:
+            return
         t0 = time.perf_counter()
         try:
-            pkv.cache_update_kv(kc, vc, kd[cap], vd[cap], [cap], 1)
+            pkv.decode_step(kc, vc, kd[cap], vd[cap], [cap], 1, qd[cap], out, ws)
             raise RuntimeError("the append past capacity was accepted")
         except pkv.PkvError as e:
             assert e.status == pkv.E_CAPACITY
@@ -1081,13 +1096,15 @@ def bench_tiny(steps, warmup, cpu):
 
     for _ in range(warmup):
         run(None)
+        run(None, fused=False)
     free_before = torch.cuda.mem_get_info()[0]
     for i in range(steps):
+        run(i, fused=False)
         run(i)
     alloc_delta = free_before - torch.cuda.mem_get_info()[0]
     before = (kc.clone(), vc.clone())
     try:
-        pkv.cache_update(kc, kd[cap], [cap], 1)
+        pkv.decode_step(kc, vc, kd[cap], vd[cap], [cap], 1, qd[cap], out, ws)
     except pkv.PkvError:
         pass
     torch.cuda.synchronize()
@@ -1132,10 +1149,13 @@ def bench_tiny(steps, warmup, cpu):
     r = _line("tiny-fixture decode step latency (append K/V + attention), us per step", mean_us, "us/step", steps,
               warmup, mean_us * cap, "f32",
               {"workload": "tiny", "batch": 1, "heads": 1, "head_dim": 4, "capacity": cap,
-               "steps_per_run": cap, "step": "in-place K and V append + decode attention, then a rejected append"},
+               "steps_per_run": cap, "step": "in-place K and V append + decode attention (one fused call), then "
+                                             "a rejected step"},
               {"bound": "latency", "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None},
               cpu, per_step_host_us=[round(float(x), 2) for x in med_host],
               per_step_device_us=[round(float(x), 2) for x in med_dev],
+              two_call_per_step_host_us=[round(float(x), 2) for x in np.median(host2, axis=0)],
+              two_call_mean_host_us=round(float(np.median(host2, axis=0).mean()), 2),
               first_token_host_us=round(float(med_host[0]), 2), token4_host_us=round(float(med_host[3]), 2),
               overflow_rejected_host_us=round(float(np.median(rejected)), 2),
               graph_per_step_host_us=[round(float(x), 2) for x in med_graph],

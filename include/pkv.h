@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 8
+#define PKV_ABI_VERSION 9
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -360,6 +360,26 @@ pkv_status pkv_decode_attention(const pkv_tensor* q, const pkv_tensor* k_cache,
                                 const pkv_tensor* v_cache, const int32_t* valid_len,
                                 float scale, int32_t left_window, pkv_tensor* out, void* workspace,
                                 size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/* One decode step on contiguous caches in one launch: the same results, cache
+ * bytes and output bits as pkv_cache_update_kv(k_cache, v_cache, k_values,
+ * v_values, position, update_length) followed by pkv_decode_attention(q,
+ * k_cache, v_cache, valid_len = position + update_length, ...) ("Mutable
+ * execution cache", "Value model" and "Model example": the updated cache is
+ * the input storage; "Persistent input/output feedback", "Kernel
+ * implementation": the current K/V take part in the attention).  The
+ * attention workgroup whose token range holds the new rows writes them
+ * before it reads them, so no separate append launch is issued.
+ * Arguments: those of the two calls; the caches must agree in batch, heads
+ * and capacity (head sizes may differ), be bound writable, and not overlap
+ * q, out, the new values or each other.  All checks of both calls run
+ * before anything is written; on an error nothing is written.  update_length
+ * 0 is a plain decode at valid_len = position. */
+pkv_status pkv_decode_step(const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                           const pkv_tensor* k_values, const pkv_tensor* v_values,
+                           const int32_t* position, int32_t update_length, const pkv_tensor* q,
+                           float scale, int32_t left_window, pkv_tensor* out, void* workspace,
+                           size_t workspace_bytes, int32_t num_splits, void* stream);
 
 /* Paged f32/bf16/f16: k_pool [num_blocks, Hkv, block_size, Dk], v_pool
  * [num_blocks, Hkv, block_size, Dv];

@@ -126,6 +126,8 @@ _SIG = {
     "pkv_decode_workspace_size": (C.c_size_t, [C.c_int32] * 6),
     "pkv_decode_attention": (C.c_int, [_T, _T, _T, _I32P, C.c_float, C.c_int32, _T, _VP, C.c_size_t, C.c_int32,
                                        _VP]),
+    "pkv_decode_step": (C.c_int, [_T, _T, _T, _T, _I32P, C.c_int32, _T, C.c_float, C.c_int32, _T, _VP, C.c_size_t,
+                                  C.c_int32, _VP]),
     "pkv_paged_decode_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
                                              C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_paged_decode_attention_noalloc": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
@@ -165,7 +167,7 @@ for _name, (_res, _args) in _SIG.items():
         _fn.argtypes = _args
 
 
-ABI_VERSION = 8      # the argument lists above follow this version of include/pkv.h
+ABI_VERSION = 9      # the argument lists above follow this version of include/pkv.h
 if _lib.pkv_abi_version() != ABI_VERSION:
     raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
                       "rebuild it (python place_persistent_kv_amd/build.py)")
@@ -434,6 +436,16 @@ def paged_gather(pool_kv, page_table, max_blocks_per_seq: int, seq: int, length:
 # ---------------------------------------------------------------------------
 def decode_workspace_size(B: int, Hq: int, Hkv: int, D: int, max_len: int, num_splits: int = 0) -> int:
     return int(_lib.pkv_decode_workspace_size(B, Hq, Hkv, D, max_len, num_splits))
+
+
+def decode_step(k_cache, v_cache, k_values, v_values, position, update_length: int, q, out, workspace=None,
+                scale: float = 0.0, num_splits: int = 0, stream=None, left_window: int = -1) -> None:
+    """``cache_update_kv`` then ``decode_attention`` at ``position + update_length``, in one launch."""
+    _check(_lib.pkv_decode_step(C.byref(desc(k_cache)), C.byref(desc(v_cache)), C.byref(desc(k_values)),
+                                C.byref(desc(v_values)), _i32_array(position), int(update_length), C.byref(desc(q)),
+                                float(scale), int(left_window), C.byref(desc(out)), _ptr(workspace),
+                                0 if workspace is None else _nbytes(workspace), int(num_splits), _stream(stream)),
+           "pkv_decode_step")
 
 
 def decode_attention(q, k_cache, v_cache, valid_len, out, workspace=None, scale: float = 0.0,

@@ -78,6 +78,46 @@ __device__ __forceinline__ SplitWork split_work(const DecodeArgs& a, int r) {
     return w;
 }
 
+// Fused append (contiguous caches): rows of the last a.app_n tokens of row
+// b that fall in [t0, t1), plus those below t0 for split 0, copied from the
+// new values into K/V head kvh of the caches by the nthreads threads of the
+// workgroup; then every wave of the workgroup sees them (the rows it reads
+// were written by this workgroup, or by another one with the same bytes).
+__device__ __forceinline__ void append_rows(const DecodeArgs& a, int b, int kvh, int split, int t0, int t1, int L,
+                                            int esz, int nthreads) {
+    const int p0 = L - a.app_n;
+    const int lo = split == 0 ? p0 : max(p0, t0);
+    const int hi = t1;
+    if (lo < hi) {
+        const int64_t src_row = (int64_t(b) * a.Hkv + kvh) * a.app_n + (lo - p0);
+        const int64_t dst_row = (int64_t(b) * a.Hkv + kvh) * a.cap + lo;
+        const int64_t kb = int64_t(a.D) * esz, vb = int64_t(a.Dv) * esz;   // row bytes
+        const uint8_t* sk = static_cast<const uint8_t*>(a.app_k) + src_row * kb;
+        const uint8_t* sv = static_cast<const uint8_t*>(a.app_v) + src_row * vb;
+        uint8_t* dk = static_cast<uint8_t*>(const_cast<void*>(a.k)) + dst_row * kb;
+        uint8_t* dv = static_cast<uint8_t*>(const_cast<void*>(a.v)) + dst_row * vb;
+        const int64_t nk = (hi - lo) * kb, nv = (hi - lo) * vb;
+        if (a.app_vec16) {
+            for (int64_t c = threadIdx.x; c < nk / 16; c += nthreads)
+                reinterpret_cast<uint4*>(dk)[c] = reinterpret_cast<const uint4*>(sk)[c];
+            for (int64_t c = threadIdx.x; c < nv / 16; c += nthreads)
+                reinterpret_cast<uint4*>(dv)[c] = reinterpret_cast<const uint4*>(sv)[c];
+        } else {
+            for (int64_t c = threadIdx.x; c < nk / esz; c += nthreads) {
+                if (esz == 4) reinterpret_cast<uint32_t*>(dk)[c] = reinterpret_cast<const uint32_t*>(sk)[c];
+                else reinterpret_cast<uint16_t*>(dk)[c] = reinterpret_cast<const uint16_t*>(sk)[c];
+            }
+            for (int64_t c = threadIdx.x; c < nv / esz; c += nthreads) {
+                if (esz == 4) reinterpret_cast<uint32_t*>(dv)[c] = reinterpret_cast<const uint32_t*>(sv)[c];
+                else reinterpret_cast<uint16_t*>(dv)[c] = reinterpret_cast<const uint16_t*>(sv)[c];
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 template <int G, bool PAGED, bool F16>   // F16: fp16 q/K/V (else bf16)
 __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     __shared__ float s_o[kWaves][G][kD];
@@ -111,6 +151,10 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeArgs a) {
     const int wbeg = t0 + wave * quarter;
     const int wend = min(t1, wbeg + quarter);
 
+    if constexpr (!PAGED) {
+        if (a.app_n > 0) append_rows(a, b, kvh, split, t0, t1, L, 2, 256);
+    }
+    // (the appended rows were written before the reads below begin)
     const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
     const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
     const int32_t* __restrict__ pt = PAGED ? a.page_table + int64_t(b) * a.maxb : nullptr;
@@ -357,6 +401,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     const int G = a.Hq / a.Hkv;
     const int kvh = h / G;
     const int D = a.D;
+    if (a.app_n > 0) append_rows(a, b, kvh, split, t0, t1, L, int(sizeof(T)), 64);
     const T* Q = static_cast<const T*>(a.q) + (int64_t(b) * a.Hq + h) * D;
     const T* K = static_cast<const T*>(a.k);
     const T* V = static_cast<const T*>(a.v);

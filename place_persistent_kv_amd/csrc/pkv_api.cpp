@@ -865,6 +865,14 @@ pkv_status check_q_out(const pkv_tensor* q, const pkv_tensor* out, QView* v, int
     return PKV_OK;
 }
 
+// New K/V rows that the attention launch writes into contiguous caches
+// before it reads them (pkv_decode_step); checked by the caller.
+struct FusedAppend {
+    const pkv_tensor* k_values;
+    const pkv_tensor* v_values;
+    int32_t n;
+};
+
 // Shared body of the bf16/f32 decode entry points.
 pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_tensor* v,
                          bool paged, const int32_t* page_table, int32_t maxb, int32_t bs,
@@ -872,7 +880,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
                          int32_t left_window, pkv_tensor* out, void* ws, size_t ws_bytes,
                          int32_t num_splits, void* stream, const pkv_tensor* page_desc = nullptr,
                          bool static_ws = false, const int32_t* len_dev = nullptr, int32_t max_len = 0,
-                         int32_t* status = nullptr) {
+                         int32_t* status = nullptr, const FusedAppend* app = nullptr) {
     const bool dev = len_dev != nullptr;   // valid lengths in device memory, bounded by max_len
     const bool mixed = page_desc != nullptr;
     QView qv;
@@ -972,7 +980,8 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         if (!ws || ws_bytes < need)
             return fail(PKV_E_NOMEM, "workspace of %zu bytes needed, %zu given (pkv_decode_workspace_size)", need, ws_bytes);
         const Span wss = span(ws, static_cast<int64_t>(need));
-        if (overlap(wss, os) || overlap(wss, span(q)) || overlap(wss, span(k)) || overlap(wss, span(v)))
+        if (overlap(wss, os) || overlap(wss, span(q)) || overlap(wss, span(k)) || overlap(wss, span(v)) ||
+            (app && (overlap(wss, span(app->k_values)) || overlap(wss, span(app->v_values)))))
             return fail(PKV_E_ALIAS, "workspace overlaps an input or the output");
         if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(PKV_E_ARG, "workspace must be 256-byte aligned");
     }
@@ -1018,6 +1027,15 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         a.scale_log2 = sc * 1.4426950408889634f;
         a.window = left_window;
         a.page_desc = mixed ? page_desc->data : nullptr;
+        if (app && app->n > 0) {
+            a.app_k = static_cast<const uint8_t*>(app->k_values->data) + b0 * Hkv * app->n * D * esz;
+            a.app_v = static_cast<const uint8_t*>(app->v_values->data) + b0 * Hkv * app->n * Dv * esz;
+            a.app_n = app->n;
+            const uintptr_t bases = reinterpret_cast<uintptr_t>(app->k_values->data) |
+                                    reinterpret_cast<uintptr_t>(app->v_values->data) |
+                                    reinterpret_cast<uintptr_t>(k->data) | reinterpret_cast<uintptr_t>(v->data);
+            a.app_vec16 = (bases % 16 == 0 && (D * esz) % 16 == 0 && (Dv * esz) % 16 == 0) ? 1 : 0;
+        }
         int total = 0;
         bool any_split = false;
         if (dev) {   // S_max split slots per row; the kernels read the lengths
@@ -1075,6 +1093,40 @@ pkv_status pkv_decode_attention(const pkv_tensor* q, const pkv_tensor* k_cache,
                                 size_t workspace_bytes, int32_t num_splits, void* stream) {
     return decode_common(q, k_cache, v_cache, false, nullptr, 0, 0, nullptr, valid_len, scale, left_window,
                          out, workspace, workspace_bytes, num_splits, stream);
+}
+
+pkv_status pkv_decode_step(const pkv_tensor* k_cache, const pkv_tensor* v_cache, const pkv_tensor* k_values,
+                           const pkv_tensor* v_values, const int32_t* position, int32_t update_length,
+                           const pkv_tensor* q, float scale, int32_t left_window, pkv_tensor* out,
+                           void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
+    const char* who = "decode_step";
+    // the append's checks (pkv_cache_update_kv) ...
+    PKV_TRY(cache_update_checks(who, k_cache, k_values, position, update_length));
+    PKV_TRY(cache_update_checks(who, v_cache, v_values, position, update_length));
+    for (int i = 0; i < 3; ++i)
+        if (k_cache->shape[i] != v_cache->shape[i])
+            return fail(PKV_E_LAYOUT, "%s: K and V caches must agree in batch, heads and capacity", who);
+    if (k_cache->dtype != v_cache->dtype) return fail(PKV_E_DTYPE, "%s: K and V caches differ in dtype", who);
+    if (overlap(span(k_cache), span(v_cache))) return fail(PKV_E_ALIAS, "%s: k_cache overlaps v_cache", who);
+    PKV_TRY(check_disjoint(k_values, "k_values", span(v_cache), "v_cache"));
+    PKV_TRY(check_disjoint(v_values, "v_values", span(k_cache), "k_cache"));
+    // ... and those of the step as a whole: the launch writes the caches
+    // while it reads q and the new rows, and writes out
+    PKV_TRY(check_tensor(q, "q", 3, 4));
+    PKV_TRY(check_tensor(out, "out", 3, 4));
+    for (const pkv_tensor* t : {k_cache, v_cache}) {
+        PKV_TRY(check_disjoint(q, "q", span(t), "a cache"));
+        PKV_TRY(check_disjoint(out, "out", span(t), "a cache"));
+    }
+    PKV_TRY(check_disjoint(k_values, "k_values", span(out), "out"));
+    PKV_TRY(check_disjoint(v_values, "v_values", span(out), "out"));
+    const int64_t B = k_cache->shape[0];
+    std::vector<int32_t> valid_len(static_cast<size_t>(B));
+    for (int64_t b = 0; b < B; ++b) valid_len[b] = position[b] + update_length;
+    const FusedAppend app{k_values, v_values, update_length};
+    return decode_common(q, k_cache, v_cache, false, nullptr, 0, 0, nullptr, valid_len.data(), scale, left_window,
+                         out, workspace, workspace_bytes, num_splits, stream, nullptr, false, nullptr, 0, nullptr,
+                         &app);
 }
 
 pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_pool,

@@ -125,6 +125,16 @@ struct DecodeArgs {
     int32_t len_limit = 0;
     int32_t nb = 0;
     int32_t* status = nullptr;
+    // Append fused into the attention (contiguous caches, host lengths): the
+    // last app_n tokens of each row's valid length are first copied from
+    // app_k / app_v ([rows, Hkv, app_n, D] and [.., Dv], the cache's element
+    // type) into the caches k / v by the workgroups whose split holds them
+    // (split 0 also takes any below its range); app_vec16: every base 16-byte
+    // aligned, so rows are copied in 16-byte pieces.
+    const void* app_k = nullptr;
+    const void* app_v = nullptr;
+    int32_t app_n = 0;
+    int32_t app_vec16 = 0;
     int32_t len[kMaxRows];       // valid length per row
     // work order (split_item): prefix sums of the rows' whole-tps splits, and
     // the rows whose last split is shorter, by that split's size, longest first

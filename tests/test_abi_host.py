@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if getattr(pkv._lib, n, None) is None]
     assert not missing, missing
     assert set(names) <= set(pkv._SIG), "binding signature table lags the header"
-    assert pkv.abi_version() == pkv.ABI_VERSION == 8
+    assert pkv.abi_version() == pkv.ABI_VERSION == 9
 
 
 def R(ptr, dtype, shape):
@@ -108,6 +108,37 @@ def test_paired_contiguous_update_checks_both_tensors():
     other = R(FAKE + 0x80000, pkv.BF16, [2, 3, 20, 8])
     with pkv.bind_writable(CACHE), pkv.bind_writable(other):
         assert status_of(f, CACHE, other, VALS, vvals, [0, 0], 4) == pkv.E_LAYOUT       # capacities differ
+
+
+def test_decode_step_checks_the_append_and_the_attention():
+    """pkv_decode_step: the append's checks, the attention's, and no overlap of what the launch writes (the
+    caches, out, the workspace) with what it reads."""
+    kc = R(FAKE + 0x100000, pkv.BF16, [2, 2, 64, 128])
+    vc = R(FAKE + 0x900000, pkv.BF16, [2, 2, 64, 128])
+    kv = R(FAKE + 0x1100000, pkv.BF16, [2, 2, 1, 128])
+    vv = R(FAKE + 0x1200000, pkv.BF16, [2, 2, 1, 128])
+    q = R(FAKE + 0x1300000, pkv.BF16, [2, 8, 128])
+    out = R(FAKE + 0x1400000, pkv.F32, [2, 8, 128])
+    f = pkv.decode_step
+    assert status_of(f, kc, vc, kv, vv, [3, 4], 1, q, out) == pkv.E_READONLY
+    with pkv.bind_writable(kc), pkv.bind_writable(vc):
+        assert status_of(f, kc, vc, kv, vv, [3, 64], 1, q, out) == pkv.E_CAPACITY
+        assert status_of(f, kc, vc, kv, vv, [3, 4], -1, q, out) == pkv.E_ARG
+        assert status_of(f, kc, vc, kv, R(vv.ptr, pkv.F16, vv.shape), [3, 4], 1, q, out) == pkv.E_DTYPE
+        assert status_of(f, kc, vc, kv, vv, [3, 4], 1, R(q.ptr, pkv.BF16, [2, 6, 128]), out) == pkv.E_LAYOUT
+        assert status_of(f, kc, vc, kv, vv, [3, 4], 1, R(kc.ptr, pkv.BF16, q.shape), out) == pkv.E_ALIAS
+        assert status_of(f, kc, vc, kv, vv, [3, 4], 1, q, R(vc.ptr, pkv.F32, out.shape)) == pkv.E_ALIAS
+        assert status_of(f, kc, vc, kv, vv, [3, 4], 1, q, R(kv.ptr, pkv.F32, out.shape)) == pkv.E_ALIAS
+        none_k, none_v = R(kv.ptr, pkv.BF16, [2, 2, 0, 128]), R(vv.ptr, pkv.BF16, [2, 2, 0, 128])
+        assert status_of(f, kc, vc, none_k, none_v, [0, 4], 0, q, out) == pkv.E_CAPACITY   # valid_len 0
+        assert status_of(f, kc, vc, kv, vv, [3, 4], 1, q, out, left_window=-2) == pkv.E_ARG
+    long_k = R(FAKE + 0x2000000, pkv.BF16, [2, 2, 2048, 128])
+    long_v = R(FAKE + 0x3000000, pkv.BF16, [2, 2, 2048, 128])
+    with pkv.bind_writable(long_k), pkv.bind_writable(long_v):
+        args = (long_k, long_v, kv, vv, [1500, 2000], 1, q, out)
+        assert status_of(f, *args, num_splits=4) == pkv.E_NOMEM
+        need = pkv.decode_workspace_size(2, 8, 2, 128, 2048, 4)
+        assert status_of(f, *args, workspace=R(kv.ptr, pkv.U8, [need]), num_splits=4) == pkv.E_ALIAS
 
 
 # --------------------------------------------------------------------------- pool
