@@ -13,6 +13,7 @@ Build the library first:  ``python place_persistent_kv_amd/build.py``.
 from __future__ import annotations
 
 import ctypes as C
+import struct
 import os
 from dataclasses import dataclass
 from typing import Optional, Sequence
@@ -101,7 +102,7 @@ class PkvError(RuntimeError):
 
 
 _P = C.POINTER
-_T = _P(PkvTensor)
+_T = C.c_void_p          # const pkv_tensor*: the packed bytes of _d()
 _VP = C.c_void_p
 _I32P = _P(C.c_int32)
 _SIG = {
@@ -239,6 +240,27 @@ def desc(x) -> PkvTensor:
     return PkvTensor(ptr, code, n, _SHAPE_T(*shape))
 
 
+# pkv_tensor as packed bytes (data, dtype, ndim, shape[6]); built with one
+# struct.pack instead of a ctypes structure, which costs about ten times as
+# much per call and adds up on the short, launch-bound calls
+_DESC = struct.Struct("<Qii%dq" % MAX_DIMS)
+_ZEROS = (0,) * MAX_DIMS
+assert _DESC.size == C.sizeof(PkvTensor)
+
+
+def _d(x) -> bytes:
+    if isinstance(x, Raw):
+        ptr, code, shape = x.ptr, x.dtype, tuple(int(s) for s in x.shape)
+    else:
+        if not x.is_contiguous():
+            raise ValueError("tensor must be contiguous (libpkv never copies inputs)")
+        ptr, code, shape = x.data_ptr(), _torch_dtype_code(x), x.shape
+    n = len(shape)
+    if not 1 <= n <= MAX_DIMS:
+        raise ValueError(f"rank {n} not supported")
+    return _DESC.pack(ptr, code, n, *shape, *_ZEROS[n:])
+
+
 def _ptr(x) -> Optional[int]:
     if x is None:
         return None
@@ -326,7 +348,7 @@ def unbind(binding: Binding) -> None:
 def cache_update(cache, values, position, update_length: int, stream=None) -> int:
     """In-place ``CacheUpdate``; returns the address of the updated cache (== cache's)."""
     out = C.c_void_p()
-    _check(_lib.pkv_cache_update(C.byref(desc(cache)), C.byref(desc(values)), _i32_array(position),
+    _check(_lib.pkv_cache_update(_d(cache), _d(values), _i32_array(position),
                                  int(update_length), C.byref(out), _stream(stream)), "pkv_cache_update")
     return out.value
 
@@ -393,24 +415,24 @@ def _pool_handle(pool):
 def paged_cache_update(pool: Pool, pool_kv, page_table, values, position, update_length: int,
                        stream=None) -> int:
     out = C.c_void_p()
-    _check(_lib.pkv_paged_cache_update(_pool_handle(pool), C.byref(desc(pool_kv)), _ptr(page_table),
-                                       C.byref(desc(values)), _i32_array(position), int(update_length),
+    _check(_lib.pkv_paged_cache_update(_pool_handle(pool), _d(pool_kv), _ptr(page_table),
+                                       _d(values), _i32_array(position), int(update_length),
                                        C.byref(out), _stream(stream)), "pkv_paged_cache_update")
     return out.value
 
 
 def cache_update_kv(k_cache, v_cache, k_values, v_values, position, update_length: int, stream=None) -> None:
     """``pkv_cache_update_kv``: K and V appended to contiguous caches at host positions in one launch."""
-    _check(_lib.pkv_cache_update_kv(C.byref(desc(k_cache)), C.byref(desc(v_cache)), C.byref(desc(k_values)),
-                                    C.byref(desc(v_values)), _i32_array(position), int(update_length),
+    _check(_lib.pkv_cache_update_kv(_d(k_cache), _d(v_cache), _d(k_values),
+                                    _d(v_values), _i32_array(position), int(update_length),
                                     _stream(stream)), "pkv_cache_update_kv")
 
 
 def paged_cache_update_kv(pool: Pool, k_pool, v_pool, page_table, k_values, v_values, position,
                           update_length: int, stream=None) -> None:
     """``pkv_paged_cache_update_kv``: K and V appended at host positions in one launch."""
-    _check(_lib.pkv_paged_cache_update_kv(_pool_handle(pool), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
-                                          _ptr(page_table), C.byref(desc(k_values)), C.byref(desc(v_values)),
+    _check(_lib.pkv_paged_cache_update_kv(_pool_handle(pool), _d(k_pool), _d(v_pool),
+                                          _ptr(page_table), _d(k_values), _d(v_values),
                                           _i32_array(position), int(update_length), _stream(stream)),
            "pkv_paged_cache_update_kv")
 
@@ -418,8 +440,8 @@ def paged_cache_update_kv(pool: Pool, k_pool, v_pool, page_table, k_values, v_va
 def paged_cache_update_int4(pool: Pool, codes_pool, params_pool, page_table, values, scale_f16_bits: int,
                             zero_point_f16_bits: int, position, update_length: int, stream=None):
     oc, op = C.c_void_p(), C.c_void_p()
-    _check(_lib.pkv_paged_cache_update_int4(_pool_handle(pool), C.byref(desc(codes_pool)),
-                                            C.byref(desc(params_pool)), _ptr(page_table), C.byref(desc(values)),
+    _check(_lib.pkv_paged_cache_update_int4(_pool_handle(pool), _d(codes_pool),
+                                            _d(params_pool), _ptr(page_table), _d(values),
                                             int(scale_f16_bits), int(zero_point_f16_bits), _i32_array(position),
                                             int(update_length), C.byref(oc), C.byref(op), _stream(stream)),
            "pkv_paged_cache_update_int4")
@@ -427,8 +449,8 @@ def paged_cache_update_int4(pool: Pool, codes_pool, params_pool, page_table, val
 
 
 def paged_gather(pool_kv, page_table, max_blocks_per_seq: int, seq: int, length: int, out, stream=None) -> None:
-    _check(_lib.pkv_paged_gather(C.byref(desc(pool_kv)), _ptr(page_table), max_blocks_per_seq, seq, length,
-                                 C.byref(desc(out)), _stream(stream)), "pkv_paged_gather")
+    _check(_lib.pkv_paged_gather(_d(pool_kv), _ptr(page_table), max_blocks_per_seq, seq, length,
+                                 _d(out), _stream(stream)), "pkv_paged_gather")
 
 
 # ---------------------------------------------------------------------------
@@ -441,9 +463,9 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, D: int, max_len: int, num_s
 def decode_step(k_cache, v_cache, k_values, v_values, position, update_length: int, q, out, workspace=None,
                 scale: float = 0.0, num_splits: int = 0, stream=None, left_window: int = -1) -> None:
     """``cache_update_kv`` then ``decode_attention`` at ``position + update_length``, in one launch."""
-    _check(_lib.pkv_decode_step(C.byref(desc(k_cache)), C.byref(desc(v_cache)), C.byref(desc(k_values)),
-                                C.byref(desc(v_values)), _i32_array(position), int(update_length), C.byref(desc(q)),
-                                float(scale), int(left_window), C.byref(desc(out)), _ptr(workspace),
+    _check(_lib.pkv_decode_step(_d(k_cache), _d(v_cache), _d(k_values),
+                                _d(v_values), _i32_array(position), int(update_length), _d(q),
+                                float(scale), int(left_window), _d(out), _ptr(workspace),
                                 0 if workspace is None else _nbytes(workspace), int(num_splits), _stream(stream)),
            "pkv_decode_step")
 
@@ -451,8 +473,8 @@ def decode_step(k_cache, v_cache, k_values, v_values, position, update_length: i
 def decode_attention(q, k_cache, v_cache, valid_len, out, workspace=None, scale: float = 0.0,
                      num_splits: int = 0, stream=None, left_window: int = -1) -> None:
     ws = _ptr(workspace)
-    _check(_lib.pkv_decode_attention(C.byref(desc(q)), C.byref(desc(k_cache)), C.byref(desc(v_cache)),
-                                     _i32_array(valid_len), float(scale), int(left_window), C.byref(desc(out)), ws,
+    _check(_lib.pkv_decode_attention(_d(q), _d(k_cache), _d(v_cache),
+                                     _i32_array(valid_len), float(scale), int(left_window), _d(out), ws,
                                      0 if workspace is None else _nbytes(workspace), int(num_splits),
                                      _stream(stream)), "pkv_decode_attention")
 
@@ -460,10 +482,10 @@ def decode_attention(q, k_cache, v_cache, valid_len, out, workspace=None, scale:
 def paged_decode_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, block_size: int, valid_len,
                            out, workspace=None, pool: Optional[Pool] = None, scale: float = 0.0,
                            num_splits: int = 0, stream=None, left_window: int = -1) -> None:
-    _check(_lib.pkv_paged_decode_attention(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+    _check(_lib.pkv_paged_decode_attention(_d(q), _d(k_pool), _d(v_pool),
                                            _ptr(page_table), int(max_blocks_per_seq), int(block_size),
                                            _pool_handle(pool), _i32_array(valid_len), float(scale),
-                                           int(left_window), C.byref(desc(out)), _ptr(workspace),
+                                           int(left_window), _d(out), _ptr(workspace),
                                            0 if workspace is None else _nbytes(workspace), int(num_splits),
                                            _stream(stream)), "pkv_paged_decode_attention")
 
@@ -477,9 +499,9 @@ def paged_decode_attention_noalloc(q, k_pool, v_pool, page_table, max_blocks_per
     """``pkv_paged_decode_attention_noalloc``: the paged decode with its split partials in the library's
     static device scratch (no workspace argument, nothing allocated)."""
     _check(_lib.pkv_paged_decode_attention_noalloc(
-        C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)), _ptr(page_table), int(max_blocks_per_seq),
+        _d(q), _d(k_pool), _d(v_pool), _ptr(page_table), int(max_blocks_per_seq),
         int(block_size), _pool_handle(pool), _i32_array(valid_len), float(scale), int(left_window),
-        C.byref(desc(out)), int(num_splits), _stream(stream)), "pkv_paged_decode_attention_noalloc")
+        _d(out), int(num_splits), _stream(stream)), "pkv_paged_decode_attention_noalloc")
 
 
 def paged_decode_attention_int4(q, k_codes, k_params, v_codes, v_params, page_table, max_blocks_per_seq: int,
@@ -487,9 +509,9 @@ def paged_decode_attention_int4(q, k_codes, k_params, v_codes, v_params, page_ta
                                 scale: float = 0.0, num_splits: int = 0, stream=None,
                                 left_window: int = -1) -> None:
     _check(_lib.pkv_paged_decode_attention_int4(
-        C.byref(desc(q)), C.byref(desc(k_codes)), C.byref(desc(k_params)), C.byref(desc(v_codes)),
-        C.byref(desc(v_params)), _ptr(page_table), int(max_blocks_per_seq), int(block_size), _pool_handle(pool),
-        _i32_array(valid_len), float(scale), int(left_window), C.byref(desc(out)), _ptr(workspace),
+        _d(q), _d(k_codes), _d(k_params), _d(v_codes),
+        _d(v_params), _ptr(page_table), int(max_blocks_per_seq), int(block_size), _pool_handle(pool),
+        _i32_array(valid_len), float(scale), int(left_window), _d(out), _ptr(workspace),
         0 if workspace is None else _nbytes(workspace), int(num_splits), _stream(stream)),
         "pkv_paged_decode_attention_int4")
 
@@ -504,16 +526,16 @@ def chunk_attention(q, k_pool, v_pool, page_table, max_blocks_per_seq: int, bloc
     """Causal chunk attention; with ``num_splits`` other than 1 (0 = library choice) the key range of every
     workgroup is split into parts whose partials ``workspace`` (``chunk_workspace_size`` bytes) holds."""
     if num_splits == 1 and workspace is None:
-        _check(_lib.pkv_chunk_attention(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+        _check(_lib.pkv_chunk_attention(_d(q), _d(k_pool), _d(v_pool),
                                         _ptr(page_table), int(max_blocks_per_seq), int(block_size),
                                         _pool_handle(pool), _i32_array(p0), float(scale), int(left_window),
-                                        C.byref(desc(out)), _stream(stream)),
+                                        _d(out), _stream(stream)),
                "pkv_chunk_attention")
         return
-    _check(_lib.pkv_chunk_attention_split(C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
+    _check(_lib.pkv_chunk_attention_split(_d(q), _d(k_pool), _d(v_pool),
                                           _ptr(page_table), int(max_blocks_per_seq), int(block_size),
                                           _pool_handle(pool), _i32_array(p0), float(scale), int(left_window),
-                                          C.byref(desc(out)), _ptr(workspace),
+                                          _d(out), _ptr(workspace),
                                           0 if workspace is None else _nbytes(workspace), int(num_splits),
                                           _stream(stream)),
            "pkv_chunk_attention_split")
@@ -530,16 +552,16 @@ def mixed_page_desc(num_blocks: int, device="cuda"):
 
 def mixed_cache_update(pool: Pool, k_pool, v_pool, page_desc, page_table, k_values, v_values, position,
                        update_length: int, k_format: PageFormat, v_format: PageFormat, stream=None) -> None:
-    _check(_lib.pkv_mixed_cache_update(_pool_handle(pool), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
-                                       C.byref(desc(page_desc)), _ptr(page_table), C.byref(desc(k_values)),
-                                       C.byref(desc(v_values)), _i32_array(position), int(update_length),
+    _check(_lib.pkv_mixed_cache_update(_pool_handle(pool), _d(k_pool), _d(v_pool),
+                                       _d(page_desc), _ptr(page_table), _d(k_values),
+                                       _d(v_values), _i32_array(position), int(update_length),
                                        k_format, v_format, _stream(stream)), "pkv_mixed_cache_update")
 
 
 def mixed_convert_pages(k_pool, v_pool, page_desc, pages, valid_rows, k_format: Optional[PageFormat] = None,
                         v_format: Optional[PageFormat] = None, stream=None) -> None:
     pages, valid_rows = list(pages), list(valid_rows)
-    _check(_lib.pkv_mixed_convert_pages(C.byref(desc(k_pool)), C.byref(desc(v_pool)), C.byref(desc(page_desc)),
+    _check(_lib.pkv_mixed_convert_pages(_d(k_pool), _d(v_pool), _d(page_desc),
                                         _i32_array(pages), _i32_array(valid_rows), len(pages),
                                         None if k_format is None else C.byref(k_format),
                                         None if v_format is None else C.byref(v_format), _stream(stream)),
@@ -551,9 +573,9 @@ def paged_decode_attention_mixed(q, k_pool, v_pool, page_desc, page_table, max_b
                                  scale: float = 0.0, num_splits: int = 0, stream=None,
                                  left_window: int = -1) -> None:
     _check(_lib.pkv_paged_decode_attention_mixed(
-        C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)), C.byref(desc(page_desc)), _ptr(page_table),
+        _d(q), _d(k_pool), _d(v_pool), _d(page_desc), _ptr(page_table),
         int(max_blocks_per_seq), int(block_size), _pool_handle(pool), _i32_array(valid_len), float(scale),
-        int(left_window), C.byref(desc(out)), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
+        int(left_window), _d(out), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
         int(num_splits), _stream(stream)), "pkv_paged_decode_attention_mixed")
 
 
@@ -565,14 +587,14 @@ def sample_workspace_size(B: int, V: int) -> int:
 
 
 def sample(logits, temperature: float, seed: int, out_ids, workspace=None, stream=None) -> None:
-    _check(_lib.pkv_sample(C.byref(desc(logits)), float(temperature), C.c_uint64(seed & (2 ** 64 - 1)),
+    _check(_lib.pkv_sample(_d(logits), float(temperature), C.c_uint64(seed & (2 ** 64 - 1)),
                            _ptr(out_ids), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
                            _stream(stream)), "pkv_sample")
 
 
 def sample_dev(logits, temperature: float, seed: int, step, out_ids, workspace=None, stream=None) -> None:
     """``pkv_sample_dev``: the seed of the iteration held in the device int64 counter ``step``."""
-    _check(_lib.pkv_sample_dev(C.byref(desc(logits)), float(temperature), C.c_uint64(seed & (2 ** 64 - 1)),
+    _check(_lib.pkv_sample_dev(_d(logits), float(temperature), C.c_uint64(seed & (2 ** 64 - 1)),
                                _ptr(step), _ptr(out_ids), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
                                _stream(stream)), "pkv_sample_dev")
 
@@ -583,16 +605,16 @@ def sample_dev(logits, temperature: float, seed: int, step, out_ids, workspace=N
 def cache_update_kv_dev(k_cache, v_cache, k_values, v_values, position, update_length: int, status,
                         stream=None) -> None:
     """``pkv_cache_update_kv_dev``: K and V appended at the device positions ``position`` (int32 [B])."""
-    _check(_lib.pkv_cache_update_kv_dev(C.byref(desc(k_cache)), C.byref(desc(v_cache)), C.byref(desc(k_values)),
-                                        C.byref(desc(v_values)), _ptr(position), int(update_length), _ptr(status),
+    _check(_lib.pkv_cache_update_kv_dev(_d(k_cache), _d(v_cache), _d(k_values),
+                                        _d(v_values), _ptr(position), int(update_length), _ptr(status),
                                         _stream(stream)), "pkv_cache_update_kv_dev")
 
 
 def paged_cache_update_kv_dev(pool: Pool, k_pool, v_pool, page_table, k_values, v_values, position,
                               update_length: int, status, stream=None) -> None:
     """``pkv_paged_cache_update_kv_dev``: the paged form."""
-    _check(_lib.pkv_paged_cache_update_kv_dev(_pool_handle(pool), C.byref(desc(k_pool)), C.byref(desc(v_pool)),
-                                              _ptr(page_table), C.byref(desc(k_values)), C.byref(desc(v_values)),
+    _check(_lib.pkv_paged_cache_update_kv_dev(_pool_handle(pool), _d(k_pool), _d(v_pool),
+                                              _ptr(page_table), _d(k_values), _d(v_values),
                                               _ptr(position), int(update_length), _ptr(status), _stream(stream)),
            "pkv_paged_cache_update_kv_dev")
 
@@ -606,9 +628,9 @@ def advance(values, delta: int, step=None, stream=None, n: Optional[int] = None)
 def decode_attention_dev(q, k_cache, v_cache, valid_len, max_len: int, out, status, workspace=None,
                          scale: float = 0.0, num_splits: int = 0, stream=None, left_window: int = -1) -> None:
     """``pkv_decode_attention_dev``: valid lengths from the device int32 tensor ``valid_len``."""
-    _check(_lib.pkv_decode_attention_dev(C.byref(desc(q)), C.byref(desc(k_cache)), C.byref(desc(v_cache)),
+    _check(_lib.pkv_decode_attention_dev(_d(q), _d(k_cache), _d(v_cache),
                                          _ptr(valid_len), int(max_len), float(scale), int(left_window),
-                                         C.byref(desc(out)), _ptr(workspace),
+                                         _d(out), _ptr(workspace),
                                          0 if workspace is None else _nbytes(workspace), int(num_splits),
                                          _ptr(status), _stream(stream)), "pkv_decode_attention_dev")
 
@@ -618,9 +640,9 @@ def paged_decode_attention_dev(q, k_pool, v_pool, page_table, max_blocks_per_seq
                                scale: float = 0.0, num_splits: int = 0, stream=None, left_window: int = -1) -> None:
     """``pkv_paged_decode_attention_dev``: the paged form."""
     _check(_lib.pkv_paged_decode_attention_dev(
-        C.byref(desc(q)), C.byref(desc(k_pool)), C.byref(desc(v_pool)), _ptr(page_table), int(max_blocks_per_seq),
+        _d(q), _d(k_pool), _d(v_pool), _ptr(page_table), int(max_blocks_per_seq),
         int(block_size), _pool_handle(pool), _ptr(valid_len), int(max_len), float(scale), int(left_window),
-        C.byref(desc(out)), _ptr(workspace), 0 if workspace is None else _nbytes(workspace), int(num_splits),
+        _d(out), _ptr(workspace), 0 if workspace is None else _nbytes(workspace), int(num_splits),
         _ptr(status), _stream(stream)), "pkv_paged_decode_attention_dev")
 
 
