@@ -1484,13 +1484,12 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
         const float sc = scale > 0 ? scale : 1.0f / std::sqrt(float(D));
         a.scale_log2 = sc * 1.4426950408889634f;
         a.window = left_window;
-        int total = 0;
         bool any_split = false;
         for (int i = 0; i < rows; ++i) {
             a.len[i] = valid_len[b0 + i];
             any_split |= full.nsplit[b0 + i] > 1;
         }
-        total = work_order(span_len.data() + b0, rows, full.tps, a.full_begin, a.tail_row);
+        const int total = work_order(span_len.data() + b0, rows, full.tps, a.full_begin, a.tail_row);
         PKV_HIP(launch_decode_int4(a, G, total * static_cast<int>(Hkv), s), "int4 decode launch");
         if (any_split) {
             MergeArgs m;
