@@ -502,16 +502,16 @@ def bench_contig(steps, warmup, cpu):
     us_two = _timed(step_two_calls, steps, warmup, stream)
     us_attn = _timed(attn_only, steps, warmup, stream)
     us_warm = _timed(lambda i: attn_only(i, False), steps, warmup, stream)
-    # captured step per replica: fused K+V append at the replica's device lengths, lengths + 1, attention
+    # captured step per replica: the append fused into the attention at the replica's device positions, then
+    # the positions + 1
     lens = [torch.from_numpy(L0.astype(np.int32)).to(dev) for _ in range(R)]
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     graphs = []
     for r in range(R):
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr):
-            pkv.cache_update_kv_dev(kc[r], vc[r], nk, nv, lens[r], 1, status)
+            pkv.decode_step_dev(kc[r], vc[r], nk, nv, lens[r], 1, q, cap, out, status, ws)
             pkv.advance(lens[r], 1)
-            pkv.decode_attention_dev(q, kc[r], vc[r], lens[r], cap, out, status, ws)
         graphs.append(gr)
     torch.cuda.synchronize()
     for r in range(R):
@@ -1109,8 +1109,8 @@ def bench_tiny(steps, warmup, cpu):
         pass
     torch.cuda.synchronize()
     unchanged = bool(torch.equal(kc, before[0]) and torch.equal(vc, before[1]))
-    # the same run as captured steps: one graph per step (its own inputs), positions and lengths held on the
-    # device (fused K+V append at the length, length + 1, attention over the length)
+    # the same run as captured steps: one graph per step (its own inputs), positions held on the device (the
+    # append fused into the attention at the device position, then the position + 1)
     kc2 = torch.zeros((1, 1, cap, 4), device=dev)
     vc2 = torch.zeros((1, 1, cap, 4), device=dev)
     bk2, bv2 = pkv.bind_writable(kc2), pkv.bind_writable(vc2)
@@ -1121,9 +1121,8 @@ def bench_tiny(steps, warmup, cpu):
     for t in range(cap):
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr):
-            pkv.cache_update_kv_dev(kc2, vc2, kd[t], vd[t], lens, 1, status)
+            pkv.decode_step_dev(kc2, vc2, kd[t], vd[t], lens, 1, qd[t], cap, out2, status, ws)
             pkv.advance(lens, 1)
-            pkv.decode_attention_dev(qd[t], kc2, vc2, lens, cap, out2, status, ws)
         graphs.append(gr)
     torch.cuda.synchronize()
     ghost = np.zeros((steps, cap))

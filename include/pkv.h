@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 9
+#define PKV_ABI_VERSION 10
 #define PKV_MAX_DIMS 6
 
 typedef enum pkv_status {
@@ -380,6 +380,25 @@ pkv_status pkv_decode_step(const pkv_tensor* k_cache, const pkv_tensor* v_cache,
                            const int32_t* position, int32_t update_length, const pkv_tensor* q,
                            float scale, int32_t left_window, pkv_tensor* out, void* workspace,
                            size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/* pkv_decode_step with the positions in device memory ("Mutable execution
+ * cache", "Existing implementations": a step captured in a graph reads its
+ * positions from shared state): position_dev is device int32[B]; row b
+ * appends at position_dev[b] and attends over position_dev[b] +
+ * update_length tokens.  The positions are not moved (pkv_advance does that
+ * after the step).  The split plan is made for max_len (1 <= max_len <=
+ * capacity) as in pkv_decode_attention_dev, whose workspace size it takes.
+ * Device check: a row with position < 0 or position + update_length outside
+ * [1, max_len] writes nothing (cache or output) and sets *status_dev =
+ * PKV_E_CAPACITY; the other rows proceed.  Host checks as for
+ * pkv_decode_step, plus: position_dev and status_dev must not overlap a
+ * cache. */
+pkv_status pkv_decode_step_dev(const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                               const pkv_tensor* k_values, const pkv_tensor* v_values,
+                               const int32_t* position_dev, int32_t update_length, const pkv_tensor* q,
+                               int32_t max_len, float scale, int32_t left_window, pkv_tensor* out,
+                               void* workspace, size_t workspace_bytes, int32_t num_splits,
+                               int32_t* status_dev, void* stream);
 
 /* Paged f32/bf16/f16: k_pool [num_blocks, Hkv, block_size, Dk], v_pool
  * [num_blocks, Hkv, block_size, Dv];

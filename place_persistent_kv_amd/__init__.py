@@ -129,6 +129,8 @@ _SIG = {
                                        _VP]),
     "pkv_decode_step": (C.c_int, [_T, _T, _T, _T, _I32P, C.c_int32, _T, C.c_float, C.c_int32, _T, _VP, C.c_size_t,
                                   C.c_int32, _VP]),
+    "pkv_decode_step_dev": (C.c_int, [_T, _T, _T, _T, _VP, C.c_int32, _T, C.c_int32, C.c_float, C.c_int32, _T,
+                                      _VP, C.c_size_t, C.c_int32, _VP, _VP]),
     "pkv_paged_decode_attention": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
                                              C.c_int32, _T, _VP, C.c_size_t, C.c_int32, _VP]),
     "pkv_paged_decode_attention_noalloc": (C.c_int, [_T, _T, _T, _VP, C.c_int32, C.c_int32, _VP, _I32P, C.c_float,
@@ -168,7 +170,7 @@ for _name, (_res, _args) in _SIG.items():
         _fn.argtypes = _args
 
 
-ABI_VERSION = 9      # the argument lists above follow this version of include/pkv.h
+ABI_VERSION = 10      # the argument lists above follow this version of include/pkv.h
 if _lib.pkv_abi_version() != ABI_VERSION:
     raise ImportError(f"libpkv.so has ABI version {_lib.pkv_abi_version()}, the binding expects {ABI_VERSION}; "
                       "rebuild it (python place_persistent_kv_amd/build.py)")
@@ -468,6 +470,16 @@ def decode_step(k_cache, v_cache, k_values, v_values, position, update_length: i
                                 float(scale), int(left_window), _d(out), _ptr(workspace),
                                 0 if workspace is None else _nbytes(workspace), int(num_splits), _stream(stream)),
            "pkv_decode_step")
+
+
+def decode_step_dev(k_cache, v_cache, k_values, v_values, position, update_length: int, q, max_len: int, out,
+                    status, workspace=None, scale: float = 0.0, num_splits: int = 0, stream=None,
+                    left_window: int = -1) -> None:
+    """``decode_step`` at the device positions ``position`` (int32 [B]); they are not advanced."""
+    _check(_lib.pkv_decode_step_dev(_d(k_cache), _d(v_cache), _d(k_values), _d(v_values), _ptr(position),
+                                    int(update_length), _d(q), int(max_len), float(scale), int(left_window),
+                                    _d(out), _ptr(workspace), 0 if workspace is None else _nbytes(workspace),
+                                    int(num_splits), _ptr(status), _stream(stream)), "pkv_decode_step_dev")
 
 
 def decode_attention(q, k_cache, v_cache, valid_len, out, workspace=None, scale: float = 0.0,

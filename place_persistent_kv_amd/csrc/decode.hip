@@ -72,8 +72,11 @@ __device__ __forceinline__ SplitWork split_work(const DecodeArgs& a, int r) {
     }
     w.b = r / a.S_max;
     w.split = r - w.b * a.S_max;
-    w.L = load_uniform(a.len_dev + a.row0 + w.b);
-    w.ok = w.L >= 1 && w.L <= a.len_limit;
+    // with a fused append the device value is the row's position and the
+    // valid length is position + app_n
+    const int pos = load_uniform(a.len_dev + a.row0 + w.b);
+    w.ok = pos >= 0 && pos <= a.len_limit - a.app_n && pos + a.app_n >= 1;
+    w.L = pos + a.app_n;
     w.nsplit = w.ok ? (w.L - split_base(w.L, a.window) + a.tps - 1) / a.tps : 0;
     return w;
 }
@@ -495,8 +498,9 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     const int b = bh / a.Hq;
     int n;
     if (a.len_dev != nullptr) {          // device lengths: the split count follows from the length
-        const int L = a.len_dev[a.row0 + b];
-        if (L < 1 || L > a.len_limit) return;
+        const int pos = a.len_dev[a.row0 + b];     // length, or position before len_add new tokens
+        if (pos < 0 || pos > a.len_limit - a.len_add || pos + a.len_add < 1) return;
+        const int L = pos + a.len_add;
         n = (L - split_base(L, a.window) + a.tps - 1) / a.tps;
     } else {
         n = a.nsplit[b];

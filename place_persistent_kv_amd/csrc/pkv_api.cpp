@@ -1076,6 +1076,7 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
                 m.len_limit = max_len;
                 m.tps = full.tps;
                 m.window = left_window;
+                m.len_add = app ? app->n : 0;
             } else {
                 for (int i = 0; i < rows; ++i) m.nsplit[i] = full.nsplit[b0 + i];
             }
@@ -1127,6 +1128,43 @@ pkv_status pkv_decode_step(const pkv_tensor* k_cache, const pkv_tensor* v_cache,
     return decode_common(q, k_cache, v_cache, false, nullptr, 0, 0, nullptr, valid_len.data(), scale, left_window,
                          out, workspace, workspace_bytes, num_splits, stream, nullptr, false, nullptr, 0, nullptr,
                          &app);
+}
+
+pkv_status pkv_decode_step_dev(const pkv_tensor* k_cache, const pkv_tensor* v_cache, const pkv_tensor* k_values,
+                               const pkv_tensor* v_values, const int32_t* position_dev, int32_t update_length,
+                               const pkv_tensor* q, int32_t max_len, float scale, int32_t left_window,
+                               pkv_tensor* out, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                               int32_t* status_dev, void* stream) {
+    const char* who = "decode_step_dev";
+    PKV_TRY(check_tensor(k_cache, "k_cache", 4, 4));
+    const int64_t B = k_cache->shape[0];
+    if (!position_dev) return fail(PKV_E_ARG, "%s: null position", who);
+    // the append's checks with every position 0 (the positions themselves are
+    // checked on the device against max_len)
+    const std::vector<int32_t> zeros(static_cast<size_t>(B), 0);
+    PKV_TRY(cache_update_checks(who, k_cache, k_values, zeros.data(), update_length));
+    PKV_TRY(cache_update_checks(who, v_cache, v_values, zeros.data(), update_length));
+    for (int i = 0; i < 3; ++i)
+        if (k_cache->shape[i] != v_cache->shape[i])
+            return fail(PKV_E_LAYOUT, "%s: K and V caches must agree in batch, heads and capacity", who);
+    if (k_cache->dtype != v_cache->dtype) return fail(PKV_E_DTYPE, "%s: K and V caches differ in dtype", who);
+    if (overlap(span(k_cache), span(v_cache))) return fail(PKV_E_ALIAS, "%s: k_cache overlaps v_cache", who);
+    PKV_TRY(check_disjoint(k_values, "k_values", span(v_cache), "v_cache"));
+    PKV_TRY(check_disjoint(v_values, "v_values", span(k_cache), "k_cache"));
+    PKV_TRY(check_tensor(q, "q", 3, 4));
+    PKV_TRY(check_tensor(out, "out", 3, 4));
+    for (const pkv_tensor* t : {k_cache, v_cache}) {
+        PKV_TRY(check_disjoint(q, "q", span(t), "a cache"));
+        PKV_TRY(check_disjoint(out, "out", span(t), "a cache"));
+        if (overlap(span(position_dev, B * 4), span(t)) || (status_dev && overlap(span(status_dev, 4), span(t))))
+            return fail(PKV_E_ALIAS, "%s: position or status overlaps a cache", who);
+    }
+    PKV_TRY(check_disjoint(k_values, "k_values", span(out), "out"));
+    PKV_TRY(check_disjoint(v_values, "v_values", span(out), "out"));
+    const FusedAppend app{k_values, v_values, update_length};
+    return decode_common(q, k_cache, v_cache, false, nullptr, 0, 0, nullptr, nullptr, scale, left_window, out,
+                         workspace, workspace_bytes, num_splits, stream, nullptr, false, position_dev, max_len,
+                         status_dev, &app);
 }
 
 pkv_status pkv_paged_decode_attention(const pkv_tensor* q, const pkv_tensor* k_pool,

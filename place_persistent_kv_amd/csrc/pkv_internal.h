@@ -125,7 +125,8 @@ struct DecodeArgs {
     int32_t len_limit = 0;
     int32_t nb = 0;
     int32_t* status = nullptr;
-    // Append fused into the attention (contiguous caches, host lengths): the
+    // Append fused into the attention (contiguous caches; with device lengths
+    // len_dev holds the positions, the lengths being app_n more): the
     // last app_n tokens of each row's valid length are first copied from
     // app_k / app_v ([rows, Hkv, app_n, D] and [.., Dv], the cache's element
     // type) into the caches k / v by the workgroups whose split holds them
@@ -172,6 +173,7 @@ struct MergeArgs {
     // length as in DecodeArgs; invalid rows are skipped
     const int32_t* len_dev = nullptr;
     int32_t len_limit = 0, tps = 0, window = -1;
+    int32_t len_add = 0;         // device values are positions len_add tokens before the lengths
     int32_t nsplit[kMaxRows];
 };
 

@@ -257,3 +257,73 @@ def test_sample_dev_follows_the_device_step_counter():
             sc = osamp.gumbel_scores(x[b], T, pkv.generate_step_seed(seed, t, B, V), b)
             assert abs(sc[got[b]] - sc[want[b]]) <= 1e-5 * max(1.0, abs(sc[want[b]]))
     assert int(step.item()) == 4
+
+
+@pytest.mark.parametrize("G,D", [(4, 128), (1, 128), (2, 64)])
+def test_fused_device_step_equals_the_three_launch_step(G, D):
+    """`decode_step_dev` (append at the device positions fused into the attention) followed by the advance, eager
+    and as a replayed graph, equals the append / advance / attention sequence bit for bit, step after step."""
+    require_gpu()
+    B, Hkv, cap, steps = 4, 2, 500, 5
+    Hq = Hkv * G
+    L0 = np.array([1, 63, 300, 490], np.int32)
+    qs, ks, vs = _step_inputs(890 + G + D, steps, B, Hq, Hkv, D)
+    insts = [_Contig(891, B, Hq, Hkv, D, cap, L0) for _ in range(3)]    # three launches; fused eager; fused graph
+
+    def fused(inst):
+        pkv.decode_step_dev(inst.kc, inst.vc, inst.k, inst.v, inst.lens, 1, inst.q, cap, inst.out, inst.status,
+                            inst.ws)
+        pkv.advance(inst.lens, 1, inst.step)
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fused(insts[2])
+    torch.cuda.synchronize()
+    for t in range(steps):
+        for inst in insts:
+            inst.q.copy_(bf16_dev(qs[t]))
+            inst.k.copy_(bf16_dev(ks[t]))
+            inst.v.copy_(bf16_dev(vs[t]))
+        insts[0].run()
+        fused(insts[1])
+        g.replay()
+        torch.cuda.synchronize()
+        for inst in insts[1:]:
+            assert torch.equal(inst.out.view(torch.int32), insts[0].out.view(torch.int32)), t
+            assert torch.equal(inst.lens, insts[0].lens), t
+    for inst in insts[1:]:
+        assert torch.equal(inst.kc.view(torch.int16), insts[0].kc.view(torch.int16))
+        assert torch.equal(inst.vc.view(torch.int16), insts[0].vc.view(torch.int16))
+        assert int(inst.status.item()) == 0 and int(inst.step.item()) == steps
+    for inst in insts:
+        inst.close()
+
+
+def test_fused_device_step_rejects_a_row_past_the_bound():
+    """A row whose position + 1 exceeds max_len writes neither its cache rows nor its output and sets the status
+    word; the other rows step as usual."""
+    require_gpu()
+    B, Hkv, G, D, cap = 3, 2, 4, 128, 256
+    Hq = Hkv * G
+    L0 = np.array([10, 200, 100], np.int32)
+    qs, ks, vs = _step_inputs(895, 1, B, Hq, Hkv, D)
+    ref, bad = _Contig(896, B, Hq, Hkv, D, cap, L0), _Contig(896, B, Hq, Hkv, D, cap, L0)
+    for inst in (ref, bad):
+        inst.q.copy_(bf16_dev(qs[0]))
+        inst.k.copy_(bf16_dev(ks[0]))
+        inst.v.copy_(bf16_dev(vs[0]))
+        inst.out.fill_(7.0)
+    max_len = 200                          # row 1 would need 201
+    pkv.decode_step_dev(ref.kc, ref.vc, ref.k, ref.v, ref.lens, 1, ref.q, 256, ref.out, ref.status, ref.ws)
+    pkv.decode_step_dev(bad.kc, bad.vc, bad.k, bad.v, bad.lens, 1, bad.q, max_len, bad.out, bad.status, bad.ws)
+    torch.cuda.synchronize()
+    assert int(bad.status.item()) == pkv.E_CAPACITY and int(ref.status.item()) == 0
+    kb, vb = bits_host(bad.kc), bits_host(bad.vc)
+    assert np.array_equal(kb[1], bad.kh[1]) and np.array_equal(vb[1], bad.vh[1])     # row 1 untouched
+    assert bool((bad.out[1] == 7.0).all())
+    for b in (0, 2):
+        assert np.array_equal(kb[b], bits_host(ref.kc)[b]) and np.array_equal(vb[b], bits_host(ref.vc)[b])
+        assert rel_err_rows(bad.out[b].double().cpu().numpy(), ref.out[b].double().cpu().numpy()) <= F32_TOL
+    for inst in (ref, bad):
+        inst.close()
