@@ -426,3 +426,45 @@ def test_mixed32k_full_size():
             assert np.array_equal(gb, refs[b].data[name]), (b, name)
         ref = om.decode_attention(refs[b], qh[b:b + 1], local, [w.L])
         assert rel_err_rows(got[b], ref[0]) <= F32_TOL, b
+
+
+def test_one_request_chunk_with_the_library_split():
+    """One row of the Qwen shape at full size (16384-token prefix, 512-token chunk): the library's split over the
+    keys (chosen from the launch size: one workgroup per K/V head and 128-token query tile, 32 in all) and its
+    merge.  Queries at both ends and at the query-tile edges against the oracle over all 16896 keys."""
+    require_gpu()
+    w = workloads.qwen(B=1, lo=16384, hi=16384)
+    B, Hq, Hkv, D, bs, C, maxb = w["B"], w["Hq"], w["Hkv"], w["D"], w["bs"], w["chunk"], w["maxb"]
+    L = w["lengths"].astype(np.int32)
+    NB = w["NB"]
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(6)
+    kd, vd = _randn_bf16((NB, Hkv, bs, D), gen), _randn_bf16((NB, Hkv, bs, D), gen)
+    lib_pool = pkv.Pool(NB, bs, B, maxb, w["order"])
+    ref_pool = ocache.PagePool(NB, bs, B, maxb, w["order"])
+    table = torch.full((B, maxb), -1, dtype=torch.int32, device=DEV)
+    lib_pool.reserve(range(B), (L + C).tolist(), table)
+    ref_pool.reserve(0, int(L[0]) + C)
+    nk, nv = _randn_bf16((B, Hkv, C, D), gen), _randn_bf16((B, Hkv, C, D), gen)
+    q = _randn_bf16((B, Hq, C, D), gen)
+    with pkv.bind_writable(kd), pkv.bind_writable(vd):
+        pkv.paged_cache_update_kv(lib_pool, kd, vd, table, nk, nv, L.tolist(), C)
+    need = pkv.chunk_workspace_size(B, Hq, Hkv, C, 0)
+    assert need > 0
+    out = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device=DEV)
+    pkv.chunk_attention(q, kd, vd, table, maxb, bs, L.tolist(), out, pool=lib_pool, workspace=workspace(need),
+                        num_splits=0)
+    got = onum.bf16_to_f64(bits_host(out))
+    qh = bits_host(q)
+    ids = ref_pool.table[0, :-(-(int(L[0]) + C) // bs)]
+    local = np.arange(len(ids), dtype=np.int32)
+    K = onum.bf16_to_f64(ocache.paged_gather(_pages_host(kd, ids), local, int(L[0]) + C, bs))
+    V = onum.bf16_to_f64(ocache.paged_gather(_pages_host(vd, ids), local, int(L[0]) + C, bs))
+    G = Hq // Hkv
+    for t in (0, 1, 127, 128, 255, 256, 384, C - 1):
+        last = int(L[0]) + t
+        qt = onum.bf16_to_f64(qh[0, :, t])
+        for h in range(Hq):
+            ref = oattn.attend(qt[h], K[h // G, :last + 1], V[h // G, :last + 1], 1 / np.sqrt(D))
+            s = K[h // G, :last + 1] @ qt[h] / np.sqrt(D)
+            assert_bf16_pv_bound(got[0, h, t], ref, s, V[h // G, :last + 1])
