@@ -205,7 +205,8 @@ def test_paged_lognormal_full_size():
 
 
 def test_contiguous_full_size_32_steps():
-    """8 x 8 x 4096 x 128 bf16 caches, initial lengths U{512..4064}, 32 appends + attention each step."""
+    """8 x 8 x 4096 x 128 bf16 caches, initial lengths U{512..4064}, 32 appends + attention each step; the same
+    steps through the fused step (`decode_step`) give the same output bits and cache bytes."""
     require_gpu()
     w = workloads.contig()
     B, Hq, Hkv, D, cap, S, seed = w["B"], w["Hq"], w["Hkv"], w["D"], w["cap"], w["steps"], w["seed"]
@@ -216,19 +217,24 @@ def test_contiguous_full_size_32_steps():
         kh[b, :, :L0[b]] = workloads.contig_cache_row(seed, 1, b, Hkv, int(L0[b]), D)
         vh[b, :, :L0[b]] = workloads.contig_cache_row(seed, 2, b, Hkv, int(L0[b]), D)
     kc, vc = bf16_dev(kh), bf16_dev(vh)
+    kf, vf = bf16_dev(kh), bf16_dev(vh)              # the same run through the fused step
     out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device=DEV)
+    outf = torch.empty_like(out)
     ws = workspace(pkv.decode_workspace_size(B, Hq, Hkv, D, cap))
     lengths = L0.copy()
     G = Hq // Hkv
-    with pkv.bind_writable(kc), pkv.bind_writable(vc):
+    with pkv.bind_writable(kc), pkv.bind_writable(vc), pkv.bind_writable(kf), pkv.bind_writable(vf):
         for step in range(S):
             qs, ks, vs = workloads.contig_step(seed, step, B, Hq, Hkv, D)
             assert pkv.cache_update(kc, bf16_dev(ks), lengths, 1) == kc.data_ptr()
             assert pkv.cache_update(vc, bf16_dev(vs), lengths, 1) == vc.data_ptr()
+            pkv.decode_step(kf, vf, bf16_dev(ks), bf16_dev(vs), lengths, 1, bf16_dev(qs).reshape(B, Hq, 1, D), outf,
+                            ws)
             ocache.cache_update(kh, ks, lengths, 1)
             ocache.cache_update(vh, vs, lengths, 1)
             lengths = lengths + 1
             pkv.decode_attention(bf16_dev(qs).reshape(B, Hq, 1, D), kc, vc, lengths, out, ws)
+            assert torch.equal(out.view(torch.int16), outf.view(torch.int16)), step
             if step in (0, 17, S - 1):
                 out32 = torch.empty((B, Hq, 1, D), dtype=torch.float32, device=DEV)
                 pkv.decode_attention(bf16_dev(qs).reshape(B, Hq, 1, D), kc, vc, lengths, out32, ws)
@@ -242,6 +248,7 @@ def test_contiguous_full_size_32_steps():
                     ref = np.stack([oattn.attend(qd[b, h], K[h // G], V[h // G], 1 / np.sqrt(D)) for h in range(Hq)])
                     assert rel_err_rows(got[b], ref) <= F32_TOL, (step, b)
     assert np.array_equal(bits_host(kc), kh) and np.array_equal(bits_host(vc), vh)   # every cache byte
+    assert np.array_equal(bits_host(kf), kh) and np.array_equal(bits_host(vf), vh)
 
 
 def test_int4_full_size():
