@@ -639,3 +639,23 @@ def test_device_step_entry_points_validate_host_arguments():
     assert status_of(pkv.advance, None, 1, n=1) == pkv.E_ARG
     assert status_of(pkv.sample_dev, R(FAKE, pkv.F32, [2, 100]), 0.5, 0, FAKE + 512,
                      FAKE + (1 << 24), R(FAKE + 256, pkv.U8, [1 << 16])) == pkv.E_ALIAS
+
+
+def test_empty_batches_of_the_new_calls_do_nothing():
+    """B = 0 through the fused step, its device-position form and the split chunk attention: every check passes
+    and nothing is launched (this runs without a GPU)."""
+    kc = R(FAKE + 0x100000, pkv.BF16, [0, 2, 64, 128])
+    vc = R(FAKE + 0x900000, pkv.BF16, [0, 2, 64, 128])
+    kv = R(FAKE + 0x1100000, pkv.BF16, [0, 2, 1, 128])
+    vv = R(FAKE + 0x1200000, pkv.BF16, [0, 2, 1, 128])
+    q = R(FAKE + 0x1300000, pkv.BF16, [0, 8, 128])
+    out = R(FAKE + 0x1400000, pkv.F32, [0, 8, 128])
+    pkv.decode_step(kc, vc, kv, vv, [], 1, q, out)
+    pkv.decode_step_dev(kc, vc, kv, vv, FAKE + 0x1500000, 1, q, 64, out, FAKE + 0x1600000)
+    qc = R(FAKE + 0x3000000, pkv.BF16, [0, 4, 32, 128])
+    oc = R(FAKE + 0x3400000, pkv.BF16, [0, 4, 32, 128])
+    kp = R(FAKE + 0x100000, pkv.BF16, [32, 2, 16, 128])
+    vp = R(FAKE + 0x900000, pkv.BF16, [32, 2, 16, 128])
+    table = R(FAKE + 0x2000000, pkv.I32, [1, 8])
+    pkv.chunk_attention(qc, kp, vp, table, 8, 16, [], oc, num_splits=4)
+    assert pkv.chunk_workspace_size(0, 4, 2, 32, 4) == 0
