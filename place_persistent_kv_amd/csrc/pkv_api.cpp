@@ -196,6 +196,22 @@ struct Plan {
 
 // Splits of one launch.  `units_per_token` weights tokens by the number of
 // workgroups that stream them (Hkv for the fast kernels, Hq for the generic).
+// Compute units of the current device (256 on a whole gfx950 part, fewer in
+// a partitioned mode); 256 when no device answers.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 Plan plan_splits(const int32_t* len, int B, int units, int num_splits, int max_tps) {
     Plan p;
     int64_t total = 0;
@@ -966,8 +982,20 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
         const int32_t L = dev ? max_len : valid_len[b];
         span_len[b] = L - split_base(L, left_window);
     }
+    // Rows of one span on the memory-bound fast kernel, with every launch group
+    // holding at least one workgroup per CU: one split per row.  All those
+    // workgroups are resident together and share HBM evenly, so they end
+    // together, and no merge launch is needed (splitting only helps when spans
+    // differ, where the long rows would otherwise be left running alone).
+    int32_t splits = num_splits;
+    if (splits == 0 && fast && !mixed && !dev) {
+        const int64_t last_group = B - (B - 1) / kMaxRows * kMaxRows;
+        bool equal = true;
+        for (int64_t b = 1; b < B && equal; ++b) equal = span_len[b] == span_len[0];
+        if (equal && last_group * Hkv >= device_cus()) splits = 1;
+    }
     Plan full = plan_splits(span_len.data(), static_cast<int>(B), fast ? static_cast<int>(Hkv) : static_cast<int>(Hq),
-                            num_splits, fast ? 0 : kGenericMaxTps);
+                            splits, fast ? 0 : kGenericMaxTps);
     const size_t need = ws_bytes_for(B, Hq, Dv, full.S_max);
     if (static_ws && (full.S_max > 1 || !fast)) {
         // after every check: the scratch's device address is the first HIP call
@@ -1551,21 +1579,6 @@ pkv_status pkv_paged_decode_attention_int4(const pkv_tensor* q, const pkv_tensor
 // ---------------------------------------------------------------------------
 namespace {
 
-// Compute units of the current device (256 on a whole gfx950 part, fewer in
-// a partitioned mode); 256 when no device answers.
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
 
 // Workgroups of one chunk launch of `rows` rows without a split.
 int64_t chunk_workgroups(int64_t rows, int64_t Hkv, int G, int64_t C) {
