@@ -185,6 +185,9 @@ pkv_status write_table(int32_t* table_dev, const std::vector<int32_t>& idx,
 namespace {
 
 constexpr int kTargetWorkgroups = 1024;  // 4 per CU on 256 CUs: 2 resident x 2 rounds
+// rows of unequal span on the bf16 / f16 fast kernel: smaller splits, so that
+// the short last splits (launched last, longest first) even out the end
+constexpr int kTargetWorkgroupsUneven = 2048;
 constexpr int kMinAutoTps = 384;         // tokens per split, library choice: >= 6 steps per wave
 constexpr int kTpsQuantum = 64;          // fast kernel: 4 waves x 16 tokens
 
@@ -212,7 +215,8 @@ int device_cus() {
     return cus;
 }
 
-Plan plan_splits(const int32_t* len, int B, int units, int num_splits, int max_tps) {
+Plan plan_splits(const int32_t* len, int B, int units, int num_splits, int max_tps,
+                 int target = kTargetWorkgroups) {
     Plan p;
     int64_t total = 0;
     int32_t lmax = 1;
@@ -224,7 +228,7 @@ Plan plan_splits(const int32_t* len, int B, int units, int num_splits, int max_t
     if (num_splits > 0) {
         tps = std::max<int64_t>(kTpsQuantum, ceil_div(ceil_div(lmax, num_splits), kTpsQuantum) * kTpsQuantum);
     } else {
-        tps = ceil_div(total * units, kTargetWorkgroups);
+        tps = ceil_div(total * units, target);
         tps = std::max<int64_t>(kMinAutoTps, ceil_div(tps, kTpsQuantum) * kTpsQuantum);
     }
     if (max_tps > 0) tps = std::min<int64_t>(tps, max_tps);
@@ -988,14 +992,16 @@ pkv_status decode_common(const pkv_tensor* q, const pkv_tensor* k, const pkv_ten
     // together, and no merge launch is needed (splitting only helps when spans
     // differ, where the long rows would otherwise be left running alone).
     int32_t splits = num_splits;
+    int target = kTargetWorkgroups;
     if (splits == 0 && fast && !mixed && !dev) {
         const int64_t last_group = B - (B - 1) / kMaxRows * kMaxRows;
         bool equal = true;
         for (int64_t b = 1; b < B && equal; ++b) equal = span_len[b] == span_len[0];
         if (equal && last_group * Hkv >= device_cus()) splits = 1;
+        if (!equal) target = kTargetWorkgroupsUneven;
     }
     Plan full = plan_splits(span_len.data(), static_cast<int>(B), fast ? static_cast<int>(Hkv) : static_cast<int>(Hq),
-                            splits, fast ? 0 : kGenericMaxTps);
+                            splits, fast ? 0 : kGenericMaxTps, target);
     const size_t need = ws_bytes_for(B, Hq, Dv, full.S_max);
     if (static_ws && (full.S_max > 1 || !fast)) {
         // after every check: the scratch's device address is the first HIP call
